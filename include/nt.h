@@ -1,0 +1,150 @@
+/*
+ * nt.h - C ABI of the fused row-reduction library for AMD MI355X (gfx950).
+ *
+ * Three memory-bound row operations over a dense row-major [M, N] matrix,
+ * each one HIP launch sequence on the caller's stream:
+ *
+ *   nt_softmax_rows    y = exp(x - max(x)) / sum(exp(x - max(x)))  per row
+ *   nt_layernorm_rows  y = (x - mean) * rstd * gamma + beta, plus mean, rstd
+ *   nt_rmsnorm_rows    y = x / sqrt(mean(x^2) + eps) * weight
+ *
+ * Definitions follow the public pages this library implements:
+ *  - softmax: "Portable Triton Kernels" (Hugging Face kernel-builder
+ *    triton-kernels skill), "Safe Softmax Pattern" and "Reference Kernel:
+ *    Softmax"; stanleyjacob.dev Triton guide, Part II "Worked example: fused
+ *    softmax" (load the row once, shift by its max, exp, sum, divide, store
+ *    once).  Rows too wide to hold on chip use the online max/denominator
+ *    rescaling of "Triton: Block-Level GPU Programming Without CUDA", section
+ *    "How Flash Attention Uses Triton".
+ *  - RMSNorm: "Portable Triton Kernels", "Reference Kernel: RMSNorm".
+ *  - LayerNorm: named in "Rebuilding Triton and Helion from Scratch in 4,000
+ *    Lines of Python" ("Memory-bound kernels", "deuteron") without a formula;
+ *    this library uses the biased variance sum((x-mean)^2)/N with eps added
+ *    inside the square root.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  Layout     x and y are dense row-major [M, N] arrays of element type `dt`
+ *             with row stride N (contiguous rows).  y has the same type as x.
+ *  Vectors    gamma, beta and weight are length-N arrays of type `dt`.  NULL
+ *             means the identity (gamma = 1, beta = 0, weight = 1).
+ *  Stats      mean and rstd are float arrays of length M; NULL means "do not
+ *             write".
+ *  Pointers   device (or device-accessible) addresses.  Each must be aligned
+ *             to the element size (mean/rstd to 4 bytes, workspace to 8);
+ *             16-byte alignment is NOT required (misaligned rows are handled).
+ *  eps        must be finite and >= 0; it is added inside the square root.
+ *  Shapes     M == 0 is a no-op returning NT_OK.  M < 0, N <= 0, or M*N
+ *             overflowing int64 returns NT_ERR_SHAPE.
+ *  Ownership  the caller allocates and owns every buffer, including the
+ *             workspace (which need not be zeroed).  The library allocates and
+ *             frees no device memory and keeps no pointer after returning.
+ *  Stream     `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *             Work is enqueued and the call returns without synchronizing;
+ *             results are valid once the stream reaches that point, and the
+ *             inputs must stay alive until then.
+ *  Errors     argument errors are returned synchronously, before anything is
+ *             enqueued.  A failed launch returns NT_ERR_HIP (the HIP error is
+ *             read and cleared with hipGetLastError).
+ *  Aliasing   y == x (in place) is allowed.  Any other overlap between y and
+ *             an input, the stats or the workspace is undefined.
+ *  Numerics   inputs are widened to fp32 and reduced in fp32 (LayerNorm keeps
+ *             its two row sums and its per-element affine step in fp64); the
+ *             result is rounded to `dt` once, round-to-nearest-even.  The
+ *             reduction order is fixed, so results are bitwise repeatable
+ *             for a given shape, type and device.
+ *  Threads    every entry point is thread-safe; the library has no mutable
+ *             global state beyond a read-only device-property cache.
+ */
+#ifndef NT_H
+#define NT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NT_F32 = 0, NT_F16 = 1, NT_BF16 = 2 } nt_dtype;
+
+typedef enum {
+    NT_OK = 0,
+    NT_ERR_NULL = 1,       /* a required pointer is NULL                       */
+    NT_ERR_SHAPE = 2,      /* M < 0, N <= 0, or M*N overflows                  */
+    NT_ERR_DTYPE = 3,      /* dt is not one of nt_dtype                        */
+    NT_ERR_EPS = 4,        /* eps is negative, infinite or NaN                 */
+    NT_ERR_ALIGN = 5,      /* a pointer is not aligned to its element size     */
+    NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes */
+    NT_ERR_HIP = 7         /* the HIP runtime reported a launch error          */
+} nt_status;
+
+/*
+ * Bytes of device workspace nt_softmax_rows needs for this shape: 0 when each
+ * row fits on chip (single pass), else 8 bytes per (row, row chunk) for the
+ * per-chunk running max and denominator of the split online path.  Returns 0
+ * for invalid arguments.
+ */
+size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
+
+/*
+ * Row softmax.  y[r, j] = exp(x[r, j] - m_r) / sum_k exp(x[r, k] - m_r) with
+ * m_r = max_k x[r, k].  -inf entries contribute exactly 0 (a row of -inf only
+ * yields NaN, as the formula does).  Rows that fit on chip are read once and
+ * written once; wider rows take the split path (two kernels: per-chunk max
+ * and denominator, then merge and write), which needs `workspace` of at least
+ * nt_softmax_workspace_bytes(M, N, dt) bytes (may be NULL when that is 0).
+ */
+nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
+                          const void *x, void *y,
+                          void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * LayerNorm over each row.  mean_r = sum_j x[r, j] / N,
+ * var_r = sum_j (x[r, j] - mean_r)^2 / N (biased), rstd_r = 1/sqrt(var_r + eps),
+ * y[r, j] = (x[r, j] - mean_r) * rstd_r * gamma[j] + beta[j].
+ * mean and rstd (fp32, length M) are written when non-NULL.
+ */
+nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
+                            const void *x, const void *gamma, const void *beta,
+                            void *y, float *mean, float *rstd, void *stream);
+
+/*
+ * RMSNorm over each row.  inv_r = 1/sqrt(sum_j x[r, j]^2 / N + eps),
+ * y[r, j] = x[r, j] * inv_r * weight[j].
+ */
+nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
+                          const void *x, const void *weight, void *y,
+                          void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *nt_status_string(nt_status s);
+
+/*
+ * Launch plan introspection (host only; touches no device).  Describes the
+ * kernels the library would launch for an operation on this shape, when
+ * every pointer is 16-byte aligned (`aligned16` != 0) or not.
+ */
+typedef enum { NT_OP_SOFTMAX = 0, NT_OP_LAYERNORM = 1, NT_OP_RMSNORM = 2 } nt_op;
+
+typedef struct {
+    int32_t split;            /* 0: single pass, row held on chip; 1: split online path */
+    int32_t waves_per_row;    /* 64-lane waves cooperating on one row (or one chunk)    */
+    int32_t chunks_per_lane;  /* 16-byte chunks each lane holds                         */
+    int32_t rows_per_block;   /* rows one workgroup processes side by side              */
+    int32_t threads_per_block;
+    int32_t aligned;          /* 1 when the 16-byte-aligned variant is used             */
+    int64_t grid;             /* workgroups per launch                                  */
+    int64_t row_chunks;       /* split path: chunks per row (0 on the single pass)      */
+    int64_t workspace_bytes;  /* split path: workspace size (0 on the single pass)      */
+} nt_plan;
+
+nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt,
+                         int aligned16, nt_plan *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NT_H */

@@ -1,0 +1,251 @@
+/*
+ * Reference oracle for the fused row reductions: row softmax, LayerNorm and
+ * RMSNorm over a dense row-major [M, N] matrix.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct CPU
+ * definition that the GPU library is checked against.  It shares no code,
+ * header, table or helper with the GPU library and never calls into it.
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it.
+ *
+ * Everything is computed in IEEE double precision from the exact input bits:
+ * inputs stored as fp32, fp16 or bf16 are decoded exactly to double by this
+ * file's own decoders, every sum runs in element index order, and results are
+ * returned as doubles.  Rounding a result to the output storage type is done
+ * once, by the caller's comparator, never here.
+ *
+ * Sources (cited by page title and section):
+ *  - softmax: "Portable Triton Kernels" (Hugging Face kernel-builder
+ *    triton-kernels skill), sections "Safe Softmax Pattern" and "Reference
+ *    Kernel: Softmax"; stanleyjacob.dev Triton guide, Part II "Worked example:
+ *    fused softmax".  y_j = exp(x_j - max_k x_k) / sum_k exp(x_k - max_k x_k).
+ *  - RMSNorm: "Portable Triton Kernels", section "Reference Kernel: RMSNorm".
+ *    variance = sum(x^2)/D, inv = 1/sqrt(variance + eps), y = x * inv * w,
+ *    with w = 1 when no weight is given.
+ *  - LayerNorm: named (not written out) in "Rebuilding Triton and Helion from
+ *    Scratch in 4,000 Lines of Python", sections "Memory-bound kernels" and
+ *    "deuteron".  No formula is printed on any page; the plainest reading is
+ *    used: mean = sum(x)/N, biased variance = sum((x-mean)^2)/N,
+ *    rstd = 1/sqrt(var + eps) (eps inside the root, as in the RMSNorm kernel),
+ *    y = (x - mean) * rstd * gamma + beta, gamma = 1 and beta = 0 when absent.
+ *  - online softmax: "Triton: Block-Level GPU Programming Without CUDA",
+ *    section "How Flash Attention Uses Triton" (running max m and
+ *    denominator l rescaled by alpha = exp(m_prev - m_new) per block; the
+ *    Milakov & Gimelshein online normalizer).  Only the (m, l) part is used.
+ *
+ * Special cases (readings where the pages are silent):
+ *  - x_j = -inf gives exp(x_j - m) = 0 exactly (the masked-load identity of
+ *    the "Safe Softmax Pattern").  A row that is entirely -inf yields NaN,
+ *    exactly as the literal formula (-inf) - (-inf) does.
+ *  - NaN anywhere in a softmax row makes the row max NaN and so the whole
+ *    row NaN.  (Parity for NaN/inf inputs is not pinned.)
+ *  - eps arrives as a C float and is widened exactly to double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* The oracle's own storage-type codes. */
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+/* Exact decode of one IEEE binary16 value to double. */
+static double or_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int mant = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)mant, -24);              /* zero or subnormal */
+    else if (expo == 31)
+        v = mant ? NAN : INFINITY;
+    else
+        v = ldexp((double)(mant | 0x400), expo - 25);
+    return sign ? -v : v;
+}
+
+/* Exact decode of one bfloat16 value: it is the top half of a binary32. */
+static double or_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double or_load(int dtype, const void *base, int64_t idx)
+{
+    switch (dtype) {
+    case OR_F32: return (double)((const float *)base)[idx];
+    case OR_F16: return or_half_to_double(((const uint16_t *)base)[idx]);
+    case OR_BF16: return or_bf16_to_double(((const uint16_t *)base)[idx]);
+    }
+    return NAN;
+}
+
+static int or_check(int64_t M, int64_t N, int dtype)
+{
+    if (M < 0 || N <= 0) return 1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return 2;
+    return 0;
+}
+
+/* Decode a whole [M, N] array (or a length-N vector with M = 1) to doubles. */
+int or_decode(int64_t count, int dtype, const void *x, double *out)
+{
+    if (count < 0) return 1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return 2;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = or_load(dtype, x, i);
+    return 0;
+}
+
+/* Row softmax, plain definition: max, shift, exp, sum, divide. */
+int or_softmax(int64_t M, int64_t N, int dtype, const void *x, double *y)
+{
+    int rc = or_check(M, N, dtype);
+    if (rc) return rc;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double *yr = y + base;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = or_load(dtype, x, base + j);
+            if (isnan(v) || isnan(m)) m = NAN;
+            else if (v > m) m = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = or_load(dtype, x, base + j);
+            /* exp(-inf - m) is exactly 0 for finite m; for m = -inf the
+             * difference is NaN, which is the all-masked row's result. */
+            double e = exp(v - m);
+            yr[j] = e;
+            s += e;
+        }
+        for (int64_t j = 0; j < N; ++j)
+            yr[j] = yr[j] / s;
+    }
+    return 0;
+}
+
+/* LayerNorm over each row: returns y, and per-row mean and rstd. */
+int or_layernorm(int64_t M, int64_t N, int dtype, float eps, const void *x,
+                 const void *gamma, const void *beta, double *y, double *mean,
+                 double *rstd)
+{
+    int rc = or_check(M, N, dtype);
+    if (rc) return rc;
+    const double deps = (double)eps;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double s1 = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            s1 += or_load(dtype, x, base + j);
+        double mu = s1 / (double)N;
+        double s2 = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double d = or_load(dtype, x, base + j) - mu;
+            s2 += d * d;
+        }
+        double var = s2 / (double)N;
+        double rs = 1.0 / sqrt(var + deps);
+        for (int64_t j = 0; j < N; ++j) {
+            double g = gamma ? or_load(dtype, gamma, j) : 1.0;
+            double b = beta ? or_load(dtype, beta, j) : 0.0;
+            y[base + j] = (or_load(dtype, x, base + j) - mu) * rs * g + b;
+        }
+        if (mean) mean[r] = mu;
+        if (rstd) rstd[r] = rs;
+    }
+    return 0;
+}
+
+/* RMSNorm over each row: y = x / sqrt(mean(x^2) + eps) * w. */
+int or_rmsnorm(int64_t M, int64_t N, int dtype, float eps, const void *x,
+               const void *w, double *y)
+{
+    int rc = or_check(M, N, dtype);
+    if (rc) return rc;
+    const double deps = (double)eps;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double ss = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = or_load(dtype, x, base + j);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)N + deps);
+        for (int64_t j = 0; j < N; ++j) {
+            double wv = w ? or_load(dtype, w, j) : 1.0;
+            y[base + j] = or_load(dtype, x, base + j) * inv * wv;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Online softmax: the row is visited in consecutive blocks of `block`
+ * elements.  Per block, in the page's order: new running max
+ * m_new = max(m_prev, max(block)); rescale factor alpha = exp(m_prev - m_new);
+ * l = l_prev * alpha + sum(exp(block - m_new)).  After the last block,
+ * y_j = exp(x_j - m) / l.  In real arithmetic this equals the plain softmax.
+ *
+ * Reading: while the running max is still -inf no mass has been seen, so
+ * alpha is taken as 1 (the page's formula would give exp(-inf + inf) = NaN
+ * for a fully masked leading block, a case attention kernels never reach).
+ */
+int or_softmax_online(int64_t M, int64_t N, int dtype, int64_t block,
+                      const void *x, double *y)
+{
+    int rc = or_check(M, N, dtype);
+    if (rc) return rc;
+    if (block <= 0) return 1;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        double m_prev = -INFINITY, l_prev = 0.0;
+        for (int64_t j0 = 0; j0 < N; j0 += block) {
+            int64_t j1 = j0 + block < N ? j0 + block : N;
+            double bmax = -INFINITY;
+            for (int64_t j = j0; j < j1; ++j) {
+                double v = or_load(dtype, x, base + j);
+                if (isnan(v) || isnan(bmax)) bmax = NAN;
+                else if (v > bmax) bmax = v;
+            }
+            double m_new = (isnan(bmax) || isnan(m_prev)) ? NAN
+                           : (bmax > m_prev ? bmax : m_prev);
+            double alpha = (m_prev == -INFINITY) ? 1.0 : exp(m_prev - m_new);
+            double psum = 0.0;
+            if (m_new != -INFINITY)
+                for (int64_t j = j0; j < j1; ++j)
+                    psum += exp(or_load(dtype, x, base + j) - m_new);
+            l_prev = l_prev * alpha + psum;
+            m_prev = m_new;
+        }
+        for (int64_t j = 0; j < N; ++j)
+            y[base + j] = exp(or_load(dtype, x, base + j) - m_prev) / l_prev;
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region of this library will use. */
+int or_num_threads(void)
+{
+    int n = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

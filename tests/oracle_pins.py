@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError when the oracle disagrees with the fact it checks.  They are
+run against the real oracle (``test_oracle_pins.py``) and against
+deliberately broken builds of it (``test_oracle_mutants.py``), which must
+each fail at least one pin.
+
+Expected values never come from the oracle itself: they are closed forms
+(written through a different formula than the oracle's), invariants, the
+independent pure-Python definition in ``oracle/brute.py``, exhaustive decoder
+checks against numpy's binary16 codec, or PyTorch's float64 CPU routines
+(an independent library implementation of the same definitions).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F32_EPS5 = float(np.float32(1e-5))   # eps as the C ABI receives it (a float)
+F32_EPS6 = float(np.float32(1e-6))
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300)))
+
+
+def _f32(rows):
+    return np.ascontiguousarray(np.asarray(rows, dtype=np.float32))
+
+
+def _rng_rows(seed, M, N, dt, scale=1.0, loc=0.0):
+    rng = np.random.default_rng(seed)
+    v = (rng.standard_normal((M, N)) * scale + loc).astype(np.float32)
+    if dt == "f32":
+        return v
+    if dt == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    u = v.view(np.uint32)
+    return ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _decode_py(bits_row, dt):
+    if dt == "f32":
+        return [float(v) for v in bits_row]
+    return [brute.decode16(int(b), dt) for b in bits_row]
+
+
+# ----------------------------------------------------------------------------
+# decoders
+# ----------------------------------------------------------------------------
+
+def pin_decode_f16_exhaustive(lib):
+    """Every binary16 bit pattern decodes to numpy's binary16 value."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = np.empty(65536, dtype=np.float64)
+    assert lib.or_decode(65536, oracle.F16, bits.ctypes.data, got.ctypes.data) == 0
+    ref = bits.view(np.float16).astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), f"{(~same).sum()} fp16 patterns decode wrongly"
+
+
+def pin_decode_bf16_exhaustive(lib):
+    """Every bfloat16 pattern decodes to the binary32 with the same top half."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = np.empty(65536, dtype=np.float64)
+    assert lib.or_decode(65536, oracle.BF16, bits.ctypes.data, got.ctypes.data) == 0
+    with np.errstate(invalid="ignore"):
+        ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), f"{(~same).sum()} bf16 patterns decode wrongly"
+
+
+# ----------------------------------------------------------------------------
+# softmax
+# ----------------------------------------------------------------------------
+
+def pin_softmax_two_logistic(lib):
+    """softmax([0, 1]) is the logistic function: [1/(1+e), 1/(1+e^-1)]."""
+    y = oracle.softmax(_f32([[0.0, 1.0]]), "f32", lib=lib)[0]
+    want = [1.0 / (1.0 + math.e), 1.0 / (1.0 + math.exp(-1.0))]
+    assert _rel(y, want) < 1e-15, (y, want)
+
+
+def pin_softmax_three_closed_form(lib):
+    """softmax([0, 1, 2]) = [1, e, e^2] / (1 + e + e^2) (geometric series)."""
+    y = oracle.softmax(_f32([[0.0, 1.0, 2.0]]), "f32", lib=lib)[0]
+    den = (math.e ** 3 - 1.0) / (math.e - 1.0)
+    want = [1.0 / den, math.e / den, math.e ** 2 / den]
+    assert _rel(y, want) < 1e-15, (y, want)
+
+
+def pin_softmax_large_logits(lib):
+    """Huge logits must not overflow: softmax([1000, 999]) = logistic(+-1)."""
+    y = oracle.softmax(_f32([[1000.0, 999.0]]), "f32", lib=lib)[0]
+    want = [1.0 / (1.0 + math.exp(-1.0)), 1.0 / (1.0 + math.e)]
+    assert _rel(y, want) < 1e-15, (y, want)
+
+
+def pin_softmax_uniform(lib):
+    """A constant row of length N gives 1/N everywhere."""
+    for N in (1, 2, 781, 4096):
+        y = oracle.softmax(np.full((1, N), 0.375, dtype=np.float32), "f32", lib=lib)
+        assert _rel(y, np.full((1, N), 1.0 / N)) < 1e-14, N
+
+
+def pin_softmax_sums_to_one(lib):
+    """Every row of a softmax sums to 1."""
+    for dt in ("f32", "f16", "bf16"):
+        x = _rng_rows(11, 64, 781, dt, scale=3.0)
+        y = oracle.softmax(x, dt, lib=lib)
+        assert np.max(np.abs(y.sum(axis=1) - 1.0)) < 1e-13, dt
+
+
+def pin_softmax_ratio_is_exp_difference(lib):
+    """y_i / y_j = exp(x_i - x_j): checks the base of the exponential."""
+    x = _rng_rows(12, 4, 50, "f32")
+    y = oracle.softmax(x, "f32", lib=lib)
+    xd = x.astype(np.float64)
+    want = np.exp(xd[:, 1:] - xd[:, :1])
+    assert _rel(y[:, 1:] / y[:, :1], want) < 1e-13
+
+
+def pin_softmax_shift_invariance(lib):
+    """softmax(x + c) = softmax(x) for inputs where x + c is exact."""
+    rng = np.random.default_rng(13)
+    cases = [("f32", 2.0 ** -10, 8192, (16.0, -64.0)),
+             ("f16", 2.0 ** -6, 512, (16.0,)),
+             ("bf16", 2.0 ** -3, 128, (16.0,))]
+    for dt, q, kmax, shifts in cases:
+        k = rng.integers(-kmax + 1, kmax, size=(8, 300))
+        base = (k * q).astype(np.float64)
+        for c in shifts:
+            a = _encode(base, dt)
+            b = _encode(base + c, dt)
+            assert np.array_equal(oracle.decode(b, dt), oracle.decode(a, dt) + c)
+            ya = oracle.softmax(a, dt, lib=lib)
+            yb = oracle.softmax(b, dt, lib=lib)
+            assert _rel(ya, yb) < 1e-14, (dt, c)
+
+
+def _encode(v64, dt):
+    f = np.asarray(v64, dtype=np.float32)
+    if dt == "f32":
+        return np.ascontiguousarray(f)
+    if dt == "f16":
+        return f.astype(np.float16).view(np.uint16)
+    u = f.view(np.uint32)
+    return ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_softmax_padding_neutral(lib):
+    """A row padded with -inf to the next power of two keeps its softmax on
+    the real entries and gets exactly 0 on the padding."""
+    with open(os.path.join(GOLDEN, "masked_fill_identities.json")) as f:
+        ident = json.load(f)
+    assert ident["max_identity"] == "-inf" and ident["exp_of_neg_inf"] == 0.0
+    x = _rng_rows(14, 3, 781, "f32")
+    pad = np.full((3, 1024), -np.inf, dtype=np.float32)
+    pad[:, :781] = x
+    y = oracle.softmax(x, "f32", lib=lib)
+    yp = oracle.softmax(pad, "f32", lib=lib)
+    assert np.array_equal(yp[:, :781], y)
+    assert np.all(yp[:, 781:] == 0.0)
+
+
+def pin_softmax_causal_rows(lib):
+    """Causally masked rows: row q has exactly q+1 non-zeros, row 0 is one-hot."""
+    N = 64
+    x = _rng_rows(15, N, N, "bf16", scale=3.0)
+    k = np.arange(N)[None, :]
+    q = np.arange(N)[:, None]
+    x[k > q] = 0xFF80
+    y = oracle.softmax(x, "bf16", lib=lib)
+    assert np.array_equal((y != 0).sum(axis=1), np.arange(N) + 1)
+    assert y[0, 0] == 1.0 and np.all(y[0, 1:] == 0.0)
+    assert np.max(np.abs(y.sum(axis=1) - 1.0)) < 1e-14
+
+
+def pin_softmax_special_rows(lib):
+    """N=1 gives 1; an all -inf row gives NaN (literal -inf - -inf)."""
+    assert oracle.softmax(_f32([[-3.5]]), "f32", lib=lib)[0, 0] == 1.0
+    y = oracle.softmax(np.full((1, 5), -np.inf, dtype=np.float32), "f32", lib=lib)
+    assert np.all(np.isnan(y))
+
+
+def pin_softmax_brute(lib):
+    """oracle.c agrees with the pure-Python fsum definition on tiny rows."""
+    for dt in ("f32", "f16", "bf16"):
+        for N in list(range(1, 65)) + [127, 255, 257, 781, 1500]:
+            x = _rng_rows(1000 + N, 2, N, dt, scale=2.0)
+            y = oracle.softmax(x, dt, lib=lib)
+            for r in range(2):
+                want = brute.softmax_row(_decode_py(x[r], dt))
+                assert _rel(y[r], want) < 1e-13, (dt, N)
+
+
+def pin_softmax_torch(lib):
+    """oracle.c agrees with torch.softmax in float64 on the CPU."""
+    import torch
+    for dt in ("f32", "f16", "bf16"):
+        x = _rng_rows(16, 16, 1500, dt, scale=3.0)
+        y = oracle.softmax(x, dt, lib=lib)
+        xt = torch.from_numpy(oracle.decode(x, dt))
+        assert _rel(y, torch.softmax(xt, dim=-1).numpy()) < 1e-13, dt
+
+
+def pin_softmax_online_matches_plain(lib):
+    """The online (running max, rescaled denominator) form equals the plain
+    softmax for every block size, including leading fully masked blocks."""
+    x = _rng_rows(17, 6, 1000, "f32", scale=2.0)
+    x[1, :300] = -np.inf           # leading masked blocks
+    x[2, 500:] = -np.inf           # trailing masked blocks
+    x[3, ::7] = 30.0               # spikes
+    x[4, 999] = 40.0               # late maximum forces a rescale
+    y = oracle.softmax(x, "f32", lib=lib)
+    for block in (1, 2, 7, 64, 128, 999, 1000, 4096):
+        yo = oracle.softmax_online(x, "f32", block, lib=lib)
+        assert _rel(yo, y) < 1e-13, block
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm
+# ----------------------------------------------------------------------------
+
+def pin_layernorm_hand_case(lib):
+    """[1, 2, 3, 4]: mean 5/2, biased variance 5/4, y = [-3, -1, 1, 3]/sqrt(5)."""
+    x = _f32([[1.0, 2.0, 3.0, 4.0]])
+    y, mu, rs = oracle.layernorm(x, "f32", 0.0, lib=lib)
+    s5 = math.sqrt(5.0)
+    assert mu[0] == 2.5
+    assert _rel(rs, [2.0 / s5]) < 1e-15
+    assert _rel(y[0], [-3 / s5, -1 / s5, 1 / s5, 3 / s5]) < 1e-15
+    _, _, rs_e = oracle.layernorm(x, "f32", 1e-5, lib=lib)
+    assert _rel(rs_e, [1.0 / math.sqrt(1.25 + F32_EPS5)]) < 1e-15
+
+
+def pin_layernorm_biased_variance(lib):
+    """[0, 2] has biased variance 1 (not 2): y = [-1, 1] with eps = 0."""
+    y, mu, rs = oracle.layernorm(_f32([[0.0, 2.0]]), "f32", 0.0, lib=lib)
+    assert mu[0] == 1.0 and rs[0] == 1.0 and list(y[0]) == [-1.0, 1.0]
+
+
+def pin_layernorm_unit_moments(lib):
+    """gamma=1, beta=0: mean(y) = 0 and mean(y^2) = var / (var + eps)."""
+    x = _rng_rows(21, 32, 4096, "f16", loc=3.0)
+    y, mu, rs = oracle.layernorm(x, "f16", 1e-5, lib=lib)
+    xd = oracle.decode(x, "f16")
+    var = ((xd - xd.mean(axis=1, keepdims=True)) ** 2).mean(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-12
+    assert _rel((y ** 2).mean(axis=1), var / (var + F32_EPS5)) < 1e-12
+
+
+def pin_layernorm_affine_invariance(lib):
+    """With eps = 0, y is unchanged by x -> a*x + c (a > 0); mean -> a*mean + c
+    and rstd -> rstd / a."""
+    rng = np.random.default_rng(22)
+    x = (rng.integers(-4000, 4000, size=(8, 300)) * 2.0 ** -10).astype(np.float32)
+    y, mu, rs = oracle.layernorm(x, "f32", 0.0, lib=lib)
+    x2 = (x.astype(np.float64) * 4.0 + 8.0).astype(np.float32)     # exact
+    assert np.array_equal(x2.astype(np.float64), x.astype(np.float64) * 4.0 + 8.0)
+    y2, mu2, rs2 = oracle.layernorm(x2, "f32", 0.0, lib=lib)
+    assert _rel(y2, y) < 1e-12
+    assert _rel(mu2, mu * 4.0 + 8.0) < 1e-12
+    assert _rel(rs2, rs / 4.0) < 1e-12
+
+
+def pin_layernorm_constant_row(lib):
+    """A constant row has variance 0: rstd = 1/sqrt(eps) and y = beta."""
+    beta = np.array([0.5, -0.25, 2.0], dtype=np.float32)
+    gamma = np.array([3.0, 4.0, 5.0], dtype=np.float32)
+    y, mu, rs = oracle.layernorm(np.full((1, 3), 7.0, np.float32), "f32", 1e-5,
+                                 gamma=gamma, beta=beta, lib=lib)
+    assert mu[0] == 7.0
+    assert _rel(rs, [1.0 / math.sqrt(F32_EPS5)]) < 1e-15
+    assert np.array_equal(y[0], beta.astype(np.float64))
+
+
+def pin_layernorm_single_element(lib):
+    """N = 1: y = beta, mean = x, rstd = 1/sqrt(eps)."""
+    y, mu, rs = oracle.layernorm(_f32([[2.5]]), "f32", 1e-5,
+                                 gamma=np.array([3.0], np.float32),
+                                 beta=np.array([-1.5], np.float32), lib=lib)
+    assert y[0, 0] == -1.5 and mu[0] == 2.5
+    assert _rel(rs, [1.0 / math.sqrt(F32_EPS5)]) < 1e-15
+
+
+def pin_layernorm_affine_columns(lib):
+    """gamma and beta act per column j: a ramp gamma_j = j+1 and beta_j = -j
+    turn column j of the plain result into (j+1)*y_j - j."""
+    x = _rng_rows(23, 4, 40, "f32")
+    N = 40
+    g = np.arange(1, N + 1, dtype=np.float32)
+    b = -np.arange(N, dtype=np.float32)
+    y0, _, _ = oracle.layernorm(x, "f32", 1e-5, lib=lib)
+    y1, _, _ = oracle.layernorm(x, "f32", 1e-5, gamma=g, beta=b, lib=lib)
+    assert np.max(np.abs(y1 - (y0 * g + b))) < 1e-12
+
+
+def pin_layernorm_brute(lib):
+    for dt in ("f32", "f16", "bf16"):
+        for N in list(range(1, 65)) + [127, 255, 257, 781, 1500]:
+            x = _rng_rows(2000 + N, 2, N, dt, loc=2.0)
+            g = _rng_rows(3000 + N, 1, N, dt, scale=0.3, loc=1.0)[0]
+            b = _rng_rows(4000 + N, 1, N, dt, scale=0.3)[0]
+            y, mu, rs = oracle.layernorm(x, dt, 1e-5, gamma=g, beta=b, lib=lib)
+            gd, bd = _decode_py(g, dt), _decode_py(b, dt)
+            for r in range(2):
+                yw, muw, rsw = brute.layernorm_row(_decode_py(x[r], dt), F32_EPS5, gd, bd)
+                scale = np.abs(np.asarray(yw)) + 1.0
+                assert np.max(np.abs(y[r] - yw) / scale) < 1e-13, (dt, N)
+                assert abs(mu[r] - muw) <= 1e-13 * max(1.0, abs(muw)), (dt, N)
+                assert _rel([rs[r]], [rsw]) < 1e-13, (dt, N)
+
+
+def pin_layernorm_torch(lib):
+    """oracle.c agrees with torch.nn.functional.layer_norm in float64."""
+    import torch
+    for dt in ("f32", "f16", "bf16"):
+        x = _rng_rows(24, 16, 1500, dt, loc=-4.0)
+        g = _rng_rows(25, 1, 1500, dt, scale=0.3, loc=1.0)[0]
+        b = _rng_rows(26, 1, 1500, dt, scale=0.3)[0]
+        y, mu, rs = oracle.layernorm(x, dt, 1e-5, gamma=g, beta=b, lib=lib)
+        xt = torch.from_numpy(oracle.decode(x, dt))
+        ref = torch.nn.functional.layer_norm(
+            xt, (1500,), torch.from_numpy(oracle.decode(g, dt)),
+            torch.from_numpy(oracle.decode(b, dt)), eps=F32_EPS5).numpy()
+        assert np.max(np.abs(y - ref) / (np.abs(ref) + 1.0)) < 1e-12, dt
+        assert _rel(mu, xt.mean(dim=1).numpy()) < 1e-12, dt
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm
+# ----------------------------------------------------------------------------
+
+def pin_rmsnorm_hand_cases(lib):
+    """[3, 4]: mean square 12.5, y = [3, 4] / sqrt(12.5 + eps);
+    [1, 1, 1, 1] with eps: every output is 1/sqrt(1 + eps)."""
+    y = oracle.rmsnorm(_f32([[3.0, 4.0]]), "f32", 0.0, lib=lib)[0]
+    assert _rel(y, [3.0 / math.sqrt(12.5), 4.0 / math.sqrt(12.5)]) < 1e-15
+    y = oracle.rmsnorm(_f32([[3.0, 4.0]]), "f32", 1e-6, lib=lib)[0]
+    d = math.sqrt(12.5 + F32_EPS6)
+    assert _rel(y, [3.0 / d, 4.0 / d]) < 1e-15
+    y = oracle.rmsnorm(np.ones((1, 4), np.float32), "f32", 1e-6, lib=lib)[0]
+    assert _rel(y, [1.0 / math.sqrt(1.0 + F32_EPS6)] * 4) < 1e-15
+
+
+def pin_rmsnorm_unit_mean_square(lib):
+    """Unit weight: mean(y^2) = ms / (ms + eps)."""
+    x = _rng_rows(31, 32, 8192, "bf16")
+    y = oracle.rmsnorm(x, "bf16", 1e-6, lib=lib)
+    xd = oracle.decode(x, "bf16")
+    ms = (xd ** 2).mean(axis=1)
+    assert _rel((y ** 2).mean(axis=1), ms / (ms + F32_EPS6)) < 1e-12
+
+
+def pin_rmsnorm_scale_invariance(lib):
+    """With eps = 0, y is unchanged by x -> a*x (a > 0)."""
+    x = _rng_rows(32, 8, 300, "f32")
+    y = oracle.rmsnorm(x, "f32", 0.0, lib=lib)
+    y2 = oracle.rmsnorm((x * np.float32(8.0)).astype(np.float32), "f32", 0.0, lib=lib)
+    assert _rel(y2, y) < 1e-13
+
+
+def pin_rmsnorm_weight_columns(lib):
+    """The weight acts per column: w_j = j+1 scales column j by j+1."""
+    x = _rng_rows(33, 4, 40, "f32")
+    w = np.arange(1, 41, dtype=np.float32)
+    y0 = oracle.rmsnorm(x, "f32", 1e-6, lib=lib)
+    y1 = oracle.rmsnorm(x, "f32", 1e-6, weight=w, lib=lib)
+    assert _rel(y1, y0 * w) < 1e-14
+
+
+def pin_rmsnorm_brute(lib):
+    for dt in ("f32", "f16", "bf16"):
+        for N in list(range(1, 65)) + [127, 255, 257, 781, 1500]:
+            x = _rng_rows(5000 + N, 2, N, dt)
+            w = _rng_rows(6000 + N, 1, N, dt, scale=0.3, loc=1.0)[0]
+            y = oracle.rmsnorm(x, dt, 1e-6, weight=w, lib=lib)
+            wd = _decode_py(w, dt)
+            for r in range(2):
+                want = brute.rmsnorm_row(_decode_py(x[r], dt), F32_EPS6, wd)
+                assert _rel(y[r], want) < 1e-13, (dt, N)
+
+
+def pin_rmsnorm_torch(lib):
+    """oracle.c agrees with torch.nn.functional.rms_norm in float64."""
+    import torch
+    for dt in ("f32", "f16", "bf16"):
+        x = _rng_rows(34, 16, 1500, dt)
+        w = _rng_rows(35, 1, 1500, dt, scale=0.3, loc=1.0)[0]
+        y = oracle.rmsnorm(x, dt, 1e-6, weight=w, lib=lib)
+        ref = torch.nn.functional.rms_norm(
+            torch.from_numpy(oracle.decode(x, dt)), (1500,),
+            torch.from_numpy(oracle.decode(w, dt)), eps=F32_EPS6).numpy()
+        assert _rel(y, ref) < 1e-13, dt
+
+
+ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

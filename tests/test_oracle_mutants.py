@@ -1,0 +1,61 @@
+"""Plant plausible mistakes in a private copy of the oracle (CPU only) and
+check that every one of them is caught by at least one pin.
+
+Each mutation is a textual edit of oracle.c compiled to a temporary library;
+the real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "ln_unbiased_variance": ("double var = s2 / (double)N;", "double var = s2 / (double)(N - 1);"),
+    "ln_eps_outside_sqrt": ("double rs = 1.0 / sqrt(var + deps);", "double rs = 1.0 / sqrt(var) + deps;"),
+    "ln_mean_wrong_count": ("double mu = s1 / (double)N;", "double mu = s1 / (double)(N + 1);"),
+    "ln_gamma_beta_swapped": ("- mu) * rs * g + b;", "- mu) * rs * b + g;"),
+    "ln_gamma_reversed": ("or_load(dtype, gamma, j)", "or_load(dtype, gamma, N - 1 - j)"),
+    "ln_beta_dropped": ("double b = beta ? or_load(dtype, beta, j) : 0.0;", "double b = 0.0;"),
+    "rms_no_mean": ("1.0 / sqrt(ss / (double)N + deps);", "1.0 / sqrt(ss + deps);"),
+    "rms_weight_first_only": ("or_load(dtype, w, j)", "or_load(dtype, w, 0)"),
+    "rms_eps_dropped": ("sqrt(ss / (double)N + deps)", "sqrt(ss / (double)N)"),
+    "softmax_no_shift": ("double e = exp(v - m);", "double e = exp(v);"),
+    "softmax_dropped_term": ("s += e;", "s += (j > 0) ? e : 0.0;"),
+    "softmax_exp2": ("double e = exp(v - m);", "double e = exp2(v - m);"),
+    "softmax_multiply": ("yr[j] = yr[j] / s;", "yr[j] = yr[j] * s;"),
+    "softmax_max_is_min": ("else if (v > m) m = v;\n        }\n        double s", "else if (v < m || m == -INFINITY) m = v;\n        }\n        double s"),
+    "f16_bias_off_by_one": ("expo - 25", "expo - 24"),
+    "f16_subnormal_scale": ("ldexp((double)mant, -24)", "ldexp((double)mant, -25)"),
+    "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    "online_no_rescale": ("l_prev = l_prev * alpha + psum;", "l_prev = l_prev + psum;"),
+    "online_alpha_sign": ("exp(m_prev - m_new)", "exp(m_new - m_prev)"),
+    "online_final_uses_first_max": ("m_prev = m_new;", "m_prev = (m_prev == -INFINITY) ? m_new : m_prev;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+    failed = []
+    # cheap pins first; the first one that fails is enough
+    order = sorted(ALL_PINS, key=lambda n: ("torch" in n, "brute" in n, n))
+    for pin_name in order:
+        try:
+            ALL_PINS[pin_name](lib)
+        except AssertionError:
+            failed.append(pin_name)
+        except Exception as e:  # a crash or NaN trap also counts as caught
+            failed.append(f"{pin_name} ({type(e).__name__})")
+        if failed:
+            break
+    assert failed, f"mutant {name} passed every pin"
