@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of the fused row reductions on one MI355X.
+
+One step = one pass over the five row-reduction workloads (all on-chip steps
+of the method: launch planning, 16-byte row loads, widening, row reductions,
+epilogue, rounding stores, and the split online softmax for vocab-width rows):
+
+  softmax   fp32  1024 x 781       single pass, masked ragged tail, 4-byte-aligned rows
+  LayerNorm fp16  4096 x 4096      y + mean + rstd
+  RMSNorm   bf16  16384 x 8192
+  softmax   bf16  131072 x 4096    causal attention scores (-inf above the diagonal)
+  softmax   fp32  64 x 262144      vocab-width rows: split online max/denominator path
+
+Inputs are generated on the host from fixed seeds, copied to HBM before the
+timed region, and each kernel is launched on torch's current stream through
+the C ABI.  value = algorithmic bytes of one step / time of one step (GB/s);
+every workload's own GB/s and the dominant kernel's roofline fraction come
+from HIP events recorded around each launch on that stream.
+
+Prints ONE JSON line.  Flags: --gpus (only 1 is supported), --steps, --warmup,
+--only NAME[,NAME] (time a subset, rotating buffer sets so the 256 MiB
+Infinity Cache cannot serve them), --no-cpu-baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+METRIC = "achieved HBM GB/s (and % of MI355X peak) for softmax/LayerNorm/RMSNorm rows"
+CACHE_BYTES = 256 << 20     # Infinity Cache (MALL) size
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "row_wise_reductions_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(bits, dt, torch, np):
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+
+class Job:
+    """One workload resident in HBM, with R rotating buffer sets."""
+
+    def __init__(self, w, data, R, torch, np, nt):
+        self.w, self.R, self.nt = w, R, nt
+        self.bytes = w.algorithmic_bytes()
+        self.dt_code = {"f32": nt.NT_F32, "f16": nt.NT_F16, "bf16": nt.NT_BF16}[w.dt]
+        x0 = to_dev(data["x"], w.dt, torch, np)
+        self.x = [x0] + [x0.clone() for _ in range(R - 1)]
+        self.y = [torch.empty_like(x0) for _ in range(R)]
+        p0 = data.get("gamma", data.get("weight"))
+        p1 = data.get("beta")
+        self.p0 = None if p0 is None else to_dev(p0, w.dt, torch, np)
+        self.p1 = None if p1 is None else to_dev(p1, w.dt, torch, np)
+        self.mean = [torch.empty(w.M, dtype=torch.float32, device="cuda") for _ in range(R)]
+        self.rstd = [torch.empty(w.M, dtype=torch.float32, device="cuda") for _ in range(R)]
+        self.wsb = nt.nt_softmax_workspace_bytes(w.M, w.N, self.dt_code) if w.op == "softmax" else 0
+        self.ws = torch.empty(max(self.wsb, 8), dtype=torch.uint8, device="cuda")
+        self.i = 0
+        self.starts, self.ends = [], []
+
+    def launch(self, stream):
+        w, nt, r = self.w, self.nt, self.i % self.R
+        self.i += 1
+        if w.op == "softmax":
+            rc = nt.nt_softmax_rows(w.M, w.N, self.dt_code, self.x[r].data_ptr(), self.y[r].data_ptr(),
+                                    self.ws.data_ptr(), self.wsb, stream)
+        elif w.op == "layernorm":
+            rc = nt.nt_layernorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.p0.data_ptr(),
+                                      self.p1.data_ptr(), self.y[r].data_ptr(), self.mean[r].data_ptr(),
+                                      self.rstd[r].data_ptr(), stream)
+        else:
+            rc = nt.nt_rmsnorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.p0.data_ptr(),
+                                    self.y[r].data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"{w.name}: {nt.nt_status_string(rc)}")
+
+
+def cpu_baseline(jobs, np, stride=8):
+    """The oracle (as it stands) on every `stride`-th row of each workload,
+    on this host's cores.  Also checks the GPU outputs on those rows."""
+    import oracle
+    from oracle import compare
+    total_bytes, total_t, ok = 0, 0.0, True
+    parts = []
+    for j in jobs:
+        w, data = j.w, j.data
+        rows = np.arange(0, w.M, stride)
+        xs = np.ascontiguousarray(data["x"][rows])
+        p0 = data.get("gamma", data.get("weight"))
+        p1 = data.get("beta")
+
+        def run():
+            if w.op == "softmax":
+                return oracle.softmax(xs, w.dt)
+            if w.op == "layernorm":
+                return oracle.layernorm(xs, w.dt, w.eps, gamma=p0, beta=p1)[0]
+            return oracle.rmsnorm(xs, w.dt, w.eps, weight=p0)
+
+        ref = run()                                  # warm-up
+        ts = []
+        for _ in range(2):
+            t0 = time.perf_counter()
+            run()
+            ts.append(time.perf_counter() - t0)
+        t = statistics.median(ts)
+        e = w.elem_bytes
+        b = 2 * len(rows) * w.N * e + (2 * w.N * e + 8 * len(rows) if w.op == "layernorm" else 0) \
+            + (w.N * e if w.op == "rmsnorm" else 0)
+        total_bytes += b
+        total_t += t
+        parts.append(f"{w.name}: {len(rows)} of {w.M} rows")
+        # parity of the timed GPU output on the same rows
+        y = j.y[0].cpu()
+        if w.dt == "f32":
+            gb = y.numpy()[rows].view(np.uint32)
+            good = compare.max_rel_err(compare.bits_to_f64(gb, "f32"), ref) <= 1e-5
+        else:
+            import torch
+            gb = y.view(torch.int16).numpy()[rows].view(np.uint16)
+            good = int(compare.ulp_distance(gb, ref, w.dt).max()) <= 1
+        ok = ok and good
+    return {"value": round(total_bytes / total_t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"every {stride}th row of each workload ({'; '.join(parts)}); median of 2 timed runs "
+                      f"after 1 warm-up; fp64 C with OpenMP over rows",
+            "seconds": round(total_t, 3), "gpu_parity_on_sample": bool(ok)}
+
+
+def traffic_for(kernel_name, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("workloads", {}).get(kernel_name)
+    return None if e is None else e.get("hbm_bytes_per_call")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, so a "
+              f"multi-GPU run would shard rows with no communication; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import row_wise_reductions_amd as nt
+    import workloads
+
+    nt.lib()   # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]
+    suite = args.only is None
+
+    jobs = []
+    for name in names:
+        w = workloads.BY_NAME[name]
+        t0 = time.perf_counter()
+        data = w.make()
+        # in the full suite the other workloads flush the Infinity Cache between
+        # two launches of the same workload; alone, rotate buffer sets instead
+        per_set = 2 * w.M * w.N * w.elem_bytes
+        R = 1 if suite else max(1, -(-(4 * CACHE_BYTES) // per_set))
+        j = Job(w, data, R, torch, np, nt)
+        j.data = data
+        jobs.append(j)
+        log(f"[bench] {name}: generated + uploaded in {time.perf_counter() - t0:.1f}s (R={R})")
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(args.warmup):
+        for j in jobs:
+            j.launch(sh)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for j in jobs:
+        j.i = 0
+        j.starts = [ev() for _ in range(args.steps)]
+        j.ends = [ev() for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for j in jobs:
+            j.starts[s].record(stream)
+            j.launch(sh)
+            j.ends[s].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    per = []
+    for j in jobs:
+        durs = [a.elapsed_time(b) for a, b in zip(j.starts, j.ends)]
+        avg = sum(durs) / len(durs)
+        per.append({"workload": j.w.name, "op": j.w.op, "dtype": j.w.dt, "M": j.w.M, "N": j.w.N,
+                    "bytes": j.bytes, "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
+                    "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "plan": nt.nt_plan_launch({"softmax": 0, "layernorm": 1, "rmsnorm": 2}[j.w.op],
+                                              j.w.M, j.w.N, j.dt_code, True)})
+    total_bytes = sum(j.bytes for j in jobs)
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(per, key=lambda p: p["avg_ms"])
+    achieved = dom["bytes"] / (dom["avg_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(dom["workload"], dom["bytes"]),
+                "kernel": dom["workload"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        cpu = cpu_baseline(jobs, np)
+        log(f"[bench] cpu baseline in {time.perf_counter() - t0:.1f}s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": ("row-reduction suite: softmax f32 1024x781, LayerNorm f16 4096x4096, "
+                                "RMSNorm bf16 16384x8192, causal softmax bf16 131072x4096, "
+                                "vocab softmax f32 64x262144") if suite else ",".join(names),
+                   "bytes_per_step": total_bytes, "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_workload": per,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

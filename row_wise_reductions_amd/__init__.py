@@ -1,0 +1,188 @@
+"""Python binding of the MI355X row-reduction library (``libnt.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/nt.h``.  The ``nt_*``
+functions take the same arguments as their C counterparts (pointers as
+integers, ``stream`` as a ``hipStream_t`` handle) and return the status code.
+``softmax``, ``layer_norm`` and ``rms_norm`` are conveniences over torch
+tensors on an AMD GPU: they check contiguity, allocate outputs (and the
+split-path workspace) with torch, and launch on torch's current stream.
+
+There is no fallback: if ``libnt.so`` is missing or the call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnt.so")
+
+NT_F32, NT_F16, NT_BF16 = 0, 1, 2
+NT_OP_SOFTMAX, NT_OP_LAYERNORM, NT_OP_RMSNORM = 0, 1, 2
+STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4: "NT_ERR_EPS",
+          5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP"}
+EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_layernorm_rows",
+            "nt_rmsnorm_rows", "nt_status_string", "nt_plan_launch")
+
+
+class NtError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({status_string(code)})")
+        self.code = code
+
+
+class nt_plan(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
+                ("chunks_per_lane", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("threads_per_block", ctypes.c_int32), ("aligned", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("row_chunks", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """Load libnt.so (built by ``row_wise_reductions_amd.build``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: run `python -m row_wise_reductions_amd.build` first")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, f32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    i32 = ctypes.c_int
+    L.nt_softmax_workspace_bytes.argtypes = [i64, i64, i32]
+    L.nt_softmax_workspace_bytes.restype = sz
+    L.nt_softmax_rows.argtypes = [i64, i64, i32, vp, vp, vp, sz, vp]
+    L.nt_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp]
+    L.nt_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp]
+    L.nt_status_string.argtypes = [i32]
+    L.nt_status_string.restype = ctypes.c_char_p
+    L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
+    for f in ("nt_softmax_rows", "nt_layernorm_rows", "nt_rmsnorm_rows", "nt_plan_launch"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+# ---- the C ABI, one to one -------------------------------------------------
+
+def nt_softmax_workspace_bytes(M: int, N: int, dt: int) -> int:
+    return int(lib().nt_softmax_workspace_bytes(M, N, dt))
+
+
+def nt_softmax_rows(M, N, dt, x, y, workspace, workspace_bytes, stream) -> int:
+    return int(lib().nt_softmax_rows(M, N, dt, x, y, workspace, workspace_bytes, stream))
+
+
+def nt_layernorm_rows(M, N, dt, eps, x, gamma, beta, y, mean, rstd, stream) -> int:
+    return int(lib().nt_layernorm_rows(M, N, dt, eps, x, gamma, beta, y, mean, rstd, stream))
+
+
+def nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream) -> int:
+    return int(lib().nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream))
+
+
+def nt_status_string(code: int) -> str:
+    return lib().nt_status_string(code).decode()
+
+
+def nt_plan_launch(op: int, M: int, N: int, dt: int, aligned16: bool = True) -> dict:
+    p = nt_plan()
+    rc = lib().nt_plan_launch(op, M, N, dt, 1 if aligned16 else 0, ctypes.byref(p))
+    if rc != 0:
+        raise NtError(rc, "nt_plan_launch")
+    return p.as_dict()
+
+
+def status_string(code: int) -> str:
+    try:
+        return nt_status_string(code)
+    except Exception:
+        return "?"
+
+
+# ---- torch conveniences ----------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: NT_F32, torch.float16: NT_F16, torch.bfloat16: NT_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return getattr(stream, "cuda_stream", stream)
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _rows(x):
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (rows of stride N)")
+    if x.dim() == 0:
+        raise ValueError("x must have at least one dimension")
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    return M, N
+
+
+def _check(code, what):
+    if code != 0:
+        raise NtError(code, what)
+
+
+def softmax(x, out=None, stream=None):
+    """Row softmax over the last dimension of a contiguous GPU tensor."""
+    torch = _torch()
+    M, N = _rows(x)
+    y = torch.empty_like(x) if out is None else out
+    dt = dtype_code(x)
+    wsb = nt_softmax_workspace_bytes(M, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    _check(nt_softmax_rows(M, N, dt, _ptr(x), _ptr(y), _ptr(ws), wsb, _stream(stream)), "nt_softmax_rows")
+    return y
+
+
+def layer_norm(x, gamma=None, beta=None, eps=1e-5, out=None, stream=None):
+    """LayerNorm over the last dimension; returns (y, mean, rstd) (stats fp32)."""
+    torch = _torch()
+    M, N = _rows(x)
+    y = torch.empty_like(x) if out is None else out
+    lead = x.shape[:-1]
+    mean = torch.empty(lead, dtype=torch.float32, device=x.device)
+    rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
+    for p in (gamma, beta):
+        if p is not None and (p.numel() != N or p.dtype != x.dtype or not p.is_contiguous()):
+            raise ValueError("gamma/beta must be contiguous, of x's dtype, with N entries")
+    _check(nt_layernorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(gamma), _ptr(beta),
+                             _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream)), "nt_layernorm_rows")
+    return y, mean, rstd
+
+
+def rms_norm(x, weight=None, eps=1e-6, out=None, stream=None):
+    """RMSNorm over the last dimension."""
+    torch = _torch()
+    M, N = _rows(x)
+    y = torch.empty_like(x) if out is None else out
+    if weight is not None and (weight.numel() != N or weight.dtype != x.dtype or not weight.is_contiguous()):
+        raise ValueError("weight must be contiguous, of x's dtype, with N entries")
+    _check(nt_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(weight), _ptr(y),
+                           _stream(stream)), "nt_rmsnorm_rows")
+    return y

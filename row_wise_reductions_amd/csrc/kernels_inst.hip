@@ -1,0 +1,96 @@
+// Instantiation of the row kernels for one element type, selected at build
+// time with -DNTK_DT=0 (fp32), 1 (fp16) or 2 (bf16).
+#include "launch.hpp"
+
+#ifndef NTK_DT
+#error "NTK_DT must be defined"
+#endif
+
+namespace ntk {
+namespace {
+
+constexpr int DT = NTK_DT;
+// 16-bit types hold 8 values per chunk: K = 16 would need 128 values per
+// lane, so the widest per-lane footprint is K = 8 for them.
+constexpr bool kWide = dt_info<DT>::VEC == 4;
+
+template <int OP, int W, int K>
+hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    constexpr int T = GroupShape<W>::THREADS;
+    if (al)
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+    else
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int OP>
+hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+#define NTK_CASE(w, k) \
+    if (W == w && K == k) return go<OP, w, k>(al, a, grid, s);
+    NTK_CASE(1, 1) NTK_CASE(1, 2) NTK_CASE(1, 4) NTK_CASE(1, 8)
+    NTK_CASE(2, 8) NTK_CASE(4, 4) NTK_CASE(4, 8) NTK_CASE(8, 8) NTK_CASE(16, 8)
+    if constexpr (kWide) {
+        NTK_CASE(1, 16) NTK_CASE(16, 16)
+    }
+#undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int W, int K>
+hipError_t split_go(bool al, const RowArgs &a, hipStream_t s) {
+    const uint32_t grid = (uint32_t)(a.M * a.P);
+    if (al) {
+        hipLaunchKernelGGL((softmax_split_partial<DT, W, K, true>), dim3(grid), dim3(64 * W), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, true>), dim3(grid), dim3(64 * W), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((softmax_split_partial<DT, W, K, false>), dim3(grid), dim3(64 * W), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, false>), dim3(grid), dim3(64 * W), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t split(int W, int K, bool al, const RowArgs &a, hipStream_t s) {
+#define NTK_CASE(w, k) \
+    if (W == w && K == k) return split_go<w, k>(al, a, s);
+    NTK_CASE(4, 8) NTK_CASE(8, 8)
+    if constexpr (kWide) {
+        NTK_CASE(4, 16) NTK_CASE(8, 16)
+    }
+#undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t resident_any(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    switch (op) {
+    case OP_SOFTMAX: return resident<OP_SOFTMAX>(W, K, al, a, grid, s);
+    case OP_LAYERNORM: return resident<OP_LAYERNORM>(W, K, al, a, grid, s);
+    case OP_RMSNORM: return resident<OP_RMSNORM>(W, K, al, a, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+#if NTK_DT == 0
+hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return resident_any(op, W, K, al, a, grid, s);
+}
+hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+#elif NTK_DT == 1
+hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return resident_any(op, W, K, al, a, grid, s);
+}
+hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+#else
+hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return resident_any(op, W, K, al, a, grid, s);
+}
+hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+#endif
+
+}  // namespace ntk

@@ -1,0 +1,24 @@
+// Host-side launchers of the row kernels (defined in kernels_inst.hip, one
+// translation unit per element type so they compile in parallel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "row_kernels.hpp"
+
+namespace ntk {
+
+// Launch the single-pass kernel for (op, dt) with W waves per row and K
+// 16-byte chunks per lane.  Returns hipErrorInvalidValue for a (W, K) pair
+// that is not instantiated.
+hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+
+// Launch the two split-softmax kernels (partials, then merge + write).
+hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s);
+
+}  // namespace ntk

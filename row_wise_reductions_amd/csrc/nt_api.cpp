@@ -1,0 +1,307 @@
+// C ABI of the row-reduction library: argument validation, launch planning
+// and dispatch to the gfx950 kernels.  Declared in include/nt.h.
+//
+// Planning rule (per element type and row width):
+//   * the row is cut into 16-byte chunks; a group of W waves (64*W lanes)
+//     holding K chunks per lane covers 64*W*K chunks;
+//   * the first (smallest) shape of the type's menu that covers the row is
+//     used for the single-pass kernel (one HBM read and one write per
+//     element, as in the fused softmax of the stanleyjacob.dev Triton guide,
+//     Part II "Worked example: fused softmax");
+//   * softmax rows wider than the widest shape take the split online path
+//     ("Triton: Block-Level GPU Programming Without CUDA", section "How Flash
+//     Attention Uses Triton"): chunks of one workgroup each, partial
+//     (max, denominator) pairs in the caller's workspace, then a merge.
+//     LayerNorm and RMSNorm rows wider than the widest shape are rejected
+//     with NT_ERR_SHAPE.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/nt.h"
+#include "launch.hpp"
+
+namespace {
+
+struct Shape {
+    int W, K;
+};
+
+// Single-pass shapes in order of capacity (64*W*K chunks of 16 bytes).
+const Shape kMenu32[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 8}, {4, 8}, {8, 8}, {16, 8}, {16, 16}};
+const Shape kMenu16[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 8}, {4, 8}, {8, 8}, {16, 8}};
+// Split-path chunk shape: 64 KiB of fp32 (or 32 KiB of 16-bit) per workgroup.
+const Shape kSplit32 = {4, 16};
+const Shape kSplit16 = {4, 8};
+
+int elem_bytes(nt_dtype dt) { return dt == NT_F32 ? 4 : 2; }
+int elems_per_chunk(nt_dtype dt) { return 16 / elem_bytes(dt); }
+
+bool valid_dtype(int dt) { return dt == NT_F32 || dt == NT_F16 || dt == NT_BF16; }
+
+bool valid_shape(int64_t M, int64_t N) {
+    if (M < 0 || N <= 0 || N > INT32_MAX) return false;
+    if (M > 0 && N > INT64_MAX / 4 / M) return false;   // M*N*4 bytes must fit int64
+    return true;
+}
+
+bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Optional "W,K" override from the environment (tuning and tests only).
+bool env_shape(const char *name, Shape *out) {
+    const char *s = std::getenv(name);
+    if (!s || !*s) return false;
+    int w = 0, k = 0;
+    if (std::sscanf(s, "%d,%d", &w, &k) != 2 || w <= 0 || k <= 0) return false;
+    *out = {w, k};
+    return true;
+}
+
+bool debug_on() {
+    const char *s = std::getenv("NT_DEBUG");
+    return s && *s && std::strcmp(s, "0") != 0;
+}
+
+// Chunks a row can touch: N*e/16 when aligned, else up to one more for the
+// partial chunk in front of a misaligned row start.
+int64_t row_chunks(int64_t N, nt_dtype dt, bool aligned) {
+    const int64_t vec = elems_per_chunk(dt);
+    if (aligned) return N / vec;
+    return (N + vec - 1 + vec - 1) / vec;
+}
+
+nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p) {
+    std::memset(p, 0, sizeof *p);
+    p->aligned = aligned ? 1 : 0;
+    const int64_t nch = row_chunks(N, dt, aligned);
+    const Shape *menu = dt == NT_F32 ? kMenu32 : kMenu16;
+    const int nmenu = dt == NT_F32 ? (int)(sizeof kMenu32 / sizeof *kMenu32)
+                                   : (int)(sizeof kMenu16 / sizeof *kMenu16);
+    const char *force = std::getenv("NT_FORCE_PATH");
+    const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
+
+    Shape pick = {0, 0};
+    if (!force_split) {
+        Shape o;
+        if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch) {
+            pick = o;
+        } else {
+            for (int i = 0; i < nmenu; ++i)
+                if ((int64_t)64 * menu[i].W * menu[i].K >= nch) {
+                    pick = menu[i];
+                    break;
+                }
+        }
+    }
+    if (pick.W) {
+        const int G = pick.W == 1 ? 4 : 1;
+        p->split = 0;
+        p->waves_per_row = pick.W;
+        p->chunks_per_lane = pick.K;
+        p->rows_per_block = G;
+        p->threads_per_block = 64 * pick.W * G;
+        // The dispatch packet counts work-items in 32 bits: keep grid*threads
+        // below 2^31; the kernel strides over any remaining rows.
+        const int64_t max_grid = ((int64_t)1 << 31) / p->threads_per_block;
+        int64_t grid = (M + G - 1) / G;
+        if (grid > max_grid) grid = max_grid;
+        p->grid = grid;
+        return NT_OK;
+    }
+    if (op != NT_OP_SOFTMAX) return NT_ERR_SHAPE;
+    Shape s = dt == NT_F32 ? kSplit32 : kSplit16;
+    Shape o;
+    if (env_shape("NT_SPLIT_SHAPE", &o)) s = o;
+    const int64_t per = (int64_t)64 * s.W * s.K;
+    const int64_t P = (nch + per - 1) / per;
+    // one workgroup per (row, chunk), no striding: the grid must fit the packet
+    if (P > INT32_MAX || (M > 0 && P > (((int64_t)1 << 31) / (64 * s.W)) / M)) return NT_ERR_SHAPE;
+    p->split = 1;
+    p->waves_per_row = s.W;
+    p->chunks_per_lane = s.K;
+    p->rows_per_block = 1;
+    p->threads_per_block = 64 * s.W;
+    p->row_chunks = P;
+    p->grid = M * P;
+    p->workspace_bytes = M * P * (int64_t)sizeof(float2);
+    return NT_OK;
+}
+
+bool all_aligned16(int64_t N, nt_dtype dt, const void *x, const void *y, const void *p0, const void *p1) {
+    if ((N * elem_bytes(dt)) % 16 != 0) return false;
+    for (const void *q : {x, y, p0, p1})
+        if (q && !aligned_to(q, 16)) return false;
+    return true;
+}
+
+hipError_t launch_resident(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
+    const bool al = p.aligned != 0;
+    switch (dt) {
+    case NT_F32: return ntk::launch_resident_f32(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    case NT_F16: return ntk::launch_resident_f16(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    case NT_BF16: return ntk::launch_resident_bf16(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
+    const bool al = p.aligned != 0;
+    switch (dt) {
+    case NT_F32: return ntk::launch_split_f32(p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_F16: return ntk::launch_split_f16(p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_BF16: return ntk::launch_split_bf16(p.waves_per_row, p.chunks_per_lane, al, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p) {
+    std::fprintf(stderr,
+                 "[nt] %s M=%lld N=%lld dt=%d: %s W=%d K=%d rows/block=%d threads=%d aligned=%d grid=%lld"
+                 " chunks/row=%lld ws=%lld\n",
+                 what, (long long)M, (long long)N, (int)dt, p.split ? "split" : "single-pass", p.waves_per_row,
+                 p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, (long long)p.grid,
+                 (long long)p.row_chunks, (long long)p.workspace_bytes);
+}
+
+nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a,
+              void *stream) {
+    if (debug_on()) debug_print(op == NT_OP_SOFTMAX ? "softmax" : op == NT_OP_LAYERNORM ? "layernorm" : "rmsnorm",
+                                M, N, dt, p);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = p.split ? launch_split(dt, p, a, s) : launch_resident(dt, (int)op, p, a, s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        if (debug_on()) std::fprintf(stderr, "[nt] launch failed: %s\n", hipGetErrorString(e));
+        return NT_ERR_HIP;
+    }
+    return NT_OK;
+}
+
+// Checks shared by every entry point, in the documented order.
+nt_status common_checks(int64_t M, int64_t N, int dt, const void *x, const void *y) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (M == 0) return NT_OK;
+    if (!x || !y) return NT_ERR_NULL;
+    const uintptr_t e = (uintptr_t)elem_bytes((nt_dtype)dt);
+    if (!aligned_to(x, e) || !aligned_to(y, e)) return NT_ERR_ALIGN;
+    return NT_OK;
+}
+
+bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+const char *nt_status_string(nt_status s) {
+    switch (s) {
+    case NT_OK: return "ok";
+    case NT_ERR_NULL: return "a required pointer is NULL";
+    case NT_ERR_SHAPE: return "invalid shape (M < 0, N <= 0, N > INT32_MAX, size overflow, or row too wide)";
+    case NT_ERR_DTYPE: return "unknown element type";
+    case NT_ERR_EPS: return "eps must be finite and >= 0";
+    case NT_ERR_ALIGN: return "pointer not aligned to its element size";
+    case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes()";
+    case NT_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt, int aligned16, nt_plan *out) {
+    if (!out) return NT_ERR_NULL;
+    if (op != NT_OP_SOFTMAX && op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM) return NT_ERR_SHAPE;
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    const bool al = aligned16 && (N * elem_bytes(dt)) % 16 == 0;
+    return make_plan(op, M, N, dt, al, out);
+}
+
+size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt) {
+    if (!valid_dtype(dt) || !valid_shape(M, N) || M == 0) return 0;
+    // Sized for the misaligned case, which touches at most one extra chunk
+    // per row, so the answer does not depend on the pointers.
+    nt_plan p;
+    if (make_plan(NT_OP_SOFTMAX, M, N, dt, false, &p) != NT_OK) return 0;
+    return (size_t)p.workspace_bytes;
+}
+
+nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    const bool al = all_aligned16(N, dt, x, y, nullptr, nullptr);
+    nt_plan p;
+    st = make_plan(NT_OP_SOFTMAX, M, N, dt, al, &p);
+    if (st != NT_OK) return st;
+    ntk::RowArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.y = static_cast<char *>(y);
+    a.M = M;
+    a.N = (int32_t)N;
+    if (p.split) {
+        if (!workspace) return NT_ERR_NULL;
+        if (!aligned_to(workspace, 8)) return NT_ERR_ALIGN;
+        // The documented requirement (sized for misaligned rows) is enforced,
+        // not the possibly smaller need of this particular call.
+        if (workspace_bytes < nt_softmax_workspace_bytes(M, N, dt)) return NT_ERR_WORKSPACE;
+        a.ws = static_cast<float2 *>(workspace);
+        a.P = (int32_t)p.row_chunks;
+    }
+    return run(NT_OP_SOFTMAX, M, N, dt, p, a, stream);
+}
+
+nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,
+                            const void *beta, void *y, float *mean, float *rstd, void *stream) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (!valid_eps(eps)) return NT_ERR_EPS;
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    const uintptr_t e = (uintptr_t)elem_bytes(dt);
+    if ((gamma && !aligned_to(gamma, e)) || (beta && !aligned_to(beta, e)) || (mean && !aligned_to(mean, 4)) ||
+        (rstd && !aligned_to(rstd, 4)))
+        return NT_ERR_ALIGN;
+    const bool al = all_aligned16(N, dt, x, y, gamma, beta);
+    nt_plan p;
+    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p);
+    if (st != NT_OK) return st;
+    ntk::RowArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.y = static_cast<char *>(y);
+    a.p0 = static_cast<const char *>(gamma);
+    a.p1 = static_cast<const char *>(beta);
+    a.mean = mean;
+    a.rstd = rstd;
+    a.M = M;
+    a.N = (int32_t)N;
+    a.eps = eps;
+    return run(NT_OP_LAYERNORM, M, N, dt, p, a, stream);
+}
+
+nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *weight, void *y,
+                          void *stream) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (!valid_eps(eps)) return NT_ERR_EPS;
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    if (weight && !aligned_to(weight, (uintptr_t)elem_bytes(dt))) return NT_ERR_ALIGN;
+    const bool al = all_aligned16(N, dt, x, y, weight, nullptr);
+    nt_plan p;
+    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p);
+    if (st != NT_OK) return st;
+    ntk::RowArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.y = static_cast<char *>(y);
+    a.p0 = static_cast<const char *>(weight);
+    a.M = M;
+    a.N = (int32_t)N;
+    a.eps = eps;
+    return run(NT_OP_RMSNORM, M, N, dt, p, a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle on
+identical seeded inputs.  fp32 outputs: max relative error <= 1e-5; fp16 and
+bf16 outputs: <= 1 ulp of the output type from the oracle's float64 result
+rounded once (round to nearest even); LayerNorm mean/rstd: relative 1e-5.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import (check_output, check_stats, empty_like_dev, oracle_for, tdt, to_dev,
+                      to_host_bits)
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import torch  # noqa: E402
+
+import row_wise_reductions_amd as nt  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DT_CODE = {"f32": nt.NT_F32, "f16": nt.NT_F16, "bf16": nt.NT_BF16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_bits(seed, M, N, dt, scale=1.0, loc=0.0):
+    rng = np.random.default_rng(seed)
+    return workloads.encode(rng.standard_normal((M, N)) * scale + loc, dt)
+
+
+def run_op(op, x_t, dt, eps=0.0, p0=None, p1=None, y_t=None):
+    """Launch through the C ABI on the current stream and wait."""
+    M, N = x_t.shape
+    code = DT_CODE[dt]
+    y = y_t if y_t is not None else empty_like_dev((M, N), dt)
+    s = torch.cuda.current_stream().cuda_stream
+    mean = rstd = None
+    if op == "softmax":
+        wsb = nt.nt_softmax_workspace_bytes(M, N, code)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        rc = nt.nt_softmax_rows(M, N, code, x_t.data_ptr(), y.data_ptr(), ws.data_ptr(), wsb, s)
+    elif op == "layernorm":
+        mean = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        rc = nt.nt_layernorm_rows(M, N, code, eps, x_t.data_ptr(),
+                                  None if p0 is None else p0.data_ptr(),
+                                  None if p1 is None else p1.data_ptr(),
+                                  y.data_ptr(), mean.data_ptr(), rstd.data_ptr(), s)
+    else:
+        rc = nt.nt_rmsnorm_rows(M, N, code, eps, x_t.data_ptr(),
+                                None if p0 is None else p0.data_ptr(), y.data_ptr(), s)
+    assert rc == 0, f"{op}: status {rc} ({nt.nt_status_string(rc)})"
+    torch.cuda.synchronize()
+    return y, mean, rstd
+
+
+def parity_case(op, x_bits, dt, eps=0.0, p0=None, p1=None, x_off=0, y_off=0, what=""):
+    M, N = x_bits.shape
+    say(f"case {what} op={op} dt={dt} M={M} N={N} x_off={x_off} y_off={y_off}")
+    x_t = to_dev(x_bits, dt, x_off)
+    p0_t = None if p0 is None else to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    y_t = empty_like_dev((M, N), dt, y_off)
+    y, mean, rstd = run_op(op, x_t, dt, eps, p0_t, p1_t, y_t)
+    ref, rmean, rrstd = oracle_for(op, x_bits, dt, eps, p0, p1)
+    check_output(to_host_bits(y, dt), ref, dt, what)
+    if op == "layernorm":
+        check_stats(mean.cpu().numpy(), rmean, what + " mean")
+        check_stats(rstd.cpu().numpy(), rrstd, what + " rstd")
+
+
+# ----------------------------------------------------------------------------
+# the five workloads at full size (sampled rows for the two largest)
+# ----------------------------------------------------------------------------
+
+def _sample_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([rows, [0, 1, M - 1]]))
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
+def test_workload_full_size(name):
+    w = workloads.BY_NAME[name]
+    say(f"workload {name}: generating {w.M}x{w.N} {w.dt}")
+    data = w.make()
+    x = data["x"]
+    p0 = data.get("gamma", data.get("weight"))
+    p1 = data.get("beta")
+    x_t = to_dev(x, w.dt)
+    p0_t = None if p0 is None else to_dev(p0, w.dt)
+    p1_t = None if p1 is None else to_dev(p1, w.dt)
+    say(f"workload {name}: launching")
+    y, mean, rstd = run_op(w.op, x_t, w.dt, w.eps, p0_t, p1_t)
+    big = w.M * w.N > 40_000_000
+    rows = _sample_rows(w.M, 4096, 7) if big else np.arange(w.M)
+    ref, rmean, rrstd = oracle_for(w.op, np.ascontiguousarray(x[rows]), w.dt, w.eps, p0, p1)
+    yb = to_host_bits(y, w.dt)[rows]
+    check_output(yb, ref, w.dt, name)
+    if w.op == "layernorm":
+        check_stats(mean.cpu().numpy()[rows], rmean, name + " mean")
+        check_stats(rstd.cpu().numpy()[rows], rrstd, name + " rstd")
+    if name == "causal_softmax_bf16":
+        # row with query q has exactly q+1 non-zero outputs; masked entries are exact 0
+        q = rows % w.extra["queries"]
+        nz = (yb & 0x7FFF) != 0
+        assert np.array_equal(nz.sum(axis=1), q + 1)
+    if name == "vocab_softmax_f32":
+        # the 8 spikes of a row are bit-identical and carry almost all the mass
+        yv = yb.view(np.float32)
+        for r in range(w.M):
+            s = yv[r, data["spikes"][r]]
+            assert np.all(s == s[0]) and abs(float(s[0]) - 0.125) < 1e-6
+
+
+# ----------------------------------------------------------------------------
+# shape sweep: ragged tails, every path, aligned and misaligned rows
+# ----------------------------------------------------------------------------
+
+SWEEP_N = [1, 2, 3, 7, 8, 63, 64, 65, 255, 256, 257, 781, 1023, 1024, 1025, 1500, 4095,
+           4097, 8192, 16384, 65536, 65537, 262144, 262147]
+
+
+def _sweep_M(N):
+    if N <= 4097:
+        return [1, 3, 1823]
+    if N <= 16384:
+        return [1, 37]
+    return [1, 5]
+
+
+SWEEP = [(op, dt, N, M) for op in ("softmax", "layernorm", "rmsnorm") for dt in ("f32", "f16", "bf16")
+         for N in SWEEP_N for M in _sweep_M(N)
+         if not (op != "softmax" and N > 65536)]
+
+
+@pytest.mark.parametrize("op,dt,N,M", SWEEP)
+def test_sweep(op, dt, N, M):
+    seed = zlib.crc32(f"{op}/{dt}/{N}/{M}".encode())
+    loc = 2.0 if op == "layernorm" else 0.0
+    x = rand_bits(seed, M, N, dt, scale=2.0, loc=loc)
+    p0 = p1 = None
+    eps = 1e-5
+    if op != "softmax":
+        p0 = rand_bits(seed + 1, 1, N, dt, scale=0.3, loc=1.0)[0]
+        if op == "layernorm":
+            p1 = rand_bits(seed + 2, 1, N, dt, scale=0.3)[0]
+    parity_case(op, x, dt, eps, p0, p1, what=f"sweep {op} {dt} {M}x{N}")
+    # misaligned rows: x and y one element past a 16-byte boundary (same phase)
+    if N >= 2 and M <= 64:
+        plan_ok = op == "softmax" or N < 65536
+        if plan_ok:
+            parity_case(op, x, dt, eps, p0, p1, x_off=1, y_off=1, what=f"sweep-misaligned {op} {dt} {M}x{N}")
+
+
+@pytest.mark.parametrize("op", ["softmax", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_phase_mismatch_and_no_params(op, dt):
+    """x and y at different 16-byte phases; parameter vectors absent."""
+    x = rand_bits(77, 19, 1000, dt, scale=1.5)
+    parity_case(op, x, dt, 1e-5, x_off=1, y_off=2, what=f"phase {op} {dt}")
+    parity_case(op, x, dt, 1e-5, x_off=3, y_off=0, what=f"phase {op} {dt}")
+
+
+def test_correctness_shapes_from_pages():
+    """The irregular shapes of the pages' correctness template."""
+    with open(os.path.join(GOLDEN, "correctness_shapes.json")) as f:
+        shapes = json.load(f)["shapes"]
+    for M, N in shapes:
+        for op in ("softmax", "layernorm", "rmsnorm"):
+            x = rand_bits(0, M, N, "f32")
+            parity_case(op, x, "f32", 1e-6, what=f"pages-shape {op} {M}x{N}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [4096, 65536, 100003])
+def test_split_path_forced(dt, N, monkeypatch):
+    """The split online path on rows that would fit on chip, and odd widths."""
+    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    x = rand_bits(N, 7, N, dt, scale=3.0)
+    x[2, :] = -np.inf if dt == "f32" else workloads.NEG_INF_BITS[dt]
+    x[2, N // 3] = x[3, 0]                       # row 2: one finite entry
+    x[4, : N // 2] = x[2, 0]                     # row 4: masked first half
+    for off in (0, 1):
+        parity_case("softmax", x, dt, x_off=off, y_off=off, what=f"split {dt} N={N} off={off}")
+
+
+# ----------------------------------------------------------------------------
+# semantics: special rows, in place, determinism, streams, no-op, errors
+# ----------------------------------------------------------------------------
+
+def test_special_rows():
+    x = np.full((4, 300), -np.inf, dtype=np.float32)
+    x[1, 7] = 2.0                                 # one finite entry -> one-hot
+    x[2, :] = 0.5                                 # uniform
+    x[3, :150] = 1.0
+    y, _, _ = run_op("softmax", to_dev(x, "f32"), "f32")
+    yh = y.cpu().numpy()
+    assert np.all(np.isnan(yh[0]))               # all -inf row: NaN, as the formula
+    assert yh[1, 7] == 1.0 and np.count_nonzero(yh[1]) == 1
+    assert np.max(np.abs(yh[2] - 1.0 / 300)) < 1e-5 / 300
+    # LayerNorm of a constant row: y = beta, rstd = 1/sqrt(eps)
+    c = np.full((2, 33), 3.0, dtype=np.float32)
+    beta = np.linspace(-1, 1, 33).astype(np.float32)
+    y, mean, rstd = run_op("layernorm", to_dev(c, "f32"), "f32", 1e-5, None, to_dev(beta, "f32"))
+    assert np.array_equal(y.cpu().numpy()[0], beta)
+    assert abs(rstd.cpu().numpy()[0] - 1 / np.sqrt(np.float64(np.float32(1e-5)))) < 1e-3
+
+
+@pytest.mark.parametrize("op", ["softmax", "layernorm", "rmsnorm"])
+def test_in_place(op):
+    x = rand_bits(5, 64, 4096, "bf16", scale=2.0)
+    ref, _, _ = oracle_for(op, x, "bf16", 1e-5)
+    x_t = to_dev(x, "bf16")
+    y, _, _ = run_op(op, x_t, "bf16", 1e-5, y_t=x_t)
+    check_output(to_host_bits(x_t, "bf16"), ref, "bf16", f"in-place {op}")
+
+
+@pytest.mark.parametrize("N", [781, 8192, 262144])
+def test_bitwise_repeatable(N):
+    x_t = to_dev(rand_bits(9, 16, N, "f32", scale=3.0), "f32")
+    a, _, _ = run_op("softmax", x_t, "f32")
+    b, _, _ = run_op("softmax", x_t, "f32")
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_side_stream_ordering():
+    x = rand_bits(10, 256, 4096, "f16", loc=1.0)
+    s = torch.cuda.Stream()
+    x_t = to_dev(x, "f16")
+    y = torch.empty_like(x_t)
+    with torch.cuda.stream(s):
+        rc = nt.nt_rmsnorm_rows(256, 4096, nt.NT_F16, 1e-6, x_t.data_ptr(), None, y.data_ptr(),
+                                s.cuda_stream)
+        assert rc == 0
+        ev = torch.cuda.Event()
+        ev.record(s)
+    torch.cuda.current_stream().wait_event(ev)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_for("rmsnorm", x, "f16", 1e-6)
+    check_output(to_host_bits(y, "f16"), ref, "f16", "side stream")
+
+
+def test_torch_wrappers_and_noop():
+    x = torch.randn(3, 5, 781, device="cuda")
+    y = nt.softmax(x)
+    assert y.shape == x.shape and torch.allclose(y.sum(-1), torch.ones(3, 5, device="cuda"), atol=1e-5)
+    yl, m, r = nt.layer_norm(x.half(), eps=1e-5)
+    assert m.shape == (3, 5) and r.shape == (3, 5)
+    e = torch.empty(0, 64, device="cuda")
+    assert nt.nt_softmax_rows(0, 64, nt.NT_F32, e.data_ptr(), e.data_ptr(), None, 0, None) == 0
+    with pytest.raises(ValueError):
+        nt.softmax(x.transpose(1, 2))
+
+
+def test_errors_before_launch():
+    """Invalid arguments are rejected before anything is enqueued.  Every
+    buffer here is sized for the nominal shape, so even a validation bug
+    could not make a kernel touch memory outside an allocation."""
+    M, N = 4, 1 << 20
+    big = torch.zeros(M * N + 64, device="cuda", dtype=torch.float32)
+    p = big.data_ptr()
+    assert nt.nt_softmax_rows(M, 8, nt.NT_F16, p + 1, p, None, 0, None) == 5     # misaligned element
+    assert nt.nt_rmsnorm_rows(M, 8, nt.NT_F16, -1.0, p, None, p, None) == 4      # eps < 0
+    assert nt.nt_softmax_rows(M, N, nt.NT_F32, p, p, None, 0, None) == 1         # needs a workspace
+    wsb = nt.nt_softmax_workspace_bytes(M, N, nt.NT_F32)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    assert nt.nt_softmax_rows(M, N, nt.NT_F32, p, p, ws.data_ptr(), wsb - 8, None) == 6
+    assert nt.nt_layernorm_rows(M, N, nt.NT_F32, 1e-5, p, None, None, p, None, None, None) == 2
+    torch.cuda.synchronize()

@@ -1,0 +1,151 @@
+"""Host side of the C ABI, checked without a GPU: the library loads, exports
+every function include/nt.h declares, validates arguments before touching
+the device, and plans launches as documented.  The pointers passed here are
+never dereferenced: every call is expected to fail validation first."""
+import os
+import re
+
+import pytest
+
+import row_wise_reductions_amd as nt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nt.h")
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+F32, F16, BF16 = nt.NT_F32, nt.NT_F16, nt.NT_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_matches_exports():
+    names = declared_functions()
+    assert set(names) == set(nt.EXPORTED), names
+    L = nt.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported by libnt.so"
+
+
+def test_exports_are_c_symbols():
+    out = os.popen(f"nm -D --defined-only {nt.LIB_PATH}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), f"{n} is not an extern \"C\" text symbol"
+
+
+def test_status_strings():
+    for code in range(8):
+        s = nt.nt_status_string(code)
+        assert s and s != "unknown status"
+    assert nt.nt_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: nt.nt_softmax_rows(4, 8, 7, FAKE, FAKE, None, 0, None), 3),
+    (lambda: nt.nt_softmax_rows(-1, 8, F32, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_rows(4, 0, F32, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_rows(4, 1 << 31, F32, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_rows(1 << 40, 1 << 30, F32, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_rows(4, 8, F32, None, FAKE, None, 0, None), 1),
+    (lambda: nt.nt_softmax_rows(4, 8, F32, FAKE, None, None, 0, None), 1),
+    (lambda: nt.nt_softmax_rows(4, 8, F32, FAKE + 2, FAKE, None, 0, None), 5),
+    (lambda: nt.nt_softmax_rows(4, 8, F16, FAKE, FAKE + 1, None, 0, None), 5),
+    (lambda: nt.nt_softmax_rows(4, 1 << 20, F32, FAKE, FAKE, None, 1 << 20, None), 1),
+    (lambda: nt.nt_softmax_rows(4, 1 << 20, F32, FAKE, FAKE, FAKE + 4, 1 << 20, None), 5),
+    (lambda: nt.nt_softmax_rows(4, 1 << 20, F32, FAKE, FAKE, FAKE, 8, None), 6),
+    (lambda: nt.nt_layernorm_rows(4, 8, F32, float("nan"), FAKE, None, None, FAKE, None, None, None), 4),
+    (lambda: nt.nt_layernorm_rows(4, 8, F32, float("inf"), FAKE, None, None, FAKE, None, None, None), 4),
+    (lambda: nt.nt_layernorm_rows(4, 8, F32, -1e-5, FAKE, None, None, FAKE, None, None, None), 4),
+    (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, FAKE + 1, None, FAKE, None, None, None), 5),
+    (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, FAKE + 1, FAKE, None, None, None), 5),
+    (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, None, FAKE, FAKE + 2, None, None), 5),
+    (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, None, FAKE, None, FAKE + 2, None), 5),
+    (lambda: nt.nt_layernorm_rows(4, 1 << 20, F16, 1e-5, FAKE, None, None, FAKE, None, None, None), 2),
+    (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 1, FAKE, None), 5),
+    (lambda: nt.nt_rmsnorm_rows(4, 8, 3, 1e-6, FAKE, None, FAKE, None), 3),
+    (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, None, None, FAKE, None), 1),
+    (lambda: nt.nt_rmsnorm_rows(4, 65536 * 2, BF16, 1e-6, FAKE, None, FAKE, None), 2),
+])
+def test_validation_before_launch(call, code):
+    assert call() == code
+
+
+def test_empty_is_noop():
+    assert nt.nt_softmax_rows(0, 8, F32, None, None, None, 0, None) == 0
+    assert nt.nt_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None) == 0
+    assert nt.nt_rmsnorm_rows(0, 8, F32, 1e-6, None, None, None, None) == 0
+    # a bad eps is still an error for an empty call
+    assert nt.nt_rmsnorm_rows(0, 8, F32, -1.0, None, None, None, None) == 4
+
+
+def test_workspace_bytes():
+    assert nt.nt_softmax_workspace_bytes(1024, 781, F32) == 0          # single pass
+    assert nt.nt_softmax_workspace_bytes(131072, 4096, BF16) == 0
+    # 1 MiB fp32 rows: 16 chunks of 64 KiB (+1 for a misaligned head) per row
+    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 17 * 8
+    assert nt.nt_softmax_workspace_bytes(-1, 8, F32) == 0
+    assert nt.nt_softmax_workspace_bytes(4, 8, 9) == 0
+
+
+def test_plans_of_the_workloads():
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1024, 781, F32, True)     # 3124-byte rows: misaligned
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["aligned"]) == (0, 1, 4, 0)
+    assert p["rows_per_block"] == 4 and p["grid"] == 256
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 4096, F16, True)
+    assert (p["split"], p["aligned"]) == (0, 1) and 64 * p["waves_per_row"] * p["chunks_per_lane"] >= 512
+    p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16384, 8192, BF16, True)
+    assert p["split"] == 0 and 64 * p["waves_per_row"] * p["chunks_per_lane"] >= 1024
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
+    assert p["split"] == 0
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
+    assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 64 * 16
+    assert p["workspace_bytes"] == 64 * 16 * 8
+
+
+def test_plan_capacity_covers_row():
+    for dt, e in ((F32, 4), (F16, 2), (BF16, 2)):
+        for N in (1, 7, 64, 255, 256, 781, 1024, 4097, 8192, 30000, 65536):
+            for al in (True, False):
+                if N == 65536 and not al:
+                    continue          # one chunk past the widest shape (test_norm_width_limits)
+                p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 8, N, dt, al)
+                vec = 16 // e
+                need = N // vec if (al and (N * e) % 16 == 0) else (N + 2 * vec - 2) // vec
+                if p["split"] == 0:
+                    assert 64 * p["waves_per_row"] * p["chunks_per_lane"] >= need, (dt, N, al, p)
+
+
+def test_norm_width_limits():
+    # the widest single-pass row: 256 KiB fp32 / 128 KiB 16-bit, aligned
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, F32, True)["split"] == 0
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, BF16, True)["split"] == 0
+    # a misaligned row of that width touches one more chunk and is rejected
+    with pytest.raises(nt.NtError):
+        nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, BF16, False)
+    with pytest.raises(nt.NtError):
+        nt.nt_plan_launch(nt.NT_OP_RMSNORM, 1, 65537, F32, True)
+    # softmax takes the split path instead
+    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1, 65537, F32, True)["split"] == 1
+
+
+def test_grid_fits_dispatch_packet():
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1 << 34, 8, F32, True)
+    assert p["grid"] * p["threads_per_block"] <= 1 << 31
+    with pytest.raises(nt.NtError):   # split path cannot stride: too many (row, chunk) pairs
+        nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1 << 24, 1 << 20, F32, True)
+
+
+def test_env_overrides(monkeypatch):
+    monkeypatch.setenv("NT_FORCE_SHAPE", "4,4")
+    p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 8192, BF16, True)
+    assert (p["waves_per_row"], p["chunks_per_lane"]) == (4, 4)
+    monkeypatch.setenv("NT_FORCE_SHAPE", "1,1")          # too small for the row: ignored
+    p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 8192, BF16, True)
+    assert 64 * p["waves_per_row"] * p["chunks_per_lane"] >= 1024
+    monkeypatch.delenv("NT_FORCE_SHAPE")
+    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 16, 4096, F32, True)
+    assert p["split"] == 1 and p["row_chunks"] == 1
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 4096, F32, True)["split"] == 0
