@@ -163,6 +163,28 @@ def traffic_for(kernel_name, launches_bytes):
     return None if e is None else e.get("hbm_bytes_per_call")
 
 
+def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
+    """Attainable-bandwidth reference: a plain copy kernel of known size
+    (read nbytes, write nbytes), rotating 4 buffer pairs."""
+    n = nbytes // 4
+    src = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(4)]
+    dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for i in range(warmup):
+        dst[i % 4].copy_(src[i % 4])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    durs = []
+    for i in range(steps):
+        a.record()
+        dst[i % 4].copy_(src[i % 4])
+        b.record()
+        b.synchronize()
+        durs.append(a.elapsed_time(b))
+    ms = statistics.median(durs)
+    print(json.dumps({"calibration": "torch copy_ fp32", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "median_ms": round(ms, 5), "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -170,6 +192,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy (torch copy_) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, so a "
@@ -184,6 +208,9 @@ def main():
 
     nt.lib()   # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate:
+        calibrate_copy(torch, args.steps, args.warmup)
+        return
     names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]
     suite = args.only is None
 

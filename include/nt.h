@@ -34,8 +34,11 @@
  *             to the element size (mean/rstd to 4 bytes, workspace to 8);
  *             16-byte alignment is NOT required (misaligned rows are handled).
  *  eps        must be finite and >= 0; it is added inside the square root.
- *  Shapes     M == 0 is a no-op returning NT_OK.  M < 0, N <= 0, or M*N
- *             overflowing int64 returns NT_ERR_SHAPE.
+ *  Shapes     M == 0 is a no-op returning NT_OK.  M < 0, N <= 0,
+ *             N > INT32_MAX, or M*N overflowing int64 returns NT_ERR_SHAPE.
+ *             Any row width is accepted: rows too wide to hold on chip take
+ *             the split online path (softmax, needs a workspace) or a looped
+ *             kernel that reads the row twice (LayerNorm, RMSNorm).
  *  Ownership  the caller allocates and owns every buffer, including the
  *             workspace (which need not be zeroed).  The library allocates and
  *             frees no device memory and keeps no pointer after returning.
@@ -71,7 +74,7 @@ typedef enum { NT_F32 = 0, NT_F16 = 1, NT_BF16 = 2 } nt_dtype;
 typedef enum {
     NT_OK = 0,
     NT_ERR_NULL = 1,       /* a required pointer is NULL                       */
-    NT_ERR_SHAPE = 2,      /* M < 0, N <= 0, or M*N overflows                  */
+    NT_ERR_SHAPE = 2,      /* M < 0, N <= 0, N > INT32_MAX, or M*N overflows   */
     NT_ERR_DTYPE = 3,      /* dt is not one of nt_dtype                        */
     NT_ERR_EPS = 4,        /* eps is negative, infinite or NaN                 */
     NT_ERR_ALIGN = 5,      /* a pointer is not aligned to its element size     */
@@ -129,7 +132,9 @@ const char *nt_status_string(nt_status s);
 typedef enum { NT_OP_SOFTMAX = 0, NT_OP_LAYERNORM = 1, NT_OP_RMSNORM = 2 } nt_op;
 
 typedef struct {
-    int32_t split;            /* 0: single pass, row held on chip; 1: split online path */
+    int32_t split;            /* 0: single pass, row held on chip; 1: split online softmax
+                                 (per-chunk workgroups and a workspace); 2: looped norm
+                                 kernel (one workgroup streams a wide row twice)          */
     int32_t waves_per_row;    /* 64-lane waves cooperating on one row (or one chunk)    */
     int32_t chunks_per_lane;  /* 16-byte chunks each lane holds                         */
     int32_t rows_per_block;   /* rows one workgroup processes side by side              */

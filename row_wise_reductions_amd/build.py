@@ -35,9 +35,9 @@ UNITS = [
 ]
 
 
-def _compile(unit, extra_flags=()):
+def _compile(unit, extra_flags=(), build_dir=BUILD_DIR):
     obj, src, defs = unit
-    out = os.path.join(BUILD_DIR, obj)
+    out = os.path.join(build_dir, obj)
     cmd = [HIPCC, *COMMON, *defs, *extra_flags, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -45,19 +45,19 @@ def _compile(unit, extra_flags=()):
     return out
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = True, extra_flags=(), out: str = LIB_PATH, build_dir: str = BUILD_DIR) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(UNITS), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda u: _compile(u, extra_flags), UNITS))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda u: _compile(u, extra_flags, build_dir), UNITS))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -10,30 +10,65 @@ namespace ntk {
 namespace {
 
 constexpr int DT = NTK_DT;
-// 16-bit types hold 8 values per chunk: K = 16 would need 128 values per
-// lane, so the widest per-lane footprint is K = 8 for them.
+// fp32 holds 4 values per chunk, 16-bit types 8.
 constexpr bool kWide = dt_info<DT>::VEC == 4;
 
-template <int OP, int W, int K>
-hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+template <int OP, int W, int K, bool PR>
+hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     constexpr int T = GroupShape<W>::THREADS;
     if (al)
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true, PR>), dim3((uint32_t)grid), dim3(T), 0, s, a);
     else
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false, PR>), dim3((uint32_t)grid), dim3(T), 0, s, a);
     return hipGetLastError();
+}
+
+// Norms with every parameter vector present take the specialised PR kernel.
+template <int OP, int W, int K>
+hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    if constexpr (OP == OP_SOFTMAX) {
+        return go_pr<OP, W, K, false>(al, a, grid, s);
+    } else {
+        const bool pr = a.p0 != nullptr && (OP == OP_RMSNORM || a.p1 != nullptr);
+        return pr ? go_pr<OP, W, K, true>(al, a, grid, s) : go_pr<OP, W, K, false>(al, a, grid, s);
+    }
+}
+
+// Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
+// arithmetic needs twice the registers), RMSNorm and softmax 64.  Wider
+// shapes would spill registers and are not built.
+template <int OP, int K>
+constexpr bool shape_built() {
+    constexpr int V = K * dt_info<DT>::VEC;
+    return OP == OP_LAYERNORM ? V <= 16 : V <= 64;
 }
 
 template <int OP>
 hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
-#define NTK_CASE(w, k) \
-    if (W == w && K == k) return go<OP, w, k>(al, a, grid, s);
-    NTK_CASE(1, 1) NTK_CASE(1, 2) NTK_CASE(1, 4) NTK_CASE(1, 8)
-    NTK_CASE(2, 8) NTK_CASE(4, 4) NTK_CASE(4, 8) NTK_CASE(8, 8) NTK_CASE(16, 8)
-    if constexpr (kWide) {
-        NTK_CASE(1, 16) NTK_CASE(16, 16)
+    // A 1024-thread workgroup caps a wave at 128 registers: W = 16 is built
+    // only with one or two chunks per lane.
+#define NTK_CASE(w, k)                                          \
+    if (W == w && K == k) {                                     \
+        if constexpr (shape_built<OP, k>()) return go<OP, w, k>(al, a, grid, s); \
+        return hipErrorInvalidValue;                            \
     }
+    NTK_CASE(1, 1) NTK_CASE(1, 2) NTK_CASE(1, 4) NTK_CASE(1, 8) NTK_CASE(1, 16)
+    NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
+    NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4) NTK_CASE(8, 8) NTK_CASE(8, 16)
+    NTK_CASE(16, 1) NTK_CASE(16, 2)
 #undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int OP>
+hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    if (W == 8 && K == 4) {
+        if (al)
+            hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+        return hipGetLastError();
+    }
     return hipErrorInvalidValue;
 }
 
@@ -57,11 +92,20 @@ hipError_t split_go(bool al, const RowArgs &a, hipStream_t s) {
 hipError_t split(int W, int K, bool al, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k) \
     if (W == w && K == k) return split_go<w, k>(al, a, s);
-    NTK_CASE(4, 8) NTK_CASE(8, 8)
+    NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8) NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4)
+    NTK_CASE(8, 8)
     if constexpr (kWide) {
         NTK_CASE(4, 16) NTK_CASE(8, 16)
     }
 #undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t looped_any(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    switch (op) {
+    case OP_LAYERNORM: return looped<OP_LAYERNORM>(W, K, al, a, grid, s);
+    case OP_RMSNORM: return looped<OP_RMSNORM>(W, K, al, a, grid, s);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -81,16 +125,25 @@ hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, 
     return resident_any(op, W, K, al, a, grid, s);
 }
 hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return looped_any(op, W, K, al, a, grid, s);
+}
 #elif NTK_DT == 1
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
 hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return looped_any(op, W, K, al, a, grid, s);
+}
 #else
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
 hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
+    return looped_any(op, W, K, al, a, grid, s);
+}
 #endif
 
 }  // namespace ntk

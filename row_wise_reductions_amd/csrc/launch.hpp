@@ -16,6 +16,12 @@ hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, 
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
 
+// Launch the looped one-workgroup-per-row kernel (LayerNorm / RMSNorm rows
+// wider than the single-pass shapes).
+hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
+
 // Launch the two split-softmax kernels (partials, then merge + write).
 hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s);
 hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s);

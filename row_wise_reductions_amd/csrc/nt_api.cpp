@@ -12,8 +12,9 @@
 //     ("Triton: Block-Level GPU Programming Without CUDA", section "How Flash
 //     Attention Uses Triton"): chunks of one workgroup each, partial
 //     (max, denominator) pairs in the caller's workspace, then a merge.
-//     LayerNorm and RMSNorm rows wider than the widest shape are rejected
-//     with NT_ERR_SHAPE.
+//     LayerNorm and RMSNorm rows wider than the widest shape take a looped
+//     kernel: one workgroup per row reads the row twice in tiles (statistics,
+//     then output), so no workspace is needed.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,12 +31,38 @@ struct Shape {
     int W, K;
 };
 
-// Single-pass shapes in order of capacity (64*W*K chunks of 16 bytes).
-const Shape kMenu32[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 8}, {4, 8}, {8, 8}, {16, 8}, {16, 16}};
-const Shape kMenu16[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {2, 8}, {4, 8}, {8, 8}, {16, 8}};
-// Split-path chunk shape: 64 KiB of fp32 (or 32 KiB of 16-bit) per workgroup.
-const Shape kSplit32 = {4, 16};
-const Shape kSplit16 = {4, 8};
+// Single-pass shapes in order of capacity (64*W*K chunks of 16 bytes).  None
+// of them spills registers.  A lane holds at most 64 values of a row, and
+// LayerNorm at most 16 (its fp64 arithmetic needs more registers); wider
+// LayerNorm and RMSNorm rows take the looped kernel, wider softmax rows the
+// split path.
+struct Menu {
+    const Shape *s;
+    int n;
+};
+// Chosen from launch-shape sweeps on MI355X: about one or two 16-byte chunks
+// per lane with up to 8 waves per row stream best.
+const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
+const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
+const Shape kRms16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
+const Shape kLn16[] = {{1, 1}, {1, 2}, {4, 1}, {4, 2}, {8, 2}};
+#define NT_MENU(a) Menu{a, (int)(sizeof(a) / sizeof(*(a)))}
+Menu menu_for(nt_op op, nt_dtype dt) {
+    const bool wide = dt == NT_F32;
+    switch (op) {
+    case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : NT_MENU(kSoftmax16);
+    case NT_OP_RMSNORM: return wide ? NT_MENU(kRms32) : NT_MENU(kRms16);
+    default: return wide ? NT_MENU(kLn32) : NT_MENU(kLn16);
+    }
+}
+#undef NT_MENU
+// Split-path chunk shape: 16 KiB per workgroup (4 waves, 4 chunks per lane).
+const Shape kSplit32 = {4, 4};
+const Shape kSplit16 = {4, 4};
+// Looped norm kernel: 512 threads, tiles of 4 chunks per lane.
+const Shape kLooped = {8, 4};
 
 int elem_bytes(nt_dtype dt) { return dt == NT_F32 ? 4 : 2; }
 int elems_per_chunk(nt_dtype dt) { return 16 / elem_bytes(dt); }
@@ -77,21 +104,20 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
-    const Shape *menu = dt == NT_F32 ? kMenu32 : kMenu16;
-    const int nmenu = dt == NT_F32 ? (int)(sizeof kMenu32 / sizeof *kMenu32)
-                                   : (int)(sizeof kMenu16 / sizeof *kMenu16);
+    const Menu menu = menu_for(op, dt);
     const char *force = std::getenv("NT_FORCE_PATH");
     const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
+    const bool force_loop = op != NT_OP_SOFTMAX && force && std::strcmp(force, "looped") == 0;
 
     Shape pick = {0, 0};
-    if (!force_split) {
+    if (!force_split && !force_loop) {
         Shape o;
         if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch) {
             pick = o;
         } else {
-            for (int i = 0; i < nmenu; ++i)
-                if ((int64_t)64 * menu[i].W * menu[i].K >= nch) {
-                    pick = menu[i];
+            for (int i = 0; i < menu.n; ++i)
+                if ((int64_t)64 * menu.s[i].W * menu.s[i].K >= nch) {
+                    pick = menu.s[i];
                     break;
                 }
         }
@@ -111,7 +137,17 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         p->grid = grid;
         return NT_OK;
     }
-    if (op != NT_OP_SOFTMAX) return NT_ERR_SHAPE;
+    if (op != NT_OP_SOFTMAX) {
+        // one workgroup per row, the row streamed twice in tiles
+        p->split = 2;
+        p->waves_per_row = kLooped.W;
+        p->chunks_per_lane = kLooped.K;
+        p->rows_per_block = 1;
+        p->threads_per_block = 64 * kLooped.W;
+        const int64_t max_grid = ((int64_t)1 << 31) / p->threads_per_block;
+        p->grid = M < max_grid ? M : max_grid;
+        return NT_OK;
+    }
     Shape s = dt == NT_F32 ? kSplit32 : kSplit16;
     Shape o;
     if (env_shape("NT_SPLIT_SHAPE", &o)) s = o;
@@ -147,6 +183,16 @@ hipError_t launch_resident(nt_dtype dt, int op, const nt_plan &p, const ntk::Row
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_looped(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
+    const bool al = p.aligned != 0;
+    switch (dt) {
+    case NT_F32: return ntk::launch_looped_f32(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    case NT_F16: return ntk::launch_looped_f16(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    case NT_BF16: return ntk::launch_looped_bf16(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
     const bool al = p.aligned != 0;
     switch (dt) {
@@ -159,9 +205,9 @@ hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hi
 
 void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p) {
     std::fprintf(stderr,
-                 "[nt] %s M=%lld N=%lld dt=%d: %s W=%d K=%d rows/block=%d threads=%d aligned=%d grid=%lld"
+                 "[nt] %s M=%lld N=%lld dt=%d: path %s W=%d K=%d rows/block=%d threads=%d aligned=%d grid=%lld"
                  " chunks/row=%lld ws=%lld\n",
-                 what, (long long)M, (long long)N, (int)dt, p.split ? "split" : "single-pass", p.waves_per_row,
+                 what, (long long)M, (long long)N, (int)dt, p.split == 1 ? "split" : p.split == 2 ? "looped" : "single-pass", p.waves_per_row,
                  p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, (long long)p.grid,
                  (long long)p.row_chunks, (long long)p.workspace_bytes);
 }
@@ -171,7 +217,9 @@ nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, con
     if (debug_on()) debug_print(op == NT_OP_SOFTMAX ? "softmax" : op == NT_OP_LAYERNORM ? "layernorm" : "rmsnorm",
                                 M, N, dt, p);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = p.split ? launch_split(dt, p, a, s) : launch_resident(dt, (int)op, p, a, s);
+    hipError_t e = p.split == 1   ? launch_split(dt, p, a, s)
+                   : p.split == 2 ? launch_looped(dt, (int)op, p, a, s)
+                                  : launch_resident(dt, (int)op, p, a, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         if (debug_on()) std::fprintf(stderr, "[nt] launch failed: %s\n", hipGetErrorString(e));
@@ -201,7 +249,7 @@ const char *nt_status_string(nt_status s) {
     switch (s) {
     case NT_OK: return "ok";
     case NT_ERR_NULL: return "a required pointer is NULL";
-    case NT_ERR_SHAPE: return "invalid shape (M < 0, N <= 0, N > INT32_MAX, size overflow, or row too wide)";
+    case NT_ERR_SHAPE: return "invalid shape (M < 0, N <= 0, N > INT32_MAX, or size overflow)";
     case NT_ERR_DTYPE: return "unknown element type";
     case NT_ERR_EPS: return "eps must be finite and >= 0";
     case NT_ERR_ALIGN: return "pointer not aligned to its element size";
@@ -242,6 +290,8 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void
     a.y = static_cast<char *>(y);
     a.M = M;
     a.N = (int32_t)N;
+    a.inv_n = (float)(1.0 / (double)N);
+    a.inv_nd = 1.0 / (double)N;
     if (p.split) {
         if (!workspace) return NT_ERR_NULL;
         if (!aligned_to(workspace, 8)) return NT_ERR_ALIGN;
@@ -278,6 +328,8 @@ nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const 
     a.rstd = rstd;
     a.M = M;
     a.N = (int32_t)N;
+    a.inv_n = (float)(1.0 / (double)N);
+    a.inv_nd = 1.0 / (double)N;
     a.eps = eps;
     return run(NT_OP_LAYERNORM, M, N, dt, p, a, stream);
 }
@@ -300,6 +352,8 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const vo
     a.p0 = static_cast<const char *>(weight);
     a.M = M;
     a.N = (int32_t)N;
+    a.inv_n = (float)(1.0 / (double)N);
+    a.inv_nd = 1.0 / (double)N;
     a.eps = eps;
     return run(NT_OP_RMSNORM, M, N, dt, p, a, stream);
 }

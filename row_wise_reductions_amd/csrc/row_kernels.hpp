@@ -56,10 +56,12 @@ struct RowArgs {
     float *mean;         // LayerNorm statistics outputs; may be null
     float *rstd;
     float2 *ws;          // split softmax: (max, denominator) per (row, chunk)
+    double inv_nd;       // 1/N in fp64
     int64_t M;
     int32_t N;
     int32_t P;           // split softmax: chunks per row
     float eps;
+    float inv_n;         // 1/N in fp32
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -72,11 +74,58 @@ constexpr float LOG2E = 1.4426950408889634f;
 // 16-byte chunk <-> fp32 values
 // ---------------------------------------------------------------------------
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Build-time memory-policy switches (see ld16_nt, st16_nt and xcd_band).
+// Measured on MI355X: streaming loads and stores together add 6-35% on the
+// row kernels; XCD banding helps some shapes and costs others up to 8%, so
+// it is off.
+#ifndef NTK_NT_LOADS
+#define NTK_NT_LOADS 1
+#endif
+#ifndef NTK_NT_STORES
+#define NTK_NT_STORES 1
+#endif
+#ifndef NTK_XCD_BAND
+#define NTK_XCD_BAND 0
+#endif
+
 __device__ __forceinline__ uint4 ld16(const char *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 __device__ __forceinline__ void st16(char *p, uint4 v) {
     *reinterpret_cast<uint4 *>(p) = v;
+}
+// Streaming (non-temporal) 16-byte load and store for row data that is
+// touched once: they keep single-use lines from displacing reused ones
+// (the parameter vectors) and measurably raise read+write HBM throughput.
+__device__ __forceinline__ uint4 ld16_nt(const char *p) {
+#if NTK_NT_LOADS
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+#else
+    return ld16(p);
+#endif
+}
+__device__ __forceinline__ void st16_nt(char *p, uint4 v) {
+#if NTK_NT_STORES
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+#else
+    st16(p, v);
+#endif
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+// b mod 8).  Renumbering so that XCD x receives a contiguous band of row
+// blocks gives each XCD's L2 and memory queues a sequential stream.
+__device__ __forceinline__ int64_t xcd_band(int64_t b, int64_t G) {
+#if NTK_XCD_BAND
+    return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+#else
+    (void)G;
+    return b;
+#endif
 }
 
 template <int DT>
@@ -93,11 +142,14 @@ __device__ __forceinline__ void unpack(uint4 r, float (&f)[dt_info<DT>::VEC]) {
             f[2 * i + 1] = p.y;
         }
     } else {
-        // bf16 is the top half of a binary32: widening is a shift.
+        // bf16 is the top half of a binary32: the widening is a shift, but
+        // written as a conversion the compiler knows the result is a
+        // canonical float and needs no quieting before v_max.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-            f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+            f32x2 p = __builtin_convertvector(__builtin_bit_cast(bf16x2, w[i]), f32x2);
+            f[2 * i] = p.x;
+            f[2 * i + 1] = p.y;
         }
     }
 }
@@ -190,6 +242,10 @@ __device__ __forceinline__ double dpp(double v) {
     const int hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
+template <int CTRL>
+__device__ __forceinline__ double2 dpp(double2 v) {
+    return double2{dpp<CTRL>(v.x), dpp<CTRL>(v.y)};
+}
 __device__ __forceinline__ float readlane(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -200,8 +256,16 @@ __device__ __forceinline__ double readlane(double v, int l) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+__device__ __forceinline__ double readlane(double v, int l);
+__device__ __forceinline__ double2 readlane(double2 v, int l) {
+    return double2{readlane(v.x, l), readlane(v.y, l)};
+}
+
 struct SumOp {
     template <class V> __device__ __forceinline__ V operator()(V a, V b) const { return a + b; }
+    __device__ __forceinline__ double2 operator()(double2 a, double2 b) const {
+        return double2{a.x + b.x, a.y + b.y};
+    }
 };
 struct MaxOp {
     __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
@@ -302,14 +366,97 @@ __device__ __forceinline__ void store_chunk(const RowGeom<DT, AL> &g, char *yr, 
                                             bool yvec, uint4 v) {
     if (c < g.nch) {
         if constexpr (AL) {
-            st16(yr + c * 16, v);
+            st16_nt(yr + c * 16, v);
         } else {
             if (yvec && g.full(c, N))
-                st16(yr - (int64_t)g.head * dt_info<DT>::E + c * 16, v);
+                st16_nt(yr - (int64_t)g.head * dt_info<DT>::E + c * 16, v);
             else
                 scatter<DT>(yr, g.col0(c), N, v);
         }
     }
+}
+
+// First step of a row load: the K chunks a lane owns, every vector load in
+// flight at once.  Each lane issues each of its K loads unconditionally,
+// with the address clamped into the row's whole chunks (a slot past the row
+// re-reads a chunk that is already in cache); finish_row() later replaces
+// out-of-row slots with the fill pattern and gathers the partial first and
+// last chunk of a misaligned row element by element.
+template <int DT, bool AL, int K, int TPR, bool NT = true>
+__device__ __forceinline__ void load_row(uint4 (&raw)[K], const RowGeom<DT, AL> &g, int t, int32_t N,
+                                         int64_t cbase = 0) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    // whole chunks of the row: [f0, f1] (empty when f1 < f0)
+    const int64_t f0 = AL ? 0 : (g.head ? 1 : 0);
+    const int64_t f1 = AL ? g.nch - 1 : ((int64_t)g.head + N) / VEC - 1;
+    // aligned rows always have a whole chunk (N >= 1): no branch, so the
+    // loaded registers need no copy (a copy would wait for the load)
+    if (AL || f1 >= f0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            int64_t c = cbase + (int64_t)k * TPR + t;
+            c = c < f0 ? f0 : (c > f1 ? f1 : c);
+            raw[k] = NT ? ld16_nt(g.xb + c * 16) : ld16(g.xb + c * 16);
+        }
+    }
+}
+
+// Second step of a row load, after every other load meant to be in flight
+// with the row (the parameter vectors) has been issued: out-of-row slots get
+// the fill pattern, partial chunks of a misaligned row are gathered, and an
+// empty asm statement pins the packed values, so their widening is not
+// moved into these branches and widened values are known to be canonical
+// floats (no quieting before v_max).
+template <int DT, bool AL, int K, int TPR>
+__device__ __forceinline__ void finish_row(uint4 (&raw)[K], const RowGeom<DT, AL> &g, const char *xr, int t,
+                                           int32_t N, uint32_t fill, int64_t cbase = 0) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    const int64_t f0 = AL ? 0 : (g.head ? 1 : 0);
+    const int64_t f1 = AL ? g.nch - 1 : ((int64_t)g.head + N) / VEC - 1;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t c = cbase + (int64_t)k * TPR + t;
+        if (AL && cbase + ((int64_t)k + 1) * TPR <= g.nch) continue;   // whole slice: uniform
+        if (c < f0 || c > f1 || f1 < f0) {
+            if (!AL && c < g.nch) {
+                raw[k] = gather<DT>(xr, g.col0(c), N, fill);
+            } else {
+                raw[k] = make_uint4(fill, fill, fill, fill);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        asm volatile("" : "+v"(raw[k].x), "+v"(raw[k].y), "+v"(raw[k].z), "+v"(raw[k].w));
+}
+
+// Load the parameter-vector chunks that line up with the row's chunks (the
+// same clamped, branch-free scheme; misaligned rows read per element).
+template <int DT, bool AL, int K, int TPR>
+__device__ __forceinline__ void load_params(uint4 (&out)[K], const RowGeom<DT, AL> &g, const char *p, int t,
+                                            int32_t N, int64_t cbase = 0) {
+    if constexpr (AL) {
+        const int64_t last = g.nch - 1;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            int64_t c = cbase + (int64_t)k * TPR + t;
+            c = c > last ? last : c;
+            out[k] = ld16(p + c * 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) out[k] = load_param<DT, AL>(g, p, cbase + (int64_t)k * TPR + t, N);
+    }
+}
+
+template <int DT, bool AL, int TPR>
+__device__ __forceinline__ void store_slice(const RowGeom<DT, AL> &g, char *yr, int k, int t, int32_t N, bool yvec,
+                                            uint4 v, int64_t cbase = 0) {
+    const int64_t c = cbase + (int64_t)k * TPR + t;
+    if (AL && cbase + ((int64_t)k + 1) * TPR <= g.nch)
+        st16_nt(yr + c * 16, v);
+    else
+        store_chunk<DT, AL>(g, yr, c, N, yvec, v);
 }
 
 // Is element i of chunk c a column of the row?
@@ -323,15 +470,50 @@ __device__ __forceinline__ bool in_row(const RowGeom<DT, AL> &g, int64_t c, int 
     }
 }
 
-__device__ __forceinline__ float fast_exp(float t) {
-    // e^t = 2^(t * log2 e); v_exp_f32 evaluates 2^x.
-    return __builtin_amdgcn_exp2f(t * LOG2E);
+// The value of the first element packed in a storage word, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float elem_of_word(uint32_t w) {
+    if constexpr (DT == DT_F32) return __builtin_bit_cast(float, w);
+    else if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(f16x2, w).x;
+    else return __builtin_bit_cast(float, w << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row scalar helpers
+// ---------------------------------------------------------------------------
+
+// 1/x and 1/sqrt(x) in fp32 from the hardware approximations (v_rcp_f32,
+// v_rsq_f32: about 1 ulp), used once per row.
+__device__ __forceinline__ float rcp_approx(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float rsq_approx(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// 1/sqrt(v) in fp64: hardware estimate refined by two Newton steps
+// r <- r * (3 - v r^2) / 2, each roughly doubling the correct bits.
+__device__ __forceinline__ double rsqrt_f64(double v) {
+    if (v == 0.0) return __builtin_inf();      // eps = 0 and a constant row
+    double r = __builtin_amdgcn_rsq(v);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r = r * __builtin_fma(-0.5 * v, r * r, 1.5);
+    return r;
+}
+
+// Per-lane max over K*VEC widened values (padding holds -inf).
+template <int K, int VEC>
+__device__ __forceinline__ float lane_max(const float (&v)[K][VEC]) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; i += 2) m = __builtin_fmaxf(m, __builtin_fmaxf(v[k][i], v[k][i + 1]));
+    return m;
 }
 
 // ---------------------------------------------------------------------------
 // Single-pass kernel: one row per group of W waves, row held in VGPRs.
 // W == 1: four independent rows per 256-thread workgroup, no LDS or barrier.
 // W >= 2: one row per workgroup of 64*W threads.
+// Each element is widened to fp32 once; every pass then works on the
+// widened registers.
 // ---------------------------------------------------------------------------
 
 template <int W>
@@ -340,11 +522,15 @@ struct GroupShape {
     static constexpr int THREADS = 64 * W * G;
 };
 
-template <int OP, int DT, int W, int K, bool AL>
+// PR (norms only): the parameter vectors are all present (gamma and beta for
+// LayerNorm, the weight for RMSNorm); otherwise absent ones act as identity.
+template <int OP, int DT, int W, int K, bool AL, bool PR>
 __global__ void __launch_bounds__(GroupShape<W>::THREADS)
 row_resident(RowArgs a) {
     using I = dt_info<DT>;
     constexpr int VEC = I::VEC, TPR = 64 * W, G = GroupShape<W>::G;
+    // LayerNorm keeps an fp64 copy of its values when they are few per lane
+    constexpr bool CACHE_D = (OP == OP_LAYERNORM) && (K * VEC <= 16);
     const int tid = threadIdx.x;
     const int g = (W == 1) ? (tid >> 6) : 0;
     const int t = (W == 1) ? (tid & 63) : tid;
@@ -352,13 +538,14 @@ row_resident(RowArgs a) {
     const int32_t N = a.N;
     const int64_t rowbytes = (int64_t)N * I::E;
     const uint32_t fill = (OP == OP_SOFTMAX) ? I::NEG_INF_WORD : 0u;
+    const bool has_p0 = PR || a.p0 != nullptr, has_p1 = PR || a.p1 != nullptr;
 
     __shared__ float red_f[2][2][W];
-    __shared__ double red_d[2][2][W];
+    __shared__ double2 red_d2[2][W];
 
     const int64_t nrb = (a.M + G - 1) / G;
     int par = 0;
-    for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x, par ^= 1) {
+    for (int64_t rb = xcd_band(blockIdx.x, gridDim.x); rb < nrb; rb += gridDim.x, par ^= 1) {
         const int64_t row = rb * G + g;
         if (row >= a.M) break;   // only possible when W == 1 (no barriers there)
         const char *xr = a.x + row * rowbytes;
@@ -367,115 +554,247 @@ row_resident(RowArgs a) {
         bool yvec = true;
         if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
 
-        // ---- load the whole row: K chunks per lane, all in flight at once
-        uint4 raw[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) raw[k] = load_chunk<DT, AL>(geo, xr, (int64_t)k * TPR + t, N, fill);
-        uint4 p0[(OP == OP_SOFTMAX) ? 1 : K];
-        uint4 p1[(OP == OP_LAYERNORM) ? K : 1];
-        if constexpr (OP != OP_SOFTMAX) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t c = (int64_t)k * TPR + t;
-                p0[k] = a.p0 ? load_param<DT, AL>(geo, a.p0, c, N) : make_uint4(0, 0, 0, 0);
-                if constexpr (OP == OP_LAYERNORM)
-                    p1[k] = a.p1 ? load_param<DT, AL>(geo, a.p1, c, N) : make_uint4(0, 0, 0, 0);
+        // ---- issue every load of the row (and of the parameter vectors,
+        // which are L2 hits after the first rows) before using any of them
+        // LayerNorm pads with its pivot (the row's first element), which adds
+        // exactly nothing to the shifted sums; softmax pads with -inf, RMSNorm 0
+        uint32_t padw = fill;
+        if constexpr (OP == OP_LAYERNORM) {
+            if constexpr (I::E == 4) {
+                padw = *reinterpret_cast<const uint32_t *>(xr);
+            } else {
+                const uint32_t h = *reinterpret_cast<const uint16_t *>(xr);
+                padw = h | (h << 16);
             }
         }
+        uint4 raw[K];
+        load_row<DT, AL, K, TPR>(raw, geo, t, N);
+        constexpr int KP0 = (OP == OP_SOFTMAX) ? 1 : K;
+        constexpr int KP1 = (OP == OP_LAYERNORM) ? K : 1;
+        uint4 p0[KP0], p1[KP1];
+        if constexpr (OP != OP_SOFTMAX) {
+            if (has_p0) load_params<DT, AL, K, TPR>(p0, geo, a.p0, t, N);
+        }
+        if constexpr (OP == OP_LAYERNORM) {
+            if (has_p1) load_params<DT, AL, K, TPR>(p1, geo, a.p1, t, N);
+        }
+        finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw);
         float v[K][VEC];
 #pragma unroll
         for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
 
         if constexpr (OP == OP_SOFTMAX) {
-            // ---- max, shift, exp, sum, scale
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) mx = __builtin_fmaxf(mx, v[k][i]);
-            mx = group_allreduce<W>(mx, MaxOp(), red_f[par][0], wv, lane);
+            // ---- softmax.  With c = m*log2(e) rounded to fp32, every element
+            // is 2^(x*log2(e) - c): one fma (exact product, one rounding) and
+            // one v_exp_f32.  Shift invariance makes any shift exact, and c is
+            // within half an ulp of m*log2(e), so no term exceeds 2^(1e-7).
+            const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red_f[par][0], wv, lane);
+            const float c = mx * LOG2E;
             float s = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    v[k][i] = fast_exp(v[k][i] - mx);
+                    v[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -c));
                     s += v[k][i];
                 }
             s = group_allreduce<W>(s, SumOp(), red_f[par][1], wv, lane);
-            const float inv = 1.0f / s;
+            const float inv = rcp_approx(s);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) v[k][i] *= inv;
-                store_chunk<DT, AL>(geo, yr, (int64_t)k * TPR + t, N, yvec, pack<DT>(v[k]));
+                store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
             }
         } else if constexpr (OP == OP_RMSNORM) {
-            // ---- sum of squares (fp32), scale by the row's 1/rms and the weight
+            // ---- RMSNorm: sum of squares in fp32, y = (x * inv) * w
             float ss = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[k][i], v[k][i], ss);
             ss = group_allreduce<W>(ss, SumOp(), red_f[par][0], wv, lane);
-            const float inv = (float)(1.0 / __builtin_sqrt((double)ss / (double)N + (double)a.eps));
+            const float inv = rsq_approx(ss * a.inv_n + a.eps);
+            if (PR) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                float w[VEC];
-                if (a.p0) {
+                for (int k = 0; k < K; ++k) {
+                    float w[VEC];
                     unpack<DT>(p0[k], w);
-                } else {
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) w[i] = 1.0f;
+                    for (int i = 0; i < VEC; ++i) v[k][i] = (v[k][i] * inv) * w[i];
+                    store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
                 }
+            } else {
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) v[k][i] = (v[k][i] * inv) * w[i];
-                store_chunk<DT, AL>(geo, yr, (int64_t)k * TPR + t, N, yvec, pack<DT>(v[k]));
+                for (int k = 0; k < K; ++k) {
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) v[k][i] *= inv;
+                    store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
+                }
             }
         } else {
-            // ---- LayerNorm: row sums and the affine step in fp64
-            double s1 = 0.0;
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) s1 += (double)v[k][i];   // padding is 0
-            s1 = group_allreduce<W>(s1, SumOp(), red_d[par][0], wv, lane);
-            const double mean = s1 / (double)N;
-            double s2 = 0.0;
+            // ---- LayerNorm.  Statistics in one pass around the pivot p (the
+            // row's first element): S1 = sum(x - p), S2 = sum((x - p)^2) in
+            // fp64, so mean = p + S1/N and var = S2/N - (S1/N)^2.  For fp16 or
+            // bf16 input every x - p and S1 are exact in fp64; the cancellation
+            // in var costs about log2((p - mean)^2 / var) of fp64's 53 bits.
+            // The affine step is fp64 too: fp32 cannot keep y within one ulp
+            // of a 16-bit output where beta cancels (x - mean) * rstd * gamma.
+            const double pv = (double)elem_of_word<DT>(padw);
+            double dp[CACHE_D ? K : 1][CACHE_D ? VEC : 1];
+            double s1 = 0.0, s2 = 0.0;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    const double d = (double)v[k][i] - mean;
-                    s2 = in_row<DT, AL>(geo, (int64_t)k * TPR + t, i, N) ? __builtin_fma(d, d, s2) : s2;
+                    const double d = (double)v[k][i] - pv;    // padding gives 0
+                    if constexpr (CACHE_D) dp[k][i] = d;
+                    s1 += d;
+                    s2 = __builtin_fma(d, d, s2);
                 }
-            s2 = group_allreduce<W>(s2, SumOp(), red_d[par][1], wv, lane);
-            const double rstd = 1.0 / __builtin_sqrt(s2 / (double)N + (double)a.eps);
+            const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red_d2[par], wv, lane);
+            const double m1 = st.x * a.inv_nd;                  // mean - p
+            const double var = __builtin_fmax(st.y * a.inv_nd - m1 * m1, 0.0);
+            const double mean = pv + m1;
+            const double rstd = rsqrt_f64(var + (double)a.eps);
+            if constexpr (PR) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                float gm[VEC], bt[VEC];
-                if (a.p0) {
+                for (int k = 0; k < K; ++k) {
+                    float gm[VEC], bt[VEC];
                     unpack<DT>(p0[k], gm);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) gm[i] = 1.0f;
-                }
-                if (a.p1) {
                     unpack<DT>(p1[k], bt);
-                } else {
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) bt[i] = 0.0f;
+                    for (int i = 0; i < VEC; ++i) {
+                        const double d = (CACHE_D ? dp[CACHE_D ? k : 0][CACHE_D ? i : 0] : (double)v[k][i] - pv) - m1;
+                        v[k][i] = (float)__builtin_fma(d * rstd, (double)gm[i], (double)bt[i]);
+                    }
+                    store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
                 }
+            } else {
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) {
-                    const double d = ((double)v[k][i] - mean) * rstd;
-                    v[k][i] = (float)__builtin_fma(d, (double)gm[i], (double)bt[i]);
+                for (int k = 0; k < K; ++k) {
+                    float gm[VEC], bt[VEC];
+                    if (has_p0) unpack<DT>(p0[k], gm);
+                    if (has_p1) unpack<DT>(p1[k], bt);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) {
+                        const double d = (CACHE_D ? dp[CACHE_D ? k : 0][CACHE_D ? i : 0] : (double)v[k][i] - pv) - m1;
+                        const double g = has_p0 ? (double)gm[i] : 1.0;
+                        const double b = has_p1 ? (double)bt[i] : 0.0;
+                        v[k][i] = (float)__builtin_fma(d * rstd, g, b);
+                    }
+                    store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
                 }
-                store_chunk<DT, AL>(geo, yr, (int64_t)k * TPR + t, N, yvec, pack<DT>(v[k]));
             }
             if (t == 0) {
                 if (a.mean) a.mean[row] = (float)mean;
                 if (a.rstd) a.rstd[row] = (float)rstd;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Looped kernel for LayerNorm / RMSNorm rows wider than the single-pass
+// shapes: one workgroup of 64*W threads per row streams the row in tiles of
+// 64*W*K chunks twice, first for the statistics, then for the output.  The
+// second read of a row is usually served by L2 or the Infinity Cache.  The
+// statistics accumulate in fp64 (a lane may sum thousands of values).
+// ---------------------------------------------------------------------------
+
+template <int OP, int DT, int W, int K, bool AL>
+__global__ void __launch_bounds__(64 * W)
+row_looped(RowArgs a) {
+    static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "looped kernel is for the norms");
+    using I = dt_info<DT>;
+    constexpr int VEC = I::VEC, TPR = 64 * W;
+    constexpr int64_t TILE = (int64_t)TPR * K;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N;
+    const int64_t rowbytes = (int64_t)N * I::E;
+    const bool has_p0 = a.p0 != nullptr, has_p1 = a.p1 != nullptr;
+    __shared__ double2 red[2][W];
+
+    int par = 0;
+    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x, par ^= 1) {
+        const char *xr = a.x + row * rowbytes;
+        char *yr = a.y + row * rowbytes;
+        const RowGeom<DT, AL> geo(xr, N);
+        bool yvec = true;
+        if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+        uint32_t padw = 0;
+        if constexpr (OP == OP_LAYERNORM) {
+            if constexpr (I::E == 4) {
+                padw = *reinterpret_cast<const uint32_t *>(xr);
+            } else {
+                const uint32_t h = *reinterpret_cast<const uint16_t *>(xr);
+                padw = h | (h << 16);
+            }
+        }
+        const double pv = (double)elem_of_word<DT>(padw);   // 0 for RMSNorm
+        const int64_t ntiles = (geo.nch + TILE - 1) / TILE;
+
+        // ---- pass 1: statistics
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t tl = 0; tl < ntiles; ++tl) {
+            uint4 raw[K];
+            load_row<DT, AL, K, TPR>(raw, geo, t, N, tl * TILE);
+            finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float v[VEC];
+                unpack<DT>(raw[k], v);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const double d = (double)v[i] - pv;          // padding gives 0
+                    if constexpr (OP == OP_LAYERNORM) s1 += d;
+                    s2 = __builtin_fma(d, d, s2);
+                }
+            }
+        }
+        const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red[par], wv, lane);
+        double m1 = 0.0, scale;
+        if constexpr (OP == OP_LAYERNORM) {
+            m1 = st.x * a.inv_nd;
+            const double var = __builtin_fmax(st.y * a.inv_nd - m1 * m1, 0.0);
+            scale = rsqrt_f64(var + (double)a.eps);
+            if (t == 0) {
+                if (a.mean) a.mean[row] = (float)(pv + m1);
+                if (a.rstd) a.rstd[row] = (float)scale;
+            }
+        } else {
+            scale = rsqrt_f64(st.y * a.inv_nd + (double)a.eps);
+        }
+        const float scale_f = (float)scale;
+
+        // ---- pass 2: normalize
+        for (int64_t tl = 0; tl < ntiles; ++tl) {
+            uint4 raw[K], g4[K], b4[(OP == OP_LAYERNORM) ? K : 1];
+            load_row<DT, AL, K, TPR>(raw, geo, t, N, tl * TILE);
+            if (has_p0) load_params<DT, AL, K, TPR>(g4, geo, a.p0, t, N, tl * TILE);
+            if constexpr (OP == OP_LAYERNORM) {
+                if (has_p1) load_params<DT, AL, K, TPR>(b4, geo, a.p1, t, N, tl * TILE);
+            }
+            finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float v[VEC], g[VEC], b[VEC];
+                unpack<DT>(raw[k], v);
+                if (has_p0) unpack<DT>(g4[k], g);
+                if constexpr (OP == OP_LAYERNORM) {
+                    if (has_p1) unpack<DT>(b4[k], b);
+                }
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    const float gi = has_p0 ? g[i] : 1.0f;
+                    if constexpr (OP == OP_LAYERNORM) {
+                        const double d = ((double)v[i] - pv) - m1;
+                        v[i] = (float)__builtin_fma(d * scale, (double)gi, has_p1 ? (double)b[i] : 0.0);
+                    } else {
+                        v[i] = (v[i] * scale_f) * gi;
+                    }
+                }
+                store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), tl * TILE);
             }
         }
     }
@@ -505,23 +824,19 @@ softmax_split_partial(RowArgs a) {
 
     uint4 raw[K];
     const int64_t cbase = j * (int64_t)(TPR * K);
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        raw[k] = load_chunk<DT, AL>(geo, xr, cbase + (int64_t)k * TPR + t, N, I::NEG_INF_WORD);
+    // temporal loads: the finalize kernel reads this chunk again
+    load_row<DT, AL, K, TPR, false>(raw, geo, t, N, cbase);
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
     float v[K][VEC];
 #pragma unroll
     for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) mx = __builtin_fmaxf(mx, v[k][i]);
-    mx = group_allreduce<W>(mx, MaxOp(), red[0], wv, lane);
+    float mx = group_allreduce<W>(lane_max(v), MaxOp(), red[0], wv, lane);
+    const float cj = mx * LOG2E;
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += fast_exp(v[k][i] - mx);
+        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -cj));
     s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
     if (mx == -__builtin_inff()) s = 0.f;    // a fully masked chunk holds no mass
     if (t == 0) a.ws[row * P + j] = make_float2(mx, s);
@@ -546,9 +861,7 @@ softmax_split_finalize(RowArgs a) {
     // issue the chunk loads first so their latency overlaps the merge
     uint4 raw[K];
     const int64_t cbase = j * (int64_t)(TPR * K);
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        raw[k] = load_chunk<DT, AL>(geo, xr, cbase + (int64_t)k * TPR + t, N, I::NEG_INF_WORD);
+    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
 
     // merge the row's P partials; every wave does it redundantly, in the
     // same order, so every workgroup of the row gets identical (m, l)
@@ -556,22 +869,28 @@ softmax_split_finalize(RowArgs a) {
     float m = -__builtin_inff();
     for (int p = lane; p < P; p += 64) m = __builtin_fmaxf(m, wr[p].x);
     m = wave_allreduce(m, MaxOp());
+    // chunk j's terms are 2^(x*log2e - c_j) with c_j = m_j*log2e rounded to
+    // fp32; rescaled to the row's c they carry the factor 2^(c_j - c)
+    const float c = m * LOG2E;
     float l = 0.f;
     for (int p = lane; p < P; p += 64) {
+#pragma clang fp contract(off)
         const float2 q = wr[p];
-        l += (q.x == -__builtin_inff()) ? 0.f : q.y * fast_exp(q.x - m);
+        const float cj = q.x * LOG2E;    // rounded exactly as in split_partial
+        l += (q.x == -__builtin_inff()) ? 0.f : q.y * __builtin_amdgcn_exp2f(cj - c);
     }
     l = wave_allreduce(l, SumOp());
     if (m == -__builtin_inff()) l = __builtin_nanf("");   // all -inf row: NaN, as the formula
-    const float inv = 1.0f / l;
+    const float inv = rcp_approx(l);
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         float v[VEC];
         unpack<DT>(raw[k], v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] = fast_exp(v[i] - m) * inv;
-        store_chunk<DT, AL>(geo, yr, cbase + (int64_t)k * TPR + t, N, yvec, pack<DT>(v));
+        for (int i = 0; i < VEC; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], LOG2E, -c)) * inv;
+        store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
     }
 }
 

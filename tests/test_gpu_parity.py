@@ -143,8 +143,7 @@ def _sweep_M(N):
 
 
 SWEEP = [(op, dt, N, M) for op in ("softmax", "layernorm", "rmsnorm") for dt in ("f32", "f16", "bf16")
-         for N in SWEEP_N for M in _sweep_M(N)
-         if not (op != "softmax" and N > 65536)]
+         for N in SWEEP_N for M in _sweep_M(N)]
 
 
 @pytest.mark.parametrize("op,dt,N,M", SWEEP)
@@ -161,9 +160,7 @@ def test_sweep(op, dt, N, M):
     parity_case(op, x, dt, eps, p0, p1, what=f"sweep {op} {dt} {M}x{N}")
     # misaligned rows: x and y one element past a 16-byte boundary (same phase)
     if N >= 2 and M <= 64:
-        plan_ok = op == "softmax" or N < 65536
-        if plan_ok:
-            parity_case(op, x, dt, eps, p0, p1, x_off=1, y_off=1, what=f"sweep-misaligned {op} {dt} {M}x{N}")
+        parity_case(op, x, dt, eps, p0, p1, x_off=1, y_off=1, what=f"sweep-misaligned {op} {dt} {M}x{N}")
 
 
 @pytest.mark.parametrize("op", ["softmax", "layernorm", "rmsnorm"])
@@ -196,6 +193,20 @@ def test_split_path_forced(dt, N, monkeypatch):
     x[4, : N // 2] = x[2, 0]                     # row 4: masked first half
     for off in (0, 1):
         parity_case("softmax", x, dt, x_off=off, y_off=off, what=f"split {dt} N={N} off={off}")
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [1000, 4096, 100003])
+def test_looped_path_forced(op, dt, N, monkeypatch):
+    """The looped one-workgroup-per-row norm kernel on rows that would fit on
+    chip, and on odd widths, aligned and misaligned."""
+    monkeypatch.setenv("NT_FORCE_PATH", "looped")
+    x = rand_bits(N + 1, 6, N, dt, scale=2.0, loc=3.0)
+    p0 = rand_bits(N + 2, 1, N, dt, scale=0.3, loc=1.0)[0]
+    p1 = rand_bits(N + 3, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
+    for off in (0, 1):
+        parity_case(op, x, dt, 1e-5, p0, p1, x_off=off, y_off=off, what=f"looped {op} {dt} N={N} off={off}")
 
 
 # ----------------------------------------------------------------------------
@@ -279,5 +290,6 @@ def test_errors_before_launch():
     wsb = nt.nt_softmax_workspace_bytes(M, N, nt.NT_F32)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     assert nt.nt_softmax_rows(M, N, nt.NT_F32, p, p, ws.data_ptr(), wsb - 8, None) == 6
-    assert nt.nt_layernorm_rows(M, N, nt.NT_F32, 1e-5, p, None, None, p, None, None, None) == 2
+    assert nt.nt_layernorm_rows(M, N, nt.NT_F32, float("nan"), p, None, None, p, None, None, None) == 4
+    assert nt.nt_layernorm_rows(-1, N, nt.NT_F32, 1e-5, p, None, None, p, None, None, None) == 2
     torch.cuda.synchronize()

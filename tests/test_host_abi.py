@@ -62,14 +62,26 @@ def test_status_strings():
     (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, FAKE + 1, FAKE, None, None, None), 5),
     (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, None, FAKE, FAKE + 2, None, None), 5),
     (lambda: nt.nt_layernorm_rows(4, 8, F16, 1e-5, FAKE, None, None, FAKE, None, FAKE + 2, None), 5),
-    (lambda: nt.nt_layernorm_rows(4, 1 << 20, F16, 1e-5, FAKE, None, None, FAKE, None, None, None), 2),
     (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 1, FAKE, None), 5),
     (lambda: nt.nt_rmsnorm_rows(4, 8, 3, 1e-6, FAKE, None, FAKE, None), 3),
     (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, None, None, FAKE, None), 1),
-    (lambda: nt.nt_rmsnorm_rows(4, 65536 * 2, BF16, 1e-6, FAKE, None, FAKE, None), 2),
+    (lambda: nt.nt_rmsnorm_rows(4, 1 << 31, BF16, 1e-6, FAKE, None, FAKE, None), 2),
 ])
 def test_validation_before_launch(call, code):
+    # every case here must fail validation; on a machine with a GPU a library
+    # bug could turn a fake pointer into a launch, so these run only without one
+    if _gpu_present():
+        pytest.skip("fake-pointer validation runs only on a host without a GPU")
+    assert code != 0
     assert call() == code
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
 
 
 def test_empty_is_noop():
@@ -83,8 +95,8 @@ def test_empty_is_noop():
 def test_workspace_bytes():
     assert nt.nt_softmax_workspace_bytes(1024, 781, F32) == 0          # single pass
     assert nt.nt_softmax_workspace_bytes(131072, 4096, BF16) == 0
-    # 1 MiB fp32 rows: 16 chunks of 64 KiB (+1 for a misaligned head) per row
-    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 17 * 8
+    # 1 MiB fp32 rows: 64 chunks of 16 KiB (+1 for a misaligned head) per row
+    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 65 * 8
     assert nt.nt_softmax_workspace_bytes(-1, 8, F32) == 0
     assert nt.nt_softmax_workspace_bytes(4, 8, 9) == 0
 
@@ -100,16 +112,14 @@ def test_plans_of_the_workloads():
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
     assert p["split"] == 0
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
-    assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 64 * 16
-    assert p["workspace_bytes"] == 64 * 16 * 8
+    assert p["split"] == 1 and p["row_chunks"] == 64 and p["grid"] == 64 * 64
+    assert p["workspace_bytes"] == 64 * 64 * 8
 
 
 def test_plan_capacity_covers_row():
     for dt, e in ((F32, 4), (F16, 2), (BF16, 2)):
-        for N in (1, 7, 64, 255, 256, 781, 1024, 4097, 8192, 30000, 65536):
+        for N in (1, 7, 64, 255, 256, 781, 1024, 4097, 8192, 30000, 32768 * 4 // e):
             for al in (True, False):
-                if N == 65536 and not al:
-                    continue          # one chunk past the widest shape (test_norm_width_limits)
                 p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 8, N, dt, al)
                 vec = 16 // e
                 need = N // vec if (al and (N * e) % 16 == 0) else (N + 2 * vec - 2) // vec
@@ -117,17 +127,18 @@ def test_plan_capacity_covers_row():
                     assert 64 * p["waves_per_row"] * p["chunks_per_lane"] >= need, (dt, N, al, p)
 
 
-def test_norm_width_limits():
-    # the widest single-pass row: 256 KiB fp32 / 128 KiB 16-bit, aligned
-    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, F32, True)["split"] == 0
-    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, BF16, True)["split"] == 0
-    # a misaligned row of that width touches one more chunk and is rejected
-    with pytest.raises(nt.NtError):
-        nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 65536, BF16, False)
-    with pytest.raises(nt.NtError):
-        nt.nt_plan_launch(nt.NT_OP_RMSNORM, 1, 65537, F32, True)
+def test_wide_rows_take_the_streaming_paths():
+    # LayerNorm holds at most 16 values per lane: 16 KiB of 16-bit row
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 8192, BF16, True)["split"] == 0
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 8193, BF16, True)
+    assert p["split"] == 2 and p["grid"] == 1 and p["threads_per_block"] == 512
+    # RMSNorm fp32 up to 128 KiB single pass, then looped
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 7, 32768, F32, True)["split"] == 0
+    p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 7, 32769, F32, True)
+    assert p["split"] == 2 and p["grid"] == 7
     # softmax takes the split path instead
-    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1, 65537, F32, True)["split"] == 1
+    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1, 32769, F32, True)["split"] == 1
+    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1, 1 << 24, BF16, True)["split"] == 1
 
 
 def test_grid_fits_dispatch_packet():

@@ -1,0 +1,112 @@
+"""Structural checks of the built gfx950 code object (CPU only): the device
+code embedded in libnt.so is unbundled and its kernel metadata read with the
+ROCm LLVM tools.  Every kernel must run in wave64 without scratch (no
+register spills), the library must contain no matrix-core (MFMA)
+instructions (this path is no contraction), and every launch shape the
+planner can choose must have an instantiated kernel."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import row_wise_reductions_amd as nt
+
+LLVM = "/opt/rocm/llvm/bin"
+TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+
+
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+@pytest.fixture(scope="module")
+def code_objects(tmp_path_factory):
+    """One gfx950 code object per translation unit: the linked .hip_fatbin
+    section is a concatenation of one offload bundle per object file."""
+    if not (shutil.which("objcopy") and os.path.exists(f"{LLVM}/clang-offload-bundler")):
+        pytest.skip("binutils / ROCm LLVM tools not available")
+    d = tmp_path_factory.mktemp("co")
+    fat = d / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", nt.LIB_PATH, str(fat)], check=True)
+    data = fat.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+    assert starts, "no offload bundle in libnt.so"
+    cos = []
+    for i, s0 in enumerate(starts):
+        end = starts[i + 1] if i + 1 < len(starts) else len(data)
+        part, co = d / f"bundle{i}.bin", d / f"k{i}.co"
+        part.write_bytes(data[s0:end])
+        subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={part}",
+                        f"--targets={TARGET}", f"--output={co}"], check=True)
+        cos.append(co)
+    return cos
+
+
+@pytest.fixture(scope="module")
+def kernels(code_objects):
+    out = {}
+    for co in code_objects:
+        notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", str(co)], check=True,
+                               capture_output=True, text=True).stdout
+        for block in notes.split("  - .agpr_count:")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", block).group(1)
+            get = lambda k: int(re.search(rf"\.{k}:\s+(\d+)", block).group(1))  # noqa: E731
+            out[name] = {"scratch": get("private_segment_fixed_size"), "vgpr": get("vgpr_count"),
+                         "lds": get("group_segment_fixed_size"), "wave": get("wavefront_size")}
+    assert out, "no kernels found in the code objects"
+    return out
+
+
+def test_no_spills_wave64(kernels):
+    bad = {k: v for k, v in kernels.items() if v["scratch"] != 0 or v["wave"] != 64}
+    assert not bad, bad
+
+
+def test_no_mfma(code_objects):
+    for co in code_objects:
+        asm = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(co)], check=True,
+                             capture_output=True, text=True).stdout
+        if "row_resident" not in asm:
+            continue
+        assert "global_load_dwordx4" in asm
+        assert not re.search(r"\bv_mfma", asm), "MFMA instruction in a row-reduction kernel"
+
+
+def test_all_types_present(kernels):
+    for dt in (0, 1, 2):
+        assert any(f"row_residentILi0ELi{dt}E" in k for k in kernels), dt
+
+
+def _shapes(kernels):
+    have = set()
+    for name in kernels:
+        m = re.search(r"row_residentILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("res",) + tuple(int(g) for g in m.groups()))
+        m = re.search(r"row_loopedILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("loop",) + tuple(int(g) for g in m.groups()))
+        m = re.search(r"softmax_split_(partial|finalize)ILi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add((m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4)), int(m.group(5))))
+    return have
+
+
+def test_every_planned_shape_is_built(kernels):
+    have = _shapes(kernels)
+    for op in (0, 1, 2):
+        for dt in (0, 1, 2):
+            for N in (1, 7, 64, 255, 781, 1000, 4096, 4097, 8192, 16384, 30000, 32768, 65536, 100000, 262144):
+                for al in (True, False):
+                    try:
+                        p = nt.nt_plan_launch(op, 64, N, dt, al)
+                    except nt.NtError:
+                        continue
+                    W, K, A = p["waves_per_row"], p["chunks_per_lane"], p["aligned"]
+                    if p["split"] == 1:
+                        assert ("partial", dt, W, K, A) in have and ("finalize", dt, W, K, A) in have
+                    elif p["split"] == 2:
+                        assert ("loop", op, dt, W, K, A) in have, (op, dt, N, al, p)
+                    else:
+                        assert ("res", op, dt, W, K, A) in have, (op, dt, N, al, p)
