@@ -24,7 +24,6 @@ Infinity Cache cannot serve them), --no-cpu-baseline.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -41,16 +40,6 @@ CACHE_BYTES = 256 << 20     # Infinity Cache (MALL) size
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "row_wise_reductions_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
 
 
 def to_dev(bits, dt, torch, np):
@@ -157,6 +146,7 @@ def traffic_for(kernel_name, launches_bytes):
         return None
     with open(path) as f:
         t = json.load(f)
+    from row_wise_reductions_amd.rocprof_summary import kernel_source_hash
     if t.get("source_hash") != kernel_source_hash():
         return None
     e = t.get("workloads", {}).get(kernel_name)
@@ -164,25 +154,37 @@ def traffic_for(kernel_name, launches_bytes):
 
 
 def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
-    """Attainable-bandwidth reference: a plain copy kernel of known size
-    (read nbytes, write nbytes), rotating 4 buffer pairs."""
+    """Attainable-bandwidth reference: the plain streaming copy kernel of
+    libntcal.so (read nbytes, write nbytes), rotating 4 buffer pairs; torch's
+    own copy_ is timed beside it."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_reductions_amd", "libntcal.so"))
+    lib.ntcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ntcal_copy.restype = ctypes.c_int
     n = nbytes // 4
     src = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(4)]
     dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
-    for i in range(warmup):
-        dst[i % 4].copy_(src[i % 4])
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    durs = []
-    for i in range(steps):
-        a.record()
-        dst[i % 4].copy_(src[i % 4])
-        b.record()
-        b.synchronize()
-        durs.append(a.elapsed_time(b))
-    ms = statistics.median(durs)
-    print(json.dumps({"calibration": "torch copy_ fp32", "bytes_read": nbytes, "bytes_written": nbytes,
-                      "median_ms": round(ms, 5), "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    sh = torch.cuda.current_stream().cuda_stream
+    out = {"calibration": "plain streaming copy (ntcal_copy_kernel), 4 KiB per workgroup, non-temporal",
+           "bytes_read": nbytes, "bytes_written": nbytes}
+    for name, fn in (("ntcal", lambda i: lib.ntcal_copy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(), nbytes, sh)),
+                     ("torch_copy", lambda i: dst[i % 4].copy_(src[i % 4]))):
+        for i in range(warmup):
+            rc = fn(i)
+            assert not isinstance(rc, int) or rc == 0, rc
+        torch.cuda.synchronize()
+        durs = []
+        for i in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(i)
+            b.record()
+            b.synchronize()
+            durs.append(a.elapsed_time(b))
+        ms = statistics.median(durs)
+        out[f"{name}_median_ms"] = round(ms, 5)
+        out[f"{name}_GBps"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(out), flush=True)
 
 
 def main():

@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libnt.so")
+CALIB_PATH = os.path.join(HERE, "libntcal.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -57,7 +58,22 @@ def build(verbose: bool = True, extra_flags=(), out: str = LIB_PATH, build_dir: 
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")
+    if out == LIB_PATH:
+        build_calibration(verbose)
     return out
+
+
+def build_calibration(verbose: bool = True) -> str:
+    """The reference copy kernel (libntcal.so), used by bench.py --calibrate."""
+    tmp = CALIB_PATH + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", os.path.join(CSRC, "calib_copy.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for calib_copy.hip:\n{r.stderr}")
+    os.replace(tmp, CALIB_PATH)
+    if verbose:
+        print(f"built {CALIB_PATH}")
+    return CALIB_PATH
 
 
 if __name__ == "__main__":

@@ -1,0 +1,193 @@
+"""Summaries of rocprofv3 output for the row-reduction kernels.
+
+Turns rocprofv3 CSV output into the short text summaries kept under
+``profiles/`` and into ``profiles/traffic.json``, which bench.py reads for
+the roofline ``traffic`` field.  Nothing here launches work on a GPU.
+
+  python -m row_wise_reductions_amd.rocprof_summary stats DIR --cmd "..." --out FILE.md
+      DIR holds *_kernel_stats.csv from `rocprofv3 --kernel-trace --stats
+      --output-format csv` of bench.py: per-workload kernel calls and
+      average durations.
+
+  python -m row_wise_reductions_amd.rocprof_summary traffic --fetch DIR --write DIR \\
+         --calib-fetch DIR --calib-write DIR --cmds FILE --md FILE.md --json FILE.json
+      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc FETCH_SIZE`
+      and `--pmc WRITE_SIZE` runs of bench.py and of `bench.py --calibrate`.
+      Counter values (KiB per dispatch) are scaled by what the same counter
+      reads for the calibration copy of known size (1 GiB read + 1 GiB
+      written), giving HBM bytes per call of each workload.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CALIB_KERNEL = "ntcal_copy_kernel"
+CALIB_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _b(x) -> str:
+    return "true" if x else "false"
+
+
+def kernels_of(w) -> list[str]:
+    """Demangled names of the kernels one call of workload `w` launches (with
+    16-byte-aligned buffers and every parameter vector present, as bench.py)."""
+    import row_wise_reductions_amd as nt
+    op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}[w.op]
+    dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dt]
+    p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
+    W, K, al = p["waves_per_row"], p["chunks_per_lane"], _b(p["aligned"])
+    if p["split"] == 1:
+        return [f"ntk::softmax_split_partial<{dt}, {W}, {K}, {al}>",
+                f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}>"]
+    if p["split"] == 2:
+        return [f"ntk::row_looped<{op}, {dt}, {W}, {K}, {al}>"]
+    return [f"ntk::row_resident<{op}, {dt}, {W}, {K}, {al}, {_b(op != 0)}>"]
+
+
+def _rows(pattern):
+    out = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def _match(name: str, key: str) -> bool:
+    return key in name
+
+
+def stats(args):
+    import workloads
+    rows = _rows(os.path.join(args.dir, "**", "*kernel_stats.csv"))
+    lines = ["# Kernel durations, rocprofv3 kernel trace", "",
+             "Command (run from the repository root on the GPU host):", "", f"    {args.cmd}", "",
+             "| workload | kernel | calls | avg duration (us) | algorithmic bytes / call | GB/s (bytes / summed kernel avg) |",
+             "|---|---|---|---|---|---|"]
+    for w in workloads.WORKLOADS:
+        ks = kernels_of(w)
+        tot = 0.0
+        found = []
+        for k in ks:
+            hit = [r for r in rows if _match(r["Name"], k)]
+            if not hit:
+                continue
+            r = hit[0]
+            avg = float(r["AverageNs"]) / 1000.0
+            tot += avg
+            found.append((k, int(r["Calls"]), avg))
+        for i, (k, calls, avg) in enumerate(found):
+            gbs = f"{w.algorithmic_bytes() / (tot * 1e-6) / 1e9:.1f}" if i == len(found) - 1 else ""
+            lines.append(f"| {w.name if i == 0 else ''} | `{k}` | {calls} | {avg:.2f} | "
+                         f"{w.algorithmic_bytes() if i == 0 else ''} | {gbs} |")
+    lines += ["", "Other kernels in the trace (input uploads and the like) are omitted.", ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def _counter_means(d: str, counter: str) -> dict:
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (statistics.mean(v), len(v)) for k, v in acc.items()}
+
+
+def _lookup(means: dict, key: str):
+    hit = [(v, n) for k, (v, n) in means.items() if key in k]
+    if not hit:
+        return None, 0
+    return hit[0]
+
+
+def traffic(args):
+    import workloads
+    fetch, write = _counter_means(args.fetch, "FETCH_SIZE"), _counter_means(args.write, "WRITE_SIZE")
+    cf, _ = _lookup(_counter_means(args.calib_fetch, "FETCH_SIZE"), CALIB_KERNEL)
+    cw, _ = _lookup(_counter_means(args.calib_write, "WRITE_SIZE"), CALIB_KERNEL)
+    if not cf or not cw:
+        raise SystemExit("calibration copy kernel not found in the counter output")
+    f_fac = (CALIB_BYTES / 1024.0) / cf
+    w_fac = (CALIB_BYTES / 1024.0) / cw
+    out = {"source_hash": kernel_source_hash(),
+           "calibration": {"kernel": CALIB_KERNEL, "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+                           "fetch_kib_per_dispatch": round(cf, 3), "write_kib_per_dispatch": round(cw, 3),
+                           "fetch_factor": round(f_fac, 6), "write_factor": round(w_fac, 6)},
+           "workloads": {}}
+    with open(args.cmds) as fh:
+        cmds = fh.read().strip().splitlines()
+    lines = ["# HBM traffic from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE)", "",
+             "Commands (each counter in a run of its own, from the repository root on the GPU host):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", f"Calibration: `{CALIB_KERNEL}` copies 1 GiB. FETCH_SIZE reads {cf:.1f} KiB and WRITE_SIZE "
+              f"{cw:.1f} KiB per dispatch for 1048576 KiB moved each way, so counter values are scaled by "
+              f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
+              "| workload | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / call (scaled) | "
+              "algorithmic bytes / call | ratio |", "|---|---|---|---|---|---|---|---|"]
+    for w in workloads.WORKLOADS:
+        total = 0.0
+        ok = True
+        for i, k in enumerate(kernels_of(w)):
+            fv, n = _lookup(fetch, k)
+            wv, _ = _lookup(write, k)
+            if fv is None or wv is None:
+                ok = False
+                continue
+            b = (fv * f_fac + wv * w_fac) * 1024.0
+            total += b
+            lines.append(f"| {w.name if i == 0 else ''} | `{k}` | {n} | {fv:.1f} | {wv:.1f} | {b:.0f} | "
+                         f"{w.algorithmic_bytes() if i == 0 else ''} | |")
+        if ok:
+            out["workloads"][w.name] = {"kernels": kernels_of(w), "hbm_bytes_per_call": round(total),
+                                        "algorithmic_bytes": w.algorithmic_bytes(),
+                                        "ratio": round(total / w.algorithmic_bytes(), 4)}
+            lines.append(f"| | **total** | | | | **{total:.0f}** | {w.algorithmic_bytes()} | "
+                         f"{total / w.algorithmic_bytes():.3f} |")
+    lines += ["", f"Kernel sources hash: `{out['source_hash']}` (bench.py reports traffic only while it matches).", ""]
+    with open(args.json, "w") as f:
+        json.dump(out, f, indent=1)
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "calib_fetch", "calib_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--cmds", required=True)
+    t.add_argument("--md", required=True)
+    t.add_argument("--json", required=True)
+    a = ap.parse_args()
+    stats(a) if a.mode == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
