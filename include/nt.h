@@ -127,7 +127,8 @@ const char *nt_status_string(nt_status s);
 /*
  * Launch plan introspection (host only; touches no device).  Describes the
  * kernels the library would launch for an operation on this shape, when
- * every pointer is 16-byte aligned (`aligned16` != 0) or not.
+ * every pointer is 16-byte aligned (`aligned16` != 0) or not, with every
+ * parameter vector present.
  */
 typedef enum { NT_OP_SOFTMAX = 0, NT_OP_LAYERNORM = 1, NT_OP_RMSNORM = 2 } nt_op;
 
@@ -140,6 +141,10 @@ typedef struct {
     int32_t rows_per_block;   /* rows one workgroup processes side by side              */
     int32_t threads_per_block;
     int32_t aligned;          /* 1 when the 16-byte-aligned variant is used             */
+    int32_t persistent;       /* 1: norm kernel with parameters held in registers across
+                                 rows; its grid is sized on the device from occupancy,
+                                 and `grid` below is then an upper bound                  */
+    int32_t reserved;
     int64_t grid;             /* workgroups per launch                                  */
     int64_t row_chunks;       /* split path: chunks per row (0 on the single pass)      */
     int64_t workspace_bytes;  /* split path: workspace size (0 on the single pass)      */

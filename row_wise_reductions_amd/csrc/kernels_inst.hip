@@ -1,5 +1,8 @@
 // Instantiation of the row kernels for one element type, selected at build
 // time with -DNTK_DT=0 (fp32), 1 (fp16) or 2 (bf16).
+#include <atomic>
+#include <cstdlib>
+
 #include "launch.hpp"
 
 #ifndef NTK_DT
@@ -57,6 +60,56 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
     NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4) NTK_CASE(8, 8) NTK_CASE(8, 16)
     NTK_CASE(16, 1) NTK_CASE(16, 2)
 #undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+// Persistent norm kernel: as many workgroups as fit on the device at once
+// (occupancy x compute units, the occupancy cached per instantiation), or
+// NT_PERSIST_GRID when set; never more than there are rows.
+template <int OP, int W, int K>
+hipError_t persist_go(const RowArgs &a, hipStream_t s) {
+    static std::atomic<int> per_cu{0};
+    int pc = per_cu.load(std::memory_order_relaxed);
+    if (pc == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_norm_persistent<OP, DT, W, K>, 64 * W, 0) !=
+                hipSuccess || n <= 0)
+            n = 1;
+        per_cu.store(n, std::memory_order_relaxed);
+        pc = n;
+    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    int64_t grid = (int64_t)pc * cus;
+    if (const char *e = std::getenv("NT_PERSIST_GRID")) {
+        const long long v = std::atoll(e);
+        if (v > 0) grid = v;
+    }
+    if (grid > a.M) grid = a.M;
+    hipLaunchKernelGGL((row_norm_persistent<OP, DT, W, K>), dim3((uint32_t)grid), dim3(64 * W), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int OP>
+hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
+#define NTK_CASE(w, k)                                                   \
+    if (W == w && K == k) {                                              \
+        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32) return persist_go<OP, w, k>(a, s); \
+        return hipErrorInvalidValue;                                     \
+    }
+    NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
+    NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4) NTK_CASE(8, 8) NTK_CASE(8, 16)
+#undef NTK_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s) {
+    switch (op) {
+    case OP_LAYERNORM: return persistent<OP_LAYERNORM>(W, K, a, s);
+    case OP_RMSNORM: return persistent<OP_RMSNORM>(W, K, a, s);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -128,6 +181,9 @@ hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t
 hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
+hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s) {
+    return persistent_any(op, W, K, a, s);
+}
 #elif NTK_DT == 1
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
@@ -136,6 +192,9 @@ hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
+hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
+    return persistent_any(op, W, K, a, s);
+}
 #else
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
@@ -143,6 +202,9 @@ hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a,
 hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
+}
+hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
+    return persistent_any(op, W, K, a, s);
 }
 #endif
 

@@ -22,6 +22,12 @@ hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, in
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
 
+// Launch the persistent norm kernel (aligned rows, every parameter vector
+// present); the grid is sized from the device's occupancy.
+hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s);
+hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s);
+hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s);
+
 // Launch the two split-softmax kernels (partials, then merge + write).
 hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s);
 hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s);

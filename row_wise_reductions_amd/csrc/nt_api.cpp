@@ -100,7 +100,12 @@ int64_t row_chunks(int64_t N, nt_dtype dt, bool aligned) {
     return (N + vec - 1 + vec - 1) / vec;
 }
 
-nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p) {
+bool persistent_enabled() {
+    const char *s = std::getenv("NT_PERSISTENT");
+    return !(s && std::strcmp(s, "0") == 0);
+}
+
+nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true) {
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
@@ -135,6 +140,14 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         int64_t grid = (M + G - 1) / G;
         if (grid > max_grid) grid = max_grid;
         p->grid = grid;
+        // Norms on aligned rows with every parameter vector present keep the
+        // parameters widened in registers across rows: persistent workgroups
+        // (grid sized on the device from occupancy; `grid` is then an upper bound).
+        // (at most 32 values per lane: the row, its prefetched successor and the
+        // cached parameters must fit without spilling)
+        if (op != NT_OP_SOFTMAX && aligned && params && pick.W >= 2 && pick.K * elems_per_chunk(dt) <= 32 &&
+            persistent_enabled())
+            p->persistent = 1;
         return NT_OK;
     }
     if (op != NT_OP_SOFTMAX) {
@@ -175,6 +188,13 @@ bool all_aligned16(int64_t N, nt_dtype dt, const void *x, const void *y, const v
 
 hipError_t launch_resident(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
     const bool al = p.aligned != 0;
+    if (p.persistent) {
+        switch (dt) {
+        case NT_F32: return ntk::launch_persistent_f32(op, p.waves_per_row, p.chunks_per_lane, a, s);
+        case NT_F16: return ntk::launch_persistent_f16(op, p.waves_per_row, p.chunks_per_lane, a, s);
+        case NT_BF16: return ntk::launch_persistent_bf16(op, p.waves_per_row, p.chunks_per_lane, a, s);
+        }
+    }
     switch (dt) {
     case NT_F32: return ntk::launch_resident_f32(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
     case NT_F16: return ntk::launch_resident_f16(op, p.waves_per_row, p.chunks_per_lane, al, a, p.grid, s);
@@ -205,10 +225,10 @@ hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hi
 
 void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p) {
     std::fprintf(stderr,
-                 "[nt] %s M=%lld N=%lld dt=%d: path %s W=%d K=%d rows/block=%d threads=%d aligned=%d grid=%lld"
-                 " chunks/row=%lld ws=%lld\n",
+                 "[nt] %s M=%lld N=%lld dt=%d: path %s W=%d K=%d rows/block=%d threads=%d aligned=%d"
+                 " persistent=%d grid=%lld chunks/row=%lld ws=%lld\n",
                  what, (long long)M, (long long)N, (int)dt, p.split == 1 ? "split" : p.split == 2 ? "looped" : "single-pass", p.waves_per_row,
-                 p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, (long long)p.grid,
+                 p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, p.persistent, (long long)p.grid,
                  (long long)p.row_chunks, (long long)p.workspace_bytes);
 }
 
@@ -317,7 +337,7 @@ nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const 
         return NT_ERR_ALIGN;
     const bool al = all_aligned16(N, dt, x, y, gamma, beta);
     nt_plan p;
-    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p);
+    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p, gamma != nullptr && beta != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
     a.x = static_cast<const char *>(x);
@@ -344,7 +364,7 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const vo
     if (weight && !aligned_to(weight, (uintptr_t)elem_bytes(dt))) return NT_ERR_ALIGN;
     const bool al = all_aligned16(N, dt, x, y, weight, nullptr);
     nt_plan p;
-    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p);
+    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
     a.x = static_cast<const char *>(x);

@@ -227,9 +227,17 @@ __device__ __forceinline__ void scatter(char *row, int64_t col0, int32_t N, uint
 // scalars and combined in a fixed order.  Every lane returns the same bits.
 // ---------------------------------------------------------------------------
 
+// Every permutation used below reads a valid lane for every lane, so the
+// "old" operand is never observed.  For fp32 the zero-old form lets the
+// compiler fold the DPP into the consuming v_add/v_max; the fp64 halves use
+// bound_ctrl moves, which need no initialized destination.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -238,8 +246,8 @@ __device__ __forceinline__ float dpp(float v) {
 template <int CTRL>
 __device__ __forceinline__ double dpp(double v) {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const int lo = dpp_i<CTRL>((int)(uint32_t)u);
-    const int hi = dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+    const int lo = dpp_mov<CTRL>((int)(uint32_t)u);
+    const int hi = dpp_mov<CTRL>((int)(uint32_t)(u >> 32));
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 template <int CTRL>
@@ -689,6 +697,137 @@ row_resident(RowArgs a) {
             if (t == 0) {
                 if (a.mean) a.mean[row] = (float)mean;
                 if (a.rstd) a.rstd[row] = (float)rstd;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent kernel for LayerNorm / RMSNorm with every parameter vector
+// present and 16-byte-aligned rows: each lane always owns the same columns,
+// so a workgroup widens its gamma/beta (fp64, LayerNorm) or weight (fp32,
+// RMSNorm) once, then strides over rows with the next row's loads in flight
+// while the current row is reduced and written.  One row per workgroup of
+// 64*W threads (W >= 2).
+// ---------------------------------------------------------------------------
+
+template <int OP, int DT, int W, int K>
+__global__ void __launch_bounds__(64 * W)
+row_norm_persistent(RowArgs a) {
+    static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "persistent kernel is for the norms");
+    static_assert(W >= 2, "one row per workgroup");
+    using I = dt_info<DT>;
+    constexpr int VEC = I::VEC, TPR = 64 * W;
+    constexpr bool LN = OP == OP_LAYERNORM;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N;
+    const int64_t rowbytes = (int64_t)N * I::E;
+    __shared__ double2 red_d2[2][W];
+    __shared__ float red_f[2][W];
+
+    int64_t row = blockIdx.x;
+    if (row >= a.M) return;
+    const RowGeom<DT, true> geo(a.x, N);     // every row has the same chunk geometry
+
+    // ---- parameters, widened once per workgroup
+    double g64[LN ? K : 1][LN ? VEC : 1], b64[LN ? K : 1][LN ? VEC : 1];
+    float w32[LN ? 1 : K][LN ? 1 : VEC];
+    {
+        uint4 p0[K], p1[LN ? K : 1];
+        load_params<DT, true, K, TPR>(p0, geo, a.p0, t, N);
+        if constexpr (LN) load_params<DT, true, K, TPR>(p1, geo, a.p1, t, N);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float g[VEC], b[VEC];
+            unpack<DT>(p0[k], g);
+            if constexpr (LN) {
+                unpack<DT>(p1[k], b);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    g64[k][i] = (double)g[i];
+                    b64[k][i] = (double)b[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) w32[k][i] = g[i];
+            }
+        }
+    }
+
+    // ---- prime the pipeline with the first row
+    uint4 raw[K];
+    uint32_t padw = 0;
+    {
+        const char *xr = a.x + row * rowbytes;
+        load_row<DT, true, K, TPR>(raw, RowGeom<DT, true>(xr, N), t, N);
+        if constexpr (LN)
+            padw = (I::E == 4) ? *reinterpret_cast<const uint32_t *>(xr)
+                               : (uint32_t)*reinterpret_cast<const uint16_t *>(xr) * 0x10001u;
+    }
+    int par = 0;
+    for (; row < a.M; row += gridDim.x, par ^= 1) {
+        const char *xr = a.x + row * rowbytes;
+        char *yr = a.y + row * rowbytes;
+        const RowGeom<DT, true> g(xr, N);
+        finish_row<DT, true, K, TPR>(raw, g, xr, t, N, padw);
+        float v[K][VEC];
+#pragma unroll
+        for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
+        const uint32_t pw = padw;
+
+        // issue the next row's loads (clamped to the last row, so no branch)
+        {
+            const int64_t nr = row + gridDim.x < a.M ? row + gridDim.x : a.M - 1;
+            const char *xn = a.x + nr * rowbytes;
+            load_row<DT, true, K, TPR>(raw, RowGeom<DT, true>(xn, N), t, N);
+            if constexpr (LN)
+                padw = (I::E == 4) ? *reinterpret_cast<const uint32_t *>(xn)
+                                   : (uint32_t)*reinterpret_cast<const uint16_t *>(xn) * 0x10001u;
+        }
+
+        if constexpr (LN) {
+            const double pv = (double)elem_of_word<DT>(pw);
+            double s1 = 0.0, s2 = 0.0;
+            double dp[K][VEC];
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    dp[k][i] = (double)v[k][i] - pv;        // padding holds p: 0
+                    s1 += dp[k][i];
+                    s2 = __builtin_fma(dp[k][i], dp[k][i], s2);
+                }
+            const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red_d2[par], wv, lane);
+            const double m1 = st.x * a.inv_nd;
+            const double var = __builtin_fmax(st.y * a.inv_nd - m1 * m1, 0.0);
+            const double rstd = rsqrt_f64(var + (double)a.eps);
+            const double nm = -m1 * rstd;                     // (dp - m1) * rstd = fma(dp, rstd, nm)
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float o[VEC];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    o[i] = (float)__builtin_fma(__builtin_fma(dp[k][i], rstd, nm), g64[k][i], b64[k][i]);
+                store_slice<DT, true, TPR>(g, yr, k, t, N, true, pack<DT>(o));
+            }
+            if (t == 0) {
+                if (a.mean) a.mean[row] = (float)(pv + m1);
+                if (a.rstd) a.rstd[row] = (float)rstd;
+            }
+        } else {
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) ss = __builtin_fmaf(v[k][i], v[k][i], ss);
+            ss = group_allreduce<W>(ss, SumOp(), red_f[par], wv, lane);
+            const float inv = rsq_approx(ss * a.inv_n + a.eps);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float o[VEC];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) o[i] = (v[k][i] * inv) * w32[k][i];
+                store_slice<DT, true, TPR>(g, yr, k, t, N, true, pack<DT>(o));
             }
         }
     }

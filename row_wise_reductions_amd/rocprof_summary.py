@@ -60,6 +60,8 @@ def kernels_of(w) -> list[str]:
                 f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}>"]
     if p["split"] == 2:
         return [f"ntk::row_looped<{op}, {dt}, {W}, {K}, {al}>"]
+    if p["persistent"]:
+        return [f"ntk::row_norm_persistent<{op}, {dt}, {W}, {K}>"]
     return [f"ntk::row_resident<{op}, {dt}, {W}, {K}, {al}, {_b(op != 0)}>"]
 
 

@@ -209,6 +209,37 @@ def test_looped_path_forced(op, dt, N, monkeypatch):
         parity_case(op, x, dt, 1e-5, p0, p1, x_off=off, y_off=off, what=f"looped {op} {dt} N={N} off={off}")
 
 
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N,M,grid", [(4096, 37, 0), (8192, 300, 7), (4096, 5, 2), (8192, 64, 3)])
+def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
+    """Persistent norm kernel (parameters held across rows, next row prefetched):
+    parity with the oracle and bitwise equality with the one-row-per-group
+    kernel, including grids much smaller than the row count."""
+    x = rand_bits(N + M, M, N, dt, scale=2.0, loc=1.5)
+    p0 = rand_bits(N + 1, 1, N, dt, scale=0.3, loc=1.0)[0]
+    p1 = rand_bits(N + 2, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
+    code = DT_CODE[dt]
+    plan = nt.nt_plan_launch({"layernorm": 1, "rmsnorm": 2}[op], M, N, code, True)
+    assert plan["persistent"] == 1, plan
+    if grid:
+        monkeypatch.setenv("NT_PERSIST_GRID", str(grid))
+    x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    say(f"case persistent {op} {dt} {M}x{N} grid={grid}")
+    y1, m1, r1 = run_op(op, x_t, dt, 1e-5, p0_t, p1_t)
+    ref, rmean, rrstd = oracle_for(op, x, dt, 1e-5, p0, p1)
+    check_output(to_host_bits(y1, dt), ref, dt, f"persistent {op} {dt}")
+    if op == "layernorm":
+        check_stats(m1.cpu().numpy(), rmean, "persistent mean")
+        check_stats(r1.cpu().numpy(), rrstd, "persistent rstd")
+    monkeypatch.setenv("NT_PERSISTENT", "0")
+    y2, m2, r2 = run_op(op, x_t, dt, 1e-5, p0_t, p1_t)
+    assert np.array_equal(to_host_bits(y1, dt), to_host_bits(y2, dt))
+    if op == "layernorm":
+        assert torch.equal(m1, m2) and torch.equal(r1, r2)
+
+
 # ----------------------------------------------------------------------------
 # semantics: special rows, in place, determinism, streams, no-op, errors
 # ----------------------------------------------------------------------------
