@@ -56,8 +56,9 @@
  *             result is rounded to `dt` once, round-to-nearest-even.  The
  *             reduction order is fixed, so results are bitwise repeatable
  *             for a given shape, type and device.
- *  Threads    every entry point is thread-safe; the library has no mutable
- *             global state beyond a read-only device-property cache.
+ *  Threads    every entry point is thread-safe; the library's only global
+ *             state is a read-only device-property cache and an atomic call
+ *             counter that tags the split path's workspace records.
  */
 #ifndef NT_H
 #define NT_H
@@ -84,9 +85,10 @@ typedef enum {
 
 /*
  * Bytes of device workspace nt_softmax_rows needs for this shape: 0 when each
- * row fits on chip (single pass), else 8 bytes per (row, row chunk) for the
+ * row fits on chip (single pass), else 16 bytes per (row, row chunk) for the
  * per-chunk running max and denominator of the split online path.  Returns 0
- * for invalid arguments.
+ * for invalid arguments.  The contents need not be initialized and are
+ * overwritten; two calls in flight at once must not share a workspace.
  */
 size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
 
@@ -94,9 +96,15 @@ size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
  * Row softmax.  y[r, j] = exp(x[r, j] - m_r) / sum_k exp(x[r, k] - m_r) with
  * m_r = max_k x[r, k].  -inf entries contribute exactly 0 (a row of -inf only
  * yields NaN, as the formula does).  Rows that fit on chip are read once and
- * written once; wider rows take the split path (two kernels: per-chunk max
- * and denominator, then merge and write), which needs `workspace` of at least
- * nt_softmax_workspace_bytes(M, N, dt) bytes (may be NULL when that is 0).
+ * written once; wider rows take the split path, which needs `workspace` of at
+ * least nt_softmax_workspace_bytes(M, N, dt) bytes (may be NULL when that is
+ * 0): each workgroup takes one chunk of a row, computes its max and
+ * denominator, merges those of the row's chunks, and writes its chunk.  Up to
+ * 128 chunks per row this is one kernel that reads x once (the workgroups of a
+ * row exchange their pairs through the workspace; a pair that does not arrive
+ * within a bounded wait is recomputed from x, so the result does not depend on
+ * scheduling); wider rows, and in-place calls, use two kernels and read x
+ * twice.  Either way the results are bitwise the same.
  */
 nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
                           const void *x, void *y,
@@ -144,7 +152,10 @@ typedef struct {
     int32_t persistent;       /* 1: norm kernel with parameters held in registers across
                                  rows; its grid is sized on the device from occupancy,
                                  and `grid` below is then an upper bound                  */
-    int32_t reserved;
+    int32_t cooperative;      /* split path: 1 when one kernel does both phases (x read once;
+                                 the workgroups of a row exchange their partial results
+                                 through the workspace); 0: two kernels, x read twice.
+                                 In-place calls (y == x) always use the two kernels    */
     int64_t grid;             /* workgroups per launch                                  */
     int64_t row_chunks;       /* split path: chunks per row (0 on the single pass)      */
     int64_t workspace_bytes;  /* split path: workspace size (0 on the single pass)      */

@@ -37,7 +37,7 @@ class nt_plan(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
                 ("chunks_per_lane", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
                 ("threads_per_block", ctypes.c_int32), ("aligned", ctypes.c_int32),
-                ("persistent", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("persistent", ctypes.c_int32), ("cooperative", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("row_chunks", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
 

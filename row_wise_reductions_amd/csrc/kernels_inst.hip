@@ -125,26 +125,28 @@ hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStre
     return hipErrorInvalidValue;
 }
 
-template <int W, int K>
-hipError_t split_go(bool al, const RowArgs &a, hipStream_t s) {
+template <int W, int K, bool AL>
+hipError_t split_al(bool coop, const RowArgs &a, hipStream_t s) {
     const uint32_t grid = (uint32_t)(a.M * a.P);
-    if (al) {
-        hipLaunchKernelGGL((softmax_split_partial<DT, W, K, true>), dim3(grid), dim3(64 * W), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, true>), dim3(grid), dim3(64 * W), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((softmax_split_partial<DT, W, K, false>), dim3(grid), dim3(64 * W), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, false>), dim3(grid), dim3(64 * W), 0, s, a);
+    if (coop) {
+        hipLaunchKernelGGL((softmax_coop<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+        return hipGetLastError();
     }
+    hipLaunchKernelGGL((softmax_split_partial<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t split(int W, int K, bool al, const RowArgs &a, hipStream_t s) {
+template <int W, int K>
+hipError_t split_go(bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return al ? split_al<W, K, true>(coop, a, s) : split_al<W, K, false>(coop, a, s);
+}
+
+hipError_t split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k) \
-    if (W == w && K == k) return split_go<w, k>(al, a, s);
+    if (W == w && K == k) return split_go<w, k>(al, coop, a, s);
     NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8) NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4)
     NTK_CASE(8, 8)
     if constexpr (kWide) {
@@ -177,7 +179,9 @@ hipError_t resident_any(int op, int W, int K, bool al, const RowArgs &a, int64_t
 hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return split(W, K, al, coop, a, s);
+}
 hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
@@ -188,7 +192,9 @@ hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStre
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return split(W, K, al, coop, a, s);
+}
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
@@ -199,7 +205,9 @@ hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStre
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s) { return split(W, K, al, a, s); }
+hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return split(W, K, al, coop, a, s);
+}
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }

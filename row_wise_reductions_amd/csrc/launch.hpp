@@ -28,9 +28,11 @@ hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStre
 hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s);
 hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s);
 
-// Launch the two split-softmax kernels (partials, then merge + write).
-hipError_t launch_split_f32(int W, int K, bool al, const RowArgs &a, hipStream_t s);
-hipError_t launch_split_f16(int W, int K, bool al, const RowArgs &a, hipStream_t s);
-hipError_t launch_split_bf16(int W, int K, bool al, const RowArgs &a, hipStream_t s);
+// Launch the split softmax: with `coop`, the one cooperative kernel
+// (a.P <= COOP_PMAX, x not aliasing y, a.tag unique to the call); otherwise
+// the two kernels (partials, then merge + write).
+hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 
 }  // namespace ntk

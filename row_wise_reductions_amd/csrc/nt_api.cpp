@@ -17,10 +17,12 @@
 //     then output), so no workspace is needed.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <random>
 
 #include "../../include/nt.h"
 #include "launch.hpp"
@@ -58,9 +60,14 @@ Menu menu_for(nt_op op, nt_dtype dt) {
     }
 }
 #undef NT_MENU
-// Split-path chunk shape: 16 KiB per workgroup (4 waves, 4 chunks per lane).
-const Shape kSplit32 = {4, 4};
-const Shape kSplit16 = {4, 4};
+// Split-path chunk shapes.  Up to COOP_PMAX chunks per row: 8 waves with 32
+// values per lane (8 chunks of fp32, 4 of 16-bit types) for the cooperative
+// kernel, so few workgroups per row wait on each other; wider rows: 4 waves,
+// 4 chunks per lane, two kernels.  The shape does not depend on whether the
+// cooperative kernel is enabled, so neither does the workspace size.
+const Shape kSplitCoop32 = {8, 8};
+const Shape kSplitCoop16 = {8, 4};
+const Shape kSplitWide = {4, 4};
 // Looped norm kernel: 512 threads, tiles of 4 chunks per lane.
 const Shape kLooped = {8, 4};
 
@@ -90,6 +97,35 @@ bool env_shape(const char *name, Shape *out) {
 bool debug_on() {
     const char *s = std::getenv("NT_DEBUG");
     return s && *s && std::strcmp(s, "0") != 0;
+}
+
+// Cooperative split softmax (one pass over x) unless NT_COOP=0.
+bool coop_enabled() {
+    const char *s = std::getenv("NT_COOP");
+    return !(s && std::strcmp(s, "0") == 0);
+}
+
+// Polls of the cooperative kernel before it recomputes a missing chunk's
+// record itself (NT_COOP_SPIN overrides; 0 recomputes every chunk that has
+// not arrived at the first look, which tests use).
+int32_t coop_spin() {
+    const char *s = std::getenv("NT_COOP_SPIN");
+    if (s && *s) {
+        const long v = std::strtol(s, nullptr, 10);
+        if (v >= 0 && v <= 65536) return (int32_t)v;
+    }
+    return 1024;
+}
+
+// Tag of the cooperative kernel's workspace records: unique per call within
+// a process (a counter), and with a random start so that records left in a
+// reused buffer by another process are not taken for this call's.
+uint32_t next_tag() {
+    static std::atomic<uint32_t> counter{[] {
+        std::random_device rd;
+        return (uint32_t)rd();
+    }()};
+    return counter.fetch_add(1, std::memory_order_relaxed);
 }
 
 // Chunks a row can touch: N*e/16 when aligned, else up to one more for the
@@ -161,7 +197,8 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         p->grid = M < max_grid ? M : max_grid;
         return NT_OK;
     }
-    Shape s = dt == NT_F32 ? kSplit32 : kSplit16;
+    Shape s = dt == NT_F32 ? kSplitCoop32 : kSplitCoop16;
+    if ((nch + 64 * s.W * s.K - 1) / (64 * s.W * s.K) > ntk::COOP_PMAX) s = kSplitWide;
     Shape o;
     if (env_shape("NT_SPLIT_SHAPE", &o)) s = o;
     const int64_t per = (int64_t)64 * s.W * s.K;
@@ -175,7 +212,10 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     p->threads_per_block = 64 * s.W;
     p->row_chunks = P;
     p->grid = M * P;
-    p->workspace_bytes = M * P * (int64_t)sizeof(float2);
+    // two 64-bit words per (row, chunk): the cooperative kernel's tagged
+    // record; the two-kernel form uses the first 8 bytes as its (m_j, l_j)
+    p->workspace_bytes = M * P * 16;
+    p->cooperative = (P <= ntk::COOP_PMAX && coop_enabled()) ? 1 : 0;
     return NT_OK;
 }
 
@@ -214,11 +254,11 @@ hipError_t launch_looped(nt_dtype dt, int op, const nt_plan &p, const ntk::RowAr
 }
 
 hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
-    const bool al = p.aligned != 0;
+    const bool al = p.aligned != 0, coop = p.cooperative != 0;
     switch (dt) {
-    case NT_F32: return ntk::launch_split_f32(p.waves_per_row, p.chunks_per_lane, al, a, s);
-    case NT_F16: return ntk::launch_split_f16(p.waves_per_row, p.chunks_per_lane, al, a, s);
-    case NT_BF16: return ntk::launch_split_bf16(p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_F32: return ntk::launch_split_f32(p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
+    case NT_F16: return ntk::launch_split_f16(p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
+    case NT_BF16: return ntk::launch_split_bf16(p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -226,9 +266,9 @@ hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hi
 void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p) {
     std::fprintf(stderr,
                  "[nt] %s M=%lld N=%lld dt=%d: path %s W=%d K=%d rows/block=%d threads=%d aligned=%d"
-                 " persistent=%d grid=%lld chunks/row=%lld ws=%lld\n",
+                 " persistent=%d cooperative=%d grid=%lld chunks/row=%lld ws=%lld\n",
                  what, (long long)M, (long long)N, (int)dt, p.split == 1 ? "split" : p.split == 2 ? "looped" : "single-pass", p.waves_per_row,
-                 p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, p.persistent, (long long)p.grid,
+                 p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, p.persistent, p.cooperative, (long long)p.grid,
                  (long long)p.row_chunks, (long long)p.workspace_bytes);
 }
 
@@ -320,6 +360,13 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void
         if (workspace_bytes < nt_softmax_workspace_bytes(M, N, dt)) return NT_ERR_WORKSPACE;
         a.ws = static_cast<float2 *>(workspace);
         a.P = (int32_t)p.row_chunks;
+        // in place, a chunk recomputed by another workgroup could already
+        // hold outputs: the two-kernel form reads x completely first
+        if (x == y) p.cooperative = 0;
+        if (p.cooperative) {
+            a.tag = next_tag();
+            a.spin = coop_spin();
+        }
     }
     return run(NT_OP_SOFTMAX, M, N, dt, p, a, stream);
 }

@@ -62,6 +62,8 @@ struct RowArgs {
     int32_t P;           // split softmax: chunks per row
     float eps;
     float inv_n;         // 1/N in fp32
+    uint32_t tag;        // cooperative split softmax: this call's record tag
+    int32_t spin;        // cooperative split softmax: polls before recomputing
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -942,17 +944,87 @@ row_looped(RowArgs a) {
 // ---------------------------------------------------------------------------
 // Split online softmax for rows too wide for one group's registers.
 // The row is cut into P chunks of 64*W*K 16-byte pieces; workgroup b handles
-// chunk j = b mod P of row r = b / P.
-//   split_partial:  (m_j, l_j) = (max of chunk, sum exp(x - m_j)) -> ws[r*P + j]
-//   split_finalize: m = max_j m_j, l = sum_j l_j * exp(m_j - m) (the online
-//                   normalizer merge), then y = exp(x - m) / l on its chunk.
+// chunk j = b mod P of row r = b / P.  Per chunk: (m_j, l_j) = (max of the
+// chunk, sum exp(x - m_j)); per row: m = max_j m_j, l = sum_j l_j*exp(m_j - m)
+// (the online normalizer merge); then y = exp(x - m) / l on every chunk.
 // ---------------------------------------------------------------------------
+
+// (max, denominator) of one chunk of a softmax row, from its loaded and
+// finished words: m_j = max over the chunk, l_j = sum of 2^(x*log2e - c_j)
+// with c_j = m_j*log2e rounded to fp32.  Every path that needs a chunk's
+// pair (the two-kernel split, the cooperative kernel for its own chunk and
+// for a chunk it recomputes) calls this, so the pair is bitwise the same
+// whichever workgroup computes it.
+template <int DT, int W, int K>
+__device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red)[2][W], int wv, int lane) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    float v[K][VEC];
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
+    const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red[0], wv, lane);
+    float cj;
+    {
+#pragma clang fp contract(off)
+        cj = mx * LOG2E;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -cj));
+    s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
+    if (mx == -__builtin_inff()) s = 0.f;    // a fully masked chunk holds no mass
+    return make_float2(mx, s);
+}
+
+// Merge of a row's P chunk pairs q[0..P) (global or LDS) by one wave, in a
+// fixed order: m = max_j m_j, l = sum_j l_j * 2^(c_j - c) with c = m*log2e
+// (the online-normalizer rescaling).  Returns c and 1/l.  Every wave that
+// calls it on the same pairs gets the same bits.
+template <class Q>
+__device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, float &inv) {
+    float m = -__builtin_inff();
+    for (int p = lane; p < P; p += 64) m = __builtin_fmaxf(m, q[p].x);
+    m = wave_allreduce(m, MaxOp());
+    float l = 0.f;
+    {
+#pragma clang fp contract(off)
+        c = m * LOG2E;
+        for (int p = lane; p < P; p += 64) {
+            const float2 e = q[p];
+            const float cj = e.x * LOG2E;    // rounded exactly as in chunk_stats
+            l += (e.x == -__builtin_inff()) ? 0.f : e.y * __builtin_amdgcn_exp2f(cj - c);
+        }
+    }
+    l = wave_allreduce(l, SumOp());
+    if (m == -__builtin_inff()) l = __builtin_nanf("");   // all -inf row: NaN, as the formula
+    inv = rcp_approx(l);
+}
+
+// Output of one chunk: y = 2^(x*log2e - c) * (1/l), rounded once to the type.
+template <int DT, int W, int K, bool AL>
+__device__ __forceinline__ void softmax_chunk_out(const uint4 (&raw)[K], const RowGeom<DT, AL> &geo, char *yr, int t,
+                                                  int32_t N, bool yvec, int64_t cbase, float c, float inv) {
+    constexpr int VEC = dt_info<DT>::VEC, TPR = 64 * W;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v[VEC];
+        unpack<DT>(raw[k], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], LOG2E, -c)) * inv;
+        store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
+    }
+}
+
+// Two-kernel form: the partial kernel writes each chunk's (m_j, l_j) to the
+// workspace, the finalize kernel merges a row's pairs and writes the chunk's
+// outputs (reading x a second time).
 
 template <int DT, int W, int K, bool AL>
 __global__ void __launch_bounds__(64 * W)
 softmax_split_partial(RowArgs a) {
     using I = dt_info<DT>;
-    constexpr int VEC = I::VEC, TPR = 64 * W;
+    constexpr int TPR = 64 * W;
     const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
     const int32_t N = a.N, P = a.P;
     const int64_t row = blockIdx.x / P;
@@ -966,26 +1038,15 @@ softmax_split_partial(RowArgs a) {
     // temporal loads: the finalize kernel reads this chunk again
     load_row<DT, AL, K, TPR, false>(raw, geo, t, N, cbase);
     finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
-    float v[K][VEC];
-#pragma unroll
-    for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
-    float mx = group_allreduce<W>(lane_max(v), MaxOp(), red[0], wv, lane);
-    const float cj = mx * LOG2E;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -cj));
-    s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
-    if (mx == -__builtin_inff()) s = 0.f;    // a fully masked chunk holds no mass
-    if (t == 0) a.ws[row * P + j] = make_float2(mx, s);
+    const float2 q = chunk_stats<DT, W, K>(raw, red, wv, lane);
+    if (t == 0) a.ws[row * P + j] = q;
 }
 
 template <int DT, int W, int K, bool AL>
 __global__ void __launch_bounds__(64 * W)
 softmax_split_finalize(RowArgs a) {
     using I = dt_info<DT>;
-    constexpr int VEC = I::VEC, TPR = 64 * W;
+    constexpr int TPR = 64 * W;
     const int t = threadIdx.x, lane = t & 63;
     const int32_t N = a.N, P = a.P;
     const int64_t row = blockIdx.x / P;
@@ -1002,35 +1063,114 @@ softmax_split_finalize(RowArgs a) {
     const int64_t cbase = j * (int64_t)(TPR * K);
     load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
 
-    // merge the row's P partials; every wave does it redundantly, in the
-    // same order, so every workgroup of the row gets identical (m, l)
-    const float2 *wr = a.ws + row * P;
-    float m = -__builtin_inff();
-    for (int p = lane; p < P; p += 64) m = __builtin_fmaxf(m, wr[p].x);
-    m = wave_allreduce(m, MaxOp());
-    // chunk j's terms are 2^(x*log2e - c_j) with c_j = m_j*log2e rounded to
-    // fp32; rescaled to the row's c they carry the factor 2^(c_j - c)
-    const float c = m * LOG2E;
-    float l = 0.f;
-    for (int p = lane; p < P; p += 64) {
-#pragma clang fp contract(off)
-        const float2 q = wr[p];
-        const float cj = q.x * LOG2E;    // rounded exactly as in split_partial
-        l += (q.x == -__builtin_inff()) ? 0.f : q.y * __builtin_amdgcn_exp2f(cj - c);
-    }
-    l = wave_allreduce(l, SumOp());
-    if (m == -__builtin_inff()) l = __builtin_nanf("");   // all -inf row: NaN, as the formula
-    const float inv = rcp_approx(l);
+    // every wave merges the row's pairs redundantly, in the same order
+    float c, inv;
+    merge_pairs(a.ws + row * P, P, lane, c, inv);
     finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
+    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv);
+}
 
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        float v[VEC];
-        unpack<DT>(raw[k], v);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], LOG2E, -c)) * inv;
-        store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
+// ---------------------------------------------------------------------------
+// Cooperative split softmax: the same chunks and arithmetic as the two
+// kernels above in ONE pass, so x is read once.  Each workgroup loads its
+// chunk, computes (m_j, l_j), and publishes it as a record of two 64-bit
+// words {tag, bits of m_j} and {tag, bits of l_j}, each written and read as
+// one relaxed device-scope atomic; `tag` is unique to the call, so a record
+// is valid only if both words carry it and the workspace needs no clearing.
+// Wave 0 then polls the row's other records.  A record still missing after
+// `spin` polls is recomputed from x by this workgroup itself (chunk_stats on
+// the same chunk gives the same bits), so the result never depends on which
+// workgroups run at the same time and every wait is bounded.  The merge and
+// the output are those of the finalize kernel, so both paths agree bitwise.
+// x must not alias y: a recomputed chunk may already have been overwritten.
+// ---------------------------------------------------------------------------
+
+constexpr int COOP_PMAX = 128;    // chunks per row the cooperative kernel accepts
+
+template <int DT, int W, int K, bool AL>
+__global__ void __launch_bounds__(64 * W)
+softmax_coop(RowArgs a) {
+    using I = dt_info<DT>;
+    constexpr int TPR = 64 * W, NB = COOP_PMAX / 64;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N, P = a.P;
+    const int64_t row = blockIdx.x / P;
+    const int j = (int)(blockIdx.x - row * P);
+    const int64_t rowbytes = (int64_t)N * I::E;
+    const char *xr = a.x + row * rowbytes;
+    char *yr = a.y + row * rowbytes;
+    const RowGeom<DT, AL> geo(xr, N);
+    bool yvec = true;
+    if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+    __shared__ float red[2][W];
+    __shared__ float2 qs[COOP_PMAX];
+    __shared__ uint64_t miss[NB];
+
+    uint4 raw[K];
+    const int64_t cbase = (int64_t)j * (TPR * K);
+    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
+    const float2 mine = chunk_stats<DT, W, K>(raw, red, wv, lane);
+
+    uint64_t *rec = reinterpret_cast<uint64_t *>(a.ws) + row * P * 2;
+    const uint64_t tg = (uint64_t)a.tag << 32;
+    if (t == 0) {
+        __hip_atomic_store(rec + 2 * j, tg | __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + 2 * j + 1, tg | __float_as_uint(mine.y), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        qs[j] = mine;
     }
+    if (wv == 0) {
+        // bit b of `pending`: this lane's record b*64 + lane is still missing
+        uint32_t pending = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int p = b * 64 + lane;
+            if (p < P && p != j) pending |= 1u << b;
+        }
+        for (int it = 0;; ++it) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (pending >> b & 1) {
+                    const int p = b * 64 + lane;
+                    const uint64_t w0 = __hip_atomic_load(rec + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint64_t w1 =
+                        __hip_atomic_load(rec + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((w0 >> 32) == a.tag && (w1 >> 32) == a.tag) {
+                        qs[p] = make_float2(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1));
+                        pending &= ~(1u << b);
+                    }
+                }
+            }
+            if (__ballot(pending != 0) == 0 || it >= a.spin) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint64_t m = __ballot((pending >> b) & 1);
+            if (lane == 0) miss[b] = m;
+        }
+    }
+    __syncthreads();
+    // records that did not arrive: recompute them here (uniform loop)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        uint64_t m = miss[b];
+        while (m) {
+            const int q = b * 64 + __builtin_ctzll(m);
+            m &= m - 1;
+            uint4 r2[K];
+            const int64_t qbase = (int64_t)q * (TPR * K);
+            load_row<DT, AL, K, TPR>(r2, geo, t, N, qbase);
+            finish_row<DT, AL, K, TPR>(r2, geo, xr, t, N, I::NEG_INF_WORD, qbase);
+            const float2 e = chunk_stats<DT, W, K>(r2, red, wv, lane);
+            if (t == 0) qs[q] = e;
+        }
+    }
+    __syncthreads();
+    float c, inv;
+    merge_pairs(static_cast<const float2 *>(qs), P, lane, c, inv);
+    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv);
 }
 
 }  // namespace ntk

@@ -55,6 +55,8 @@ def kernels_of(w) -> list[str]:
     dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dt]
     p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
     W, K, al = p["waves_per_row"], p["chunks_per_lane"], _b(p["aligned"])
+    if p["split"] == 1 and p["cooperative"]:
+        return [f"ntk::softmax_coop<{dt}, {W}, {K}, {al}>"]
     if p["split"] == 1:
         return [f"ntk::softmax_split_partial<{dt}, {W}, {K}, {al}>",
                 f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}>"]

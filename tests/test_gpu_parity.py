@@ -195,6 +195,87 @@ def test_split_path_forced(dt, N, monkeypatch):
         parity_case("softmax", x, dt, x_off=off, y_off=off, what=f"split {dt} N={N} off={off}")
 
 
+def softmax_with_ws(x_t, dt, ws, y_t=None):
+    """nt_softmax_rows with a caller-provided workspace tensor (uint8)."""
+    M, N = x_t.shape
+    y = y_t if y_t is not None else torch.empty_like(x_t)
+    rc = nt.nt_softmax_rows(M, N, DT_CODE[dt], x_t.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
+                            torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, nt.nt_status_string(rc)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [65536, 100003, 262144, 2097152])
+def test_cooperative_split_bitwise(dt, N, monkeypatch):
+    """The one-kernel cooperative split (x read once), the same kernel with
+    every record that has not arrived at the first look recomputed by the
+    waiting workgroup (NT_COOP_SPIN=0), and the two-kernel split give
+    bitwise identical outputs, which match the oracle; up to the largest
+    cooperative width (128 chunks per row)."""
+    M = 9
+    code = DT_CODE[dt]
+    x = rand_bits(N + 7, M, N, dt, scale=2.0)
+    rng = np.random.default_rng(N)
+    spike = workloads.encode(np.array([30.0]), dt)[0]
+    for r in range(M):
+        x[r, rng.choice(N, 8, replace=False)] = spike
+    x[3, : N // 2] = -np.inf if dt == "f32" else workloads.NEG_INF_BITS[dt]   # masked first half
+    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    ref, _, _ = oracle_for("softmax", x, dt)
+    for off in (0, 1):
+        al = off == 0 and (N * (4 if dt == "f32" else 2)) % 16 == 0
+        plan = nt.nt_plan_launch(0, M, N, code, al)
+        # a misaligned row of 2^21 elements touches a 129th chunk: two kernels
+        assert plan["split"] == 1 and plan["cooperative"] == (plan["row_chunks"] <= 128), plan
+        say(f"case coop {dt} N={N} off={off} P={plan['row_chunks']}")
+        x_t = to_dev(x, dt, off)
+        ws = torch.empty(nt.nt_softmax_workspace_bytes(M, N, code), dtype=torch.uint8, device="cuda")
+        y_coop = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
+        check_output(y_coop, ref, dt, f"coop {dt} N={N} off={off}")
+        monkeypatch.setenv("NT_COOP_SPIN", "0")
+        y_rec = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
+        monkeypatch.delenv("NT_COOP_SPIN")
+        monkeypatch.setenv("NT_COOP", "0")
+        y_two = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
+        monkeypatch.delenv("NT_COOP")
+        assert np.array_equal(y_coop, y_rec), "recomputed records differ from published ones"
+        assert np.array_equal(y_coop, y_two), "cooperative and two-kernel split differ"
+
+
+def test_cooperative_split_ignores_stale_and_garbage_workspace():
+    """Records left in the workspace by an earlier call, or arbitrary bytes,
+    are never taken for this call's (each call tags its records)."""
+    M, N = 16, 262144
+    a = rand_bits(1, M, N, "f32", scale=2.0)
+    b = rand_bits(2, M, N, "f32", scale=5.0, loc=-3.0)
+    assert nt.nt_plan_launch(0, M, N, nt.NT_F32, True)["cooperative"] == 1
+    ws = torch.empty(nt.nt_softmax_workspace_bytes(M, N, nt.NT_F32), dtype=torch.uint8, device="cuda")
+    for i, x in enumerate((a, b, a)):                 # the same workspace, one call after another
+        say(f"case coop stale-workspace call {i}")
+        y = softmax_with_ws(to_dev(x, "f32"), "f32", ws)
+        check_output(to_host_bits(y, "f32"), oracle_for("softmax", x, "f32")[0], "f32", f"stale call {i}")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
+    say("case coop garbage workspace")
+    y = softmax_with_ws(to_dev(b, "f32"), "f32", ws)
+    check_output(to_host_bits(y, "f32"), oracle_for("softmax", b, "f32")[0], "f32", "garbage workspace")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_in_place(dt):
+    """In place on the split path (the two-kernel form reads x completely
+    before any output is written)."""
+    M, N = 4, 262144 if dt == "f32" else 524288
+    x = rand_bits(3, M, N, dt, scale=2.0)
+    ref, _, _ = oracle_for("softmax", x, dt)
+    x_t = to_dev(x, dt)
+    say(f"case split in place {dt}")
+    y, _, _ = run_op("softmax", x_t, dt, y_t=x_t)
+    check_output(to_host_bits(x_t, dt), ref, dt, f"split in place {dt}")
+
+
 @pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [1000, 4096, 100003])

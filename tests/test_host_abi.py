@@ -95,8 +95,9 @@ def test_empty_is_noop():
 def test_workspace_bytes():
     assert nt.nt_softmax_workspace_bytes(1024, 781, F32) == 0          # single pass
     assert nt.nt_softmax_workspace_bytes(131072, 4096, BF16) == 0
-    # 1 MiB fp32 rows: 64 chunks of 16 KiB (+1 for a misaligned head) per row
-    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 65 * 8
+    # 1 MiB fp32 rows: 16 chunks of 64 KiB (+1 for a misaligned head) per
+    # row, a 16-byte record (two tagged 64-bit words) per chunk
+    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 17 * 16
     assert nt.nt_softmax_workspace_bytes(-1, 8, F32) == 0
     assert nt.nt_softmax_workspace_bytes(4, 8, 9) == 0
 
@@ -112,8 +113,29 @@ def test_plans_of_the_workloads():
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
     assert p["split"] == 0
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
-    assert p["split"] == 1 and p["row_chunks"] == 64 and p["grid"] == 64 * 64
-    assert p["workspace_bytes"] == 64 * 64 * 8
+    assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 64 * 16
+    assert (p["waves_per_row"], p["chunks_per_lane"]) == (8, 8)
+    assert p["workspace_bytes"] == 64 * 16 * 16 and p["cooperative"] == 1
+
+
+def test_cooperative_split_limits():
+    # one kernel up to 128 chunks per row (16384 elements each: 8 waves with
+    # 32 values per lane), two kernels (16 KiB chunks) beyond
+    for dt in (F32, F16, BF16):
+        p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 2, 128 * 16384, dt, True)
+        assert (p["split"], p["row_chunks"], p["cooperative"]) == (1, 128, 1)
+        assert p["waves_per_row"] * p["chunks_per_lane"] * 16 // (4 if dt == F32 else 2) == 256
+        p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 2, 128 * 16384 + 8, dt, True)
+        assert (p["split"], p["cooperative"], p["waves_per_row"], p["chunks_per_lane"]) == (1, 0, 4, 4)
+        assert p["row_chunks"] == -(-(128 * 16384 + 8) * (4 if dt == F32 else 2) // 16 // 1024)
+    # never on the single pass
+    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 2, 4096, F32, True)["cooperative"] == 0
+
+
+def test_cooperative_split_can_be_switched_off(monkeypatch):
+    monkeypatch.setenv("NT_COOP", "0")
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
+    assert (p["split"], p["cooperative"]) == (1, 0)
 
 
 def test_plan_capacity_covers_row():
