@@ -103,8 +103,9 @@ size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
  * 128 chunks per row this is one kernel that reads x once (the workgroups of a
  * row exchange their pairs through the workspace; a pair that does not arrive
  * within a bounded wait is recomputed from x, so the result does not depend on
- * scheduling); wider rows, and in-place calls, use two kernels and read x
- * twice.  Either way the results are bitwise the same.
+ * scheduling); wider rows, in-place calls and calls on a stream that is being
+ * captured into a graph use two kernels and read x twice.  Either way the
+ * results are bitwise the same.
  */
 nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
                           const void *x, void *y,
@@ -155,7 +156,8 @@ typedef struct {
     int32_t cooperative;      /* split path: 1 when one kernel does both phases (x read once;
                                  the workgroups of a row exchange their partial results
                                  through the workspace); 0: two kernels, x read twice.
-                                 In-place calls (y == x) always use the two kernels    */
+                                 In-place calls (y == x) and calls during stream capture
+                                 always use the two kernels                             */
     int64_t grid;             /* workgroups per launch                                  */
     int64_t row_chunks;       /* split path: chunks per row (0 on the single pass)      */
     int64_t workspace_bytes;  /* split path: workspace size (0 on the single pass)      */

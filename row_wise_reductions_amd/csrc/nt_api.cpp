@@ -363,6 +363,16 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void
         // in place, a chunk recomputed by another workgroup could already
         // hold outputs: the two-kernel form reads x completely first
         if (x == y) p.cooperative = 0;
+        // a captured graph would replay this call's tag, and a replay could
+        // take the previous replay's records for its own
+        if (p.cooperative) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+                (void)hipGetLastError();
+                return NT_ERR_HIP;
+            }
+            if (cs != hipStreamCaptureStatusNone) p.cooperative = 0;
+        }
         if (p.cooperative) {
             a.tag = next_tag();
             a.spin = coop_spin();

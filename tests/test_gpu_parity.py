@@ -360,6 +360,50 @@ def test_bitwise_repeatable(N):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+def test_graph_capture_and_replay():
+    """Calls captured into a HIP graph (torch.cuda.graph) and replayed with
+    new inputs copied in (eagerly) between replays: every replay matches the
+    oracle.  Under capture the split softmax takes its two-kernel form (a
+    replayed call reuses its record tag, so the cooperative kernel is not
+    captured)."""
+    M, N = 8, 262144
+    xs = [rand_bits(40 + i, M, N, "f32", scale=2.0 + i) for i in range(3)]
+    rs = [rand_bits(50 + i, 16, 8192, "bf16") for i in range(3)]
+    w = rand_bits(60, 1, 8192, "bf16", scale=0.3, loc=1.0)[0]
+    x_t, r_t, w_t = to_dev(xs[0], "f32"), to_dev(rs[0], "bf16"), to_dev(w, "bf16")
+    y_t, ry_t = torch.empty_like(x_t), torch.empty_like(r_t)
+    wsb = nt.nt_softmax_workspace_bytes(M, N, nt.NT_F32)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    assert nt.nt_plan_launch(0, M, N, nt.NT_F32, True)["cooperative"] == 1
+    assert nt.nt_plan_launch(2, 16, 8192, nt.NT_BF16, True)["persistent"] == 1
+
+    def calls(stream):
+        assert nt.nt_softmax_rows(M, N, nt.NT_F32, x_t.data_ptr(), y_t.data_ptr(), ws.data_ptr(), wsb,
+                                  stream) == 0
+        assert nt.nt_rmsnorm_rows(16, 8192, nt.NT_BF16, 1e-6, r_t.data_ptr(), w_t.data_ptr(),
+                                  ry_t.data_ptr(), stream) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(torch.cuda.current_stream().cuda_stream)
+    for i in (1, 0, 2, 2, 1):
+        say(f"case graph replay inputs {i}")
+        x_t.copy_(to_dev(xs[i], "f32"))
+        r_t.copy_(to_dev(rs[i], "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_output(to_host_bits(y_t, "f32"), oracle_for("softmax", xs[i], "f32")[0], "f32", f"graph softmax {i}")
+        check_output(to_host_bits(ry_t, "bf16"), oracle_for("rmsnorm", rs[i], "bf16", 1e-6, w)[0], "bf16",
+                     f"graph rmsnorm {i}")
+
+
 def test_side_stream_ordering():
     x = rand_bits(10, 256, 4096, "f16", loc=1.0)
     s = torch.cuda.Stream()
