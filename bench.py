@@ -21,7 +21,10 @@ every launch gives each workload's own GB/s (per_workload).
 
 Prints ONE JSON line.  Flags: --gpus (only 1 is supported), --steps, --warmup,
 --only NAME[,NAME] (time a subset, rotating buffer sets so the 256 MiB
-Infinity Cache cannot serve them), --no-cpu-baseline.
+Infinity Cache cannot serve them), --no-cpu-baseline; --calibrate (the plain
+1 GiB copy: attainable bandwidth, and the counter calibration) and
+--copy-at-sizes (the plain copy at each workload's byte count) replace the
+suite.
 """
 from __future__ import annotations
 
@@ -197,6 +200,40 @@ def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
     print(json.dumps(out), flush=True)
 
 
+def copy_at_sizes(torch, steps, warmup, workloads):
+    """The plain streaming copy of libntcal.so moving each workload's bytes
+    (read M*N*e, write M*N*e), rotating buffer sets of >= 1 GiB so the
+    Infinity Cache cannot serve them: what a kernel that only streams its
+    rows could reach at that size (launch and ramp included).  Event-timed
+    like the breakdown pass; median of `steps` launches."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_reductions_amd", "libntcal.so"))
+    lib.ntcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ntcal_copy.restype = ctypes.c_int
+    sh = torch.cuda.current_stream().cuda_stream
+    out = {"copy_at_sizes": "plain streaming copy (ntcal_copy_kernel) of each workload's read bytes", "workloads": []}
+    for w in workloads:
+        nb = w.M * w.N * w.elem_bytes // 16 * 16
+        R = max(1, -(-(1 << 30) // (2 * nb)))
+        src = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
+        dst = [torch.empty(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
+        for i in range(warmup):
+            assert lib.ntcal_copy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, sh) == 0
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            lib.ntcal_copy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, sh)
+            b.record()
+        torch.cuda.synchronize()
+        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+        out["workloads"].append({"workload": w.name, "bytes_read": nb, "bytes_written": nb, "buffer_sets": R,
+                                 "median_ms": round(ms, 5), "GBps": round(2 * nb / (ms * 1e-3) / 1e9, 1)})
+        del src, dst
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -205,7 +242,9 @@ def main():
     ap.add_argument("--only", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
-                    help="time a plain 1 GiB device-to-device copy (torch copy_) instead")
+                    help="time the plain 1 GiB streaming copy (and torch copy_) instead")
+    ap.add_argument("--copy-at-sizes", action="store_true",
+                    help="time the plain streaming copy at each workload's byte count instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): rows are independent, so a "
@@ -222,6 +261,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate:
         calibrate_copy(torch, args.steps, args.warmup)
+        return
+    if args.copy_at_sizes:
+        names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]
+        copy_at_sizes(torch, args.steps, args.warmup, [workloads.BY_NAME[n] for n in names])
         return
     names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]
     suite = args.only is None
