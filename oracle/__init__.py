@@ -60,9 +60,10 @@ def load(path: str = _LIB_PATH):
     lib.or_layernorm.argtypes = [i64, i64, i32, ctypes.c_float, vp, vp, vp, dp, dp, dp]
     lib.or_rmsnorm.argtypes = [i64, i64, i32, ctypes.c_float, vp, vp, dp]
     lib.or_softmax_online.argtypes = [i64, i64, i32, i64, vp, dp]
+    lib.or_add.argtypes = [i64, i32, vp, vp, dp]
     lib.or_num_threads.argtypes = []
     for f in ("or_decode", "or_softmax", "or_layernorm", "or_rmsnorm",
-              "or_softmax_online", "or_num_threads"):
+              "or_softmax_online", "or_add", "or_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
@@ -147,6 +148,41 @@ def rmsnorm(x: np.ndarray, dt, eps: float, weight=None, lib=None) -> np.ndarray:
     y = np.empty((M, N), dtype=np.float64)
     _check((lib or load()).or_rmsnorm(M, N, code, float(eps), _ptr(xb), _ptr(w), _ptr(y)))
     return y
+
+
+def add(x: np.ndarray, r: np.ndarray, dt, lib=None) -> np.ndarray:
+    """Residual add h = x + r in float64 (same shape as x); round it once to
+    the storage type with ``compare.round_to`` to get the stored h."""
+    code = dtype_code(dt)
+    xb, rb = _as_bits(x, code), _as_bits(r, code)
+    if xb.shape != rb.shape:
+        raise ValueError("x and r must have the same shape")
+    h = np.empty(xb.shape, dtype=np.float64)
+    _check((lib or load()).or_add(xb.size, code, _ptr(xb), _ptr(rb), _ptr(h)))
+    return h
+
+
+def _stored(h64: np.ndarray, dt) -> np.ndarray:
+    """float64 -> the stored values of `dt`, in the layout the other oracle
+    functions take (float32 array for f32, raw uint16 bits otherwise)."""
+    from . import compare
+    bits = compare.round_to(h64, dt)
+    return bits.view(np.float32) if dtype_code(dt) == F32 else bits
+
+
+def add_rmsnorm(x: np.ndarray, r: np.ndarray, dt, eps: float, weight=None, lib=None):
+    """Fused residual add + RMSNorm, plain definition, unfused: h = x + r
+    stored in the input type, then the RMSNorm of that stored h.  Returns
+    (h as stored values, y in float64)."""
+    h = _stored(add(x, r, dt, lib=lib), dt)
+    return h, rmsnorm(h, dt, eps, weight=weight, lib=lib)
+
+
+def add_layernorm(x: np.ndarray, r: np.ndarray, dt, eps: float, gamma=None, beta=None, lib=None):
+    """Fused residual add + LayerNorm, plain definition, unfused.  Returns
+    (h as stored values, y, mean, rstd), the last three in float64."""
+    h = _stored(add(x, r, dt, lib=lib), dt)
+    return (h,) + tuple(layernorm(h, dt, eps, gamma=gamma, beta=beta, lib=lib))
 
 
 def num_threads() -> int:

@@ -28,6 +28,9 @@
  *    used: mean = sum(x)/N, biased variance = sum((x-mean)^2)/N,
  *    rstd = 1/sqrt(var + eps) (eps inside the root, as in the RMSNorm kernel),
  *    y = (x - mean) * rstd * gamma + beta, gamma = 1 and beta = 0 when absent.
+ *  - residual add of a fused add + norm (or_add): named as a kernel pattern
+ *    in "Portable Triton Kernels" (References), no formula printed; h = x + r
+ *    stored in the input type, then the plain norm of that stored h.
  *  - online softmax: "Triton: Block-Level GPU Programming Without CUDA",
  *    section "How Flash Attention Uses Triton" (running max m and
  *    denominator l rescaled by alpha = exp(m_prev - m_new) per block; the
@@ -185,6 +188,29 @@ int or_rmsnorm(int64_t M, int64_t N, int dtype, float eps, const void *x,
             y[base + j] = or_load(dtype, x, base + j) * inv * wv;
         }
     }
+    return 0;
+}
+
+/*
+ * Residual add: h = x + r elementwise over `count` stored values of one type,
+ * the first half of a fused "add + norm" step.  The pages name a fused
+ * add + norm pattern ("Portable Triton Kernels", References) and explain
+ * fusion as reading each input once and writing each result once ("Triton:
+ * Block-Level GPU Programming Without CUDA", kernel fusion), but print no
+ * formula.  Reading taken: the updated residual stream h is stored in the
+ * input type, rounded once from the exact sum (by the caller's comparator),
+ * and the norm is the plain norm of that stored h.  The double sum returned
+ * here rounds to the storage type exactly as the exact real sum does: double
+ * has at least 29 more significand bits than any storage type, so when the
+ * sum is not exact in double its error is far below the distance to the
+ * nearest storage-type rounding boundary.
+ */
+int or_add(int64_t count, int dtype, const void *x, const void *r, double *h)
+{
+    if (count < 0 || (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16)) return 1;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);
     return 0;
 }
 

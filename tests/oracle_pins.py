@@ -405,4 +405,82 @@ def pin_rmsnorm_torch(lib):
         assert _rel(y, ref) < 1e-13, dt
 
 
+# ----------------------------------------------------------------------------
+# residual add (fused add + norm): h = x + r stored in the input type
+# ----------------------------------------------------------------------------
+
+def _wide_pairs(seed, n, dt):
+    """Random stored values of `dt` spread over many binades (subnormals,
+    exact cancellations and large exponent gaps included), as raw storage."""
+    rng = np.random.default_rng(seed)
+    if dt == "f32":
+        mag = rng.standard_normal(n) * np.exp2(rng.integers(-140, 100, n).astype(np.float64))
+        x = mag.astype(np.float32)
+        r = (rng.standard_normal(n) * np.exp2(rng.integers(-140, 100, n).astype(np.float64))).astype(np.float32)
+        r[: n // 8] = -x[: n // 8]                       # exact cancellation
+        return np.nan_to_num(x, posinf=1.0, neginf=-1.0), np.nan_to_num(r, posinf=1.0, neginf=-1.0)
+    # every 16-bit pattern except inf/NaN, paired at random
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp_all_ones = (bits & (0x7C00 if dt == "f16" else 0x7F80)) == (0x7C00 if dt == "f16" else 0x7F80)
+    finite = bits[~exp_all_ones]
+    x = rng.choice(finite, n)
+    r = rng.choice(finite, n)
+    r[: n // 8] = x[: n // 8] ^ np.uint16(0x8000)        # exact cancellation
+    return x, r
+
+
+def pin_add_matches_ieee_libraries(lib):
+    """The stored h (oracle sum rounded once) equals the IEEE sum computed by
+    independent libraries: numpy float32 and float16 addition, torch
+    bfloat16 addition on the CPU (each rounds a float32 sum once, which for
+    these types equals rounding the exact sum)."""
+    import torch
+    from oracle import compare
+    for dt in ("f32", "f16", "bf16"):
+        x, r = _wide_pairs(71, 400000, dt)
+        got = compare.round_to(oracle.add(x, r, dt, lib=lib), dt)
+        if dt == "f32":
+            want = (x + r).view(np.uint32)
+        elif dt == "f16":
+            with np.errstate(over="ignore"):       # sums beyond 65504 round to inf on both sides
+                want = (x.view(np.float16) + r.view(np.float16)).view(np.uint16)
+        else:
+            tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+            tr = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+            want = (tx + tr).view(torch.int16).numpy().view(np.uint16)
+        same = (got == want) | ((compare.ordinal(got, dt) == 0) & (compare.ordinal(want, dt) == 0))
+        assert same.all(), (dt, int((~same).sum()))
+
+
+def pin_add_norm_is_norm_of_stored_sum(lib):
+    """The fused definitions are the norms of the stored sum: h equals the
+    numpy / torch IEEE sum, and y (and LayerNorm's mean) equal the
+    pure-Python norms of that h."""
+    for dt in ("f32", "f16", "bf16"):
+        for N in (1, 7, 64, 781):
+            x = _rng_rows(7000 + N, 3, N, dt, scale=2.0)
+            r = _rng_rows(7100 + N, 3, N, dt, scale=0.5, loc=-1.0)
+            w = _rng_rows(7200 + N, 1, N, dt, scale=0.3, loc=1.0)[0]
+            b = _rng_rows(7300 + N, 1, N, dt, scale=0.3)[0]
+            h, y = oracle.add_rmsnorm(x, r, dt, 1e-6, weight=w, lib=lib)
+            h2, y2, mean, rstd = oracle.add_layernorm(x, r, dt, 1e-5, gamma=w, beta=b, lib=lib)
+            if dt == "f32":
+                want = (x + r)
+            elif dt == "f16":
+                want = (x.view(np.float16) + r.view(np.float16)).view(np.uint16)
+            else:
+                import torch
+                tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+                tr = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+                want = (tx + tr).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(np.asarray(h).view(np.uint8), np.asarray(want).view(np.uint8)), (dt, N)
+            assert np.array_equal(np.asarray(h2).view(np.uint8), np.asarray(want).view(np.uint8)), (dt, N)
+            wd, bd = _decode_py(w, dt), _decode_py(b, dt)
+            for i in range(3):
+                hd = _decode_py(np.asarray(want)[i], dt)
+                assert _rel(y[i], brute.rmsnorm_row(hd, F32_EPS6, wd)) < 1e-13, (dt, N)
+                yl, ml, rl = brute.layernorm_row(hd, F32_EPS5, wd, bd)
+                assert _rel(y2[i], yl) < 1e-12 and _rel([mean[i]], [ml]) < 1e-12, (dt, N)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -34,6 +34,11 @@ MUTANTS = {
     "online_no_rescale": ("l_prev = l_prev * alpha + psum;", "l_prev = l_prev + psum;"),
     "online_alpha_sign": ("exp(m_prev - m_new)", "exp(m_new - m_prev)"),
     "online_final_uses_first_max": ("m_prev = m_new;", "m_prev = (m_prev == -INFINITY) ? m_new : m_prev;"),
+    "add_subtracts": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);",
+                      "h[i] = or_load(dtype, x, i) - or_load(dtype, r, i);"),
+    "add_drops_residual": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);", "h[i] = or_load(dtype, x, i);"),
+    "add_residual_shifted": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);",
+                             "h[i] = or_load(dtype, x, i) + or_load(dtype, r, i > 0 ? i - 1 : i);"),
 }
 
 

@@ -30,6 +30,11 @@ Workloads (name -> shapes, distributions, seeds):
   vocab_softmax_f32        softmax  fp32  M=64 N=262144, x ~ 2 N(0,1), and in every row 8
                                           distinct positions (uniform, without replacement)
                                           set to +30.0                                    seeds 501, 502
+
+Next-row workloads (fused residual add + norm, at the norm workloads' shapes;
+not part of the five-workload suite):
+  add_rmsnorm_bf16_16384x8192  x, w as rmsnorm_bf16_16384x8192; residual r ~ N(0,1)  seed 303
+  add_layernorm_f16_4096       x, gamma, beta as layernorm_f16_4096; r ~ N(0,1)      seed 205
 """
 from __future__ import annotations
 
@@ -113,12 +118,15 @@ class Workload:
 
     def algorithmic_bytes(self) -> int:
         """Bytes the method must move per call: read x once, write y once,
-        read each length-N parameter vector once, write the per-row stats."""
+        read each length-N parameter vector once, write the per-row stats;
+        the fused add + norm also reads the residual once and writes h once."""
         e = self.elem_bytes
         b = 2 * self.M * self.N * e
-        if self.op == "layernorm":
+        if self.op.startswith("add_"):
+            b += 2 * self.M * self.N * e
+        if self.op in ("layernorm", "add_layernorm"):
             b += 2 * self.N * e + 2 * self.M * 4
-        elif self.op == "rmsnorm":
+        elif self.op in ("rmsnorm", "add_rmsnorm"):
             b += self.N * e
         return b
 
@@ -185,12 +193,26 @@ def _mk_vocab(w, rows, M):
     return {"x": x, "spikes": spikes[sel]}
 
 
+def _mk_add_rmsnorm(w, rows, M):
+    d = _mk_rmsnorm(w, rows, M)
+    d["residual"] = normal_rows(303, M, w.N, BF16, rows=rows)
+    return d
+
+
+def _mk_add_layernorm(w, rows, M):
+    d = _mk_layernorm(w, rows, M)
+    d["residual"] = normal_rows(205, M, w.N, F16, rows=rows)
+    return d
+
+
 _MAKERS = {
     "softmax_f32_1024x781": _mk_softmax_f32,
     "layernorm_f16_4096": _mk_layernorm,
     "rmsnorm_bf16_16384x8192": _mk_rmsnorm,
     "causal_softmax_bf16": _mk_causal,
     "vocab_softmax_f32": _mk_vocab,
+    "add_rmsnorm_bf16_16384x8192": _mk_add_rmsnorm,
+    "add_layernorm_f16_4096": _mk_add_layernorm,
 }
 
 WORKLOADS = [
@@ -206,4 +228,10 @@ WORKLOADS = [
     Workload("vocab_softmax_f32", "softmax", F32, 64, 262144,
              desc="vocab-width softmax fp32 64 x 262144 with 8 spikes of +30 per row"),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+NEXT_WORKLOADS = [
+    Workload("add_rmsnorm_bf16_16384x8192", "add_rmsnorm", BF16, 16384, 8192, eps=1e-6,
+             desc="fused residual add + RMSNorm bf16 16384 x 8192"),
+    Workload("add_layernorm_f16_4096", "add_layernorm", F16, 4096, 4096, eps=1e-5,
+             desc="fused residual add + LayerNorm fp16 4096 x 4096"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
