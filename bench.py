@@ -21,7 +21,9 @@ every launch gives each workload's own GB/s (per_workload).
 
 Prints ONE JSON line.  Flags: --gpus (only 1 is supported), --steps, --warmup,
 --only NAME[,NAME] (time a subset, rotating buffer sets so the 256 MiB
-Infinity Cache cannot serve them), --no-cpu-baseline; --calibrate (the plain
+Infinity Cache cannot serve them), --no-cpu-baseline, --no-next (skip the
+fused residual add + norm rows, which are timed after the suite and
+reported under next_rows, outside value); --calibrate (the plain
 1 GiB copy: attainable bandwidth, and the counter calibration) and
 --copy-at-sizes (the plain copy at each workload's byte count) replace the
 suite.
@@ -70,6 +72,11 @@ class Job:
         self.p1 = None if p1 is None else to_dev(p1, w.dt, torch, np)
         self.mean = [torch.empty(w.M, dtype=torch.float32, device="cuda") for _ in range(R)]
         self.rstd = [torch.empty(w.M, dtype=torch.float32, device="cuda") for _ in range(R)]
+        self.fused = w.op.startswith("add_")
+        if self.fused:                               # fused add + norm: residual in, h out
+            r0 = to_dev(data["residual"], w.dt, torch, np)
+            self.r = [r0] + [r0.clone() for _ in range(R - 1)]
+            self.h = [torch.empty_like(x0) for _ in range(R)]
         self.wsb = nt.nt_softmax_workspace_bytes(w.M, w.N, self.dt_code) if w.op == "softmax" else 0
         self.ws = torch.empty(max(self.wsb, 8), dtype=torch.uint8, device="cuda")
         self.i = 0
@@ -81,6 +88,14 @@ class Job:
         if w.op == "softmax":
             rc = nt.nt_softmax_rows(w.M, w.N, self.dt_code, self.x[r].data_ptr(), self.y[r].data_ptr(),
                                     self.ws.data_ptr(), self.wsb, stream)
+        elif w.op == "add_layernorm":
+            rc = nt.nt_add_layernorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.r[r].data_ptr(),
+                                          self.p0.data_ptr(), self.p1.data_ptr(), self.h[r].data_ptr(),
+                                          self.y[r].data_ptr(), self.mean[r].data_ptr(), self.rstd[r].data_ptr(),
+                                          stream)
+        elif w.op == "add_rmsnorm":
+            rc = nt.nt_add_rmsnorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.r[r].data_ptr(),
+                                        self.p0.data_ptr(), self.h[r].data_ptr(), self.y[r].data_ptr(), stream)
         elif w.op == "layernorm":
             rc = nt.nt_layernorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.p0.data_ptr(),
                                       self.p1.data_ptr(), self.y[r].data_ptr(), self.mean[r].data_ptr(),
@@ -241,6 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the fused add + norm rows (timed after the suite, not part of value)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the plain 1 GiB streaming copy (and torch copy_) instead")
     ap.add_argument("--copy-at-sizes", action="store_true",
@@ -349,6 +366,38 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(dom["workload"], dom["bytes"]),
                 "kernel": dom["workload"], "avg_launch_ms": round(dom_ms, 5)}
 
+    # Next rows (fused residual add + norm): timed on their own after the
+    # timed region, not part of `value`; buffer sets rotate past the cache.
+    next_rows = []
+    if suite and not args.no_next:
+        for w in workloads.NEXT_WORKLOADS:
+            data = w.make()
+            per_set = 4 * w.M * w.N * w.elem_bytes
+            j = Job(w, data, max(1, -(-(4 * CACHE_BYTES) // per_set)), torch, np, nt)
+            for _ in range(args.warmup):
+                j.launch(sh)
+            evs = [(ev(), ev()) for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                a.record(stream)
+                j.launch(sh)
+                b.record(stream)
+            torch.cuda.synchronize()
+            durs = [a.elapsed_time(b) for a, b in evs]
+            avg = sum(durs) / len(durs)
+            op = {"add_layernorm": 3, "add_rmsnorm": 4}[w.op]
+            e = w.elem_bytes
+            next_rows.append({"workload": w.name, "op": w.op, "dtype": w.dt, "M": w.M, "N": w.N,
+                              "bytes": j.bytes, "unfused_bytes": j.bytes + 2 * w.M * w.N * e,
+                              "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
+                              "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
+                              "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "traffic": traffic_for(w.name, j.bytes),
+                              "plan": nt.nt_plan_launch(op, w.M, w.N, j.dt_code, True)})
+            log(f"[bench] next row {w.name}: {next_rows[-1]['GBps']} GB/s")
+            del j, data
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
@@ -367,6 +416,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_workload": per,   # from the breakdown pass
+        "next_rows": next_rows,
     }
     print(json.dumps(out), flush=True)
 

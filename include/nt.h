@@ -80,7 +80,8 @@ typedef enum {
     NT_ERR_EPS = 4,        /* eps is negative, infinite or NaN                 */
     NT_ERR_ALIGN = 5,      /* a pointer is not aligned to its element size     */
     NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes */
-    NT_ERR_HIP = 7         /* the HIP runtime reported a launch error          */
+    NT_ERR_HIP = 7,        /* the HIP runtime reported a launch error          */
+    NT_ERR_ALIAS = 8       /* fused add + norm: h and y are the same buffer    */
 } nt_status;
 
 /*
@@ -130,6 +131,40 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
                           const void *x, const void *weight, void *y,
                           void *stream);
 
+/*
+ * Fused residual add + norm: the step right before a norm in a residual
+ * block, in one pass.  h = x + residual, rounded once to `dt` (the updated
+ * residual stream), and the norm of that stored h:
+ *
+ *   nt_add_layernorm_rows  h, y = LayerNorm(h) as nt_layernorm_rows, mean, rstd
+ *   nt_add_rmsnorm_rows    h, y = RMSNorm(h) as nt_rmsnorm_rows
+ *
+ * The pages list fused add + norm among the kernel patterns of "Portable
+ * Triton Kernels" (References) and give fusion's point in "Triton:
+ * Block-Level GPU Programming Without CUDA" (read each input once, write each
+ * result once); no formula is printed.  The reading here: fusing changes no
+ * bit, h is what an add kernel would store and y is bitwise what the plain
+ * norm entry point computes from that h.  Traffic: x and residual read once,
+ * h and y written once (against an extra write and read of h unfused).
+ *
+ * x, residual, h and y are [M, N] arrays of `dt` with the conventions above;
+ * gamma, beta, weight, mean and rstd as in the plain norms.  residual and h
+ * must be non-NULL (NT_ERR_NULL) and lie at the same address modulo 16 as x
+ * (NT_ERR_ALIGN); y may have any element-aligned address.  h may be x or
+ * residual (in place); y may be x or residual; y == h is NT_ERR_ALIAS.
+ * Any other overlap is undefined.
+ */
+nt_status nt_add_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
+                                const void *x, const void *residual,
+                                const void *gamma, const void *beta,
+                                void *h, void *y, float *mean, float *rstd,
+                                void *stream);
+
+nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
+                              const void *x, const void *residual,
+                              const void *weight, void *h, void *y,
+                              void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *nt_status_string(nt_status s);
 
@@ -139,7 +174,13 @@ const char *nt_status_string(nt_status s);
  * every pointer is 16-byte aligned (`aligned16` != 0) or not, with every
  * parameter vector present.
  */
-typedef enum { NT_OP_SOFTMAX = 0, NT_OP_LAYERNORM = 1, NT_OP_RMSNORM = 2 } nt_op;
+typedef enum {
+    NT_OP_SOFTMAX = 0,
+    NT_OP_LAYERNORM = 1,
+    NT_OP_RMSNORM = 2,
+    NT_OP_ADD_LAYERNORM = 3,  /* nt_add_layernorm_rows */
+    NT_OP_ADD_RMSNORM = 4     /* nt_add_rmsnorm_rows   */
+} nt_op;
 
 typedef struct {
     int32_t split;            /* 0: single pass, row held on chip; 1: split online softmax

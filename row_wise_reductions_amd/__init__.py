@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/nt.h``.  The ``nt_*``
 functions take the same arguments as their C counterparts (pointers as
 integers, ``stream`` as a ``hipStream_t`` handle) and return the status code.
-``softmax``, ``layer_norm`` and ``rms_norm`` are conveniences over torch
+``softmax``, ``layer_norm``, ``rms_norm``, ``add_layer_norm`` and
+``add_rms_norm`` are conveniences over torch
 tensors on an AMD GPU: they check contiguity, allocate outputs (and the
 split-path workspace) with torch, and launch on torch's current stream.
 
@@ -20,11 +21,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnt.so")
 
 NT_F32, NT_F16, NT_BF16 = 0, 1, 2
-NT_OP_SOFTMAX, NT_OP_LAYERNORM, NT_OP_RMSNORM = 0, 1, 2
+NT_OP_SOFTMAX, NT_OP_LAYERNORM, NT_OP_RMSNORM, NT_OP_ADD_LAYERNORM, NT_OP_ADD_RMSNORM = 0, 1, 2, 3, 4
 STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4: "NT_ERR_EPS",
-          5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP"}
+          5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP", 8: "NT_ERR_ALIAS"}
 EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_layernorm_rows",
-            "nt_rmsnorm_rows", "nt_status_string", "nt_plan_launch")
+            "nt_rmsnorm_rows", "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
+            "nt_status_string", "nt_plan_launch")
 
 
 class NtError(RuntimeError):
@@ -63,10 +65,13 @@ def lib():
     L.nt_softmax_rows.argtypes = [i64, i64, i32, vp, vp, vp, sz, vp]
     L.nt_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     L.nt_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp]
+    L.nt_add_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.nt_add_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp]
     L.nt_status_string.argtypes = [i32]
     L.nt_status_string.restype = ctypes.c_char_p
     L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
-    for f in ("nt_softmax_rows", "nt_layernorm_rows", "nt_rmsnorm_rows", "nt_plan_launch"):
+    for f in ("nt_softmax_rows", "nt_layernorm_rows", "nt_rmsnorm_rows", "nt_add_layernorm_rows",
+              "nt_add_rmsnorm_rows", "nt_plan_launch"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -88,6 +93,14 @@ def nt_layernorm_rows(M, N, dt, eps, x, gamma, beta, y, mean, rstd, stream) -> i
 
 def nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream) -> int:
     return int(lib().nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream))
+
+
+def nt_add_layernorm_rows(M, N, dt, eps, x, residual, gamma, beta, h, y, mean, rstd, stream) -> int:
+    return int(lib().nt_add_layernorm_rows(M, N, dt, eps, x, residual, gamma, beta, h, y, mean, rstd, stream))
+
+
+def nt_add_rmsnorm_rows(M, N, dt, eps, x, residual, weight, h, y, stream) -> int:
+    return int(lib().nt_add_rmsnorm_rows(M, N, dt, eps, x, residual, weight, h, y, stream))
 
 
 def nt_status_string(code: int) -> str:
@@ -187,3 +200,43 @@ def rms_norm(x, weight=None, eps=1e-6, out=None, stream=None):
     _check(nt_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(weight), _ptr(y),
                            _stream(stream)), "nt_rmsnorm_rows")
     return y
+
+
+def _same_rows(x, r):
+    if r.shape != x.shape or r.dtype != x.dtype or not r.is_contiguous():
+        raise ValueError("residual must be contiguous, of x's shape and dtype")
+
+
+def add_layer_norm(x, residual, gamma=None, beta=None, eps=1e-5, h_out=None, out=None, stream=None):
+    """Fused residual add + LayerNorm: h = x + residual (rounded to x's
+    dtype), y = LayerNorm(h).  Returns (h, y, mean, rstd)."""
+    torch = _torch()
+    M, N = _rows(x)
+    _same_rows(x, residual)
+    h = torch.empty_like(x) if h_out is None else h_out
+    y = torch.empty_like(x) if out is None else out
+    lead = x.shape[:-1]
+    mean = torch.empty(lead, dtype=torch.float32, device=x.device)
+    rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
+    for p in (gamma, beta):
+        if p is not None and (p.numel() != N or p.dtype != x.dtype or not p.is_contiguous()):
+            raise ValueError("gamma/beta must be contiguous, of x's dtype, with N entries")
+    _check(nt_add_layernorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(gamma),
+                                 _ptr(beta), _ptr(h), _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream)),
+           "nt_add_layernorm_rows")
+    return h, y, mean, rstd
+
+
+def add_rms_norm(x, residual, weight=None, eps=1e-6, h_out=None, out=None, stream=None):
+    """Fused residual add + RMSNorm: h = x + residual (rounded to x's dtype),
+    y = RMSNorm(h).  Returns (h, y)."""
+    torch = _torch()
+    M, N = _rows(x)
+    _same_rows(x, residual)
+    h = torch.empty_like(x) if h_out is None else h_out
+    y = torch.empty_like(x) if out is None else out
+    if weight is not None and (weight.numel() != N or weight.dtype != x.dtype or not weight.is_contiguous()):
+        raise ValueError("weight must be contiguous, of x's dtype, with N entries")
+    _check(nt_add_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(weight), _ptr(h),
+                               _ptr(y), _stream(stream)), "nt_add_rmsnorm_rows")
+    return h, y

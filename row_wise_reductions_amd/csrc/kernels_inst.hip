@@ -16,34 +16,41 @@ constexpr int DT = NTK_DT;
 // fp32 holds 4 values per chunk, 16-bit types 8.
 constexpr bool kWide = dt_info<DT>::VEC == 4;
 
-template <int OP, int W, int K, bool PR>
+template <int OP, int W, int K, bool PR, bool RES>
 hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     constexpr int T = GroupShape<W>::THREADS;
     if (al)
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true, PR>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true, PR, RES>), dim3((uint32_t)grid), dim3(T), 0, s, a);
     else
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false, PR>), dim3((uint32_t)grid), dim3(T), 0, s, a);
+        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false, PR, RES>), dim3((uint32_t)grid), dim3(T), 0, s, a);
     return hipGetLastError();
 }
 
-// Norms with every parameter vector present take the specialised PR kernel.
+// Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
+// arithmetic needs twice the registers), RMSNorm and softmax 64, and a fused
+// residual add (which also holds the residual's words) 32.  Wider shapes
+// would spill registers and are not built.
+template <int OP, int K, bool RES = false>
+constexpr bool shape_built() {
+    constexpr int V = K * dt_info<DT>::VEC;
+    return OP == OP_LAYERNORM ? V <= 16 : V <= (RES ? 32 : 64);
+}
+
+// Norms with every parameter vector present take the specialised PR kernel;
+// a residual input (a.r) selects the fused add + norm kernel.
 template <int OP, int W, int K>
 hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     if constexpr (OP == OP_SOFTMAX) {
-        return go_pr<OP, W, K, false>(al, a, grid, s);
+        return go_pr<OP, W, K, false, false>(al, a, grid, s);
     } else {
         const bool pr = a.p0 != nullptr && (OP == OP_RMSNORM || a.p1 != nullptr);
-        return pr ? go_pr<OP, W, K, true>(al, a, grid, s) : go_pr<OP, W, K, false>(al, a, grid, s);
+        if (a.r) {
+            if constexpr (shape_built<OP, K, true>())
+                return pr ? go_pr<OP, W, K, true, true>(al, a, grid, s) : go_pr<OP, W, K, false, true>(al, a, grid, s);
+            return hipErrorInvalidValue;
+        }
+        return pr ? go_pr<OP, W, K, true, false>(al, a, grid, s) : go_pr<OP, W, K, false, false>(al, a, grid, s);
     }
-}
-
-// Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
-// arithmetic needs twice the registers), RMSNorm and softmax 64.  Wider
-// shapes would spill registers and are not built.
-template <int OP, int K>
-constexpr bool shape_built() {
-    constexpr int V = K * dt_info<DT>::VEC;
-    return OP == OP_LAYERNORM ? V <= 16 : V <= 64;
 }
 
 template <int OP>
@@ -66,13 +73,13 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
 // Persistent norm kernel: as many workgroups as fit on the device at once
 // (occupancy x compute units, the occupancy cached per instantiation), or
 // NT_PERSIST_GRID when set; never more than there are rows.
-template <int OP, int W, int K>
+template <int OP, int W, int K, bool RES>
 hipError_t persist_go(const RowArgs &a, hipStream_t s) {
     static std::atomic<int> per_cu{0};
     int pc = per_cu.load(std::memory_order_relaxed);
     if (pc == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_norm_persistent<OP, DT, W, K>, 64 * W, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_norm_persistent<OP, DT, W, K, RES>, 64 * W, 0) !=
                 hipSuccess || n <= 0)
             n = 1;
         per_cu.store(n, std::memory_order_relaxed);
@@ -88,7 +95,7 @@ hipError_t persist_go(const RowArgs &a, hipStream_t s) {
         if (v > 0) grid = v;
     }
     if (grid > a.M) grid = a.M;
-    hipLaunchKernelGGL((row_norm_persistent<OP, DT, W, K>), dim3((uint32_t)grid), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((row_norm_persistent<OP, DT, W, K, RES>), dim3((uint32_t)grid), dim3(64 * W), 0, s, a);
     return hipGetLastError();
 }
 
@@ -96,7 +103,8 @@ template <int OP>
 hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k)                                                   \
     if (W == w && K == k) {                                              \
-        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32) return persist_go<OP, w, k>(a, s); \
+        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32)                 \
+            return a.r ? persist_go<OP, w, k, true>(a, s) : persist_go<OP, w, k, false>(a, s); \
         return hipErrorInvalidValue;                                     \
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
@@ -116,10 +124,18 @@ hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s)
 template <int OP>
 hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     if (W == 8 && K == 4) {
-        if (al)
-            hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true>), dim3((uint32_t)grid), dim3(512), 0, s, a);
-        else
-            hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+        const dim3 g((uint32_t)grid), b(512);
+        if (a.r) {
+            if (al)
+                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true, true>), g, b, 0, s, a);
+            else
+                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false, true>), g, b, 0, s, a);
+        } else {
+            if (al)
+                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true, false>), g, b, 0, s, a);
+            else
+                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false, false>), g, b, 0, s, a);
+        }
         return hipGetLastError();
     }
     return hipErrorInvalidValue;

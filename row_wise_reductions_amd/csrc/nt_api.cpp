@@ -141,7 +141,14 @@ bool persistent_enabled() {
     return !(s && std::strcmp(s, "0") == 0);
 }
 
-nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true) {
+// `res`: the fused residual add + norm, whose lanes also hold the residual's
+// words (at most 32 values per lane for RMSNorm; LayerNorm is capped at 16).
+bool shape_fits(nt_op op, nt_dtype dt, bool res, Shape sh) {
+    return !(res && op == NT_OP_RMSNORM && sh.K * elems_per_chunk(dt) > 32);
+}
+
+nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true,
+                    bool res = false) {
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
@@ -153,11 +160,11 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     Shape pick = {0, 0};
     if (!force_split && !force_loop) {
         Shape o;
-        if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch) {
+        if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch && shape_fits(op, dt, res, o)) {
             pick = o;
         } else {
             for (int i = 0; i < menu.n; ++i)
-                if ((int64_t)64 * menu.s[i].W * menu.s[i].K >= nch) {
+                if ((int64_t)64 * menu.s[i].W * menu.s[i].K >= nch && shape_fits(op, dt, res, menu.s[i])) {
                     pick = menu.s[i];
                     break;
                 }
@@ -274,8 +281,11 @@ void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_p
 
 nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a,
               void *stream) {
-    if (debug_on()) debug_print(op == NT_OP_SOFTMAX ? "softmax" : op == NT_OP_LAYERNORM ? "layernorm" : "rmsnorm",
-                                M, N, dt, p);
+    if (debug_on())
+        debug_print(op == NT_OP_SOFTMAX     ? "softmax"
+                    : op == NT_OP_LAYERNORM ? (a.r ? "add+layernorm" : "layernorm")
+                                            : (a.r ? "add+rmsnorm" : "rmsnorm"),
+                    M, N, dt, p);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = p.split == 1   ? launch_split(dt, p, a, s)
                    : p.split == 2 ? launch_looped(dt, (int)op, p, a, s)
@@ -315,17 +325,22 @@ const char *nt_status_string(nt_status s) {
     case NT_ERR_ALIGN: return "pointer not aligned to its element size";
     case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes()";
     case NT_ERR_HIP: return "HIP launch error";
+    case NT_ERR_ALIAS: return "h and y must be different buffers";
     }
     return "unknown status";
 }
 
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt, int aligned16, nt_plan *out) {
     if (!out) return NT_ERR_NULL;
-    if (op != NT_OP_SOFTMAX && op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM) return NT_ERR_SHAPE;
+    if (op != NT_OP_SOFTMAX && op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM && op != NT_OP_ADD_LAYERNORM &&
+        op != NT_OP_ADD_RMSNORM)
+        return NT_ERR_SHAPE;
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
     const bool al = aligned16 && (N * elem_bytes(dt)) % 16 == 0;
-    return make_plan(op, M, N, dt, al, out);
+    const bool res = op == NT_OP_ADD_LAYERNORM || op == NT_OP_ADD_RMSNORM;
+    const nt_op base = op == NT_OP_ADD_LAYERNORM ? NT_OP_LAYERNORM : op == NT_OP_ADD_RMSNORM ? NT_OP_RMSNORM : op;
+    return make_plan(base, M, N, dt, al, out, true, res);
 }
 
 size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt) {
@@ -426,6 +441,81 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const vo
     ntk::RowArgs a{};
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
+    a.p0 = static_cast<const char *>(weight);
+    a.M = M;
+    a.N = (int32_t)N;
+    a.inv_n = (float)(1.0 / (double)N);
+    a.inv_nd = 1.0 / (double)N;
+    a.eps = eps;
+    return run(NT_OP_RMSNORM, M, N, dt, p, a, stream);
+}
+
+// Checks of the fused add + norm entry points beyond common_checks: the
+// residual and h present, element-aligned and in x's 16-byte phase, y != h.
+static nt_status residual_checks(nt_dtype dt, const void *x, const void *residual, const void *h,
+                                 const void *y) {
+    if (!residual || !h) return NT_ERR_NULL;
+    const uintptr_t e = (uintptr_t)elem_bytes(dt);
+    if (!aligned_to(residual, e) || !aligned_to(h, e)) return NT_ERR_ALIGN;
+    if ((((uintptr_t)residual ^ (uintptr_t)x) & 15) || (((uintptr_t)h ^ (uintptr_t)x) & 15)) return NT_ERR_ALIGN;
+    if (h == y) return NT_ERR_ALIAS;
+    return NT_OK;
+}
+
+nt_status nt_add_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *residual,
+                                const void *gamma, const void *beta, void *h, void *y, float *mean, float *rstd,
+                                void *stream) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (!valid_eps(eps)) return NT_ERR_EPS;
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    st = residual_checks(dt, x, residual, h, y);
+    if (st != NT_OK) return st;
+    const uintptr_t e = (uintptr_t)elem_bytes(dt);
+    if ((gamma && !aligned_to(gamma, e)) || (beta && !aligned_to(beta, e)) || (mean && !aligned_to(mean, 4)) ||
+        (rstd && !aligned_to(rstd, 4)))
+        return NT_ERR_ALIGN;
+    const bool al = all_aligned16(N, dt, x, y, gamma, beta) && aligned_to(residual, 16) && aligned_to(h, 16);
+    nt_plan p;
+    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p, gamma != nullptr && beta != nullptr, true);
+    if (st != NT_OK) return st;
+    ntk::RowArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.y = static_cast<char *>(y);
+    a.r = static_cast<const char *>(residual);
+    a.h = static_cast<char *>(h);
+    a.p0 = static_cast<const char *>(gamma);
+    a.p1 = static_cast<const char *>(beta);
+    a.mean = mean;
+    a.rstd = rstd;
+    a.M = M;
+    a.N = (int32_t)N;
+    a.inv_n = (float)(1.0 / (double)N);
+    a.inv_nd = 1.0 / (double)N;
+    a.eps = eps;
+    return run(NT_OP_LAYERNORM, M, N, dt, p, a, stream);
+}
+
+nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *residual,
+                              const void *weight, void *h, void *y, void *stream) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (!valid_eps(eps)) return NT_ERR_EPS;
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    st = residual_checks(dt, x, residual, h, y);
+    if (st != NT_OK) return st;
+    if (weight && !aligned_to(weight, (uintptr_t)elem_bytes(dt))) return NT_ERR_ALIGN;
+    const bool al = all_aligned16(N, dt, x, y, weight, nullptr) && aligned_to(residual, 16) && aligned_to(h, 16);
+    nt_plan p;
+    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr, true);
+    if (st != NT_OK) return st;
+    ntk::RowArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.y = static_cast<char *>(y);
+    a.r = static_cast<const char *>(residual);
+    a.h = static_cast<char *>(h);
     a.p0 = static_cast<const char *>(weight);
     a.M = M;
     a.N = (int32_t)N;

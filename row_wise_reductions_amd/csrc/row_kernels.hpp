@@ -51,6 +51,8 @@ template <> struct dt_info<DT_BF16> {
 struct RowArgs {
     const char *x;
     char *y;
+    const char *r;       // fused add + norm: residual input (null otherwise)
+    char *h;             // fused add + norm: h = x + r output
     const char *p0;      // gamma (LayerNorm) or weight (RMSNorm); may be null
     const char *p1;      // beta (LayerNorm); may be null
     float *mean;         // LayerNorm statistics outputs; may be null
@@ -488,6 +490,55 @@ __device__ __forceinline__ float elem_of_word(uint32_t w) {
     else return __builtin_bit_cast(float, w << 16);
 }
 
+// The word a LayerNorm row is padded with: its first element (the pivot of
+// the shifted sums), repeated in both halves for 16-bit types.
+template <int DT>
+__device__ __forceinline__ uint32_t pivot_word(const char *xr) {
+    if constexpr (dt_info<DT>::E == 4) {
+        return *reinterpret_cast<const uint32_t *>(xr);
+    } else {
+        const uint32_t e = *reinterpret_cast<const uint16_t *>(xr);
+        return e | (e << 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused residual add (the step before a norm): h = x + r, summed in fp32 and
+// rounded once to the element type.  For two fp32, fp16 or bf16 values the
+// rounded fp32 sum rounds to the element type exactly as the exact sum does,
+// so h is the stored sum of an add kernel run on its own.
+// ---------------------------------------------------------------------------
+
+// Pivot word of the fused row: the first element of h.
+template <int DT>
+__device__ __forceinline__ uint32_t pivot_word_sum(const char *xr, const char *rr) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    const float s = elem_of_word<DT>(pivot_word<DT>(xr)) + elem_of_word<DT>(pivot_word<DT>(rr));
+    float f[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) f[i] = s;
+    return pack<DT>(f).x;
+}
+
+// raw holds the row's x words, rr its residual words (same chunk geometry:
+// x, r and h share their 16-byte phase).  On return raw holds the words of h,
+// which are also stored to the h row.  Padding slots hold pad + 0 = pad.
+template <int DT, bool AL, int K, int TPR>
+__device__ __forceinline__ void add_residual(uint4 (&raw)[K], const uint4 (&rr)[K], const RowGeom<DT, AL> &g,
+                                             char *hrow, int t, int32_t N, int64_t cbase = 0) {
+    constexpr int VEC = dt_info<DT>::VEC;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float xv[VEC], rv[VEC];
+        unpack<DT>(raw[k], xv);
+        unpack<DT>(rr[k], rv);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xv[i] += rv[i];
+        raw[k] = pack<DT>(xv);
+        store_slice<DT, AL, TPR>(g, hrow, k, t, N, true, raw[k], cbase);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per-row scalar helpers
 // ---------------------------------------------------------------------------
@@ -534,9 +585,10 @@ struct GroupShape {
 
 // PR (norms only): the parameter vectors are all present (gamma and beta for
 // LayerNorm, the weight for RMSNorm); otherwise absent ones act as identity.
-template <int OP, int DT, int W, int K, bool AL, bool PR>
+template <int OP, int DT, int W, int K, bool AL, bool PR, bool RES = false>
 __global__ void __launch_bounds__(GroupShape<W>::THREADS)
 row_resident(RowArgs a) {
+    static_assert(!RES || OP != OP_SOFTMAX, "the residual add precedes a norm");
     using I = dt_info<DT>;
     constexpr int VEC = I::VEC, TPR = 64 * W, G = GroupShape<W>::G;
     // LayerNorm keeps an fp64 copy of its values when they are few per lane
@@ -568,17 +620,12 @@ row_resident(RowArgs a) {
         // which are L2 hits after the first rows) before using any of them
         // LayerNorm pads with its pivot (the row's first element), which adds
         // exactly nothing to the shifted sums; softmax pads with -inf, RMSNorm 0
+        const char *rr = RES ? a.r + row * rowbytes : nullptr;
         uint32_t padw = fill;
-        if constexpr (OP == OP_LAYERNORM) {
-            if constexpr (I::E == 4) {
-                padw = *reinterpret_cast<const uint32_t *>(xr);
-            } else {
-                const uint32_t h = *reinterpret_cast<const uint16_t *>(xr);
-                padw = h | (h << 16);
-            }
-        }
-        uint4 raw[K];
+        if constexpr (OP == OP_LAYERNORM) padw = RES ? pivot_word_sum<DT>(xr, rr) : pivot_word<DT>(xr);
+        uint4 raw[K], rraw[RES ? K : 1];
         load_row<DT, AL, K, TPR>(raw, geo, t, N);
+        if constexpr (RES) load_row<DT, AL, K, TPR>(rraw, RowGeom<DT, AL>(rr, N), t, N);
         constexpr int KP0 = (OP == OP_SOFTMAX) ? 1 : K;
         constexpr int KP1 = (OP == OP_LAYERNORM) ? K : 1;
         uint4 p0[KP0], p1[KP1];
@@ -589,6 +636,11 @@ row_resident(RowArgs a) {
             if (has_p1) load_params<DT, AL, K, TPR>(p1, geo, a.p1, t, N);
         }
         finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw);
+        if constexpr (RES) {
+            // x padded with the pivot of h, r with 0: h's padding is the pivot
+            finish_row<DT, AL, K, TPR>(rraw, RowGeom<DT, AL>(rr, N), rr, t, N, 0u);
+            add_residual<DT, AL, K, TPR>(raw, rraw, geo, a.h + row * rowbytes, t, N);
+        }
         float v[K][VEC];
 #pragma unroll
         for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
@@ -713,7 +765,7 @@ row_resident(RowArgs a) {
 // 64*W threads (W >= 2).
 // ---------------------------------------------------------------------------
 
-template <int OP, int DT, int W, int K>
+template <int OP, int DT, int W, int K, bool RES = false>
 __global__ void __launch_bounds__(64 * W)
 row_norm_persistent(RowArgs a) {
     static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "persistent kernel is for the norms");
@@ -756,15 +808,14 @@ row_norm_persistent(RowArgs a) {
         }
     }
 
-    // ---- prime the pipeline with the first row
-    uint4 raw[K];
+    // ---- prime the pipeline with the first row (and its residual)
+    uint4 raw[K], rraw[RES ? K : 1];
     uint32_t padw = 0;
     {
         const char *xr = a.x + row * rowbytes;
         load_row<DT, true, K, TPR>(raw, RowGeom<DT, true>(xr, N), t, N);
-        if constexpr (LN)
-            padw = (I::E == 4) ? *reinterpret_cast<const uint32_t *>(xr)
-                               : (uint32_t)*reinterpret_cast<const uint16_t *>(xr) * 0x10001u;
+        if constexpr (RES) load_row<DT, true, K, TPR>(rraw, RowGeom<DT, true>(a.r + row * rowbytes, N), t, N);
+        if constexpr (LN) padw = RES ? pivot_word_sum<DT>(xr, a.r + row * rowbytes) : pivot_word<DT>(xr);
     }
     int par = 0;
     for (; row < a.M; row += gridDim.x, par ^= 1) {
@@ -772,6 +823,11 @@ row_norm_persistent(RowArgs a) {
         char *yr = a.y + row * rowbytes;
         const RowGeom<DT, true> g(xr, N);
         finish_row<DT, true, K, TPR>(raw, g, xr, t, N, padw);
+        if constexpr (RES) {
+            const char *rr = a.r + row * rowbytes;
+            finish_row<DT, true, K, TPR>(rraw, RowGeom<DT, true>(rr, N), rr, t, N, 0u);
+            add_residual<DT, true, K, TPR>(raw, rraw, g, a.h + row * rowbytes, t, N);
+        }
         float v[K][VEC];
 #pragma unroll
         for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
@@ -782,9 +838,8 @@ row_norm_persistent(RowArgs a) {
             const int64_t nr = row + gridDim.x < a.M ? row + gridDim.x : a.M - 1;
             const char *xn = a.x + nr * rowbytes;
             load_row<DT, true, K, TPR>(raw, RowGeom<DT, true>(xn, N), t, N);
-            if constexpr (LN)
-                padw = (I::E == 4) ? *reinterpret_cast<const uint32_t *>(xn)
-                                   : (uint32_t)*reinterpret_cast<const uint16_t *>(xn) * 0x10001u;
+            if constexpr (RES) load_row<DT, true, K, TPR>(rraw, RowGeom<DT, true>(a.r + nr * rowbytes, N), t, N);
+            if constexpr (LN) padw = RES ? pivot_word_sum<DT>(xn, a.r + nr * rowbytes) : pivot_word<DT>(xn);
         }
 
         if constexpr (LN) {
@@ -843,7 +898,7 @@ row_norm_persistent(RowArgs a) {
 // statistics accumulate in fp64 (a lane may sum thousands of values).
 // ---------------------------------------------------------------------------
 
-template <int OP, int DT, int W, int K, bool AL>
+template <int OP, int DT, int W, int K, bool AL, bool RES = false>
 __global__ void __launch_bounds__(64 * W)
 row_looped(RowArgs a) {
     static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "looped kernel is for the norms");
@@ -863,24 +918,28 @@ row_looped(RowArgs a) {
         const RowGeom<DT, AL> geo(xr, N);
         bool yvec = true;
         if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+        const char *rr = RES ? a.r + row * rowbytes : nullptr;
+        char *hr = RES ? a.h + row * rowbytes : nullptr;
         uint32_t padw = 0;
-        if constexpr (OP == OP_LAYERNORM) {
-            if constexpr (I::E == 4) {
-                padw = *reinterpret_cast<const uint32_t *>(xr);
-            } else {
-                const uint32_t h = *reinterpret_cast<const uint16_t *>(xr);
-                padw = h | (h << 16);
-            }
-        }
+        if constexpr (OP == OP_LAYERNORM) padw = RES ? pivot_word_sum<DT>(xr, rr) : pivot_word<DT>(xr);
         const double pv = (double)elem_of_word<DT>(padw);   // 0 for RMSNorm
         const int64_t ntiles = (geo.nch + TILE - 1) / TILE;
 
-        // ---- pass 1: statistics
+        // ---- pass 1: statistics (of h = x + r, which is stored on the way)
         double s1 = 0.0, s2 = 0.0;
         for (int64_t tl = 0; tl < ntiles; ++tl) {
             uint4 raw[K];
             load_row<DT, AL, K, TPR>(raw, geo, t, N, tl * TILE);
-            finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+            if constexpr (RES) {
+                uint4 rraw[K];
+                const RowGeom<DT, AL> gr(rr, N);
+                load_row<DT, AL, K, TPR>(rraw, gr, t, N, tl * TILE);
+                finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+                finish_row<DT, AL, K, TPR>(rraw, gr, rr, t, N, 0u, tl * TILE);
+                add_residual<DT, AL, K, TPR>(raw, rraw, geo, hr, t, N, tl * TILE);
+            } else {
+                finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+            }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 float v[VEC];
@@ -908,15 +967,20 @@ row_looped(RowArgs a) {
         }
         const float scale_f = (float)scale;
 
-        // ---- pass 2: normalize
+        // ---- pass 2: normalize.  With the residual add it reads back h:
+        // every lane reads exactly the chunks it stored in pass 1, so a
+        // workgroup-scope fence (stores complete before these loads) orders it.
+        const char *src = RES ? hr : xr;
+        if constexpr (RES) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        const RowGeom<DT, AL> gs(src, N);
         for (int64_t tl = 0; tl < ntiles; ++tl) {
             uint4 raw[K], g4[K], b4[(OP == OP_LAYERNORM) ? K : 1];
-            load_row<DT, AL, K, TPR>(raw, geo, t, N, tl * TILE);
+            load_row<DT, AL, K, TPR>(raw, gs, t, N, tl * TILE);
             if (has_p0) load_params<DT, AL, K, TPR>(g4, geo, a.p0, t, N, tl * TILE);
             if constexpr (OP == OP_LAYERNORM) {
                 if (has_p1) load_params<DT, AL, K, TPR>(b4, geo, a.p1, t, N, tl * TILE);
             }
-            finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, tl * TILE);
+            finish_row<DT, AL, K, TPR>(raw, gs, src, t, N, padw, tl * TILE);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 float v[VEC], g[VEC], b[VEC];

@@ -51,7 +51,8 @@ def kernels_of(w) -> list[str]:
     """Demangled names of the kernels one call of workload `w` launches (with
     16-byte-aligned buffers and every parameter vector present, as bench.py)."""
     import row_wise_reductions_amd as nt
-    op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2}[w.op]
+    op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4}[w.op]
+    base, res = {3: (1, True), 4: (2, True)}.get(op, (op, False))
     dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dt]
     p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
     W, K, al = p["waves_per_row"], p["chunks_per_lane"], _b(p["aligned"])
@@ -61,10 +62,10 @@ def kernels_of(w) -> list[str]:
         return [f"ntk::softmax_split_partial<{dt}, {W}, {K}, {al}>",
                 f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}>"]
     if p["split"] == 2:
-        return [f"ntk::row_looped<{op}, {dt}, {W}, {K}, {al}>"]
+        return [f"ntk::row_looped<{base}, {dt}, {W}, {K}, {al}, {_b(res)}>"]
     if p["persistent"]:
-        return [f"ntk::row_norm_persistent<{op}, {dt}, {W}, {K}>"]
-    return [f"ntk::row_resident<{op}, {dt}, {W}, {K}, {al}, {_b(op != 0)}>"]
+        return [f"ntk::row_norm_persistent<{base}, {dt}, {W}, {K}, {_b(res)}>"]
+    return [f"ntk::row_resident<{base}, {dt}, {W}, {K}, {al}, {_b(base != 0)}, {_b(res)}>"]
 
 
 def _rows(pattern):
@@ -86,7 +87,7 @@ def stats(args):
              "Command (run from the repository root on the GPU host):", "", f"    {args.cmd}", "",
              "| workload | kernel | calls | avg duration (us) | algorithmic bytes / call | GB/s (bytes / summed kernel avg) |",
              "|---|---|---|---|---|---|"]
-    for w in workloads.WORKLOADS:
+    for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS:
         ks = kernels_of(w)
         tot = 0.0
         found = []
@@ -149,7 +150,7 @@ def traffic(args):
               f"{f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
               "| workload | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / call (scaled) | "
               "algorithmic bytes / call | ratio |", "|---|---|---|---|---|---|---|---|"]
-    for w in workloads.WORKLOADS:
+    for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS:
         total = 0.0
         ok = True
         for i, k in enumerate(kernels_of(w)):

@@ -36,7 +36,7 @@ def test_exports_are_c_symbols():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = nt.nt_status_string(code)
         assert s and s != "unknown status"
     assert nt.nt_status_string(99) == "unknown status"
@@ -66,6 +66,30 @@ def test_status_strings():
     (lambda: nt.nt_rmsnorm_rows(4, 8, 3, 1e-6, FAKE, None, FAKE, None), 3),
     (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, None, None, FAKE, None), 1),
     (lambda: nt.nt_rmsnorm_rows(4, 1 << 31, BF16, 1e-6, FAKE, None, FAKE, None), 2),
+    # fused add + norm: residual and h required, in x's 16-byte phase, h != y
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, None, None, FAKE + 64, FAKE + 128, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, None, FAKE + 128, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, None, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 33, None, FAKE + 64, FAKE + 128, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 34, None, FAKE + 64, FAKE + 128, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 66, FAKE + 128, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, FAKE + 1, FAKE + 64, FAKE + 128, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 64, None), 8),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, -1.0, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 4),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, 5, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 3),
+    (lambda: nt.nt_add_rmsnorm_rows(-2, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 2),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, None, None, None, FAKE + 64, FAKE + 128,
+                                      None, None, None), 1),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 36, None, None, FAKE + 64, FAKE + 128,
+                                      None, None, None), 5),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, FAKE + 2, None, FAKE + 64, FAKE + 128,
+                                      None, None, None), 5),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 128,
+                                      FAKE + 2, None, None), 5),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 64,
+                                      None, None, None), 8),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, float("nan"), FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 128,
+                                      None, None, None), 4),
 ])
 def test_validation_before_launch(call, code):
     # every case here must fail validation; on a machine with a GPU a library
@@ -88,6 +112,8 @@ def test_empty_is_noop():
     assert nt.nt_softmax_rows(0, 8, F32, None, None, None, 0, None) == 0
     assert nt.nt_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None) == 0
     assert nt.nt_rmsnorm_rows(0, 8, F32, 1e-6, None, None, None, None) == 0
+    assert nt.nt_add_rmsnorm_rows(0, 8, F32, 1e-6, None, None, None, None, None, None) == 0
+    assert nt.nt_add_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None, None, None) == 0
     # a bad eps is still an error for an empty call
     assert nt.nt_rmsnorm_rows(0, 8, F32, -1.0, None, None, None, None) == 4
 
@@ -182,3 +208,21 @@ def test_env_overrides(monkeypatch):
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 16, 4096, F32, True)
     assert p["split"] == 1 and p["row_chunks"] == 1
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 4096, F32, True)["split"] == 0
+
+
+def test_fused_add_norm_plans():
+    # the fused kernels hold the residual too: RMSNorm at most 32 values per
+    # lane in one pass, wider rows take the looped kernel
+    p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 16384, 8192, BF16, True)
+    assert (p["split"], p["persistent"]) == (0, 1) and p["chunks_per_lane"] * 8 <= 32
+    p = nt.nt_plan_launch(nt.NT_OP_ADD_LAYERNORM, 4096, 4096, F16, True)
+    assert (p["split"], p["persistent"]) == (0, 1)
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 4, 8192 * 4, BF16, True)["split"] == 0      # 64 per lane
+    assert nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 4, 8192 * 4, BF16, True)["split"] == 2  # looped
+    assert nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 4, 8192 * 2, BF16, True)["split"] == 0
+    for dt in (F32, F16, BF16):
+        for N in (1, 7, 781, 4096, 8192, 30000, 100000):
+            for al in (True, False):
+                p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 8, N, dt, al)
+                if p["split"] == 0:
+                    assert p["chunks_per_lane"] * (4 if dt == F32 else 8) <= 32, (dt, N, al, p)

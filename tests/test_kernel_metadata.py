@@ -81,21 +81,30 @@ def test_all_types_present(kernels):
 def _shapes(kernels):
     have = set()
     for name in kernels:
-        m = re.search(r"row_residentILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        m = re.search(r"row_residentILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb\dELb(\d)", name)
         if m:
             have.add(("res",) + tuple(int(g) for g in m.groups()))
-        m = re.search(r"row_loopedILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        m = re.search(r"row_loopedILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", name)
         if m:
             have.add(("loop",) + tuple(int(g) for g in m.groups()))
+        m = re.search(r"row_norm_persistentILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("pers",) + tuple(int(g) for g in m.groups()))
         m = re.search(r"softmax_split_(partial|finalize)ILi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
         if m:
             have.add((m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4)), int(m.group(5))))
+        m = re.search(r"softmax_coopILi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("coop",) + tuple(int(g) for g in m.groups()))
     return have
 
 
 def test_every_planned_shape_is_built(kernels):
+    """Every launch the planner can choose (fused add + norm included) has an
+    instantiated kernel: (op, type, W, K, aligned, residual)."""
     have = _shapes(kernels)
-    for op in (0, 1, 2):
+    for op in (0, 1, 2, 3, 4):
+        base, res = {3: (1, 1), 4: (2, 1)}.get(op, (op, 0))
         for dt in (0, 1, 2):
             for N in (1, 7, 64, 255, 781, 1000, 4096, 4097, 8192, 16384, 30000, 32768, 65536, 100000, 262144):
                 for al in (True, False):
@@ -105,8 +114,12 @@ def test_every_planned_shape_is_built(kernels):
                         continue
                     W, K, A = p["waves_per_row"], p["chunks_per_lane"], p["aligned"]
                     if p["split"] == 1:
+                        if p["cooperative"]:
+                            assert ("coop", dt, W, K, A) in have, (dt, N, al, p)
                         assert ("partial", dt, W, K, A) in have and ("finalize", dt, W, K, A) in have
                     elif p["split"] == 2:
-                        assert ("loop", op, dt, W, K, A) in have, (op, dt, N, al, p)
+                        assert ("loop", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
                     else:
-                        assert ("res", op, dt, W, K, A) in have, (op, dt, N, al, p)
+                        assert ("res", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
+                        if p["persistent"]:
+                            assert ("pers", base, dt, W, K, res) in have, (op, dt, N, al, p)
