@@ -61,9 +61,10 @@ def load(path: str = _LIB_PATH):
     lib.or_rmsnorm.argtypes = [i64, i64, i32, ctypes.c_float, vp, vp, dp]
     lib.or_softmax_online.argtypes = [i64, i64, i32, i64, vp, dp]
     lib.or_add.argtypes = [i64, i32, vp, vp, dp]
+    lib.or_softmax_causal.argtypes = [i64, i64, i32, ctypes.c_float, i64, i64, vp, dp]
     lib.or_num_threads.argtypes = []
     for f in ("or_decode", "or_softmax", "or_layernorm", "or_rmsnorm",
-              "or_softmax_online", "or_add", "or_num_threads"):
+              "or_softmax_online", "or_add", "or_softmax_causal", "or_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
@@ -108,6 +109,18 @@ def softmax(x: np.ndarray, dt, lib=None) -> np.ndarray:
     M, N = xb.shape
     y = np.empty((M, N), dtype=np.float64)
     _check((lib or load()).or_softmax(M, N, code, _ptr(xb), _ptr(y)))
+    return y
+
+
+def softmax_causal(x: np.ndarray, dt, scale: float, queries: int, offset: int = 0, lib=None) -> np.ndarray:
+    """Causal scaled softmax: row r (query r mod queries) sees keys
+    k <= q + offset; masked outputs are 0 and masked inputs are not read."""
+    code = dtype_code(dt)
+    xb = _as_bits(x, code)
+    M, N = xb.shape
+    y = np.empty((M, N), dtype=np.float64)
+    _check((lib or load()).or_softmax_causal(M, N, code, float(scale), int(queries), int(offset),
+                                             _ptr(xb), _ptr(y)))
     return y
 
 

@@ -31,6 +31,9 @@
  *  - residual add of a fused add + norm (or_add): named as a kernel pattern
  *    in "Portable Triton Kernels" (References), no formula printed; h = x + r
  *    stored in the input type, then the plain norm of that stored h.
+ *  - causal scaled softmax (or_softmax_causal): attention-score rows whose
+ *    keys after the query are masked; the plain softmax of the row with the
+ *    masked scores at -inf, masked inputs never read, masked outputs 0.
  *  - online softmax: "Triton: Block-Level GPU Programming Without CUDA",
  *    section "How Flash Attention Uses Triton" (running max m and
  *    denominator l rescaled by alpha = exp(m_prev - m_new) per block; the
@@ -211,6 +214,51 @@ int or_add(int64_t count, int dtype, const void *x, const void *r, double *h)
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i)
         h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);
+    return 0;
+}
+
+/*
+ * Causal, scaled row softmax (attention scores): row r holds the scores of
+ * query q = r mod `queries` against N keys, and key k is visible to it iff
+ * k <= q + offset.  Over the visible keys, with s = scale:
+ *   m = max_k s*x[r,k],  y[r,k] = exp(s*x[r,k] - m) / sum_k exp(s*x[r,k] - m),
+ * and y = 0 at masked keys, whose inputs are never read.  This is the plain
+ * softmax of the row with its masked scores set to -inf: the masked-load
+ * identity of "Portable Triton Kernels" ("Safe Softmax Pattern": a -inf
+ * entry contributes exactly nothing), with the causal pattern of attention
+ * scores (keys after the query masked, the diagonal kept).  `scale` arrives
+ * as a C float and is widened exactly.
+ */
+int or_softmax_causal(int64_t M, int64_t N, int dtype, float scale, int64_t queries,
+                      int64_t offset, const void *x, double *y)
+{
+    int rc = or_check(M, N, dtype);
+    if (rc) return rc;
+    if (queries <= 0 || offset < 0) return 1;
+    const double sc = (double)scale;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < M; ++r) {
+        int64_t base = r * N;
+        int64_t q = r % queries;
+        int64_t vis = q + offset + 1;            /* keys 0 .. vis-1 are visible */
+        if (vis > N) vis = N;
+        double m = -INFINITY;
+        for (int64_t k = 0; k < vis; ++k) {
+            double v = sc * or_load(dtype, x, base + k);
+            if (isnan(v) || isnan(m)) m = NAN;
+            else if (v > m) m = v;
+        }
+        double s = 0.0;
+        for (int64_t k = 0; k < vis; ++k) {
+            double v = sc * or_load(dtype, x, base + k);
+            s += (v == -INFINITY) ? 0.0 : exp(v - m);
+        }
+        for (int64_t k = 0; k < vis; ++k) {
+            double v = sc * or_load(dtype, x, base + k);
+            y[base + k] = ((v == -INFINITY) ? 0.0 : exp(v - m)) / s;
+        }
+        for (int64_t k = vis; k < N; ++k) y[base + k] = 0.0;
+    }
     return 0;
 }
 

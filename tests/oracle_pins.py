@@ -483,4 +483,81 @@ def pin_add_norm_is_norm_of_stored_sum(lib):
                 assert _rel(y2[i], yl) < 1e-12 and _rel([mean[i]], [ml]) < 1e-12, (dt, N)
 
 
+# ----------------------------------------------------------------------------
+# causal scaled softmax (attention scores with the future keys masked)
+# ----------------------------------------------------------------------------
+
+_NAN_BITS = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+
+
+def _causal_cases():
+    # (M, N, queries, offset): square causal, wrap over heads, bottom-right
+    # alignment (offset = N - queries), offsets past the row
+    return [(8, 8, 8, 0), (12, 5, 5, 0), (7, 33, 7, 26), (6, 40, 3, 1), (5, 17, 5, 100), (9, 1, 4, 0)]
+
+
+def pin_softmax_causal_matches_torch_masked(lib):
+    """Causal scaled softmax = torch.softmax (float64) of scale*x with the
+    masked keys set to -inf."""
+    import torch
+    for dt in ("f32", "f16", "bf16"):
+        for (M, N, Q, off) in _causal_cases():
+            for scale in (1.0, 0.125, 3.0):
+                x = _rng_rows(900 + M + N + off, M, N, dt, scale=3.0)
+                y = oracle.softmax_causal(x, dt, scale, Q, off, lib=lib)
+                xd = torch.from_numpy(oracle.decode(x, dt)) * float(np.float32(scale))
+                k = torch.arange(N)[None, :]
+                q = (torch.arange(M) % Q)[:, None]
+                ref = torch.softmax(xd.masked_fill(k > q + off, float("-inf")), dim=1).numpy()
+                assert _rel(y, ref) < 1e-13 or np.abs(y - ref).max() < 1e-15, (dt, M, N, Q, off, scale)
+                assert np.all(y[np.broadcast_to((k > q + off).numpy(), y.shape)] == 0.0)
+
+
+def pin_softmax_causal_never_reads_masked(lib):
+    """NaN planted in every masked input changes nothing: masked keys are not
+    read, their outputs are exactly 0."""
+    for dt in ("f32", "f16", "bf16"):
+        M, N, Q, off = 10, 24, 10, 3
+        x = _rng_rows(950, M, N, dt, scale=2.0)
+        clean = oracle.softmax_causal(x, dt, 0.5, Q, off, lib=lib)
+        k = np.arange(N)[None, :]
+        masked = k > (np.arange(M) % Q)[:, None] + off
+        x2 = x.copy()
+        x2[masked] = np.float32(np.nan) if dt == "f32" else _NAN_BITS[dt]
+        dirty = oracle.softmax_causal(x2, dt, 0.5, Q, off, lib=lib)
+        assert np.array_equal(clean, dirty), dt
+        assert np.all(dirty[masked] == 0.0) and np.all(np.isfinite(dirty))
+
+
+def pin_softmax_causal_closed_forms(lib):
+    """Query 0 sees only key 0: [1, 0, ...]; a constant row gives 1/(q+1)
+    over the visible keys; two visible keys a, b give the logistic of
+    scale*(b - a)."""
+    x = np.full((4, 6), 2.5, dtype=np.float32)
+    y = oracle.softmax_causal(x, "f32", 0.7, 4, lib=lib)
+    for q in range(4):
+        assert np.all(y[q, : q + 1] == y[q, 0]) and abs(y[q, 0] - 1.0 / (q + 1)) < 1e-15
+        assert np.all(y[q, q + 1:] == 0.0)
+    x = np.array([[0.0, 0.0, 9.0], [1.0, 3.0, -5.0]], dtype=np.float32)
+    y = oracle.softmax_causal(x, "f32", 0.5, 2, lib=lib)
+    assert y[0, 0] == 1.0 and y[0, 1] == 0.0 and y[0, 2] == 0.0
+    want = 1.0 / (1.0 + math.exp(-0.5 * 2.0))
+    assert abs(y[1, 1] - want) < 1e-15 and abs(y[1, 0] - (1.0 - want)) < 1e-15 and y[1, 2] == 0.0
+
+
+def pin_softmax_causal_brute(lib):
+    """Pure-Python softmax of the scaled visible prefix (tiny rows)."""
+    for dt in ("f32", "f16", "bf16"):
+        for N in (1, 2, 3, 7, 16, 33):
+            M, Q, off = 6, 4, 1
+            x = _rng_rows(960 + N, M, N, dt, scale=2.0)
+            sc = float(np.float32(0.3))
+            y = oracle.softmax_causal(x, dt, 0.3, Q, off, lib=lib)
+            for r in range(M):
+                vis = min(N, r % Q + off + 1)
+                want = brute.softmax_row([sc * v for v in _decode_py(x[r], dt)[:vis]])
+                assert _rel(y[r, :vis], want) < 1e-13, (dt, N, r)
+                assert np.all(y[r, vis:] == 0.0)
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -37,6 +37,12 @@ MUTANTS = {
     "add_subtracts": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);",
                       "h[i] = or_load(dtype, x, i) - or_load(dtype, r, i);"),
     "add_drops_residual": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);", "h[i] = or_load(dtype, x, i);"),
+    "causal_drops_diagonal": ("int64_t vis = q + offset + 1;", "int64_t vis = q + offset;"),
+    "causal_ignores_offset": ("int64_t vis = q + offset + 1;", "int64_t vis = q + 1;"),
+    "causal_query_is_row": ("int64_t q = r % queries;", "int64_t q = r;"),
+    "causal_scale_dropped": ("double v = sc * or_load(dtype, x, base + k);", "double v = or_load(dtype, x, base + k);"),
+    "causal_masked_outputs_uniform": ("for (int64_t k = vis; k < N; ++k) y[base + k] = 0.0;",
+                                      "for (int64_t k = vis; k < N; ++k) y[base + k] = 1.0 / (double)N;"),
     "add_residual_shifted": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);",
                              "h[i] = or_load(dtype, x, i) + or_load(dtype, r, i > 0 ? i - 1 : i);"),
 }

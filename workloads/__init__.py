@@ -35,6 +35,9 @@ Next-row workloads (fused residual add + norm, at the norm workloads' shapes;
 not part of the five-workload suite):
   add_rmsnorm_bf16_16384x8192  x, w as rmsnorm_bf16_16384x8192; residual r ~ N(0,1)  seed 303
   add_layernorm_f16_4096       x, gamma, beta as layernorm_f16_4096; r ~ N(0,1)      seed 205
+  causal_entry_softmax_bf16    the causal_softmax_bf16 inputs through the causal entry point
+                               (scale 1, 4096 queries per head, offset 0): masked keys are
+                               not read, so its bytes are the visible reads plus all writes
 """
 from __future__ import annotations
 
@@ -121,6 +124,10 @@ class Workload:
         read each length-N parameter vector once, write the per-row stats;
         the fused add + norm also reads the residual once and writes h once."""
         e = self.elem_bytes
+        if self.op == "softmax_causal":
+            Q, off = self.extra["queries"], self.extra.get("offset", 0)
+            q = np.arange(self.M, dtype=np.int64) % Q
+            return int(np.minimum(self.N, q + off + 1).sum()) * e + self.M * self.N * e
         b = 2 * self.M * self.N * e
         if self.op.startswith("add_"):
             b += 2 * self.M * self.N * e
@@ -213,6 +220,7 @@ _MAKERS = {
     "vocab_softmax_f32": _mk_vocab,
     "add_rmsnorm_bf16_16384x8192": _mk_add_rmsnorm,
     "add_layernorm_f16_4096": _mk_add_layernorm,
+    "causal_entry_softmax_bf16": _mk_causal,
 }
 
 WORKLOADS = [
@@ -233,5 +241,8 @@ NEXT_WORKLOADS = [
              desc="fused residual add + RMSNorm bf16 16384 x 8192"),
     Workload("add_layernorm_f16_4096", "add_layernorm", F16, 4096, 4096, eps=1e-5,
              desc="fused residual add + LayerNorm fp16 4096 x 4096"),
+    Workload("causal_entry_softmax_bf16", "softmax_causal", BF16, 131072, 4096,
+             desc="causal softmax entry (masked keys not read), 32 heads x 4096 q x 4096 k",
+             extra={"queries": 4096, "heads": 32, "offset": 0, "scale": 1.0}),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
