@@ -22,8 +22,8 @@ every launch gives each workload's own GB/s (per_workload).
 Prints ONE JSON line.  Flags: --gpus (only 1 is supported), --steps, --warmup,
 --only NAME[,NAME] (time a subset, rotating buffer sets so the 256 MiB
 Infinity Cache cannot serve them), --no-cpu-baseline, --no-next (skip the
-fused residual add + norm rows, which are timed after the suite and
-reported under next_rows, outside value); --calibrate (the plain
+next rows -- fused residual add + norm, the causal softmax entry -- which
+are timed after the suite and reported under next_rows, outside value); --calibrate (the plain
 1 GiB copy: attainable bandwidth, and the counter calibration) and
 --copy-at-sizes (the plain copy at each workload's byte count) replace the
 suite.
@@ -43,6 +43,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
 METRIC = "achieved HBM GB/s (and % of MI355X peak) for softmax/LayerNorm/RMSNorm rows"
 CACHE_BYTES = 256 << 20     # Infinity Cache (MALL) size
+# workload op -> nt_op code of nt_plan_launch
+OP_CODES = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4, "softmax_causal": 5}
 
 
 def log(*a):
@@ -77,7 +79,8 @@ class Job:
             r0 = to_dev(data["residual"], w.dt, torch, np)
             self.r = [r0] + [r0.clone() for _ in range(R - 1)]
             self.h = [torch.empty_like(x0) for _ in range(R)]
-        self.wsb = nt.nt_softmax_workspace_bytes(w.M, w.N, self.dt_code) if w.op == "softmax" else 0
+        self.wsb = (nt.nt_softmax_workspace_bytes(w.M, w.N, self.dt_code)
+                    if w.op in ("softmax", "softmax_causal") else 0)
         self.ws = torch.empty(max(self.wsb, 8), dtype=torch.uint8, device="cuda")
         self.i = 0
         self.starts, self.ends = [], []
@@ -88,6 +91,11 @@ class Job:
         if w.op == "softmax":
             rc = nt.nt_softmax_rows(w.M, w.N, self.dt_code, self.x[r].data_ptr(), self.y[r].data_ptr(),
                                     self.ws.data_ptr(), self.wsb, stream)
+        elif w.op == "softmax_causal":
+            e = w.extra
+            rc = nt.nt_softmax_causal_rows(w.M, w.N, self.dt_code, e["scale"], e["queries"], e["offset"],
+                                           self.x[r].data_ptr(), self.y[r].data_ptr(), self.ws.data_ptr(), self.wsb,
+                                           stream)
         elif w.op == "add_layernorm":
             rc = nt.nt_add_layernorm_rows(w.M, w.N, self.dt_code, w.eps, self.x[r].data_ptr(), self.r[r].data_ptr(),
                                           self.p0.data_ptr(), self.p1.data_ptr(), self.h[r].data_ptr(),
@@ -257,7 +265,7 @@ def main():
     ap.add_argument("--only", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the fused add + norm rows (timed after the suite, not part of value)")
+                    help="skip the next rows (timed after the suite, not part of value)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the plain 1 GiB streaming copy (and torch copy_) instead")
     ap.add_argument("--copy-at-sizes", action="store_true",
@@ -330,8 +338,7 @@ def main():
                     "bytes": j.bytes, "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
                     "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "plan": nt.nt_plan_launch({"softmax": 0, "layernorm": 1, "rmsnorm": 2}[j.w.op],
-                                              j.w.M, j.w.N, j.dt_code, True)})
+                    "plan": nt.nt_plan_launch(OP_CODES[j.w.op], j.w.M, j.w.N, j.dt_code, True)})
     dom_i = max(range(len(jobs)), key=lambda i: per[i]["avg_ms"])
     dom_job = jobs[dom_i]
 
@@ -366,13 +373,14 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(dom["workload"], dom["bytes"]),
                 "kernel": dom["workload"], "avg_launch_ms": round(dom_ms, 5)}
 
-    # Next rows (fused residual add + norm): timed on their own after the
-    # timed region, not part of `value`; buffer sets rotate past the cache.
+    # Next rows (fused residual add + norm, causal softmax entry): timed on
+    # their own after the timed region, not part of `value`; buffer sets
+    # rotate past the cache.
     next_rows = []
     if suite and not args.no_next:
         for w in workloads.NEXT_WORKLOADS:
             data = w.make()
-            per_set = 4 * w.M * w.N * w.elem_bytes
+            per_set = (2 if w.op == "softmax_causal" else 4) * w.M * w.N * w.elem_bytes
             j = Job(w, data, max(1, -(-(4 * CACHE_BYTES) // per_set)), torch, np, nt)
             for _ in range(args.warmup):
                 j.launch(sh)
@@ -385,10 +393,14 @@ def main():
             torch.cuda.synchronize()
             durs = [a.elapsed_time(b) for a, b in evs]
             avg = sum(durs) / len(durs)
-            op = {"add_layernorm": 3, "add_rmsnorm": 4}[w.op]
+            op = OP_CODES[w.op]
             e = w.elem_bytes
+            if w.op == "softmax_causal":     # the generic softmax reads the masked keys too
+                base = {"baseline": "generic softmax of the -inf-masked rows", "baseline_bytes": 2 * w.M * w.N * e}
+            else:                            # an add kernel, then the norm of its output
+                base = {"baseline": "add, then norm (unfused)", "baseline_bytes": j.bytes + 2 * w.M * w.N * e}
             next_rows.append({"workload": w.name, "op": w.op, "dtype": w.dt, "M": w.M, "N": w.N,
-                              "bytes": j.bytes, "unfused_bytes": j.bytes + 2 * w.M * w.N * e,
+                              "bytes": j.bytes, **base,
                               "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
                               "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                               "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

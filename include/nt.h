@@ -81,7 +81,8 @@ typedef enum {
     NT_ERR_ALIGN = 5,      /* a pointer is not aligned to its element size     */
     NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes */
     NT_ERR_HIP = 7,        /* the HIP runtime reported a launch error          */
-    NT_ERR_ALIAS = 8       /* fused add + norm: h and y are the same buffer    */
+    NT_ERR_ALIAS = 8,      /* fused add + norm: h and y are the same buffer    */
+    NT_ERR_SCALE = 9       /* causal softmax: scale is not finite and > 0      */
 } nt_status;
 
 /*
@@ -112,6 +113,31 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
                           const void *x, void *y,
                           void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Causal, scaled softmax of attention-score rows.  Row r holds the scores of
+ * query q = r mod `queries` (rows of several heads follow one another) against
+ * N keys; key k is visible to it iff k <= q + offset (offset 0: square causal
+ * attention, the diagonal kept; offset N - queries aligns the last query with
+ * the last key).  Over the visible keys
+ *   y[r, k] = exp(scale*x[r, k] - m) / sum_k' exp(scale*x[r, k'] - m),
+ * m the max of scale*x over them, and y[r, k] = 0 at masked keys, whose x is
+ * never read (it may hold anything).  The result is the plain softmax of the
+ * row with its masked scores at -inf ("Portable Triton Kernels", "Safe
+ * Softmax Pattern": a -inf entry contributes exactly nothing), computed
+ * while reading only the visible part of each row: for square causal rows
+ * about half the bytes of nt_softmax_rows.
+ *
+ * scale must be finite and > 0 (NT_ERR_SCALE); queries >= 1 and offset >= 0
+ * (NT_ERR_SHAPE).  Layout, dtypes, alignment, workspace (sized by
+ * nt_softmax_workspace_bytes for rows too wide to hold on chip), in-place
+ * calls and errors as nt_softmax_rows.
+ */
+nt_status nt_softmax_causal_rows(int64_t M, int64_t N, nt_dtype dt, float scale,
+                                 int64_t queries, int64_t offset,
+                                 const void *x, void *y,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /*
  * LayerNorm over each row.  mean_r = sum_j x[r, j] / N,
@@ -179,7 +205,8 @@ typedef enum {
     NT_OP_LAYERNORM = 1,
     NT_OP_RMSNORM = 2,
     NT_OP_ADD_LAYERNORM = 3,  /* nt_add_layernorm_rows */
-    NT_OP_ADD_RMSNORM = 4     /* nt_add_rmsnorm_rows   */
+    NT_OP_ADD_RMSNORM = 4,    /* nt_add_rmsnorm_rows   */
+    NT_OP_SOFTMAX_CAUSAL = 5  /* nt_softmax_causal_rows */
 } nt_op;
 
 typedef struct {

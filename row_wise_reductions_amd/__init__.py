@@ -4,8 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/nt.h``.  The ``nt_*``
 functions take the same arguments as their C counterparts (pointers as
 integers, ``stream`` as a ``hipStream_t`` handle) and return the status code.
-``softmax``, ``layer_norm``, ``rms_norm``, ``add_layer_norm`` and
-``add_rms_norm`` are conveniences over torch
+``softmax``, ``softmax_causal``, ``layer_norm``, ``rms_norm``,
+``add_layer_norm`` and ``add_rms_norm`` are conveniences over torch
 tensors on an AMD GPU: they check contiguity, allocate outputs (and the
 split-path workspace) with torch, and launch on torch's current stream.
 
@@ -22,9 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libnt.so")
 
 NT_F32, NT_F16, NT_BF16 = 0, 1, 2
 NT_OP_SOFTMAX, NT_OP_LAYERNORM, NT_OP_RMSNORM, NT_OP_ADD_LAYERNORM, NT_OP_ADD_RMSNORM = 0, 1, 2, 3, 4
+NT_OP_SOFTMAX_CAUSAL = 5
 STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4: "NT_ERR_EPS",
-          5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP", 8: "NT_ERR_ALIAS"}
-EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_layernorm_rows",
+          5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP", 8: "NT_ERR_ALIAS",
+          9: "NT_ERR_SCALE"}
+EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows",
             "nt_rmsnorm_rows", "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
             "nt_status_string", "nt_plan_launch")
 
@@ -63,6 +65,7 @@ def lib():
     L.nt_softmax_workspace_bytes.argtypes = [i64, i64, i32]
     L.nt_softmax_workspace_bytes.restype = sz
     L.nt_softmax_rows.argtypes = [i64, i64, i32, vp, vp, vp, sz, vp]
+    L.nt_softmax_causal_rows.argtypes = [i64, i64, i32, f32, i64, i64, vp, vp, vp, sz, vp]
     L.nt_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     L.nt_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp]
     L.nt_add_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -70,7 +73,8 @@ def lib():
     L.nt_status_string.argtypes = [i32]
     L.nt_status_string.restype = ctypes.c_char_p
     L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
-    for f in ("nt_softmax_rows", "nt_layernorm_rows", "nt_rmsnorm_rows", "nt_add_layernorm_rows",
+    for f in ("nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
+              "nt_add_layernorm_rows",
               "nt_add_rmsnorm_rows", "nt_plan_launch"):
         getattr(L, f).restype = i32
     _lib = L
@@ -85,6 +89,11 @@ def nt_softmax_workspace_bytes(M: int, N: int, dt: int) -> int:
 
 def nt_softmax_rows(M, N, dt, x, y, workspace, workspace_bytes, stream) -> int:
     return int(lib().nt_softmax_rows(M, N, dt, x, y, workspace, workspace_bytes, stream))
+
+
+def nt_softmax_causal_rows(M, N, dt, scale, queries, offset, x, y, workspace, workspace_bytes, stream) -> int:
+    return int(lib().nt_softmax_causal_rows(M, N, dt, scale, queries, offset, x, y, workspace, workspace_bytes,
+                                            stream))
 
 
 def nt_layernorm_rows(M, N, dt, eps, x, gamma, beta, y, mean, rstd, stream) -> int:
@@ -171,6 +180,23 @@ def softmax(x, out=None, stream=None):
     wsb = nt_softmax_workspace_bytes(M, N, dt)
     ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
     _check(nt_softmax_rows(M, N, dt, _ptr(x), _ptr(y), _ptr(ws), wsb, _stream(stream)), "nt_softmax_rows")
+    return y
+
+
+def softmax_causal(x, scale=1.0, queries=None, offset=0, out=None, stream=None):
+    """Causal softmax of scale*x over the last dimension: row r is query
+    r mod `queries` (default: the second-to-last dimension) and sees keys
+    k <= q + offset; masked outputs are 0 and masked inputs are not read."""
+    torch = _torch()
+    M, N = _rows(x)
+    if queries is None:
+        queries = x.shape[-2] if x.dim() >= 2 else 1
+    y = torch.empty_like(x) if out is None else out
+    dt = dtype_code(x)
+    wsb = nt_softmax_workspace_bytes(M, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    _check(nt_softmax_causal_rows(M, N, dt, float(scale), int(queries), int(offset), _ptr(x), _ptr(y), _ptr(ws),
+                                  wsb, _stream(stream)), "nt_softmax_causal_rows")
     return y
 
 

@@ -40,7 +40,7 @@ constexpr bool shape_built() {
 // a residual input (a.r) selects the fused add + norm kernel.
 template <int OP, int W, int K>
 hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
-    if constexpr (OP == OP_SOFTMAX) {
+    if constexpr (OP == OP_SOFTMAX || OP == OP_SOFTMAX_CAUSAL) {
         return go_pr<OP, W, K, false, false>(al, a, grid, s);
     } else {
         const bool pr = a.p0 != nullptr && (OP == OP_RMSNORM || a.p1 != nullptr);
@@ -141,23 +141,35 @@ hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStre
     return hipErrorInvalidValue;
 }
 
-template <int W, int K, bool AL>
+template <int W, int K, bool AL, bool CAUSAL>
 hipError_t split_al(bool coop, const RowArgs &a, hipStream_t s) {
     const uint32_t grid = (uint32_t)(a.M * a.P);
     if (coop) {
-        hipLaunchKernelGGL((softmax_coop<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+        hipLaunchKernelGGL((softmax_coop<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((softmax_split_partial<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((softmax_split_partial<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
     return hipGetLastError();
+}
+
+// The causal split kernels are built for the planner's split shapes only:
+// 32 values per lane on 8 waves (the cooperative shape) and (4, 4).
+template <int W, int K>
+constexpr bool causal_split_built() {
+    return (W == 8 && K * dt_info<DT>::VEC == 32) || (W == 4 && K == 4);
 }
 
 template <int W, int K>
 hipError_t split_go(bool al, bool coop, const RowArgs &a, hipStream_t s) {
-    return al ? split_al<W, K, true>(coop, a, s) : split_al<W, K, false>(coop, a, s);
+    if (a.queries > 0) {
+        if constexpr (causal_split_built<W, K>())
+            return al ? split_al<W, K, true, true>(coop, a, s) : split_al<W, K, false, true>(coop, a, s);
+        return hipErrorInvalidValue;
+    }
+    return al ? split_al<W, K, true, false>(coop, a, s) : split_al<W, K, false, false>(coop, a, s);
 }
 
 hipError_t split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
@@ -185,6 +197,7 @@ hipError_t resident_any(int op, int W, int K, bool al, const RowArgs &a, int64_t
     case OP_SOFTMAX: return resident<OP_SOFTMAX>(W, K, al, a, grid, s);
     case OP_LAYERNORM: return resident<OP_LAYERNORM>(W, K, al, a, grid, s);
     case OP_RMSNORM: return resident<OP_RMSNORM>(W, K, al, a, grid, s);
+    case OP_SOFTMAX_CAUSAL: return resident<OP_SOFTMAX_CAUSAL>(W, K, al, a, grid, s);
     }
     return hipErrorInvalidValue;
 }

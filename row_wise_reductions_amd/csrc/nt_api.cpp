@@ -43,18 +43,23 @@ struct Menu {
     int n;
 };
 // Chosen from launch-shape sweeps on MI355X: about one or two 16-byte chunks
-// per lane with up to 8 waves per row stream best.
+// per lane with up to 8 waves per row stream best.  Causal rows, whose loads
+// stop at the diagonal, are latency-bound rather than bandwidth-bound: for
+// 16-bit rows of 512 chunks (4096 elements) 4 waves with 2 chunks each keep
+// twice the rows in flight of 8 waves with 1 (1.27x on causal rows; 8 waves
+// stay ahead by about 1% on full rows).
 const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
 const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kCausal16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
 const Shape kRms16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
 const Shape kLn16[] = {{1, 1}, {1, 2}, {4, 1}, {4, 2}, {8, 2}};
 #define NT_MENU(a) Menu{a, (int)(sizeof(a) / sizeof(*(a)))}
-Menu menu_for(nt_op op, nt_dtype dt) {
+Menu menu_for(nt_op op, nt_dtype dt, bool causal) {
     const bool wide = dt == NT_F32;
     switch (op) {
-    case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : NT_MENU(kSoftmax16);
+    case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : causal ? NT_MENU(kCausal16) : NT_MENU(kSoftmax16);
     case NT_OP_RMSNORM: return wide ? NT_MENU(kRms32) : NT_MENU(kRms16);
     default: return wide ? NT_MENU(kLn32) : NT_MENU(kLn16);
     }
@@ -148,11 +153,11 @@ bool shape_fits(nt_op op, nt_dtype dt, bool res, Shape sh) {
 }
 
 nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true,
-                    bool res = false) {
+                    bool res = false, bool causal = false) {
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
-    const Menu menu = menu_for(op, dt);
+    const Menu menu = menu_for(op, dt, causal);
     const char *force = std::getenv("NT_FORCE_PATH");
     const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
     const bool force_loop = op != NT_OP_SOFTMAX && force && std::strcmp(force, "looped") == 0;
@@ -282,14 +287,16 @@ void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_p
 nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a,
               void *stream) {
     if (debug_on())
-        debug_print(op == NT_OP_SOFTMAX     ? "softmax"
+        debug_print(op == NT_OP_SOFTMAX     ? (a.queries ? "causal softmax" : "softmax")
                     : op == NT_OP_LAYERNORM ? (a.r ? "add+layernorm" : "layernorm")
                                             : (a.r ? "add+rmsnorm" : "rmsnorm"),
                     M, N, dt, p);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // kernel op codes: the causal softmax is a kernel op of its own
+    const int kop = (op == NT_OP_SOFTMAX && a.queries > 0) ? (int)ntk::OP_SOFTMAX_CAUSAL : (int)op;
     hipError_t e = p.split == 1   ? launch_split(dt, p, a, s)
-                   : p.split == 2 ? launch_looped(dt, (int)op, p, a, s)
-                                  : launch_resident(dt, (int)op, p, a, s);
+                   : p.split == 2 ? launch_looped(dt, kop, p, a, s)
+                                  : launch_resident(dt, kop, p, a, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         if (debug_on()) std::fprintf(stderr, "[nt] launch failed: %s\n", hipGetErrorString(e));
@@ -326,6 +333,7 @@ const char *nt_status_string(nt_status s) {
     case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes()";
     case NT_ERR_HIP: return "HIP launch error";
     case NT_ERR_ALIAS: return "h and y must be different buffers";
+    case NT_ERR_SCALE: return "scale must be finite and > 0";
     }
     return "unknown status";
 }
@@ -333,14 +341,17 @@ const char *nt_status_string(nt_status s) {
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt, int aligned16, nt_plan *out) {
     if (!out) return NT_ERR_NULL;
     if (op != NT_OP_SOFTMAX && op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM && op != NT_OP_ADD_LAYERNORM &&
-        op != NT_OP_ADD_RMSNORM)
+        op != NT_OP_ADD_RMSNORM && op != NT_OP_SOFTMAX_CAUSAL)
         return NT_ERR_SHAPE;
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
     const bool al = aligned16 && (N * elem_bytes(dt)) % 16 == 0;
     const bool res = op == NT_OP_ADD_LAYERNORM || op == NT_OP_ADD_RMSNORM;
-    const nt_op base = op == NT_OP_ADD_LAYERNORM ? NT_OP_LAYERNORM : op == NT_OP_ADD_RMSNORM ? NT_OP_RMSNORM : op;
-    return make_plan(base, M, N, dt, al, out, true, res);
+    const nt_op base = op == NT_OP_ADD_LAYERNORM   ? NT_OP_LAYERNORM
+                       : op == NT_OP_ADD_RMSNORM   ? NT_OP_RMSNORM
+                       : op == NT_OP_SOFTMAX_CAUSAL ? NT_OP_SOFTMAX
+                                                    : op;
+    return make_plan(base, M, N, dt, al, out, true, res, op == NT_OP_SOFTMAX_CAUSAL);
 }
 
 size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt) {
@@ -352,15 +363,15 @@ size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt) {
     return (size_t)p.workspace_bytes;
 }
 
-nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *workspace,
-                          size_t workspace_bytes, void *stream) {
-    nt_status st = common_checks(M, N, dt, x, y);
-    if (st != NT_OK || M == 0) return st;
+// Softmax launch shared by the plain and the causal entry points (a.queries
+// > 0 selects the causal kernels); arguments already validated up to the
+// workspace.
+static nt_status softmax_launch(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream, ntk::RowArgs &a) {
     const bool al = all_aligned16(N, dt, x, y, nullptr, nullptr);
     nt_plan p;
-    st = make_plan(NT_OP_SOFTMAX, M, N, dt, al, &p);
+    nt_status st = make_plan(NT_OP_SOFTMAX, M, N, dt, al, &p, true, false, a.queries > 0);
     if (st != NT_OK) return st;
-    ntk::RowArgs a{};
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
     a.M = M;
@@ -394,6 +405,29 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void
         }
     }
     return run(NT_OP_SOFTMAX, M, N, dt, p, a, stream);
+}
+
+nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    ntk::RowArgs a{};
+    return softmax_launch(M, N, dt, x, y, workspace, workspace_bytes, stream, a);
+}
+
+nt_status nt_softmax_causal_rows(int64_t M, int64_t N, nt_dtype dt, float scale, int64_t queries, int64_t offset,
+                                 const void *x, void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(dt)) return NT_ERR_DTYPE;
+    if (!valid_shape(M, N)) return NT_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return NT_ERR_SCALE;
+    if (queries < 1 || offset < 0) return NT_ERR_SHAPE;
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    ntk::RowArgs a{};
+    a.queries = queries < M ? queries : M;            // rows r < M: r mod queries is unchanged
+    a.offset = offset < N ? offset : N;              // every key visible from there on
+    a.s2 = (float)((double)scale * 1.4426950408889634074);
+    return softmax_launch(M, N, dt, x, y, workspace, workspace_bytes, stream, a);
 }
 
 nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,

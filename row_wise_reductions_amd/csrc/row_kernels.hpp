@@ -30,7 +30,7 @@
 
 namespace ntk {
 
-enum { OP_SOFTMAX = 0, OP_LAYERNORM = 1, OP_RMSNORM = 2 };
+enum { OP_SOFTMAX = 0, OP_LAYERNORM = 1, OP_RMSNORM = 2, OP_SOFTMAX_CAUSAL = 3 };
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 template <int DT> struct dt_info;
@@ -66,6 +66,9 @@ struct RowArgs {
     float inv_n;         // 1/N in fp32
     uint32_t tag;        // cooperative split softmax: this call's record tag
     int32_t spin;        // cooperative split softmax: polls before recomputing
+    int64_t queries;     // causal softmax: row r is query r mod queries (0: not causal)
+    int64_t offset;      // causal softmax: query q sees keys k <= q + offset
+    float s2;            // causal softmax: scale * log2(e), rounded to fp32
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -540,6 +543,91 @@ __device__ __forceinline__ void add_residual(uint4 (&raw)[K], const uint4 (&rr)[
 }
 
 // ---------------------------------------------------------------------------
+// Causal softmax rows: query q = row mod queries sees keys 0 .. q + offset.
+// A row is loaded as if it were only its visible prefix of L columns (the
+// general, element-gathering geometry, so a partial last chunk is read
+// element by element and nothing past column L is fetched: clamped loads
+// past the prefix re-read its last whole chunk, a cache hit), and padded
+// with -inf, which turns into exact zeros in the output; the store covers
+// the whole row.  Both geometries give chunk c the same columns.
+// ---------------------------------------------------------------------------
+
+// The host clamps `queries` to M, so a 32-bit remainder serves whenever the
+// row index fits in 32 bits (a 64-bit one is a long instruction sequence).
+__device__ __forceinline__ int32_t visible_len(const RowArgs &a, int64_t row) {
+    const int64_t q = (a.M <= 0xFFFFFFFFll) ? (int64_t)((uint32_t)row % (uint32_t)a.queries) : row % a.queries;
+    const int64_t v = q + a.offset + 1;
+    return v < (int64_t)a.N ? (int32_t)v : a.N;
+}
+
+// Elements i >= rem of a chunk set to -inf (rem in 1 .. VEC-1).
+template <int DT>
+__device__ __forceinline__ uint4 mask_tail(uint4 r, int rem) {
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (dt_info<DT>::E == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i >= rem) w[i] = dt_info<DT>::NEG_INF_WORD;
+    } else {
+        const uint32_t ninf = dt_info<DT>::NEG_INF_WORD & 0xFFFFu;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i >= rem) w[i >> 1] = (i & 1) ? ((w[i >> 1] & 0xFFFFu) | (ninf << 16)) : ((w[i >> 1] & 0xFFFF0000u) | ninf);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Issue the loads of a softmax row slice.  Causal rows read their visible
+// prefix only: on 16-byte-aligned rows the chunk holding the last visible
+// column is loaded whole (it lies inside the row) and masked in registers;
+// misaligned rows use the element-gathering geometry on the prefix.
+template <int DT, bool AL, int K, int TPR, bool CAUSAL, bool NT = true>
+__device__ __forceinline__ void softmax_issue(uint4 (&raw)[K], const RowGeom<DT, AL> &geo, const char *xr, int t,
+                                              int32_t N, int32_t L, int64_t cbase = 0) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    if constexpr (CAUSAL && AL) {
+        const int64_t f1 = (L + VEC - 1) / VEC - 1;      // chunk holding column L - 1
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            int64_t c = cbase + (int64_t)k * TPR + t;
+            c = c > f1 ? f1 : c;
+            raw[k] = NT ? ld16_nt(xr + c * 16) : ld16(xr + c * 16);
+        }
+    } else if constexpr (CAUSAL) {
+        load_row<DT, false, K, TPR, NT>(raw, RowGeom<DT, false>(xr, L), t, L, cbase);
+    } else {
+        load_row<DT, AL, K, TPR, NT>(raw, geo, t, N, cbase);
+    }
+}
+
+// Complete it: -inf outside the row (causal: outside the visible prefix).
+template <int DT, bool AL, int K, int TPR, bool CAUSAL>
+__device__ __forceinline__ void softmax_finish(uint4 (&raw)[K], const RowGeom<DT, AL> &geo, const char *xr, int t,
+                                               int32_t N, int32_t L, int64_t cbase = 0) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    constexpr uint32_t NI = dt_info<DT>::NEG_INF_WORD;
+    if constexpr (CAUSAL && AL) {
+        const int64_t f1 = (L + VEC - 1) / VEC - 1;
+        const int rem = L - (int)(f1 * VEC);                // visible elements of chunk f1: 1 .. VEC
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t c = cbase + (int64_t)k * TPR + t;
+            if (c > f1)
+                raw[k] = make_uint4(NI, NI, NI, NI);
+            else if (c == f1 && rem < VEC)
+                raw[k] = mask_tail<DT>(raw[k], rem);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            asm volatile("" : "+v"(raw[k].x), "+v"(raw[k].y), "+v"(raw[k].z), "+v"(raw[k].w));
+    } else if constexpr (CAUSAL) {
+        finish_row<DT, false, K, TPR>(raw, RowGeom<DT, false>(xr, L), xr, t, L, NI, cbase);
+    } else {
+        finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, NI, cbase);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-row scalar helpers
 // ---------------------------------------------------------------------------
 
@@ -588,7 +676,9 @@ struct GroupShape {
 template <int OP, int DT, int W, int K, bool AL, bool PR, bool RES = false>
 __global__ void __launch_bounds__(GroupShape<W>::THREADS)
 row_resident(RowArgs a) {
-    static_assert(!RES || OP != OP_SOFTMAX, "the residual add precedes a norm");
+    constexpr bool SM = OP == OP_SOFTMAX || OP == OP_SOFTMAX_CAUSAL;
+    constexpr bool CAUSAL = OP == OP_SOFTMAX_CAUSAL;
+    static_assert(!RES || !SM, "the residual add precedes a norm");
     using I = dt_info<DT>;
     constexpr int VEC = I::VEC, TPR = 64 * W, G = GroupShape<W>::G;
     // LayerNorm keeps an fp64 copy of its values when they are few per lane
@@ -599,7 +689,7 @@ row_resident(RowArgs a) {
     const int wv = t >> 6, lane = t & 63;
     const int32_t N = a.N;
     const int64_t rowbytes = (int64_t)N * I::E;
-    const uint32_t fill = (OP == OP_SOFTMAX) ? I::NEG_INF_WORD : 0u;
+    const uint32_t fill = SM ? I::NEG_INF_WORD : 0u;
     const bool has_p0 = PR || a.p0 != nullptr, has_p1 = PR || a.p1 != nullptr;
 
     __shared__ float red_f[2][2][W];
@@ -624,18 +714,25 @@ row_resident(RowArgs a) {
         uint32_t padw = fill;
         if constexpr (OP == OP_LAYERNORM) padw = RES ? pivot_word_sum<DT>(xr, rr) : pivot_word<DT>(xr);
         uint4 raw[K], rraw[RES ? K : 1];
-        load_row<DT, AL, K, TPR>(raw, geo, t, N);
+        const int32_t L = CAUSAL ? visible_len(a, row) : N;
+        if constexpr (SM)
+            softmax_issue<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L);
+        else
+            load_row<DT, AL, K, TPR>(raw, geo, t, N);
         if constexpr (RES) load_row<DT, AL, K, TPR>(rraw, RowGeom<DT, AL>(rr, N), t, N);
-        constexpr int KP0 = (OP == OP_SOFTMAX) ? 1 : K;
+        constexpr int KP0 = SM ? 1 : K;
         constexpr int KP1 = (OP == OP_LAYERNORM) ? K : 1;
         uint4 p0[KP0], p1[KP1];
-        if constexpr (OP != OP_SOFTMAX) {
+        if constexpr (!SM) {
             if (has_p0) load_params<DT, AL, K, TPR>(p0, geo, a.p0, t, N);
         }
         if constexpr (OP == OP_LAYERNORM) {
             if (has_p1) load_params<DT, AL, K, TPR>(p1, geo, a.p1, t, N);
         }
-        finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw);
+        if constexpr (SM)
+            softmax_finish<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L);
+        else
+            finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw);
         if constexpr (RES) {
             // x padded with the pivot of h, r with 0: h's padding is the pivot
             finish_row<DT, AL, K, TPR>(rraw, RowGeom<DT, AL>(rr, N), rr, t, N, 0u);
@@ -645,19 +742,22 @@ row_resident(RowArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
 
-        if constexpr (OP == OP_SOFTMAX) {
+        if constexpr (SM) {
             // ---- softmax.  With c = m*log2(e) rounded to fp32, every element
             // is 2^(x*log2(e) - c): one fma (exact product, one rounding) and
             // one v_exp_f32.  Shift invariance makes any shift exact, and c is
             // within half an ulp of m*log2(e), so no term exceeds 2^(1e-7).
+            // The causal softmax of scale*x uses s2 = scale*log2(e) in place
+            // of log2(e) (scale > 0, so the max of x gives the max of scale*x).
+            const float s2 = CAUSAL ? a.s2 : LOG2E;
             const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red_f[par][0], wv, lane);
-            const float c = mx * LOG2E;
+            const float c = mx * s2;
             float s = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    v[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -c));
+                    v[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], s2, -c));
                     s += v[k][i];
                 }
             s = group_allreduce<W>(s, SumOp(), red_f[par][1], wv, lane);
@@ -1020,7 +1120,8 @@ row_looped(RowArgs a) {
 // for a chunk it recomputes) calls this, so the pair is bitwise the same
 // whichever workgroup computes it.
 template <int DT, int W, int K>
-__device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red)[2][W], int wv, int lane) {
+__device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red)[2][W], int wv, int lane,
+                                              float s2 = LOG2E) {
     constexpr int VEC = dt_info<DT>::VEC;
     float v[K][VEC];
 #pragma unroll
@@ -1029,13 +1130,13 @@ __device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red
     float cj;
     {
 #pragma clang fp contract(off)
-        cj = mx * LOG2E;
+        cj = mx * s2;
     }
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k)
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], LOG2E, -cj));
+        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], s2, -cj));
     s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
     if (mx == -__builtin_inff()) s = 0.f;    // a fully masked chunk holds no mass
     return make_float2(mx, s);
@@ -1046,17 +1147,17 @@ __device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red
 // (the online-normalizer rescaling).  Returns c and 1/l.  Every wave that
 // calls it on the same pairs gets the same bits.
 template <class Q>
-__device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, float &inv) {
+__device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, float &inv, float s2 = LOG2E) {
     float m = -__builtin_inff();
     for (int p = lane; p < P; p += 64) m = __builtin_fmaxf(m, q[p].x);
     m = wave_allreduce(m, MaxOp());
     float l = 0.f;
     {
 #pragma clang fp contract(off)
-        c = m * LOG2E;
+        c = m * s2;
         for (int p = lane; p < P; p += 64) {
             const float2 e = q[p];
-            const float cj = e.x * LOG2E;    // rounded exactly as in chunk_stats
+            const float cj = e.x * s2;       // rounded exactly as in chunk_stats
             l += (e.x == -__builtin_inff()) ? 0.f : e.y * __builtin_amdgcn_exp2f(cj - c);
         }
     }
@@ -1068,14 +1169,15 @@ __device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, 
 // Output of one chunk: y = 2^(x*log2e - c) * (1/l), rounded once to the type.
 template <int DT, int W, int K, bool AL>
 __device__ __forceinline__ void softmax_chunk_out(const uint4 (&raw)[K], const RowGeom<DT, AL> &geo, char *yr, int t,
-                                                  int32_t N, bool yvec, int64_t cbase, float c, float inv) {
+                                                  int32_t N, bool yvec, int64_t cbase, float c, float inv,
+                                                  float s2 = LOG2E) {
     constexpr int VEC = dt_info<DT>::VEC, TPR = 64 * W;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         float v[VEC];
         unpack<DT>(raw[k], v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], LOG2E, -c)) * inv;
+        for (int i = 0; i < VEC; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], s2, -c)) * inv;
         store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
     }
 }
@@ -1084,7 +1186,7 @@ __device__ __forceinline__ void softmax_chunk_out(const uint4 (&raw)[K], const R
 // workspace, the finalize kernel merges a row's pairs and writes the chunk's
 // outputs (reading x a second time).
 
-template <int DT, int W, int K, bool AL>
+template <int DT, int W, int K, bool AL, bool CAUSAL = false>
 __global__ void __launch_bounds__(64 * W)
 softmax_split_partial(RowArgs a) {
     using I = dt_info<DT>;
@@ -1099,14 +1201,16 @@ softmax_split_partial(RowArgs a) {
 
     uint4 raw[K];
     const int64_t cbase = j * (int64_t)(TPR * K);
+    const int32_t L = CAUSAL ? visible_len(a, row) : N;
+    const float s2 = CAUSAL ? a.s2 : LOG2E;
     // temporal loads: the finalize kernel reads this chunk again
-    load_row<DT, AL, K, TPR, false>(raw, geo, t, N, cbase);
-    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
-    const float2 q = chunk_stats<DT, W, K>(raw, red, wv, lane);
+    softmax_issue<DT, AL, K, TPR, CAUSAL, false>(raw, geo, xr, t, N, L, cbase);
+    softmax_finish<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L, cbase);
+    const float2 q = chunk_stats<DT, W, K>(raw, red, wv, lane, s2);
     if (t == 0) a.ws[row * P + j] = q;
 }
 
-template <int DT, int W, int K, bool AL>
+template <int DT, int W, int K, bool AL, bool CAUSAL = false>
 __global__ void __launch_bounds__(64 * W)
 softmax_split_finalize(RowArgs a) {
     using I = dt_info<DT>;
@@ -1125,13 +1229,15 @@ softmax_split_finalize(RowArgs a) {
     // issue the chunk loads first so their latency overlaps the merge
     uint4 raw[K];
     const int64_t cbase = j * (int64_t)(TPR * K);
-    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
+    const int32_t L = CAUSAL ? visible_len(a, row) : N;
+    const float s2 = CAUSAL ? a.s2 : LOG2E;
+    softmax_issue<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L, cbase);
 
     // every wave merges the row's pairs redundantly, in the same order
     float c, inv;
-    merge_pairs(a.ws + row * P, P, lane, c, inv);
-    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
-    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv);
+    merge_pairs(a.ws + row * P, P, lane, c, inv, s2);
+    softmax_finish<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L, cbase);
+    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv, s2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,7 +1257,7 @@ softmax_split_finalize(RowArgs a) {
 
 constexpr int COOP_PMAX = 128;    // chunks per row the cooperative kernel accepts
 
-template <int DT, int W, int K, bool AL>
+template <int DT, int W, int K, bool AL, bool CAUSAL = false>
 __global__ void __launch_bounds__(64 * W)
 softmax_coop(RowArgs a) {
     using I = dt_info<DT>;
@@ -1172,9 +1278,11 @@ softmax_coop(RowArgs a) {
 
     uint4 raw[K];
     const int64_t cbase = (int64_t)j * (TPR * K);
-    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
-    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, I::NEG_INF_WORD, cbase);
-    const float2 mine = chunk_stats<DT, W, K>(raw, red, wv, lane);
+    const int32_t L = CAUSAL ? visible_len(a, row) : N;
+    const float s2 = CAUSAL ? a.s2 : LOG2E;
+    softmax_issue<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L, cbase);
+    softmax_finish<DT, AL, K, TPR, CAUSAL>(raw, geo, xr, t, N, L, cbase);
+    const float2 mine = chunk_stats<DT, W, K>(raw, red, wv, lane, s2);
 
     uint64_t *rec = reinterpret_cast<uint64_t *>(a.ws) + row * P * 2;
     const uint64_t tg = (uint64_t)a.tag << 32;
@@ -1225,16 +1333,16 @@ softmax_coop(RowArgs a) {
             m &= m - 1;
             uint4 r2[K];
             const int64_t qbase = (int64_t)q * (TPR * K);
-            load_row<DT, AL, K, TPR>(r2, geo, t, N, qbase);
-            finish_row<DT, AL, K, TPR>(r2, geo, xr, t, N, I::NEG_INF_WORD, qbase);
-            const float2 e = chunk_stats<DT, W, K>(r2, red, wv, lane);
+            softmax_issue<DT, AL, K, TPR, CAUSAL>(r2, geo, xr, t, N, L, qbase);
+            softmax_finish<DT, AL, K, TPR, CAUSAL>(r2, geo, xr, t, N, L, qbase);
+            const float2 e = chunk_stats<DT, W, K>(r2, red, wv, lane, s2);
             if (t == 0) qs[q] = e;
         }
     }
     __syncthreads();
     float c, inv;
-    merge_pairs(static_cast<const float2 *>(qs), P, lane, c, inv);
-    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv);
+    merge_pairs(static_cast<const float2 *>(qs), P, lane, c, inv, s2);
+    softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv, s2);
 }
 
 }  // namespace ntk

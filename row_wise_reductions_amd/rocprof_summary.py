@@ -51,21 +51,24 @@ def kernels_of(w) -> list[str]:
     """Demangled names of the kernels one call of workload `w` launches (with
     16-byte-aligned buffers and every parameter vector present, as bench.py)."""
     import row_wise_reductions_amd as nt
-    op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4}[w.op]
-    base, res = {3: (1, True), 4: (2, True)}.get(op, (op, False))
+    op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4,
+          "softmax_causal": 5}[w.op]
+    # public op -> kernel op, residual, causal
+    base, res, causal = {3: (1, True, False), 4: (2, True, False), 5: (3, False, True)}.get(op, (op, False, False))
     dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dt]
     p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
     W, K, al = p["waves_per_row"], p["chunks_per_lane"], _b(p["aligned"])
+    c = _b(causal)
     if p["split"] == 1 and p["cooperative"]:
-        return [f"ntk::softmax_coop<{dt}, {W}, {K}, {al}>"]
+        return [f"ntk::softmax_coop<{dt}, {W}, {K}, {al}, {c}>"]
     if p["split"] == 1:
-        return [f"ntk::softmax_split_partial<{dt}, {W}, {K}, {al}>",
-                f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}>"]
+        return [f"ntk::softmax_split_partial<{dt}, {W}, {K}, {al}, {c}>",
+                f"ntk::softmax_split_finalize<{dt}, {W}, {K}, {al}, {c}>"]
     if p["split"] == 2:
         return [f"ntk::row_looped<{base}, {dt}, {W}, {K}, {al}, {_b(res)}>"]
     if p["persistent"]:
         return [f"ntk::row_norm_persistent<{base}, {dt}, {W}, {K}, {_b(res)}>"]
-    return [f"ntk::row_resident<{base}, {dt}, {W}, {K}, {al}, {_b(base != 0)}, {_b(res)}>"]
+    return [f"ntk::row_resident<{base}, {dt}, {W}, {K}, {al}, {_b(base in (1, 2))}, {_b(res)}>"]
 
 
 def _rows(pattern):

@@ -1,0 +1,197 @@
+"""GPU parity of the causal, scaled softmax entry point (nt_softmax_causal_rows)
+against the oracle: fp32 outputs within relative 1e-5, fp16/bf16 within
+1 ulp of the oracle's float64 result rounded once, masked outputs exactly 0.
+Also: the masked inputs are never used (NaN planted there changes nothing),
+bitwise agreement with the generic softmax of the -inf-masked row, the
+one-pass, cooperative and two-kernel split forms, in place."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import check_output, empty_like_dev, to_dev, to_host_bits
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import torch  # noqa: E402
+
+import row_wise_reductions_amd as nt  # noqa: E402
+
+DT_CODE = {"f32": nt.NT_F32, "f16": nt.NT_F16, "bf16": nt.NT_BF16}
+NAN_BITS = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+NEG_INF = {"f32": np.float32(-np.inf), "f16": np.uint16(0xFC00), "bf16": np.uint16(0xFF80)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_bits(seed, M, N, dt, scale=1.0, loc=0.0):
+    rng = np.random.default_rng(seed)
+    return workloads.encode(rng.standard_normal((M, N)) * scale + loc, dt)
+
+
+def masked_of(M, N, Q, off):
+    k = np.arange(N)[None, :]
+    return k > (np.arange(M) % Q)[:, None] + off
+
+
+def run_causal(x_t, dt, scale, Q, off, y_t=None, ws=None):
+    M, N = x_t.shape
+    code = DT_CODE[dt]
+    y = torch.empty_like(x_t) if y_t is None else y_t
+    wsb = nt.nt_softmax_workspace_bytes(M, N, code)
+    if ws is None:
+        ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
+    rc = nt.nt_softmax_causal_rows(M, N, code, scale, Q, off, x_t.data_ptr(), y.data_ptr(), ws.data_ptr(), wsb,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, f"status {rc} ({nt.nt_status_string(rc)})"
+    torch.cuda.synchronize()
+    return y
+
+
+def causal_case(x, dt, scale, Q, off, x_off=0, y_off=0, what=""):
+    M, N = x.shape
+    say(f"case {what} dt={dt} M={M} N={N} Q={Q} off={off} scale={scale} x_off={x_off} y_off={y_off}")
+    x_t = to_dev(x, dt, x_off)
+    y = run_causal(x_t, dt, scale, Q, off, empty_like_dev((M, N), dt, y_off))
+    yb = to_host_bits(y, dt)
+    ref = oracle.softmax_causal(x, dt, scale, Q, off)
+    check_output(yb, ref, dt, what)
+    m = masked_of(M, N, Q, off)
+    assert np.all(yb[m] == 0), f"{what}: masked outputs are not +0"
+    return yb
+
+
+# ----------------------------------------------------------------------------
+# the causal attention-score workload through the causal entry
+# ----------------------------------------------------------------------------
+
+def test_causal_workload_full_size():
+    """131072 x 4096 bf16 (32 heads x 4096 queries): parity on sampled rows,
+    q + 1 non-zeros per row, and agreement with the generic softmax of the
+    same -inf-masked input (bitwise when both plan the same lane shape)."""
+    w = workloads.BY_NAME["causal_entry_softmax_bf16"]
+    say("workload causal entry: generating")
+    d = w.make()
+    x_t = to_dev(d["x"], w.dt)
+    say("workload causal entry: launching")
+    Q = w.extra["queries"]
+    y = run_causal(x_t, w.dt, w.extra["scale"], Q, w.extra["offset"])
+    y_gen = torch.empty_like(x_t)
+    wsb = nt.nt_softmax_workspace_bytes(w.M, w.N, nt.NT_BF16)
+    assert wsb == 0
+    assert nt.nt_softmax_rows(w.M, w.N, nt.NT_BF16, x_t.data_ptr(), y_gen.data_ptr(), None, 0,
+                              torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    same_plan = (nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, w.M, w.N, nt.NT_BF16, True) ==
+                 nt.nt_plan_launch(nt.NT_OP_SOFTMAX, w.M, w.N, nt.NT_BF16, True))
+    if same_plan:
+        assert torch.equal(y.view(torch.int16), y_gen.view(torch.int16)), "causal entry differs from generic softmax"
+    else:                   # other lane shapes sum in another order: within 1 ulp of each other
+        from oracle import compare
+        a = compare.ordinal(to_host_bits(y, w.dt), w.dt)
+        b = compare.ordinal(to_host_bits(y_gen, w.dt), w.dt)
+        assert int(np.abs(a - b).max()) <= 1, "causal entry and generic softmax differ by more than 1 ulp"
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([rng.choice(w.M, 4096, replace=False), [0, 1, Q - 1, Q, w.M - 1]]))
+    yb = to_host_bits(y, w.dt)[rows]
+    # a sampled row keeps its query through the offset: one row, queries = 1
+    # (so q = 0) and offset = its query index
+    ref = np.zeros(yb.shape, dtype=np.float64)
+    for i, r in enumerate(rows):
+        q = r % Q
+        ref[i] = oracle.softmax_causal(np.ascontiguousarray(d["x"][r:r + 1]), w.dt, 1.0, 1, q)[0]
+    check_output(yb, ref, w.dt, "causal entry")
+    assert np.array_equal(((yb & 0x7FFF) != 0).sum(axis=1), rows % Q + 1)
+
+
+# ----------------------------------------------------------------------------
+# widths (one pass, cooperative split, wide two-kernel split), queries and
+# offsets, scales, alignment
+# ----------------------------------------------------------------------------
+
+CAUSAL_N = [1, 7, 64, 781, 4096, 4097, 32768, 32769, 65537, 262144, (1 << 21) + 8]
+CASES = [(dt, N) for dt in ("f32", "f16", "bf16") for N in CAUSAL_N]
+
+
+@pytest.mark.parametrize("dt,N", CASES)
+def test_causal_sweep(dt, N):
+    M = 40 if N <= 4097 else (10 if N <= 65537 else 4)
+    x = rand_bits(N + 5, M, N, dt, scale=3.0)
+    combos = [(M, 0, 1.0), (max(1, M // 3), min(N, 5), 0.0884), (7, max(0, N - 7), 1.0)]
+    for (Q, off, scale) in combos:
+        for x_off, y_off in ((0, 0), (1, 3)):
+            causal_case(x, dt, scale, Q, off, x_off, y_off, what=f"sweep {dt} N={N}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [4096, 262144])
+def test_causal_masked_inputs_unused(dt, N):
+    """NaN in every masked input: the output is unchanged (bitwise)."""
+    M, Q, off = 12, 12, 2 if N == 4096 else N // 2
+    x = rand_bits(3, M, N, dt, scale=2.0)
+    x_t = to_dev(x, dt)
+    y0 = to_host_bits(run_causal(x_t, dt, 0.5, Q, off), dt)
+    x2 = x.copy()
+    x2[masked_of(M, N, Q, off)] = np.float32(np.nan) if dt == "f32" else NAN_BITS[dt]
+    say(f"case causal NaN-masked {dt} N={N}")
+    y1 = to_host_bits(run_causal(to_dev(x2, dt), dt, 0.5, Q, off), dt)
+    assert np.array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [65536, 262147, (1 << 21) + 8])
+def test_causal_split_forms_bitwise(dt, N, monkeypatch):
+    """Cooperative kernel, its recompute-everything form and the two-kernel
+    form agree bitwise on causal rows (chunks wholly past the visible prefix
+    included)."""
+    M, Q, off = 6, 6, N // 3
+    x = rand_bits(9, M, N, dt, scale=2.0)
+    x_t = to_dev(x, dt)
+    ref = oracle.softmax_causal(x, dt, 0.3, Q, off)
+    outs = []
+    for env in ({}, {"NT_COOP_SPIN": "0"}, {"NT_COOP": "0"}):
+        for k in ("NT_COOP_SPIN", "NT_COOP"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        say(f"case causal split {dt} N={N} {env}")
+        yb = to_host_bits(run_causal(x_t, dt, 0.3, Q, off), dt)
+        check_output(yb, ref, dt, f"causal split {env}")
+        outs.append(yb)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("N", [4096, 262144])
+def test_causal_in_place(N):
+    dt, M = "bf16", 16
+    x = rand_bits(5, M, N, dt, scale=2.0)
+    ref = oracle.softmax_causal(x, dt, 1.0, M, 0)
+    x_t = to_dev(x, dt)
+    say(f"case causal in place N={N}")
+    run_causal(x_t, dt, 1.0, M, 0, y_t=x_t)
+    check_output(to_host_bits(x_t, dt), ref, dt, "causal in place")
+
+
+def test_causal_errors_and_wrapper():
+    x = torch.randn(2, 8, 64, device="cuda")
+    y = torch.empty_like(x)
+    s = torch.cuda.current_stream().cuda_stream
+    assert nt.nt_softmax_causal_rows(16, 64, nt.NT_F32, 0.0, 8, 0, x.data_ptr(), y.data_ptr(), None, 0, s) == 9
+    assert nt.nt_softmax_causal_rows(16, 64, nt.NT_F32, 1.0, 0, 0, x.data_ptr(), y.data_ptr(), None, 0, s) == 2
+    ys = nt.softmax_causal(x, scale=0.125)                 # queries default to x.shape[-2] = 8
+    k = torch.arange(64, device="cuda")[None, :]
+    q = torch.arange(8, device="cuda")[:, None]
+    ref = torch.softmax((x.double() * float(np.float32(0.125))).masked_fill(k > q, float("-inf")), dim=-1)
+    assert float(((ys.double() - ref).abs() / ref.clamp_min(1e-300)).masked_fill(k > q, 0).max()) < 1e-5
+    assert torch.all(ys.masked_select((k > q).expand_as(ys)) == 0)

@@ -36,7 +36,7 @@ def test_exports_are_c_symbols():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = nt.nt_status_string(code)
         assert s and s != "unknown status"
     assert nt.nt_status_string(99) == "unknown status"
@@ -66,6 +66,19 @@ def test_status_strings():
     (lambda: nt.nt_rmsnorm_rows(4, 8, 3, 1e-6, FAKE, None, FAKE, None), 3),
     (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, None, None, FAKE, None), 1),
     (lambda: nt.nt_rmsnorm_rows(4, 1 << 31, BF16, 1e-6, FAKE, None, FAKE, None), 2),
+    # causal softmax: scale finite and > 0, queries >= 1, offset >= 0
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, 0.0, 4, 0, FAKE, FAKE, None, 0, None), 9),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, -1.0, 4, 0, FAKE, FAKE, None, 0, None), 9),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, float("inf"), 4, 0, FAKE, FAKE, None, 0, None), 9),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, float("nan"), 4, 0, FAKE, FAKE, None, 0, None), 9),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, 1.0, 0, 0, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, 1.0, 4, -1, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, 4, 1.0, 4, 0, FAKE, FAKE, None, 0, None), 3),
+    (lambda: nt.nt_softmax_causal_rows(4, 0, F32, 1.0, 4, 0, FAKE, FAKE, None, 0, None), 2),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, F32, 1.0, 4, 0, None, FAKE, None, 0, None), 1),
+    (lambda: nt.nt_softmax_causal_rows(4, 8, BF16, 1.0, 4, 0, FAKE, FAKE + 1, None, 0, None), 5),
+    (lambda: nt.nt_softmax_causal_rows(4, 1 << 20, F32, 1.0, 4, 0, FAKE, FAKE, None, 1 << 20, None), 1),
+    (lambda: nt.nt_softmax_causal_rows(4, 1 << 20, F32, 1.0, 4, 0, FAKE, FAKE, FAKE, 8, None), 6),
     # fused add + norm: residual and h required, in x's 16-byte phase, h != y
     (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, None, None, FAKE + 64, FAKE + 128, None), 1),
     (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, None, FAKE + 128, None), 1),
@@ -113,6 +126,7 @@ def test_empty_is_noop():
     assert nt.nt_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None) == 0
     assert nt.nt_rmsnorm_rows(0, 8, F32, 1e-6, None, None, None, None) == 0
     assert nt.nt_add_rmsnorm_rows(0, 8, F32, 1e-6, None, None, None, None, None, None) == 0
+    assert nt.nt_softmax_causal_rows(0, 8, F32, 1.0, 4, 0, None, None, None, 0, None) == 0
     assert nt.nt_add_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None, None, None) == 0
     # a bad eps is still an error for an empty call
     assert nt.nt_rmsnorm_rows(0, 8, F32, -1.0, None, None, None, None) == 4
@@ -226,3 +240,14 @@ def test_fused_add_norm_plans():
                 p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 8, N, dt, al)
                 if p["split"] == 0:
                     assert p["chunks_per_lane"] * (4 if dt == F32 else 8) <= 32, (dt, N, al, p)
+
+
+def test_causal_softmax_plans():
+    # as the softmax, except 16-bit rows of 512 chunks: 4 waves x 2 chunks
+    for (M, N, dt) in ((64, 262144, F32), (3, 781, F32), (2, 1 << 22, F16), (8, 4096, F32), (8, 16384, BF16)):
+        a = nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, M, N, dt, True)
+        b = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, dt, True)
+        assert a == b, (M, N, dt)
+    a = nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, 131072, 4096, BF16, True)
+    b = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
+    assert (a["waves_per_row"], a["chunks_per_lane"]) == (4, 2) and (b["waves_per_row"], b["chunks_per_lane"]) == (8, 1)

@@ -90,10 +90,10 @@ def _shapes(kernels):
         m = re.search(r"row_norm_persistentILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
         if m:
             have.add(("pers",) + tuple(int(g) for g in m.groups()))
-        m = re.search(r"softmax_split_(partial|finalize)ILi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        m = re.search(r"softmax_split_(partial|finalize)ILi(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", name)
         if m:
-            have.add((m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4)), int(m.group(5))))
-        m = re.search(r"softmax_coopILi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+            have.add((m.group(1),) + tuple(int(g) for g in m.groups()[1:]))
+        m = re.search(r"softmax_coopILi(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", name)
         if m:
             have.add(("coop",) + tuple(int(g) for g in m.groups()))
     return have
@@ -103,8 +103,9 @@ def test_every_planned_shape_is_built(kernels):
     """Every launch the planner can choose (fused add + norm included) has an
     instantiated kernel: (op, type, W, K, aligned, residual)."""
     have = _shapes(kernels)
-    for op in (0, 1, 2, 3, 4):
-        base, res = {3: (1, 1), 4: (2, 1)}.get(op, (op, 0))
+    for op in (0, 1, 2, 3, 4, 5):
+        # public op -> (kernel op, residual, causal)
+        base, res, causal = {3: (1, 1, 0), 4: (2, 1, 0), 5: (3, 0, 1)}.get(op, (op, 0, 0))
         for dt in (0, 1, 2):
             for N in (1, 7, 64, 255, 781, 1000, 4096, 4097, 8192, 16384, 30000, 32768, 65536, 100000, 262144):
                 for al in (True, False):
@@ -115,8 +116,9 @@ def test_every_planned_shape_is_built(kernels):
                     W, K, A = p["waves_per_row"], p["chunks_per_lane"], p["aligned"]
                     if p["split"] == 1:
                         if p["cooperative"]:
-                            assert ("coop", dt, W, K, A) in have, (dt, N, al, p)
-                        assert ("partial", dt, W, K, A) in have and ("finalize", dt, W, K, A) in have
+                            assert ("coop", dt, W, K, A, causal) in have, (dt, N, al, p)
+                        assert ("partial", dt, W, K, A, causal) in have, (op, dt, N, al, p)
+                        assert ("finalize", dt, W, K, A, causal) in have, (op, dt, N, al, p)
                     elif p["split"] == 2:
                         assert ("loop", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
                     else:
