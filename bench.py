@@ -25,8 +25,9 @@ Infinity Cache cannot serve them), --no-cpu-baseline, --no-next (skip the
 next rows -- fused residual add + norm, the causal softmax entry -- which
 are timed after the suite and reported under next_rows, outside value); --calibrate (the plain
 1 GiB copy: attainable bandwidth, and the counter calibration) and
---copy-at-sizes (the plain copy at each workload's byte count) replace the
-suite.
+--copy-at-sizes (the plain copy at each workload's byte count) and --sweep
+(fp32 softmax and RMSNorm over the pages' benchmark widths, beside torch's
+softmax; --sweep-md FILE writes a summary) replace the suite.
 """
 from __future__ import annotations
 
@@ -257,6 +258,85 @@ def copy_at_sizes(torch, steps, warmup, workloads):
     print(json.dumps(out), flush=True)
 
 
+SWEEP_M = 4096
+SWEEP_N = [128 * i for i in range(2, 100)]      # the pages' GB/s harness: M = 4096, N = 128 i
+
+
+def width_sweep(torch, steps, warmup, md_path=None):
+    """Launch-table check over the widths of the pages' benchmark harness
+    ("Portable Triton Kernels", "Benchmark Harness Template": fp32 softmax,
+    M = 4096, N = 128*i for i = 2..99, GB/s = 2*numel*4 / time, against
+    torch's softmax), plus RMSNorm fp32 (weight present) on the same widths.
+    Inputs rotate through 1 GiB pools so the Infinity Cache cannot serve
+    them; event-timed median of `steps` launches after `warmup`."""
+    import row_wise_reductions_amd as nt
+    M = SWEEP_M
+    pool = 1 << 28                                   # floats: 1 GiB
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    px = torch.randn(pool, device="cuda", generator=gen)
+    py = torch.empty(pool, device="cuda")
+    w = torch.randn(max(SWEEP_N), device="cuda", generator=gen) * 0.3 + 1.0
+    sh = torch.cuda.current_stream().cuda_stream
+    rows = []
+
+    def timed(fn, R):
+        for i in range(warmup):
+            fn(i % R)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(i % R)
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+    for N in SWEEP_N:
+        n = M * N
+        R = pool // n
+        xs = [px[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+        ys = [py[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+
+        def ours(i):
+            assert nt.nt_softmax_rows(M, N, nt.NT_F32, xs[i].data_ptr(), ys[i].data_ptr(), None, 0, sh) == 0
+
+        def theirs(i):
+            torch.softmax(xs[i], dim=-1)
+
+        def rms(i):
+            assert nt.nt_rmsnorm_rows(M, N, nt.NT_F32, 1e-6, xs[i].data_ptr(), w.data_ptr(), ys[i].data_ptr(),
+                                      sh) == 0
+
+        ms_ours, ms_torch, ms_rms = timed(ours, R), timed(theirs, R), timed(rms, R)
+        p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, nt.NT_F32, True)
+        gb = 2 * n * 4 / 1e9
+        rows.append({"N": N, "softmax_ms": round(ms_ours, 5), "softmax_GBps": round(gb / (ms_ours * 1e-3), 1),
+                     "torch_softmax_GBps": round(gb / (ms_torch * 1e-3), 1),
+                     "rmsnorm_GBps": round((gb + N * 4 / 1e9) / (ms_rms * 1e-3), 1),
+                     "shape": f"{p['waves_per_row']}x{p['chunks_per_lane']}"})
+        log(f"[sweep] N={N}: softmax {rows[-1]['softmax_GBps']} GB/s, torch {rows[-1]['torch_softmax_GBps']}, "
+            f"rmsnorm {rows[-1]['rmsnorm_GBps']}")
+    out = {"sweep": "fp32 softmax and RMSNorm, M = 4096, N = 128 i (i = 2..99)", "M": M, "points": rows}
+    print(json.dumps(out), flush=True)
+    if md_path:
+        lines = ["# Width sweep: fp32 softmax and RMSNorm, M = 4096, N = 128 i (i = 2..99)", "",
+                 "Command (repository root, GPU host):", "",
+                 f"    python3 bench.py --sweep --steps {steps} --warmup {warmup} --sweep-md {md_path}", "",
+                 "The widths of the pages' GB/s benchmark harness; GB/s = bytes read + written / median event-timed "
+                 "launch, inputs rotating through 1 GiB pools.  `torch` is torch.softmax on the same buffers.", "",
+                 "| N | launch shape (W x K) | softmax us | softmax GB/s | torch softmax GB/s | ratio | "
+                 "RMSNorm GB/s |", "|---|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['N']} | {r['shape']} | {r['softmax_ms'] * 1000:.2f} | {r['softmax_GBps']} | "
+                         f"{r['torch_softmax_GBps']} | {r['softmax_GBps'] / r['torch_softmax_GBps']:.2f} | "
+                         f"{r['rmsnorm_GBps']} |")
+        ratios = [r["softmax_GBps"] / r["torch_softmax_GBps"] for r in rows]
+        lines += ["", f"softmax / torch: min {min(ratios):.2f}, median {statistics.median(ratios):.2f}, "
+                      f"max {max(ratios):.2f} over {len(rows)} widths.", ""]
+        with open(md_path, "w") as f:
+            f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -268,6 +348,9 @@ def main():
                     help="skip the next rows (timed after the suite, not part of value)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time the plain 1 GiB streaming copy (and torch copy_) instead")
+    ap.add_argument("--sweep", action="store_true",
+                    help="fp32 softmax / RMSNorm over the pages' benchmark widths (M=4096, N=128 i), vs torch")
+    ap.add_argument("--sweep-md", default=None, help="with --sweep: also write a markdown summary here")
     ap.add_argument("--copy-at-sizes", action="store_true",
                     help="time the plain streaming copy at each workload's byte count instead")
     args = ap.parse_args()
@@ -286,6 +369,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate:
         calibrate_copy(torch, args.steps, args.warmup)
+        return
+    if args.sweep:
+        width_sweep(torch, args.steps, args.warmup, args.sweep_md)
         return
     if args.copy_at_sizes:
         names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]

@@ -42,24 +42,27 @@ struct Menu {
     const Shape *s;
     int n;
 };
-// Chosen from launch-shape sweeps on MI355X: about one or two 16-byte chunks
-// per lane with up to 8 waves per row stream best.  Causal rows, whose loads
-// stop at the diagonal, are latency-bound rather than bandwidth-bound: for
-// 16-bit rows of 512 chunks (4096 elements) 4 waves with 2 chunks each keep
-// twice the rows in flight of 8 waves with 1 (1.27x on causal rows; 8 waves
-// stay ahead by about 1% on full rows).
-const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
-const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kCausal16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
+// Chosen from launch-shape sweeps on MI355X (every shape that covers the row,
+// timed interleaved at M = 4096 and on the workloads): about one or two
+// 16-byte chunks per lane with up to 8 waves per row stream best.  For rows
+// of 257..512 chunks 4 waves with 2 chunks each beat 8 waves with 1 by 3-15%
+// (no idle lanes on part-filled rows, twice the rows in flight; on causal
+// rows, whose loads stop at the diagonal, by 27%).  Exception: 16-bit rows
+// that fill all 512 chunks (4096 elements) keep 8 waves with 1 chunk, which
+// streams the 131072-row causal-score workload about 1-2% faster
+// (full_row_shape).  RMSNorm fp32 prefers one wave with 8 chunks there and 16
+// waves with 2 chunks for rows of 1025..2048 chunks (2-5%).
+const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
+const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
 const Shape kRms16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
 const Shape kLn16[] = {{1, 1}, {1, 2}, {4, 1}, {4, 2}, {8, 2}};
 #define NT_MENU(a) Menu{a, (int)(sizeof(a) / sizeof(*(a)))}
-Menu menu_for(nt_op op, nt_dtype dt, bool causal) {
+Menu menu_for(nt_op op, nt_dtype dt) {
     const bool wide = dt == NT_F32;
     switch (op) {
-    case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : causal ? NT_MENU(kCausal16) : NT_MENU(kSoftmax16);
+    case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : NT_MENU(kSoftmax16);
     case NT_OP_RMSNORM: return wide ? NT_MENU(kRms32) : NT_MENU(kRms16);
     default: return wide ? NT_MENU(kLn32) : NT_MENU(kLn16);
     }
@@ -152,12 +155,19 @@ bool shape_fits(nt_op op, nt_dtype dt, bool res, Shape sh) {
     return !(res && op == NT_OP_RMSNORM && sh.K * elems_per_chunk(dt) > 32);
 }
 
+// 16-bit softmax rows of exactly 512 chunks (not causal): 8 waves, 1 chunk.
+bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
+    if (op != NT_OP_SOFTMAX || dt == NT_F32 || causal || nch != 512) return false;
+    *s = {8, 1};
+    return true;
+}
+
 nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true,
                     bool res = false, bool causal = false) {
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
-    const Menu menu = menu_for(op, dt, causal);
+    const Menu menu = menu_for(op, dt);
     const char *force = std::getenv("NT_FORCE_PATH");
     const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
     const bool force_loop = op != NT_OP_SOFTMAX && force && std::strcmp(force, "looped") == 0;
@@ -166,6 +176,8 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     if (!force_split && !force_loop) {
         Shape o;
         if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch && shape_fits(op, dt, res, o)) {
+            pick = o;
+        } else if (full_row_shape(op, dt, nch, causal, &o)) {
             pick = o;
         } else {
             for (int i = 0; i < menu.n; ++i)
@@ -192,9 +204,9 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         // parameters widened in registers across rows: persistent workgroups
         // (grid sized on the device from occupancy; `grid` is then an upper bound).
         // (at most 32 values per lane: the row, its prefetched successor and the
-        // cached parameters must fit without spilling)
-        if (op != NT_OP_SOFTMAX && aligned && params && pick.W >= 2 && pick.K * elems_per_chunk(dt) <= 32 &&
-            persistent_enabled())
+        // cached parameters must fit without spilling; built for 2 to 8 waves)
+        if (op != NT_OP_SOFTMAX && aligned && params && pick.W >= 2 && pick.W <= 8 &&
+            pick.K * elems_per_chunk(dt) <= 32 && persistent_enabled())
             p->persistent = 1;
         return NT_OK;
     }

@@ -297,12 +297,14 @@ def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
     """Persistent norm kernel (parameters held across rows, next row prefetched):
     parity with the oracle and bitwise equality with the one-row-per-group
     kernel, including grids much smaller than the row count."""
+    code = DT_CODE[dt]
+    opc = {"layernorm": 1, "rmsnorm": 2}[op]
+    while not nt.nt_plan_launch(opc, M, N, code, True)["persistent"]:
+        N //= 2                      # a width whose plan is the persistent kernel
+        assert N >= 512, (op, dt)
     x = rand_bits(N + M, M, N, dt, scale=2.0, loc=1.5)
     p0 = rand_bits(N + 1, 1, N, dt, scale=0.3, loc=1.0)[0]
     p1 = rand_bits(N + 2, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
-    code = DT_CODE[dt]
-    plan = nt.nt_plan_launch({"layernorm": 1, "rmsnorm": 2}[op], M, N, code, True)
-    assert plan["persistent"] == 1, plan
     if grid:
         monkeypatch.setenv("NT_PERSIST_GRID", str(grid))
     x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)

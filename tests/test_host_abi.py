@@ -243,11 +243,17 @@ def test_fused_add_norm_plans():
 
 
 def test_causal_softmax_plans():
-    # as the softmax, except 16-bit rows of 512 chunks: 4 waves x 2 chunks
-    for (M, N, dt) in ((64, 262144, F32), (3, 781, F32), (2, 1 << 22, F16), (8, 4096, F32), (8, 16384, BF16)):
+    # as the softmax, except full 16-bit rows of 512 chunks: the softmax
+    # keeps 8 waves x 1 chunk there, causal rows (loads stop at the
+    # diagonal) take 4 waves x 2 chunks like part-filled rows
+    for (M, N, dt) in ((64, 262144, F32), (3, 781, F32), (2, 1 << 22, F16), (8, 4096, F32), (8, 16384, BF16),
+                       (8, 3000, BF16)):
         a = nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, M, N, dt, True)
         b = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, dt, True)
         assert a == b, (M, N, dt)
     a = nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, 131072, 4096, BF16, True)
     b = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
     assert (a["waves_per_row"], a["chunks_per_lane"]) == (4, 2) and (b["waves_per_row"], b["chunks_per_lane"]) == (8, 1)
+    # part-filled 16-bit rows of 257..511 chunks: 4 waves x 2 chunks
+    p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 8, 3000, BF16, True)
+    assert (p["waves_per_row"], p["chunks_per_lane"]) == (4, 2)
