@@ -16,6 +16,7 @@ import pytest
 from conftest import gpu_available
 from gpu_util import (check_output, check_stats, empty_like_dev, oracle_for, tdt, to_dev,
                       to_host_bits)
+import oracle
 import workloads
 
 pytestmark = pytest.mark.gpu
