@@ -324,6 +324,35 @@ def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
         assert torch.equal(m1, m2) and torch.equal(r1, r2)
 
 
+def test_grid_cap_striding():
+    """More rows than one launch may hold (grid x threads < 2^31): the
+    kernels stride over the rows beyond the capped grid.  N = 1, so 4 rows
+    per 256-thread workgroup and 2^25 + 7 rows exceed 2^23 workgroups."""
+    M, N = (1 << 25) + 7, 1
+    for op in (0, 1, 2):
+        p = nt.nt_plan_launch(op, M, N, nt.NT_F32, True)
+        assert p["grid"] * p["rows_per_block"] < M, p
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((M, N)) * 2.0).astype(np.float32)
+    w = np.array([0.75], dtype=np.float32)
+    b = np.array([-0.25], dtype=np.float32)
+    x_t = to_dev(x, "f32")
+    w_t, b_t = to_dev(w, "f32"), to_dev(b, "f32")
+    tail = np.arange(M - 4096, M)                    # the rows only striding reaches, and more
+    for op in ("softmax", "rmsnorm", "layernorm"):
+        say(f"case grid cap {op} M={M}")
+        y, mean, rstd = run_op(op, x_t, "f32", 1e-5, w_t if op != "softmax" else None, b_t if op == "layernorm" else None)
+        yb = to_host_bits(y, "f32")
+        ref, rmean, rrstd = oracle_for(op, np.ascontiguousarray(x[tail]), "f32", 1e-5,
+                                       w if op != "softmax" else None, b if op == "layernorm" else None)
+        check_output(yb[tail], ref, "f32", f"grid cap {op}")
+        head, href = yb[:4096], oracle_for(op, np.ascontiguousarray(x[:4096]), "f32", 1e-5,
+                                           w if op != "softmax" else None, b if op == "layernorm" else None)[0]
+        check_output(head, href, "f32", f"grid cap {op} head")
+        if op == "layernorm":
+            check_stats(mean.cpu().numpy()[tail], rmean, "grid cap mean")
+
+
 # ----------------------------------------------------------------------------
 # semantics: special rows, in place, determinism, streams, no-op, errors
 # ----------------------------------------------------------------------------
