@@ -353,6 +353,36 @@ def test_grid_cap_striding():
             check_stats(mean.cpu().numpy()[tail], rmean, "grid cap mean")
 
 
+@pytest.mark.parametrize("op,dt,M,N", [("softmax", "f32", 3, (1 << 28) + 3), ("rmsnorm", "bf16", 5, (1 << 28) + 5)])
+def test_rows_past_2gib_offsets(op, dt, M, N):
+    """Rows of 512 MiB to 1 GiB, so the last row starts beyond 2^31 bytes
+    (64-bit offsets throughout): the split softmax (two-kernel form, ragged
+    misaligned rows) and the looped RMSNorm, against the oracle on every
+    element, compared in column blocks.  Inputs drawn in float32 (rounded
+    once to bf16) to keep the host side small."""
+    rng = np.random.default_rng(N)
+    x32 = rng.standard_normal((M, N), dtype=np.float32) * np.float32(2.0)
+    x = x32 if dt == "f32" else workloads.to_bf16_bits(x32)
+    del x32
+    w = workloads.to_bf16_bits(np.float32(1.0) + np.float32(0.3) * rng.standard_normal(N, dtype=np.float32)) \
+        if op == "rmsnorm" else None
+    assert (M - 1) * N * (4 if dt == "f32" else 2) > (1 << 31)
+    p = nt.nt_plan_launch({"softmax": 0, "rmsnorm": 2}[op], M, N, DT_CODE[dt], True)
+    assert p["split"] in (1, 2) and (p["split"] == 2 or p["cooperative"] == 0), p
+    say(f"case 2GiB-offset {op} {dt} M={M} N={N}")
+    x_t = to_dev(x, dt)
+    w_t = None if w is None else to_dev(w, dt)
+    y, _, _ = run_op(op, x_t, dt, 1e-6, w_t)
+    del x_t
+    yb = to_host_bits(y, dt)
+    del y
+    ref = oracle.softmax(x, dt) if op == "softmax" else oracle.rmsnorm(x, dt, 1e-6, weight=w)
+    blk = 1 << 25
+    for r in range(M):
+        for j0 in range(0, N, blk):
+            check_output(yb[r, j0:j0 + blk], ref[r, j0:j0 + blk], dt, f"2GiB-offset {op} row {r} col {j0}")
+
+
 # ----------------------------------------------------------------------------
 # semantics: special rows, in place, determinism, streams, no-op, errors
 # ----------------------------------------------------------------------------
