@@ -11,10 +11,16 @@
 //   * softmax rows wider than the widest shape take the split online path
 //     ("Triton: Block-Level GPU Programming Without CUDA", section "How Flash
 //     Attention Uses Triton"): chunks of one workgroup each, partial
-//     (max, denominator) pairs in the caller's workspace, then a merge.
+//     (max, denominator) pairs in the caller's workspace, then a merge -- in
+//     one cooperative kernel up to 128 chunks per row, else in two kernels.
 //     LayerNorm and RMSNorm rows wider than the widest shape take a looped
 //     kernel: one workgroup per row reads the row twice in tiles (statistics,
-//     then output), so no workspace is needed.
+//     then output), so no workspace is needed;
+//   * norms on aligned rows with every parameter vector present run
+//     persistent workgroups (parameters widened once, next row prefetched).
+// The fused residual add + norm entry points and the causal softmax entry
+// point plan as their norm / the softmax, with the limits noted where they
+// differ (values per lane, the causal 16-bit menu exception).
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -16,13 +16,25 @@
 // Constraints", "Safe Softmax Pattern"): -inf for the max, so exp() of a
 // padding lane is exactly 0, and 0 for sums.
 //
-// Two variants of every kernel exist:
+// Two variants of most kernels exist:
 //   AL = true   every row start, x, y and the parameter vectors are 16-byte
 //               aligned and N*sizeof(T) is a multiple of 16: whole chunks only.
 //   AL = false  rows start anywhere (element-aligned).  Chunks are cut on the
 //               16-byte grid of x; the partial first and last chunk of a row
 //               are gathered and scattered element by element, and the
 //               parameter vectors are read per element.
+//
+// Kernels:
+//   row_resident          one row per group of W waves (W = 1: 4 rows per
+//                         workgroup): softmax, causal softmax, LayerNorm,
+//                         RMSNorm, and the fused residual add + norm (RES)
+//   row_norm_persistent   norms with the parameters held in registers across
+//                         rows and the next row prefetched (aligned rows)
+//   row_looped            norms of rows too wide for registers (two passes)
+//   softmax_coop          split softmax in one pass: the workgroups of a row
+//                         exchange (max, denominator) records
+//   softmax_split_partial / softmax_split_finalize
+//                         the same split softmax in two kernels
 #pragma once
 
 #include <hip/hip_runtime.h>
