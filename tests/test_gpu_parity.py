@@ -466,6 +466,78 @@ def test_graph_capture_and_replay():
                      f"graph rmsnorm {i}")
 
 
+def test_cooperative_split_on_concurrent_streams():
+    """Cooperative split softmax calls in flight on two streams at once (each
+    with its own workspace), repeatedly: every result matches the oracle and
+    is bitwise the single-stream result, whatever share of the GPU each
+    call's workgroups get."""
+    M, N = 48, 262144
+    xa = rand_bits(71, M, N, "f32", scale=2.0)
+    xb = rand_bits(72, M, N, "f32", scale=4.0, loc=1.0)
+    assert nt.nt_plan_launch(0, M, N, nt.NT_F32, True)["cooperative"] == 1
+    ta, tb = to_dev(xa, "f32"), to_dev(xb, "f32")
+    wsb = nt.nt_softmax_workspace_bytes(M, N, nt.NT_F32)
+    wsa = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    wsb_t = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ref_a = softmax_with_ws(ta, "f32", wsa)
+    ref_b = softmax_with_ws(tb, "f32", wsb_t)
+    check_output(to_host_bits(ref_a, "f32"), oracle.softmax(xa, "f32"), "f32", "stream a")
+    check_output(to_host_bits(ref_b, "f32"), oracle.softmax(xb, "f32"), "f32", "stream b")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for it in range(8):
+        ya, yb = torch.empty_like(ta), torch.empty_like(tb)
+        assert nt.nt_softmax_rows(M, N, nt.NT_F32, ta.data_ptr(), ya.data_ptr(), wsa.data_ptr(), wsb,
+                                  sa.cuda_stream) == 0
+        assert nt.nt_softmax_rows(M, N, nt.NT_F32, tb.data_ptr(), yb.data_ptr(), wsb_t.data_ptr(), wsb,
+                                  sb.cuda_stream) == 0
+        outs.append((ya, yb))
+    torch.cuda.synchronize()
+    say("case cooperative split on two streams")
+    for ya, yb in outs:
+        assert torch.equal(ya, ref_a) and torch.equal(yb, ref_b)
+
+
+def test_graph_capture_fused_and_causal():
+    """The fused add + RMSNorm and the causal softmax entry captured in a
+    graph and replayed with new inputs: every replay matches the oracle."""
+    M, N = 32, 4096
+    xs = [rand_bits(80 + i, M, N, "bf16", scale=2.0) for i in range(3)]
+    rs = [rand_bits(90 + i, M, N, "bf16") for i in range(3)]
+    w = rand_bits(99, 1, N, "bf16", scale=0.3, loc=1.0)[0]
+    x_t, r_t, w_t = to_dev(xs[0], "bf16"), to_dev(rs[0], "bf16"), to_dev(w, "bf16")
+    h_t, y_t, c_t = torch.empty_like(x_t), torch.empty_like(x_t), torch.empty_like(x_t)
+
+    def calls(stream):
+        assert nt.nt_add_rmsnorm_rows(M, N, nt.NT_BF16, 1e-6, x_t.data_ptr(), r_t.data_ptr(), w_t.data_ptr(),
+                                      h_t.data_ptr(), y_t.data_ptr(), stream) == 0
+        assert nt.nt_softmax_causal_rows(M, N, nt.NT_BF16, 0.125, 16, 2, x_t.data_ptr(), c_t.data_ptr(), None, 0,
+                                         stream) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(torch.cuda.current_stream().cuda_stream)
+    for i in (2, 0, 1, 1):
+        say(f"case graph replay fused/causal inputs {i}")
+        x_t.copy_(to_dev(xs[i], "bf16"))
+        r_t.copy_(to_dev(rs[i], "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rh, ry = oracle.add_rmsnorm(xs[i], rs[i], "bf16", 1e-6, weight=w)
+        assert np.array_equal(to_host_bits(h_t, "bf16"), rh)
+        check_output(to_host_bits(y_t, "bf16"), ry, "bf16", f"graph add+rmsnorm {i}")
+        check_output(to_host_bits(c_t, "bf16"), oracle.softmax_causal(xs[i], "bf16", 0.125, 16, 2), "bf16",
+                     f"graph causal {i}")
+
+
 def test_side_stream_ordering():
     x = rand_bits(10, 256, 4096, "f16", loc=1.0)
     s = torch.cuda.Stream()
