@@ -156,10 +156,10 @@ hipError_t split_al(bool coop, const RowArgs &a, hipStream_t s) {
 }
 
 // The causal split kernels are built for the planner's split shapes only:
-// 32 values per lane on 8 waves (the cooperative shape) and (4, 4).
+// the cooperative ones (fp32 8 x 8, 16-bit 4 x 8) and the wide (4, 4).
 template <int W, int K>
 constexpr bool causal_split_built() {
-    return (W == 8 && K * dt_info<DT>::VEC == 32) || (W == 4 && K == 4);
+    return (kWide ? (W == 8 && K == 8) : (W == 4 && K == 8)) || (W == 4 && K == 4);
 }
 
 template <int W, int K>

@@ -74,13 +74,14 @@ Menu menu_for(nt_op op, nt_dtype dt) {
     }
 }
 #undef NT_MENU
-// Split-path chunk shapes.  Up to COOP_PMAX chunks per row: 8 waves with 32
-// values per lane (8 chunks of fp32, 4 of 16-bit types) for the cooperative
-// kernel, so few workgroups per row wait on each other; wider rows: 4 waves,
-// 4 chunks per lane, two kernels.  The shape does not depend on whether the
-// cooperative kernel is enabled, so neither does the workspace size.
+// Split-path chunk shapes.  Up to COOP_PMAX chunks per row, large chunks for
+// the cooperative kernel, so few workgroups per row wait on each other: fp32
+// 8 waves x 8 chunks (32 values per lane), 16-bit 4 waves x 8 chunks (64
+// values per lane; 3% ahead of 8 x 4 on 64 x 262144 bf16 rows); wider rows:
+// 4 waves, 4 chunks per lane, two kernels.  The shape does not depend on
+// whether the cooperative kernel is enabled, so neither does the workspace.
 const Shape kSplitCoop32 = {8, 8};
-const Shape kSplitCoop16 = {8, 4};
+const Shape kSplitCoop16 = {4, 8};
 const Shape kSplitWide = {4, 4};
 // Looped norm kernel: 512 threads, tiles of 4 chunks per lane.
 const Shape kLooped = {8, 4};
