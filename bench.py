@@ -166,13 +166,48 @@ def cpu_baseline(jobs, np, stride=1, check_every=16):
         ok = ok and good
         del ref
     threads = oracle.num_threads()
+    # one thread on the small softmax workload (every row), then back
+    single = None
+    c1 = next((j for j in jobs if j.w.op == "softmax" and j.w.dt == "f32" and j.w.M * j.w.N <= 1 << 20), None)
+    if c1 is not None:
+        oracle.set_num_threads(1)
+        try:
+            oracle.softmax(c1.data["x"], "f32")
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.softmax(c1.data["x"], "f32")
+                ts.append(time.perf_counter() - t0)
+        finally:
+            oracle.set_num_threads(threads)
+        t1 = statistics.median(ts)
+        single = {"workload": c1.w.name, "seconds": round(t1, 5),
+                  "GBps": round(c1.bytes / t1 / 1e9, 3)}
     return {"value": round(total_bytes / total_t / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "cpu_model": cpu_model(), "single_thread": single,
             "kind": "oracle",
             "sample": (("all rows" if stride == 1 else f"every {stride}th row") +
                        f" of each workload ({'; '.join(parts)}); median of 3 timed runs after 1 warm-up; "
                        f"fp64 C with OpenMP over rows on {threads} threads"),
             "seconds": round(total_t, 3), "core_seconds": round(total_t * threads, 2),
             "gpu_parity_on_sample": bool(ok)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def pct(durs, q):
+    """q-th percentile (nearest rank) of a list of durations."""
+    d = sorted(durs)
+    return d[min(len(d) - 1, max(0, int(round(q / 100.0 * (len(d) - 1)))))]
 
 
 def traffic_for(kernel_name, launches_bytes):
@@ -190,21 +225,32 @@ def traffic_for(kernel_name, launches_bytes):
     return None if e is None else e.get("hbm_bytes_per_call")
 
 
-def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
-    """Attainable-bandwidth reference: the plain streaming copy kernel of
-    libntcal.so (read nbytes, write nbytes), rotating 4 buffer pairs; torch's
-    own copy_ is timed beside it."""
+def _ntcal():
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_reductions_amd", "libntcal.so"))
-    lib.ntcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    lib.ntcal_copy.restype = ctypes.c_int
+    lib.ntcal_copy_policy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.ntcal_copy_policy.restype = ctypes.c_int
+    return lib
+
+
+def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
+    """Attainable-bandwidth reference: the plain streaming copy kernels of
+    libntcal.so (read nbytes, write nbytes), rotating 4 buffer pairs, with
+    non-temporal stores (ntcal, the counter calibration) and with the
+    device-scope streaming stores of the row kernels (ntcal_sc1); torch's own
+    copy_ is timed beside them."""
+    lib = _ntcal()
     n = nbytes // 4
     src = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(4)]
     dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
     sh = torch.cuda.current_stream().cuda_stream
-    out = {"calibration": "plain streaming copy (ntcal_copy_kernel), 4 KiB per workgroup, non-temporal",
+    out = {"calibration": "plain streaming copy (ntcal_copy_kernel), 4 KiB per workgroup, non-temporal; "
+                          "ntcal_sc1: the same with device-scope streaming stores",
            "bytes_read": nbytes, "bytes_written": nbytes}
-    for name, fn in (("ntcal", lambda i: lib.ntcal_copy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(), nbytes, sh)),
+    for name, fn in (("ntcal", lambda i: lib.ntcal_copy_policy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(),
+                                                               nbytes, 0, sh)),
+                     ("ntcal_sc1", lambda i: lib.ntcal_copy_policy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(),
+                                                                   nbytes, 1, sh)),
                      ("torch_copy", lambda i: dst[i % 4].copy_(src[i % 4]))):
         for i in range(warmup):
             rc = fn(i)
@@ -228,12 +274,10 @@ def copy_at_sizes(torch, steps, warmup, workloads):
     """The plain streaming copy of libntcal.so moving each workload's bytes
     (read M*N*e, write M*N*e), rotating buffer sets of >= 1 GiB so the
     Infinity Cache cannot serve them: what a kernel that only streams its
-    rows could reach at that size (launch and ramp included).  Event-timed
-    like the breakdown pass; median of `steps` launches."""
-    import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_reductions_amd", "libntcal.so"))
-    lib.ntcal_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
-    lib.ntcal_copy.restype = ctypes.c_int
+    rows could reach at that size (launch and ramp included), with each
+    store policy.  Event-timed like the breakdown pass; median of `steps`
+    launches."""
+    lib = _ntcal()
     sh = torch.cuda.current_stream().cuda_stream
     out = {"copy_at_sizes": "plain streaming copy (ntcal_copy_kernel) of each workload's read bytes", "workloads": []}
     for w in workloads:
@@ -241,18 +285,22 @@ def copy_at_sizes(torch, steps, warmup, workloads):
         R = max(1, -(-(1 << 30) // (2 * nb)))
         src = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
         dst = [torch.empty(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
-        for i in range(warmup):
-            assert lib.ntcal_copy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, sh) == 0
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i, (a, b) in enumerate(evs):
-            a.record()
-            lib.ntcal_copy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, sh)
-            b.record()
-        torch.cuda.synchronize()
-        ms = statistics.median(a.elapsed_time(b) for a, b in evs)
-        out["workloads"].append({"workload": w.name, "bytes_read": nb, "bytes_written": nb, "buffer_sets": R,
-                                 "median_ms": round(ms, 5), "GBps": round(2 * nb / (ms * 1e-3) / 1e9, 1)})
+        row = {"workload": w.name, "bytes_read": nb, "bytes_written": nb, "buffer_sets": R}
+        for pol, tag in ((0, ""), (1, "sc1_")):
+            for i in range(warmup):
+                assert lib.ntcal_copy_policy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, pol, sh) == 0
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for i, (a, b) in enumerate(evs):
+                a.record()
+                lib.ntcal_copy_policy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, pol, sh)
+                b.record()
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in evs)
+            row[f"{tag}median_ms"] = round(ms, 5)
+            row[f"{tag}GBps"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+        out["workloads"].append(row)
         del src, dst
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
@@ -422,6 +470,7 @@ def main():
         avg = sum(durs) / len(durs)
         per.append({"workload": j.w.name, "op": j.w.op, "dtype": j.w.dt, "M": j.w.M, "N": j.w.N,
                     "bytes": j.bytes, "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
+                    "p10_ms": round(pct(durs, 10), 5), "p90_ms": round(pct(durs, 90), 5),
                     "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "plan": nt.nt_plan_launch(OP_CODES[j.w.op], j.w.M, j.w.N, j.dt_code, True)})
@@ -488,6 +537,7 @@ def main():
             next_rows.append({"workload": w.name, "op": w.op, "dtype": w.dt, "M": w.M, "N": w.N,
                               "bytes": j.bytes, **base,
                               "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
+                              "p10_ms": round(pct(durs, 10), 5), "p90_ms": round(pct(durs, 90), 5),
                               "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                               "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                               "traffic": traffic_for(w.name, j.bytes),

@@ -66,6 +66,8 @@ def load(path: str = _LIB_PATH):
     for f in ("or_decode", "or_softmax", "or_layernorm", "or_rmsnorm",
               "or_softmax_online", "or_add", "or_softmax_causal", "or_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
+    lib.or_set_num_threads.argtypes = [ctypes.c_int]
+    lib.or_set_num_threads.restype = None
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -200,3 +202,8 @@ def add_layernorm(x: np.ndarray, r: np.ndarray, dt, eps: float, gamma=None, beta
 
 def num_threads() -> int:
     return int(load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (timing only; results do not depend on it)."""
+    load().or_set_num_threads(int(n))

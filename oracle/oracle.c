@@ -307,6 +307,18 @@ int or_softmax_online(int64_t M, int64_t N, int dtype, int64_t block,
     return 0;
 }
 
+/* Sets the number of OpenMP threads later parallel regions use (n >= 1);
+ * timing only, the results do not depend on it. */
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads a parallel region of this library will use. */
 int or_num_threads(void)
 {

@@ -99,12 +99,25 @@ hipError_t persist_go(const RowArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The persistent kernel is planned for LayerNorm (plain, and fused with the
+// residual add), plain 16-bit RMSNorm and fp32 RMSNorm at 8 waves x 8
+// chunks; other norms stream faster one row per workgroup, and their
+// persistent forms are not built.
+template <int OP, int W, int K>
+hipError_t persist_pick(const RowArgs &a, hipStream_t s) {
+    if (a.r) {
+        if constexpr (OP == OP_LAYERNORM) return persist_go<OP, W, K, true>(a, s);
+        return hipErrorInvalidValue;
+    }
+    if constexpr (OP == OP_LAYERNORM || !kWide || (W == 8 && K == 8)) return persist_go<OP, W, K, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
 template <int OP>
 hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k)                                                   \
     if (W == w && K == k) {                                              \
-        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32)                 \
-            return a.r ? persist_go<OP, w, k, true>(a, s) : persist_go<OP, w, k, false>(a, s); \
+        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32) return persist_pick<OP, w, k>(a, s); \
         return hipErrorInvalidValue;                                     \
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)

@@ -49,28 +49,44 @@ struct Menu {
     int n;
 };
 // Chosen from launch-shape sweeps on MI355X (every shape that covers the row,
-// timed interleaved at M = 4096 and on the workloads): about one or two
-// 16-byte chunks per lane with up to 8 waves per row stream best.  For rows
-// of 257..512 chunks 4 waves with 2 chunks each beat 8 waves with 1 by 3-15%
-// (no idle lanes on part-filled rows, twice the rows in flight; on causal
-// rows, whose loads stop at the diagonal, by 27%).  Exception: 16-bit rows
-// that fill all 512 chunks (4096 elements) keep 8 waves with 1 chunk, which
-// streams the 131072-row causal-score workload about 1-2% faster
-// (full_row_shape).  RMSNorm fp32 prefers one wave with 8 chunks there and 16
-// waves with 2 chunks for rows of 1025..2048 chunks (2-5%).
+// timed interleaved at M = 4096 and at 2^27 elements per matrix, and on the
+// workloads): about one or two 16-byte chunks per lane with up to 8 waves per
+// row stream best.  For softmax rows of 257..512 chunks 4 waves with 2 chunks
+// each beat 8 waves with 1 by 3-15% (no idle lanes on part-filled rows, twice
+// the rows in flight; on causal rows, whose loads stop at the diagonal, by
+// 27%).  Exception: 16-bit softmax rows that fill all 512 chunks (4096
+// elements) keep 8 waves with 1 chunk, which streams the 131072-row
+// causal-score workload about 1-2% faster (full_row_shape).  RMSNorm: 4 waves
+// x 1 chunk for rows of 129..256 chunks (3% over one wave x 4 at large M),
+// 8 x 1 for 257..512 (6% over 1 x 8), fp32 16 x 2 for 1025..2048.  LayerNorm,
+// whose fp64 statistics lengthen each row's compute, prefers fewer waves:
+// f16 2 x 2 for 129..256 chunks, fp32 2 x 4 for 257..512 (2-5%).  The fused
+// residual add + norm entries have menus of their own (below).
 const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
 const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {1, 8}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
-const Shape kRms16[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
-const Shape kLn16[] = {{1, 1}, {1, 2}, {4, 1}, {4, 2}, {8, 2}};
+const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
+const Shape kRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}};
+const Shape kLn16[] = {{1, 1}, {1, 2}, {2, 2}, {4, 2}, {8, 2}};
+// Fused residual add + norm (two input and two output streams per row): more
+// waves per row than the plain norms at the same width.  16-bit RMSNorm rows
+// of 1025..2048 chunks take 16 waves x 2 (7% over 8 x 4); f16 LayerNorm rows
+// of up to 512 chunks 4 x 1 and 8 x 1 (3-4% over 4 x 2); fp32 RMSNorm uses
+// the plain menu (wider shapes are cut at 32 values per lane by shape_fits).
+const Shape kAddRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {16, 2}};
+const Shape kAddLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
+const Shape kAddLn16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}};
 #define NT_MENU(a) Menu{a, (int)(sizeof(a) / sizeof(*(a)))}
-Menu menu_for(nt_op op, nt_dtype dt) {
+Menu menu_for(nt_op op, nt_dtype dt, bool res) {
     const bool wide = dt == NT_F32;
     switch (op) {
     case NT_OP_SOFTMAX: return wide ? NT_MENU(kSoftmax32) : NT_MENU(kSoftmax16);
-    case NT_OP_RMSNORM: return wide ? NT_MENU(kRms32) : NT_MENU(kRms16);
-    default: return wide ? NT_MENU(kLn32) : NT_MENU(kLn16);
+    case NT_OP_RMSNORM:
+        if (res && !wide) return NT_MENU(kAddRms16);
+        return wide ? NT_MENU(kRms32) : NT_MENU(kRms16);
+    default:
+        if (res) return wide ? NT_MENU(kAddLn32) : NT_MENU(kAddLn16);
+        return wide ? NT_MENU(kLn32) : NT_MENU(kLn16);
     }
 }
 #undef NT_MENU
@@ -151,9 +167,36 @@ int64_t row_chunks(int64_t N, nt_dtype dt, bool aligned) {
     return (N + vec - 1 + vec - 1) / vec;
 }
 
-bool persistent_enabled() {
+// Persistent norm kernels: NT_PERSISTENT=0 never, "always" wherever the
+// kernel is built (tuning), else where it pays (persistent_pays).
+int persistent_mode() {
     const char *s = std::getenv("NT_PERSISTENT");
-    return !(s && std::strcmp(s, "0") == 0);
+    if (s && std::strcmp(s, "0") == 0) return 0;
+    if (s && std::strcmp(s, "always") == 0) return 2;
+    return 1;
+}
+
+// Whether persistent workgroups beat one workgroup per row, from sweeps with
+// both forced on every planned shape and row fill (M = 4096 and 256 MiB
+// matrices).  The persistent kernel overlaps the next row's loads with this
+// row's arithmetic but holds two rows in registers, so fewer waves fit.
+//  - LayerNorm (fp64 statistics, long per-row arithmetic): always, by 4-54%.
+//  - Fused add + LayerNorm: when a lane holds 16 values or more (9-29%);
+//    with fewer, one row per workgroup is 1-14% faster.
+//  - 16-bit RMSNorm: rows of 1024 chunks or more (a tie at 1024, 5-13% from
+//    1280); narrower rows stream 2-12% faster one row per workgroup.
+//  - fp32 RMSNorm: only the part-filled 8 x 8 shape (2049..3072 chunks,
+//    2-8%); the fused add + RMSNorm never (its two input streams keep enough
+//    bytes in flight without it).
+bool persistent_built(nt_op op, nt_dtype dt, bool res, Shape sh) {
+    if (op == NT_OP_LAYERNORM) return true;
+    return !res && (dt != NT_F32 || (sh.W == 8 && sh.K == 8));
+}
+
+bool persistent_pays(nt_op op, nt_dtype dt, bool res, Shape sh, int64_t nch) {
+    if (op == NT_OP_LAYERNORM) return !res || sh.K * elems_per_chunk(dt) >= 16;
+    if (res) return false;
+    return dt != NT_F32 ? nch >= 1024 : (sh.W == 8 && sh.K == 8 && nch <= 3072);
 }
 
 // `res`: the fused residual add + norm, whose lanes also hold the residual's
@@ -174,7 +217,7 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
-    const Menu menu = menu_for(op, dt);
+    const Menu menu = menu_for(op, dt, res);
     const char *force = std::getenv("NT_FORCE_PATH");
     const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
     const bool force_loop = op != NT_OP_SOFTMAX && force && std::strcmp(force, "looped") == 0;
@@ -207,13 +250,15 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         int64_t grid = (M + G - 1) / G;
         if (grid > max_grid) grid = max_grid;
         p->grid = grid;
-        // Norms on aligned rows with every parameter vector present keep the
-        // parameters widened in registers across rows: persistent workgroups
-        // (grid sized on the device from occupancy; `grid` is then an upper bound).
-        // (at most 32 values per lane: the row, its prefetched successor and the
-        // cached parameters must fit without spilling; built for 2 to 8 waves)
+        // Norms on aligned rows with every parameter vector present can keep
+        // the parameters widened in registers across rows: persistent
+        // workgroups (grid sized on the device from occupancy; `grid` is then
+        // an upper bound), where that pays (persistent_pays).  At most 32
+        // values per lane: the row, its prefetched successor and the cached
+        // parameters must fit without spilling; built for 2 to 8 waves.
         if (op != NT_OP_SOFTMAX && aligned && params && pick.W >= 2 && pick.W <= 8 &&
-            pick.K * elems_per_chunk(dt) <= 32 && persistent_enabled())
+            pick.K * elems_per_chunk(dt) <= 32 && persistent_built(op, dt, res, pick) &&
+            (persistent_mode() == 2 || (persistent_mode() == 1 && persistent_pays(op, dt, res, pick, nch))))
             p->persistent = 1;
         return NT_OK;
     }

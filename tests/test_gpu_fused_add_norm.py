@@ -125,8 +125,8 @@ def test_fused_workload_full_size(name):
     p0_t = to_dev(p0, w.dt)
     p1_t = None if p1 is None else to_dev(p1, w.dt)
     plan = nt.nt_plan_launch(OP_CODE[w.op], w.M, w.N, DT_CODE[w.dt], True)
-    assert plan["persistent"] == 1, plan
-    say(f"workload {name}: launching")
+    say(f"workload {name}: launching ({plan['waves_per_row']}x{plan['chunks_per_lane']}, "
+        f"persistent={plan['persistent']})")
     h, y, mean, rstd = run_fused(w.op, x_t, r_t, w.dt, w.eps, p0_t, p1_t)
     rows = np.arange(w.M)
     if w.M * w.N > 40_000_000:
@@ -180,12 +180,12 @@ def test_fused_in_place(op, path, monkeypatch):
         check_fused(op, dt, h, y, mean, rstd, ref, f"in place {op} {path} h={h_is} y={y_is}")
 
 
-@pytest.mark.parametrize("op", ["add_rmsnorm", "add_layernorm"])
+@pytest.mark.parametrize("op", ["add_layernorm"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_fused_persistent_small_grids(op, dt, monkeypatch):
-    """The persistent fused kernel on grids far smaller than M is bitwise the
-    one-row fused kernel."""
-    M, N = 300, 4096
+    """The persistent fused kernel (fused add + LayerNorm rows of 1024 chunks
+    or more) on grids far smaller than M is bitwise the one-row fused kernel."""
+    M, N = 300, 8192
     x = rand_bits(21, M, N, dt, scale=2.0, loc=1.5)
     r = rand_bits(22, M, N, dt)
     p0, p1 = params(op, N, dt, 23)

@@ -224,12 +224,44 @@ def test_env_overrides(monkeypatch):
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 4096, F32, True)["split"] == 0
 
 
+def test_persistent_rule():
+    """Persistent workgroups: every LayerNorm; fused add + LayerNorm with 16
+    values or more per lane; 16-bit RMSNorm from 1024 chunks per row; fp32
+    RMSNorm only on part-filled 8 x 8 shapes (2049..3072 chunks); never the
+    fused add + RMSNorm; only on aligned rows with the parameters present."""
+    cases = [  # (op, dt, N) -> persistent
+        (nt.NT_OP_LAYERNORM, F16, 2048, 1), (nt.NT_OP_LAYERNORM, F16, 4096, 1), (nt.NT_OP_LAYERNORM, F32, 2048, 1),
+        (nt.NT_OP_LAYERNORM, F32, 8192, 1), (nt.NT_OP_ADD_LAYERNORM, F16, 4096, 0),
+        (nt.NT_OP_ADD_LAYERNORM, F16, 5120, 1), (nt.NT_OP_ADD_LAYERNORM, F16, 8192, 1),
+        (nt.NT_OP_ADD_LAYERNORM, F32, 2048, 0), (nt.NT_OP_ADD_LAYERNORM, F32, 4096, 0),
+        (nt.NT_OP_ADD_LAYERNORM, F32, 5120, 1), (nt.NT_OP_RMSNORM, BF16, 4096, 0), (nt.NT_OP_RMSNORM, BF16, 8192, 1),
+        (nt.NT_OP_RMSNORM, F16, 16384, 1), (nt.NT_OP_RMSNORM, F32, 4096, 0), (nt.NT_OP_RMSNORM, F32, 8320, 1),
+        (nt.NT_OP_RMSNORM, F32, 12288, 1), (nt.NT_OP_RMSNORM, F32, 12800, 0), (nt.NT_OP_RMSNORM, F32, 16384, 0),
+        (nt.NT_OP_ADD_RMSNORM, BF16, 8192, 0), (nt.NT_OP_ADD_RMSNORM, F32, 4096, 0),
+        (nt.NT_OP_ADD_RMSNORM, F32, 10240, 0)]
+    for op, dt, N, want in cases:
+        p = nt.nt_plan_launch(op, 4096, N, dt, True)
+        assert p["split"] == 0 and p["persistent"] == want, (op, dt, N, p)
+        assert nt.nt_plan_launch(op, 4096, N, dt, False)["persistent"] == 0
+    # the shapes the sweeps chose for the plain norms
+    assert [(nt.nt_plan_launch(nt.NT_OP_RMSNORM, 4096, n, dt, True)["waves_per_row"],
+             nt.nt_plan_launch(nt.NT_OP_RMSNORM, 4096, n, dt, True)["chunks_per_lane"])
+            for n, dt in ((2048, BF16), (4096, BF16), (2048, F32), (4096, F32))] == [(4, 1), (8, 1), (8, 1), (8, 2)]
+    assert [(nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, n, dt, True)["waves_per_row"],
+             nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, n, dt, True)["chunks_per_lane"])
+            for n, dt in ((2048, F16), (4096, F16), (2048, F32))] == [(2, 2), (4, 2), (2, 4)]
+
+
 def test_fused_add_norm_plans():
     # the fused kernels hold the residual too: RMSNorm at most 32 values per
     # lane in one pass, wider rows take the looped kernel
     p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 16384, 8192, BF16, True)
-    assert (p["split"], p["persistent"]) == (0, 1) and p["chunks_per_lane"] * 8 <= 32
+    assert (p["split"], p["persistent"], p["waves_per_row"], p["chunks_per_lane"]) == (0, 0, 8, 2)
+    p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 8192, 16384, BF16, True)
+    assert (p["split"], p["persistent"], p["waves_per_row"], p["chunks_per_lane"]) == (0, 0, 16, 2)
     p = nt.nt_plan_launch(nt.NT_OP_ADD_LAYERNORM, 4096, 4096, F16, True)
+    assert (p["split"], p["persistent"], p["waves_per_row"], p["chunks_per_lane"]) == (0, 0, 8, 1)
+    p = nt.nt_plan_launch(nt.NT_OP_ADD_LAYERNORM, 4096, 8192, F16, True)
     assert (p["split"], p["persistent"]) == (0, 1)
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 4, 8192 * 4, BF16, True)["split"] == 0      # 64 per lane
     assert nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 4, 8192 * 4, BF16, True)["split"] == 2  # looped
