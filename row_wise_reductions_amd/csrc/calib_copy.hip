@@ -21,8 +21,8 @@ __global__ void __launch_bounds__(256) ntcal_copy_sc1_kernel(const u32x4 *__rest
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n16) {
         const u32x4 v = __builtin_nontemporal_load(src + i);
-        // s_nop: the data registers must not be overwritten in the next cycle.
-        asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 0" : : "v"(dst + i), "v"(v) : "memory");
+        // s_nop 1: no VALU may overwrite the data registers within 2 wait states.
+        asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(dst + i), "v"(v) : "memory");
     }
 }
 }  // namespace

@@ -139,12 +139,14 @@ __device__ __forceinline__ uint4 ld16_nt(const char *p) {
 }
 __device__ __forceinline__ void st16_nt(char *p, uint4 v) {
 #if NTK_NT_STORES && NTK_STORE_SC1
-    // The compiler does not see this store: the s_nop covers the hazard of a
-    // VALU overwriting the store's data registers in the next cycle, and a
-    // kernel that reads back what it stored waits on vmcnt itself
-    // (wait_own_stores).
+    // The compiler does not see this store, so it neither counts it for
+    // s_waitcnt nor keeps its hazards.  A VALU must not overwrite the data
+    // registers of a store wider than 64 bits within 2 wait states of it on
+    // gfx950 (1 is not enough: stores then write the new values); s_nop 1
+    // gives the 2.  A kernel that reads back what it stored waits on vmcnt
+    // itself (wait_own_stores).
     const u32x4 t = {v.x, v.y, v.z, v.w};
-    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 0" : : "v"(p), "v"(t) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(p), "v"(t) : "memory");
 #elif NTK_NT_STORES
     const u32x4 t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));

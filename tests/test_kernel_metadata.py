@@ -73,6 +73,75 @@ def test_no_mfma(code_objects):
         assert not re.search(r"\bv_mfma", asm), "MFMA instruction in a row-reduction kernel"
 
 
+def _vregs(spec):
+    m = re.match(r"v\[(\d+):(\d+)\]", spec)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", spec)
+    return {int(m.group(1))} if m else set()
+
+
+def _store_hazards(code_object, need=2):
+    """Inline-assembly 16-byte stores (`nt sc1`) followed, within `need` wait
+    states, by a VALU writing one of their data registers (s_nop N counts
+    N + 1, any other instruction 1).  gfx950 needs 2: with 1 the store
+    writes the new register values."""
+    asm = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(code_object)], check=True,
+                         capture_output=True, text=True).stdout.splitlines()
+    ins, fn = [], None
+    for line in asm:
+        if line.endswith(">:"):
+            fn = line
+            continue
+        m = re.match(r"\s+([a-z_0-9]+)(?:\s+([^/]*))?", line)
+        if m and fn:
+            ins.append((fn, m.group(1), (m.group(2) or "").strip()))
+    stores, bad = 0, []
+    for j, (f, op, args) in enumerate(ins):
+        if op != "global_store_dwordx4" or "nt sc1" not in args:
+            continue
+        stores += 1
+        data = _vregs(args.split(",")[1].strip())
+        ws = 0
+        for f2, op2, a2 in ins[j + 1:j + 1 + 2 * need]:
+            if f2 != f or ws >= need:
+                break
+            if op2.startswith("v_") and _vregs(a2.split(",")[0].strip()) & data:
+                bad.append(f"{f} {op} {args} -> {op2} {a2} after {ws} wait states")
+                break
+            ws += int(a2.split()[0], 0) + 1 if op2 == "s_nop" else 1
+    return stores, bad
+
+
+def test_inline_store_data_hazard(code_objects):
+    """The device-scope streaming stores are inline assembly, outside the
+    compiler's hazard tracking: every one must be followed by 2 wait states
+    before its data registers are rewritten."""
+    total, bad = 0, []
+    for co in code_objects:
+        n, b = _store_hazards(co)
+        total += n
+        bad += b
+    assert total > 0, "no inline nt sc1 stores found"
+    assert not bad, bad[:5]
+
+
+def test_calibration_copy_store_hazard(tmp_path):
+    cal = os.path.join(os.path.dirname(nt.LIB_PATH), "libntcal.so")
+    if not os.path.exists(cal) or not shutil.which("objcopy"):
+        pytest.skip("libntcal.so or objcopy not available")
+    fat = tmp_path / "cal.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", cal, str(fat)], check=True)
+    data = fat.read_bytes()
+    s0 = data.index(MAGIC)
+    part, co = tmp_path / "b.bin", tmp_path / "cal.co"
+    part.write_bytes(data[s0:])
+    subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={part}",
+                    f"--targets={TARGET}", f"--output={co}"], check=True)
+    n, bad = _store_hazards(co)
+    assert n == 1 and not bad, (n, bad)
+
+
 def test_all_types_present(kernels):
     for dt in (0, 1, 2):
         assert any(f"row_residentILi0ELi{dt}E" in k for k in kernels), dt
