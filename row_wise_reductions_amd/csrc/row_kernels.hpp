@@ -730,7 +730,13 @@ row_resident(RowArgs a) {
     const int64_t nrb = (a.M + G - 1) / G;
     int par = 0;
     for (int64_t rb = xcd_band(blockIdx.x, gridDim.x); rb < nrb; rb += gridDim.x, par ^= 1) {
-        const int64_t row = rb * G + g;
+        int64_t row = rb * G + g;
+        // Causal rows (one per workgroup): workgroups alternate between rows
+        // from the two ends of the matrix, so a short and a long visible
+        // prefix stream side by side (in the square layout each pair reads
+        // N + 1 elements) instead of runs of read-light then read-heavy rows:
+        // 5-6% faster on 131072 x 4096 and 32768 x 8192 bf16 scores.
+        if constexpr (CAUSAL && G == 1) row = (rb & 1) ? a.M - 1 - (rb >> 1) : (rb >> 1);
         if (row >= a.M) break;   // only possible when W == 1 (no barriers there)
         const char *xr = a.x + row * rowbytes;
         char *yr = a.y + row * rowbytes;

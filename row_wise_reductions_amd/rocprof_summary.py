@@ -11,6 +11,12 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
 
   python -m row_wise_reductions_amd.rocprof_summary traffic --fetch DIR --write DIR \\
          --calib-fetch DIR --calib-write DIR --cmds FILE --md FILE.md --json FILE.json
+
+  python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR --cmds FILE --md FILE.md
+      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`
+      and `--pmc MeanOccupancyPerActiveCU` runs of bench.py; beside them, each
+      kernel's registers, LDS and static occupancy limit from the built code
+      object (codeobj.py).
       DIRs hold *_counter_collection.csv from `rocprofv3 --pmc FETCH_SIZE`
       and `--pmc WRITE_SIZE` runs of bench.py and of `bench.py --calibrate`.
       Counter values (KiB per dispatch) are scaled by what the same counter
@@ -181,6 +187,54 @@ def traffic(args):
     print("\n".join(lines))
 
 
+def occupancy(args):
+    import tempfile
+
+    import row_wise_reductions_amd as nt
+    import workloads
+    from . import codeobj
+    occ = _counter_means(args.occ, "OccupancyPercent")
+    act = _counter_means(args.active, "MeanOccupancyPerActiveCU")
+    meta = codeobj.kernel_metadata(codeobj.code_objects(nt.LIB_PATH, tempfile.mkdtemp()))
+    dm = codeobj.demangle(list(meta))
+    by_name = {dm[k]: v for k, v in meta.items()}
+    with open(args.cmds) as fh:
+        cmds = fh.read().strip().splitlines()
+    lines = ["# Occupancy: registers, LDS and resident waves of each workload's kernels", "",
+             "Static limits from the built gfx950 code object (`row_wise_reductions_amd/codeobj.py`: 512 registers",
+             "per lane per SIMD in granules of 8, at most 8 waves per SIMD, 160 KiB LDS per CU, whole workgroups);",
+             "measured occupancy from rocprofv3 derived counters, each in a run of its own, from the repository",
+             "root on the GPU host:", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "`OccupancyPercent` = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CUs / 32 (resident waves as a share",
+              "of 32 per CU, over the kernel's whole duration, launch ramp and tail included);",
+              "`MeanOccupancyPerActiveCU` = accumulated SQ_LEVEL_WAVES / SQ_BUSY_CU_CYCLES, as reported: on these",
+              "kernels it tracks resident waves per SIMD while the CU is busy (it reaches 7.7 where the static",
+              "limit is 8 waves per SIMD, i.e. 32 per CU).", "",
+              "| workload | kernel | threads / WG | VGPRs (allocated) | LDS B | static waves / SIMD (registers, LDS) | "
+              "OccupancyPercent | MeanOccupancyPerActiveCU |", "|---|---|---|---|---|---|---|---|"]
+    for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS:
+        op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4,
+              "softmax_causal": 5}[w.op]
+        dt = {"f32": 0, "f16": 1, "bf16": 2}[w.dt]
+        p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
+        threads = p["threads_per_block"]
+        for i, k in enumerate(kernels_of(w)):
+            m = next((v for n, v in by_name.items() if n.startswith(f"void {k}(")), None)
+            if m is None:
+                continue
+            st = codeobj.waves_per_simd(m, threads)
+            o, _ = _lookup(occ, k)
+            a, _ = _lookup(act, k)
+            lines.append(f"| {w.name if i == 0 else ''} | `{k}` | {threads} | {m['vgpr']} ({st['regs_allocated']}) | "
+                         f"{m['lds']} | {st['waves_per_simd']:g} ({st['by_regs']}, {st['by_lds']}) | "
+                         f"{'' if o is None else f'{o:.1f}%'} | {'' if a is None else f'{a:.1f}'} |")
+    lines.append("")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -194,8 +248,13 @@ def main():
     t.add_argument("--cmds", required=True)
     t.add_argument("--md", required=True)
     t.add_argument("--json", required=True)
+    o = sub.add_parser("occupancy")
+    o.add_argument("--occ", required=True)
+    o.add_argument("--active", required=True)
+    o.add_argument("--cmds", required=True)
+    o.add_argument("--md", required=True)
     a = ap.parse_args()
-    stats(a) if a.mode == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "occupancy": occupancy}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -13,47 +13,24 @@ import pytest
 
 import row_wise_reductions_amd as nt
 
-LLVM = "/opt/rocm/llvm/bin"
-TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+from row_wise_reductions_amd import codeobj
 
-
-MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+LLVM = codeobj.LLVM
+TARGET = codeobj.TARGET
+MAGIC = codeobj.MAGIC
 
 
 @pytest.fixture(scope="module")
 def code_objects(tmp_path_factory):
-    """One gfx950 code object per translation unit: the linked .hip_fatbin
-    section is a concatenation of one offload bundle per object file."""
-    if not (shutil.which("objcopy") and os.path.exists(f"{LLVM}/clang-offload-bundler")):
+    """One gfx950 code object per translation unit of libnt.so."""
+    if not codeobj.tools_available():
         pytest.skip("binutils / ROCm LLVM tools not available")
-    d = tmp_path_factory.mktemp("co")
-    fat = d / "fatbin.bin"
-    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", nt.LIB_PATH, str(fat)], check=True)
-    data = fat.read_bytes()
-    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
-    assert starts, "no offload bundle in libnt.so"
-    cos = []
-    for i, s0 in enumerate(starts):
-        end = starts[i + 1] if i + 1 < len(starts) else len(data)
-        part, co = d / f"bundle{i}.bin", d / f"k{i}.co"
-        part.write_bytes(data[s0:end])
-        subprocess.run([f"{LLVM}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={part}",
-                        f"--targets={TARGET}", f"--output={co}"], check=True)
-        cos.append(co)
-    return cos
+    return codeobj.code_objects(nt.LIB_PATH, str(tmp_path_factory.mktemp("co")))
 
 
 @pytest.fixture(scope="module")
 def kernels(code_objects):
-    out = {}
-    for co in code_objects:
-        notes = subprocess.run([f"{LLVM}/llvm-readelf", "--notes", str(co)], check=True,
-                               capture_output=True, text=True).stdout
-        for block in notes.split("  - .agpr_count:")[1:]:
-            name = re.search(r"\.name:\s+(\S+)", block).group(1)
-            get = lambda k: int(re.search(rf"\.{k}:\s+(\d+)", block).group(1))  # noqa: E731
-            out[name] = {"scratch": get("private_segment_fixed_size"), "vgpr": get("vgpr_count"),
-                         "lds": get("group_segment_fixed_size"), "wave": get("wavefront_size")}
+    out = codeobj.kernel_metadata(code_objects)
     assert out, "no kernels found in the code objects"
     return out
 
