@@ -1169,10 +1169,18 @@ template <int DT, int W, int K>
 __device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red)[2][W], int wv, int lane,
                                               float s2 = LOG2E) {
     constexpr int VEC = dt_info<DT>::VEC;
-    float v[K][VEC];
+    // Each pass widens one 16-byte slice at a time (the same order as a
+    // whole-chunk lane_max and sum), so no widened copy of the chunk stays
+    // live beside the packed words the caller keeps for its output.
+    float lm = -__builtin_inff();
 #pragma unroll
-    for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
-    const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red[0], wv, lane);
+    for (int k = 0; k < K; ++k) {
+        float v[VEC];
+        unpack<DT>(raw[k], v);
+#pragma unroll
+        for (int i = 0; i < VEC; i += 2) lm = __builtin_fmaxf(lm, __builtin_fmaxf(v[i], v[i + 1]));
+    }
+    const float mx = group_allreduce<W>(lm, MaxOp(), red[0], wv, lane);
     float cj;
     {
 #pragma clang fp contract(off)
@@ -1180,11 +1188,60 @@ __device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red
     }
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+    for (int k = 0; k < K; ++k) {
+        uint4 r = raw[k];
+        if constexpr (DT != DT_F32)   // widen again rather than keep the first pass's values
+            asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+        float v[VEC];
+        unpack<DT>(r, v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], s2, -cj));
+        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], s2, -cj));
+    }
     s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
     if (mx == -__builtin_inff()) s = 0.f;    // a fully masked chunk holds no mass
+    return make_float2(mx, s);
+}
+
+// chunk_stats of a chunk that is not in registers (the cooperative kernel's
+// recomputation of a missing record), reading it one 16-byte slice per lane
+// at a time, twice: slice k holds exactly the words slot k of a whole-chunk
+// load would (every slot depends only on its own chunk index), and the
+// arithmetic runs in the same order, so the pair is bitwise chunk_stats'.
+template <int DT, int W, int K, bool AL, bool CAUSAL>
+__device__ __forceinline__ float2 chunk_stats_reload(const RowGeom<DT, AL> &geo, const char *xr, int t,
+                                                        int32_t N, int32_t L, int64_t qbase,
+                                                        float (&red)[2][W], int wv, int lane, float s2) {
+    constexpr int VEC = dt_info<DT>::VEC, TPR = 64 * W;
+    float lm = -__builtin_inff();
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+        uint4 r[1];
+        softmax_issue<DT, AL, 1, TPR, CAUSAL>(r, geo, xr, t, N, L, qbase + (int64_t)k * TPR);
+        softmax_finish<DT, AL, 1, TPR, CAUSAL>(r, geo, xr, t, N, L, qbase + (int64_t)k * TPR);
+        float v[VEC];
+        unpack<DT>(r[0], v);
+#pragma unroll
+        for (int i = 0; i < VEC; i += 2) lm = __builtin_fmaxf(lm, __builtin_fmaxf(v[i], v[i + 1]));
+    }
+    const float mx = group_allreduce<W>(lm, MaxOp(), red[0], wv, lane);
+    float cj;
+    {
+#pragma clang fp contract(off)
+        cj = mx * s2;
+    }
+    float s = 0.f;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+        uint4 r[1];
+        softmax_issue<DT, AL, 1, TPR, CAUSAL>(r, geo, xr, t, N, L, qbase + (int64_t)k * TPR);
+        softmax_finish<DT, AL, 1, TPR, CAUSAL>(r, geo, xr, t, N, L, qbase + (int64_t)k * TPR);
+        float v[VEC];
+        unpack<DT>(r[0], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], s2, -cj));
+    }
+    s = group_allreduce<W>(s, SumOp(), red[1], wv, lane);
+    if (mx == -__builtin_inff()) s = 0.f;
     return make_float2(mx, s);
 }
 
@@ -1377,11 +1434,8 @@ softmax_coop(RowArgs a) {
         while (m) {
             const int q = b * 64 + __builtin_ctzll(m);
             m &= m - 1;
-            uint4 r2[K];
-            const int64_t qbase = (int64_t)q * (TPR * K);
-            softmax_issue<DT, AL, K, TPR, CAUSAL>(r2, geo, xr, t, N, L, qbase);
-            softmax_finish<DT, AL, K, TPR, CAUSAL>(r2, geo, xr, t, N, L, qbase);
-            const float2 e = chunk_stats<DT, W, K>(r2, red, wv, lane, s2);
+            const float2 e = chunk_stats_reload<DT, W, K, AL, CAUSAL>(geo, xr, t, N, L, (int64_t)q * (TPR * K), red,
+                                                                      wv, lane, s2);
             if (t == 0) qs[q] = e;
         }
     }
