@@ -12,9 +12,9 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
   python -m row_wise_reductions_amd.rocprof_summary traffic --fetch DIR --write DIR \\
          --calib-fetch DIR --calib-write DIR --cmds FILE --md FILE.md --json FILE.json
 
-  python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR --cmds FILE --md FILE.md
-      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`
-      and `--pmc MeanOccupancyPerActiveCU` runs of bench.py; beside them, each
+  python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR [--valu DIR] --cmds FILE --md FILE.md
+      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`,
+      `--pmc MeanOccupancyPerActiveCU` and `--pmc VALUBusy` runs of bench.py; beside them, each
       kernel's registers, LDS and static occupancy limit from the built code
       object (codeobj.py).
       DIRs hold *_counter_collection.csv from `rocprofv3 --pmc FETCH_SIZE`
@@ -195,6 +195,7 @@ def occupancy(args):
     from . import codeobj
     occ = _counter_means(args.occ, "OccupancyPercent")
     act = _counter_means(args.active, "MeanOccupancyPerActiveCU")
+    valu = _counter_means(args.valu, "VALUBusy") if args.valu else {}
     meta = codeobj.kernel_metadata(codeobj.code_objects(nt.LIB_PATH, tempfile.mkdtemp()))
     dm = codeobj.demangle(list(meta))
     by_name = {dm[k]: v for k, v in meta.items()}
@@ -210,9 +211,10 @@ def occupancy(args):
               "of 32 per CU, over the kernel's whole duration, launch ramp and tail included);",
               "`MeanOccupancyPerActiveCU` = accumulated SQ_LEVEL_WAVES / SQ_BUSY_CU_CYCLES, as reported: on these",
               "kernels it tracks resident waves per SIMD while the CU is busy (it reaches 7.7 where the static",
-              "limit is 8 waves per SIMD, i.e. 32 per CU).", "",
+              "limit is 8 waves per SIMD, i.e. 32 per CU); `VALUBusy` = 100 * SQ_ACTIVE_INST_VALU / CUs /",
+              "GRBM_GUI_ACTIVE (share of the kernel's time the vector ALUs are issuing).", "",
               "| workload | kernel | threads / WG | VGPRs (allocated) | LDS B | static waves / SIMD (registers, LDS) | "
-              "OccupancyPercent | MeanOccupancyPerActiveCU |", "|---|---|---|---|---|---|---|---|"]
+              "OccupancyPercent | MeanOccupancyPerActiveCU | VALUBusy |", "|---|---|---|---|---|---|---|---|---|"]
     for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS:
         op = {"softmax": 0, "layernorm": 1, "rmsnorm": 2, "add_layernorm": 3, "add_rmsnorm": 4,
               "softmax_causal": 5}[w.op]
@@ -226,9 +228,11 @@ def occupancy(args):
             st = codeobj.waves_per_simd(m, threads)
             o, _ = _lookup(occ, k)
             a, _ = _lookup(act, k)
+            v, _ = _lookup(valu, k)
             lines.append(f"| {w.name if i == 0 else ''} | `{k}` | {threads} | {m['vgpr']} ({st['regs_allocated']}) | "
                          f"{m['lds']} | {st['waves_per_simd']:g} ({st['by_regs']}, {st['by_lds']}) | "
-                         f"{'' if o is None else f'{o:.1f}%'} | {'' if a is None else f'{a:.1f}'} |")
+                         f"{'' if o is None else f'{o:.1f}%'} | {'' if a is None else f'{a:.1f}'} | "
+                         f"{'' if v is None else f'{v:.1f}%'} |")
     lines.append("")
     with open(args.md, "w") as f:
         f.write("\n".join(lines))
@@ -251,6 +255,7 @@ def main():
     o = sub.add_parser("occupancy")
     o.add_argument("--occ", required=True)
     o.add_argument("--active", required=True)
+    o.add_argument("--valu", default=None, help="DIR of a `rocprofv3 --pmc VALUBusy` run")
     o.add_argument("--cmds", required=True)
     o.add_argument("--md", required=True)
     a = ap.parse_args()
