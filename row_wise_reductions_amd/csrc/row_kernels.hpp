@@ -790,20 +790,35 @@ row_resident(RowArgs a) {
             const float s2 = CAUSAL ? a.s2 : LOG2E;
             const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red_f[par][0], wv, lane);
             const float c = mx * s2;
+            // fp32 rows of 4 or 8 chunks per lane recompute each exponential
+            // for the output instead of keeping them all (the same arguments,
+            // so the same bits): their stores then leave one chunk at a time,
+            // 1-3% faster; with fewer values per lane, with 16-bit types and
+            // on causal rows keeping them is as fast or faster.
+            constexpr bool RECOMP = DT == DT_F32 && (K == 4 || K == 8) && !CAUSAL;
             float s = 0.f;
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    v[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], s2, -c));
-                    s += v[k][i];
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][i], s2, -c));
+                    if constexpr (!RECOMP) v[k][i] = e;
+                    s += e;
                 }
             s = group_allreduce<W>(s, SumOp(), red_f[par][1], wv, lane);
             const float inv = rcp_approx(s);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) v[k][i] *= inv;
+                for (int i = 0; i < VEC; ++i) {
+                    if constexpr (RECOMP) {
+                        float x = v[k][i];
+                        asm volatile("" : "+v"(x));      // recompute: no reuse of the first pass
+                        v[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, s2, -c)) * inv;
+                    } else {
+                        v[k][i] *= inv;
+                    }
+                }
                 store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
             }
         } else if constexpr (OP == OP_RMSNORM) {
