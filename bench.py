@@ -29,7 +29,9 @@ are timed after the suite and reported under next_rows, outside value); --calibr
 1 GiB copy: attainable bandwidth, and the counter calibration) and
 --copy-at-sizes (the plain copy at each workload's byte count) and --sweep
 (fp32 softmax and RMSNorm over the pages' benchmark widths, beside torch's
-softmax; --sweep-md FILE writes a summary) replace the suite.
+softmax; --sweep-md FILE writes a summary) and --sweep-ops f32|f16|bf16 (all
+three ops over those widths in one type, each beside torch's kernel) replace
+the suite.
 """
 from __future__ import annotations
 
@@ -410,10 +412,105 @@ def width_sweep(torch, steps, warmup, md_path=None):
             f.write("\n".join(lines))
 
 
+def op_sweep(torch, dt, steps, warmup, md_path=None):
+    """Every op over the widths of the pages' harness (M = 4096, N = 128 i,
+    i = 2..99) in one element type, each beside torch's own kernel on the same
+    buffers (torch.softmax, F.rms_norm, F.layer_norm with weight and bias):
+    the launch table of each op across widths.  GB/s = the op's algorithmic
+    bytes (rows in and out, parameter vectors, LayerNorm's mean and rstd) /
+    median event-timed launch; torch is credited with the same bytes."""
+    import torch.nn.functional as F
+
+    import row_wise_reductions_amd as nt
+    M = SWEEP_M
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    code = {"f32": nt.NT_F32, "f16": nt.NT_F16, "bf16": nt.NT_BF16}[dt]
+    e = 4 if dt == "f32" else 2
+    pool = (1 << 30) // e
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    px = torch.randn(pool, device="cuda", generator=gen).to(tdt)
+    py = torch.empty(pool, device="cuda", dtype=tdt)
+    g = (torch.randn(max(SWEEP_N), device="cuda", generator=gen) * 0.3 + 1.0).to(tdt)
+    b = (torch.randn(max(SWEEP_N), device="cuda", generator=gen) * 0.3).to(tdt)
+    mean = torch.empty(M, device="cuda")
+    rstd = torch.empty(M, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, R):
+        warm_up(lambda: fn(0), warmup, 20.0, torch)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, bb) in enumerate(evs):
+            a.record()
+            fn(i % R)
+            bb.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(bb) for a, bb in evs)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(nt.nt_status_string(rc))
+
+    rows = []
+    for N in SWEEP_N:
+        n = M * N
+        R = pool // n
+        xs = [px[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+        ys = [py[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+        gN, bN = g[:N], b[:N]
+        fns = {
+            "softmax": lambda i: ok(nt.nt_softmax_rows(M, N, code, xs[i].data_ptr(), ys[i].data_ptr(), None, 0,
+                                                       sh)),
+            "torch_softmax": lambda i: torch.softmax(xs[i], dim=-1),
+            "rmsnorm": lambda i: ok(nt.nt_rmsnorm_rows(M, N, code, 1e-6, xs[i].data_ptr(), gN.data_ptr(),
+                                                       ys[i].data_ptr(), sh)),
+            "torch_rmsnorm": lambda i: F.rms_norm(xs[i], (N,), gN, 1e-6),
+            "layernorm": lambda i: ok(nt.nt_layernorm_rows(M, N, code, 1e-5, xs[i].data_ptr(), gN.data_ptr(),
+                                                           bN.data_ptr(), ys[i].data_ptr(), mean.data_ptr(),
+                                                           rstd.data_ptr(), sh)),
+            "torch_layernorm": lambda i: F.layer_norm(xs[i], (N,), gN, bN, 1e-5),
+        }
+        gb = {"softmax": 2 * n * e, "rmsnorm": 2 * n * e + N * e, "layernorm": 2 * n * e + 2 * N * e + 8 * M}
+        r = {"N": N}
+        for k, fn in fns.items():
+            ms = timed(fn, R)
+            r[k + "_GBps"] = round(gb[k.replace("torch_", "")] / (ms * 1e-3) / 1e9, 1)
+        for op, c in (("softmax", nt.NT_OP_SOFTMAX), ("rmsnorm", nt.NT_OP_RMSNORM), ("layernorm", nt.NT_OP_LAYERNORM)):
+            p = nt.nt_plan_launch(c, M, N, code, True)
+            r[op + "_plan"] = ("split" if p["split"] == 1 else "looped" if p["split"] == 2 else
+                               f"{p['waves_per_row']}x{p['chunks_per_lane']}" + (" p" if p["persistent"] else ""))
+        rows.append(r)
+        log(f"[op sweep {dt}] N={N}: " + ", ".join(f"{k} {v}" for k, v in r.items() if k.endswith("GBps")))
+    out = {"op_sweep": f"{dt} softmax, RMSNorm, LayerNorm, M = 4096, N = 128 i (i = 2..99)", "points": rows}
+    print(json.dumps(out), flush=True)
+    if md_path:
+        lines = [f"# Width sweep of every op: {dt}, M = 4096, N = 128 i (i = 2..99)", "",
+                 "Command (repository root, GPU host):", "",
+                 f"    python3 bench.py --sweep-ops {dt} --steps {steps} --warmup {warmup} --sweep-md {md_path}", "",
+                 "GB/s = the op's algorithmic bytes / median event-timed launch, inputs rotating through a 1 GiB pool; "
+                 "torch (torch.softmax, F.rms_norm, F.layer_norm with weight and bias, on the same buffers) is credited "
+                 "with the same bytes.  Plan: W x K of the single-pass kernel (p: persistent workgroups).", "",
+                 "| N | softmax plan | softmax | torch | RMSNorm plan | RMSNorm | torch | LayerNorm plan | LayerNorm | "
+                 "torch |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['N']} | {r['softmax_plan']} | {r['softmax_GBps']} | {r['torch_softmax_GBps']} | "
+                         f"{r['rmsnorm_plan']} | {r['rmsnorm_GBps']} | {r['torch_rmsnorm_GBps']} | "
+                         f"{r['layernorm_plan']} | {r['layernorm_GBps']} | {r['torch_layernorm_GBps']} |")
+        lines.append("")
+        for op in ("softmax", "rmsnorm", "layernorm"):
+            q = [r[op + "_GBps"] / r["torch_" + op + "_GBps"] for r in rows]
+            lines.append(f"{op} / torch: min {min(q):.2f}, median {statistics.median(q):.2f}, max {max(q):.2f} "
+                         f"over {len(rows)} widths.  ")
+        lines.append("")
+        with open(md_path, "w") as f:
+            f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--sweep-ops", dest="sweep_ops", choices=["f32", "f16", "bf16"], default=None,
+                    help="softmax, RMSNorm and LayerNorm over the pages' widths in one type, beside torch")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--warm-ms", dest="warm_ms", type=float, default=200.0,
                     help="minimum wall time of the untimed warm-up before each timed pass")
@@ -447,6 +544,9 @@ def main():
         return
     if args.sweep:
         width_sweep(torch, args.steps, args.warmup, args.sweep_md)
+        return
+    if args.sweep_ops:
+        op_sweep(torch, args.sweep_ops, args.steps, args.warmup, args.sweep_md)
         return
     if args.copy_at_sizes:
         names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]

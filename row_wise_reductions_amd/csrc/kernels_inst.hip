@@ -27,13 +27,16 @@ hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
 }
 
 // Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
-// arithmetic needs twice the registers), RMSNorm and softmax 64, and a fused
-// residual add (which also holds the residual's words) 32.  Wider shapes
-// would spill registers and are not built.
-template <int OP, int K, bool RES = false>
+// arithmetic needs twice the registers) except 32 at 8 waves (rows of up to
+// 16384 elements in one pass; 512-thread workgroups leave a wave 256
+// registers; the persistent fp32 form would spill and is not built), RMSNorm
+// and softmax 64, and a fused residual add (which also
+// holds the residual's words) 32.  Wider shapes would spill registers and are
+// not built.
+template <int OP, int K, bool RES = false, int W = 0>
 constexpr bool shape_built() {
     constexpr int V = K * dt_info<DT>::VEC;
-    return OP == OP_LAYERNORM ? V <= 16 : V <= (RES ? 32 : 64);
+    return OP == OP_LAYERNORM ? (V <= 16 || (W == 8 && V == 32)) : V <= (RES ? 32 : 64);
 }
 
 // Norms with every parameter vector present take the specialised PR kernel;
@@ -45,7 +48,7 @@ hipError_t go(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     } else {
         const bool pr = a.p0 != nullptr && (OP == OP_RMSNORM || a.p1 != nullptr);
         if (a.r) {
-            if constexpr (shape_built<OP, K, true>())
+            if constexpr (shape_built<OP, K, true, W>())
                 return pr ? go_pr<OP, W, K, true, true>(al, a, grid, s) : go_pr<OP, W, K, false, true>(al, a, grid, s);
             return hipErrorInvalidValue;
         }
@@ -59,7 +62,7 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
     // only with one or two chunks per lane.
 #define NTK_CASE(w, k)                                          \
     if (W == w && K == k) {                                     \
-        if constexpr (shape_built<OP, k>()) return go<OP, w, k>(al, a, grid, s); \
+        if constexpr (shape_built<OP, k, false, w>()) return go<OP, w, k>(al, a, grid, s); \
         return hipErrorInvalidValue;                            \
     }
     NTK_CASE(1, 1) NTK_CASE(1, 2) NTK_CASE(1, 4) NTK_CASE(1, 8) NTK_CASE(1, 16)
@@ -123,7 +126,9 @@ template <int OP>
 hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k)                                                   \
     if (W == w && K == k) {                                              \
-        if constexpr (shape_built<OP, k>() && k * dt_info<DT>::VEC <= 32) return persist_pick<OP, w, k>(a, s); \
+        if constexpr (shape_built<OP, k, false, w>() && k * dt_info<DT>::VEC <= 32 &&                       \
+                      !(OP == OP_LAYERNORM && kWide && k * dt_info<DT>::VEC > 16))                        \
+            return persist_pick<OP, w, k>(a, s);                                                          \
         return hipErrorInvalidValue;                                     \
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)

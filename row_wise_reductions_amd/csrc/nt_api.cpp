@@ -41,9 +41,11 @@ struct Shape {
 
 // Single-pass shapes in order of capacity (64*W*K chunks of 16 bytes).  None
 // of them spills registers.  A lane holds at most 64 values of a row, and
-// LayerNorm at most 16 (its fp64 arithmetic needs more registers); wider
-// LayerNorm and RMSNorm rows take the looped kernel, wider softmax rows the
-// split path.
+// LayerNorm at most 16 (its fp64 arithmetic needs more registers) except 32
+// at 8 waves (rows of up to 16384 elements, where the looped kernel ran at
+// 0.6-0.9x torch's layer_norm; fp32 at 32 values is never persistent, which
+// would spill); wider LayerNorm and RMSNorm rows take the looped kernel, wider
+// softmax rows the split path.
 struct Menu {
     const Shape *s;
     int n;
@@ -66,16 +68,16 @@ const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 
 const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
 const Shape kRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}};
-const Shape kLn16[] = {{1, 1}, {1, 2}, {2, 2}, {4, 2}, {8, 2}};
+const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kLn16[] = {{1, 1}, {1, 2}, {2, 2}, {4, 2}, {8, 2}, {8, 4}};
 // Fused residual add + norm (two input and two output streams per row): more
 // waves per row than the plain norms at the same width.  16-bit RMSNorm rows
 // of 1025..2048 chunks take 16 waves x 2 (7% over 8 x 4); f16 LayerNorm rows
 // of up to 512 chunks 4 x 1 and 8 x 1 (3-4% over 4 x 2); fp32 RMSNorm uses
 // the plain menu (wider shapes are cut at 32 values per lane by shape_fits).
 const Shape kAddRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {16, 2}};
-const Shape kAddLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}};
-const Shape kAddLn16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}};
+const Shape kAddLn32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
+const Shape kAddLn16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {8, 4}};
 #define NT_MENU(a) Menu{a, (int)(sizeof(a) / sizeof(*(a)))}
 Menu menu_for(nt_op op, nt_dtype dt, bool res) {
     const bool wide = dt == NT_F32;
@@ -189,7 +191,7 @@ int persistent_mode() {
 //    2-8%); the fused add + RMSNorm never (its two input streams keep enough
 //    bytes in flight without it).
 bool persistent_built(nt_op op, nt_dtype dt, bool res, Shape sh) {
-    if (op == NT_OP_LAYERNORM) return true;
+    if (op == NT_OP_LAYERNORM) return !(dt == NT_F32 && sh.K * elems_per_chunk(dt) > 16);
     return !res && (dt != NT_F32 || (sh.W == 8 && sh.K == 8));
 }
 

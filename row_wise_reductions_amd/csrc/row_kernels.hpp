@@ -883,7 +883,14 @@ row_resident(RowArgs a) {
                     unpack<DT>(p1[k], bt);
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) {
-                        const double d = CACHE_D ? dp[CACHE_D ? k : 0][CACHE_D ? i : 0] : (double)v[k][i] - pv;
+                        double d;
+                        if constexpr (CACHE_D) {
+                            d = dp[CACHE_D ? k : 0][CACHE_D ? i : 0];
+                        } else {
+                            float x = v[k][i];
+                            asm volatile("" : "+v"(x));  // recompute, no fp64 copy of the row kept
+                            d = (double)x - pv;
+                        }
                         v[k][i] = (float)__builtin_fma(__builtin_fma(d, rstd, nm), (double)gm[i], (double)bt[i]);
                     }
                     store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v[k]));
@@ -896,7 +903,14 @@ row_resident(RowArgs a) {
                     if (has_p1) unpack<DT>(p1[k], bt);
 #pragma unroll
                     for (int i = 0; i < VEC; ++i) {
-                        const double d = CACHE_D ? dp[CACHE_D ? k : 0][CACHE_D ? i : 0] : (double)v[k][i] - pv;
+                        double d;
+                        if constexpr (CACHE_D) {
+                            d = dp[CACHE_D ? k : 0][CACHE_D ? i : 0];
+                        } else {
+                            float x = v[k][i];
+                            asm volatile("" : "+v"(x));
+                            d = (double)x - pv;
+                        }
                         const double g = has_p0 ? (double)gm[i] : 1.0;
                         const double b = has_p1 ? (double)bt[i] : 0.0;
                         v[k][i] = (float)__builtin_fma(__builtin_fma(d, rstd, nm), g, b);
@@ -939,9 +953,15 @@ row_norm_persistent(RowArgs a) {
     if (row >= a.M) return;
     const RowGeom<DT, true> geo(a.x, N);     // every row has the same chunk geometry
 
-    // ---- parameters, widened once per workgroup
-    double g64[LN ? K : 1][LN ? VEC : 1], b64[LN ? K : 1][LN ? VEC : 1];
-    float w32[LN ? 1 : K][LN ? 1 : VEC];
+    // ---- parameters, widened once per workgroup.  LayerNorm with 32 values
+    // per lane keeps gamma, beta as fp32 (widened to fp64 at use: exact) and
+    // recomputes x - p in the epilogue, so the row, its successor and the
+    // parameters fit a 512-thread workgroup's registers; the values are the
+    // same either way.
+    constexpr bool LN_WIDE = LN && K * VEC > 16;
+    constexpr bool LN_D = LN && !LN_WIDE;
+    double g64[LN_D ? K : 1][LN_D ? VEC : 1], b64[LN_D ? K : 1][LN_D ? VEC : 1];
+    float w32[LN_D ? 1 : K][LN_D ? 1 : VEC], b32[LN_WIDE ? K : 1][LN_WIDE ? VEC : 1];
     {
         uint4 p0[K], p1[LN ? K : 1];
         load_params<DT, true, K, TPR>(p0, geo, a.p0, t, N);
@@ -950,7 +970,7 @@ row_norm_persistent(RowArgs a) {
         for (int k = 0; k < K; ++k) {
             float g[VEC], b[VEC];
             unpack<DT>(p0[k], g);
-            if constexpr (LN) {
+            if constexpr (LN_D) {
                 unpack<DT>(p1[k], b);
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
@@ -960,6 +980,11 @@ row_norm_persistent(RowArgs a) {
             } else {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) w32[k][i] = g[i];
+                if constexpr (LN_WIDE) {
+                    unpack<DT>(p1[k], b);
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) b32[k][i] = b[i];
+                }
             }
         }
     }
@@ -1001,14 +1026,15 @@ row_norm_persistent(RowArgs a) {
         if constexpr (LN) {
             const double pv = (double)elem_of_word<DT>(pw);
             double s1 = 0.0, s2 = 0.0;
-            double dp[K][VEC];
+            double dp[LN_D ? K : 1][LN_D ? VEC : 1];
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    dp[k][i] = (double)v[k][i] - pv;        // padding holds p: 0
-                    s1 += dp[k][i];
-                    s2 = __builtin_fma(dp[k][i], dp[k][i], s2);
+                    const double d = (double)v[k][i] - pv;  // padding holds p: 0
+                    if constexpr (LN_D) dp[LN_D ? k : 0][LN_D ? i : 0] = d;
+                    s1 += d;
+                    s2 = __builtin_fma(d, d, s2);
                 }
             const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red_d2[par], wv, lane);
             const double m1 = st.x * a.inv_nd;
@@ -1019,8 +1045,17 @@ row_norm_persistent(RowArgs a) {
             for (int k = 0; k < K; ++k) {
                 float o[VEC];
 #pragma unroll
-                for (int i = 0; i < VEC; ++i)
-                    o[i] = (float)__builtin_fma(__builtin_fma(dp[k][i], rstd, nm), g64[k][i], b64[k][i]);
+                for (int i = 0; i < VEC; ++i) {
+                    if constexpr (LN_D) {
+                        o[i] = (float)__builtin_fma(__builtin_fma(dp[k][i], rstd, nm), g64[k][i], b64[k][i]);
+                    } else {
+                        float x = v[k][i];
+                        asm volatile("" : "+v"(x));      // recompute x - p, no copy of the first pass's
+                        const double d = (double)x - pv;
+                        o[i] = (float)__builtin_fma(__builtin_fma(d, rstd, nm), (double)w32[k][i],
+                                                    (double)b32[LN_WIDE ? k : 0][LN_WIDE ? i : 0]);
+                    }
+                }
                 store_slice<DT, true, TPR>(g, yr, k, t, N, true, pack<DT>(o));
             }
             if (t == 0) {

@@ -190,10 +190,20 @@ def test_plan_capacity_covers_row():
 
 
 def test_wide_rows_take_the_streaming_paths():
-    # LayerNorm holds at most 16 values per lane: 16 KiB of 16-bit row
-    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 8192, BF16, True)["split"] == 0
-    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 8193, BF16, True)
+    # LayerNorm holds at most 16 values per lane, 32 at 8 waves: 32 KiB of
+    # 16-bit row, 64 KiB of fp32 row in one pass
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16384, BF16, True)["split"] == 0
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, BF16, True)      # 1025 whole chunks
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 8, 4, 1)
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8193, BF16, True)["waves_per_row"] == 8
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16385, BF16, True)
     assert p["split"] == 2 and p["grid"] == 1 and p["threads_per_block"] == 512
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, F32, True)       # fp32 8 x 8: one row per workgroup
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 8, 8, 0)
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16384, F32, True)["split"] == 0
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16385, F32, True)["split"] == 2
+    assert nt.nt_plan_launch(nt.NT_OP_ADD_LAYERNORM, 1, 16384, F16, True)["split"] == 0
+    assert nt.nt_plan_launch(nt.NT_OP_ADD_LAYERNORM, 1, 16385, F16, True)["split"] == 2
     # RMSNorm fp32 up to 128 KiB single pass, then looped
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 7, 32768, F32, True)["split"] == 0
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 7, 32769, F32, True)
