@@ -505,6 +505,115 @@ def op_sweep(torch, dt, steps, warmup, md_path=None):
             f.write("\n".join(lines))
 
 
+WIDE_NORM_CASES = (("bf16", 32768), ("bf16", 262144), ("bf16", 1 << 20), ("f32", 65536), ("f32", 262144))
+WIDE_NORM_M = (4, 16, 64, 256, 1024, 2048)
+
+
+def wide_norm_sweep(torch, steps, warmup, md_path=None):
+    """LayerNorm and RMSNorm on rows too wide for one pass (64 KiB to 2 MiB),
+    few to many rows: the split norm (the workspace entry points, split
+    forced at every row count), the looped one-workgroup-per-row kernel (the
+    plain entry points) and torch (F.layer_norm, F.rms_norm), on the same
+    buffers, rotating through a 1 GiB pool.  GB/s = algorithmic bytes (rows
+    in and out, parameter vectors, LayerNorm's mean and rstd) / median
+    event-timed launch.  `plan` is what the workspace entry point picks by
+    itself at that row count."""
+    import torch.nn.functional as F
+
+    import row_wise_reductions_amd as nt
+
+    def timed(fn, R):
+        warm_up(lambda: fn(0), warmup, 20.0, torch)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, bb) in enumerate(evs):
+            a.record()
+            fn(i % R)
+            bb.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(bb) for a, bb in evs)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(nt.nt_status_string(rc))
+
+    sh = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    rows = []
+    for dt, N in WIDE_NORM_CASES:
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dt]
+        code = {"f32": nt.NT_F32, "bf16": nt.NT_BF16}[dt]
+        e = 4 if dt == "f32" else 2
+        pool = (1 << 30) // e
+        px = torch.randn(pool, device="cuda", generator=gen).to(tdt)
+        py = torch.empty(pool, device="cuda", dtype=tdt)
+        g = (torch.randn(N, device="cuda", generator=gen) * 0.3 + 1.0).to(tdt)
+        b = (torch.randn(N, device="cuda", generator=gen) * 0.3).to(tdt)
+        for M in WIDE_NORM_M:
+            n = M * N
+            if n > pool:
+                continue
+            R = pool // n
+            xs = [px[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+            ys = [py[i * n:(i + 1) * n].view(M, N) for i in range(R)]
+            mean = torch.empty(M, device="cuda")
+            rstd = torch.empty(M, device="cuda")
+            r = {"dt": dt, "N": N, "M": M}
+            for op, opc in (("layernorm", nt.NT_OP_LAYERNORM), ("rmsnorm", nt.NT_OP_RMSNORM)):
+                wop = nt.NT_OP_LAYERNORM_WS if op == "layernorm" else nt.NT_OP_RMSNORM_WS
+                p = nt.nt_plan_launch(wop, M, N, code, True)
+                r[op + "_plan"] = "split" if p["split"] == 3 else "looped"
+                os.environ["NT_NORM_SPLIT_ROWS"] = str(1 << 40)
+                try:
+                    wsb = nt.nt_norm_workspace_bytes(opc, M, N, code)
+                    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
+                    if op == "layernorm":
+                        split = lambda i: ok(nt.nt_layernorm_rows_ws(  # noqa: E731
+                            M, N, code, 1e-5, xs[i].data_ptr(), g.data_ptr(), b.data_ptr(), ys[i].data_ptr(),
+                            mean.data_ptr(), rstd.data_ptr(), ws.data_ptr(), wsb, sh))
+                    else:
+                        split = lambda i: ok(nt.nt_rmsnorm_rows_ws(  # noqa: E731
+                            M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), ws.data_ptr(),
+                            wsb, sh))
+                    ms_split = timed(split, R)
+                finally:
+                    del os.environ["NT_NORM_SPLIT_ROWS"]
+                if op == "layernorm":
+                    looped = lambda i: ok(nt.nt_layernorm_rows(  # noqa: E731
+                        M, N, code, 1e-5, xs[i].data_ptr(), g.data_ptr(), b.data_ptr(), ys[i].data_ptr(),
+                        mean.data_ptr(), rstd.data_ptr(), sh))
+                    theirs = lambda i: F.layer_norm(xs[i], (N,), g, b, 1e-5)  # noqa: E731
+                    gb = 2 * n * e + 2 * N * e + 8 * M
+                else:
+                    looped = lambda i: ok(nt.nt_rmsnorm_rows(  # noqa: E731
+                        M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), sh))
+                    theirs = lambda i: F.rms_norm(xs[i], (N,), g, 1e-6)  # noqa: E731
+                    gb = 2 * n * e + N * e
+                for k, ms in (("split", ms_split), ("looped", timed(looped, R)), ("torch", timed(theirs, R))):
+                    r[f"{op}_{k}_us"] = round(ms * 1e3, 1)
+                    r[f"{op}_{k}_GBps"] = round(gb / (ms * 1e-3) / 1e9, 1)
+            rows.append(r)
+            log(f"[wide norms] {dt} N={N} M={M}: " + ", ".join(f"{k} {v}" for k, v in r.items() if k.endswith("GBps")))
+        del px, py
+    print(json.dumps({"wide_norm_sweep": "LayerNorm / RMSNorm, rows of 64 KiB to 2 MiB", "points": rows}), flush=True)
+    if md_path:
+        lines = ["# Wide-row norms: split vs looped vs torch", "", "Command (repository root, GPU host):", "",
+                 f"    python3 bench.py --sweep-wide-norms --steps {steps} --warmup {warmup} --sweep-md {md_path}", "",
+                 "GB/s = algorithmic bytes (rows in and out, parameter vectors, LayerNorm's mean and rstd) / median "
+                 "event-timed launch, inputs rotating through a 1 GiB pool.  split: nt_*_rows_ws with the split "
+                 "forced at every row count (two kernels, the row's chunks on many workgroups); looped: the plain "
+                 "entry point (one workgroup per row, the row streamed twice); torch: F.layer_norm / F.rms_norm on "
+                 "the same buffers.  plan: what nt_*_rows_ws picks by itself.", "",
+                 "| type | N | M | LN plan | LN split | LN looped | LN torch | RMS plan | RMS split | RMS looped | "
+                 "RMS torch |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['dt']} | {r['N']} | {r['M']} | {r['layernorm_plan']} | {r['layernorm_split_GBps']} | "
+                         f"{r['layernorm_looped_GBps']} | {r['layernorm_torch_GBps']} | {r['rmsnorm_plan']} | "
+                         f"{r['rmsnorm_split_GBps']} | {r['rmsnorm_looped_GBps']} | {r['rmsnorm_torch_GBps']} |")
+        lines.append("")
+        with open(md_path, "w") as f:
+            f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -522,7 +631,9 @@ def main():
                     help="time the plain 1 GiB streaming copy (and torch copy_) instead")
     ap.add_argument("--sweep", action="store_true",
                     help="fp32 softmax / RMSNorm over the pages' benchmark widths (M=4096, N=128 i), vs torch")
-    ap.add_argument("--sweep-md", default=None, help="with --sweep: also write a markdown summary here")
+    ap.add_argument("--sweep-wide-norms", dest="sweep_wide_norms", action="store_true",
+                    help="LayerNorm / RMSNorm on rows of 64 KiB to 2 MiB: split vs looped vs torch")
+    ap.add_argument("--sweep-md", default=None, help="with a sweep: also write a markdown summary here")
     ap.add_argument("--copy-at-sizes", action="store_true",
                     help="time the plain streaming copy at each workload's byte count instead")
     args = ap.parse_args()
@@ -547,6 +658,9 @@ def main():
         return
     if args.sweep_ops:
         op_sweep(torch, args.sweep_ops, args.steps, args.warmup, args.sweep_md)
+        return
+    if args.sweep_wide_norms:
+        wide_norm_sweep(torch, args.steps, args.warmup, args.sweep_md)
         return
     if args.copy_at_sizes:
         names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]

@@ -79,7 +79,8 @@ typedef enum {
     NT_ERR_DTYPE = 3,      /* dt is not one of nt_dtype                        */
     NT_ERR_EPS = 4,        /* eps is negative, infinite or NaN                 */
     NT_ERR_ALIGN = 5,      /* a pointer is not aligned to its element size     */
-    NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes */
+    NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes
+                              (or nt_norm_workspace_bytes)                    */
     NT_ERR_HIP = 7,        /* the HIP runtime reported a launch error          */
     NT_ERR_ALIAS = 8,      /* fused add + norm: h and y are the same buffer    */
     NT_ERR_SCALE = 9       /* causal softmax: scale is not finite and > 0      */
@@ -158,6 +159,44 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
                           void *stream);
 
 /*
+ * The norms with a workspace, for a few rows too wide for one pass.  There
+ * the plain entry points stream each row with one workgroup, so M rows keep
+ * at most M compute units busy.  With a workspace the row is cut into
+ * chunks, one workgroup each: a first kernel writes every chunk's partial
+ * sums (LayerNorm: sum(x - p) and sum((x - p)^2) around the row's first
+ * element p, RMSNorm: sum(x^2); in fp64) to the workspace, a second combines
+ * a row's partial sums in a fixed order and writes the chunk's outputs,
+ * reading x a second time.  The statistics are those of the definitions
+ * above, summed in another order than the one-workgroup kernels' (results
+ * within the same tolerances, not necessarily bitwise equal to them;
+ * repeated calls are bitwise equal).  This is the split softmax's scheme
+ * ("How Flash Attention Uses Triton") applied to the norms' sums.
+ *
+ * nt_norm_workspace_bytes(op, M, N, dt): bytes the split needs (16 per row
+ * chunk, 8 per row) for op NT_OP_LAYERNORM or NT_OP_RMSNORM, 0 when the plain plan is
+ * used (rows that fit one pass, or enough rows to fill the GPU) or for
+ * invalid arguments.
+ *
+ * nt_layernorm_rows_ws / nt_rmsnorm_rows_ws take the plain entry points'
+ * arguments, with their conventions and checks, plus `workspace` and
+ * `workspace_bytes`: NULL runs the plain plan; otherwise workspace must be
+ * 8-byte aligned (NT_ERR_ALIGN) and hold nt_norm_workspace_bytes(op, M, N, dt)
+ * bytes (NT_ERR_WORKSPACE).  Contents need not be initialized; two calls in
+ * flight at once must not share a workspace, which must not overlap x, y or
+ * the parameters.  In place (y == x) is allowed.
+ */
+size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt);
+
+nt_status nt_layernorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps,
+                               const void *x, const void *gamma, const void *beta,
+                               void *y, float *mean, float *rstd,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+nt_status nt_rmsnorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps,
+                             const void *x, const void *weight, void *y,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Fused residual add + norm: the step right before a norm in a residual
  * block, in one pass.  h = x + residual, rounded once to `dt` (the updated
  * residual stream), and the norm of that stored h:
@@ -206,13 +245,16 @@ typedef enum {
     NT_OP_RMSNORM = 2,
     NT_OP_ADD_LAYERNORM = 3,  /* nt_add_layernorm_rows */
     NT_OP_ADD_RMSNORM = 4,    /* nt_add_rmsnorm_rows   */
-    NT_OP_SOFTMAX_CAUSAL = 5  /* nt_softmax_causal_rows */
+    NT_OP_SOFTMAX_CAUSAL = 5, /* nt_softmax_causal_rows */
+    NT_OP_LAYERNORM_WS = 6,   /* nt_layernorm_rows_ws with a workspace */
+    NT_OP_RMSNORM_WS = 7      /* nt_rmsnorm_rows_ws with a workspace   */
 } nt_op;
 
 typedef struct {
     int32_t split;            /* 0: single pass, row held on chip; 1: split online softmax
                                  (per-chunk workgroups and a workspace); 2: looped norm
-                                 kernel (one workgroup streams a wide row twice)          */
+                                 kernel (one workgroup streams a wide row twice); 3: split
+                                 norm (per-chunk workgroups, partial sums in a workspace) */
     int32_t waves_per_row;    /* 64-lane waves cooperating on one row (or one chunk)    */
     int32_t chunks_per_lane;  /* 16-byte chunks each lane holds                         */
     int32_t rows_per_block;   /* rows one workgroup processes side by side              */
@@ -227,8 +269,8 @@ typedef struct {
                                  In-place calls (y == x) and calls during stream capture
                                  always use the two kernels                             */
     int64_t grid;             /* workgroups per launch                                  */
-    int64_t row_chunks;       /* split path: chunks per row (0 on the single pass)      */
-    int64_t workspace_bytes;  /* split path: workspace size (0 on the single pass)      */
+    int64_t row_chunks;       /* split paths: chunks per row (0 otherwise)              */
+    int64_t workspace_bytes;  /* split paths: workspace size (0 otherwise)              */
 } nt_plan;
 
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt,

@@ -23,11 +23,14 @@ LIB_PATH = os.path.join(_HERE, "libnt.so")
 NT_F32, NT_F16, NT_BF16 = 0, 1, 2
 NT_OP_SOFTMAX, NT_OP_LAYERNORM, NT_OP_RMSNORM, NT_OP_ADD_LAYERNORM, NT_OP_ADD_RMSNORM = 0, 1, 2, 3, 4
 NT_OP_SOFTMAX_CAUSAL = 5
+NT_OP_LAYERNORM_WS = 6
+NT_OP_RMSNORM_WS = 7
 STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4: "NT_ERR_EPS",
           5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP", 8: "NT_ERR_ALIAS",
           9: "NT_ERR_SCALE"}
 EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows",
-            "nt_rmsnorm_rows", "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
+            "nt_rmsnorm_rows", "nt_norm_workspace_bytes", "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws",
+            "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
             "nt_status_string", "nt_plan_launch")
 
 
@@ -68,13 +71,17 @@ def lib():
     L.nt_softmax_causal_rows.argtypes = [i64, i64, i32, f32, i64, i64, vp, vp, vp, sz, vp]
     L.nt_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     L.nt_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp]
+    L.nt_norm_workspace_bytes.argtypes = [i32, i64, i64, i32]
+    L.nt_norm_workspace_bytes.restype = sz
+    L.nt_layernorm_rows_ws.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.nt_rmsnorm_rows_ws.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, sz, vp]
     L.nt_add_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.nt_add_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp]
     L.nt_status_string.argtypes = [i32]
     L.nt_status_string.restype = ctypes.c_char_p
     L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
     for f in ("nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
-              "nt_add_layernorm_rows",
+              "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws", "nt_add_layernorm_rows",
               "nt_add_rmsnorm_rows", "nt_plan_launch"):
         getattr(L, f).restype = i32
     _lib = L
@@ -102,6 +109,19 @@ def nt_layernorm_rows(M, N, dt, eps, x, gamma, beta, y, mean, rstd, stream) -> i
 
 def nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream) -> int:
     return int(lib().nt_rmsnorm_rows(M, N, dt, eps, x, weight, y, stream))
+
+
+def nt_norm_workspace_bytes(op: int, M: int, N: int, dt: int) -> int:
+    return int(lib().nt_norm_workspace_bytes(op, M, N, dt))
+
+
+def nt_layernorm_rows_ws(M, N, dt, eps, x, gamma, beta, y, mean, rstd, workspace, workspace_bytes, stream) -> int:
+    return int(lib().nt_layernorm_rows_ws(M, N, dt, eps, x, gamma, beta, y, mean, rstd, workspace, workspace_bytes,
+                                          stream))
+
+
+def nt_rmsnorm_rows_ws(M, N, dt, eps, x, weight, y, workspace, workspace_bytes, stream) -> int:
+    return int(lib().nt_rmsnorm_rows_ws(M, N, dt, eps, x, weight, y, workspace, workspace_bytes, stream))
 
 
 def nt_add_layernorm_rows(M, N, dt, eps, x, residual, gamma, beta, h, y, mean, rstd, stream) -> int:
@@ -211,8 +231,11 @@ def layer_norm(x, gamma=None, beta=None, eps=1e-5, out=None, stream=None):
     for p in (gamma, beta):
         if p is not None and (p.numel() != N or p.dtype != x.dtype or not p.is_contiguous()):
             raise ValueError("gamma/beta must be contiguous, of x's dtype, with N entries")
-    _check(nt_layernorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(gamma), _ptr(beta),
-                             _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream)), "nt_layernorm_rows")
+    dt = dtype_code(x)
+    wsb = nt_norm_workspace_bytes(NT_OP_LAYERNORM, M, N, dt)     # a few rows too wide for one pass
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    _check(nt_layernorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean),
+                                _ptr(rstd), _ptr(ws), wsb, _stream(stream)), "nt_layernorm_rows_ws")
     return y, mean, rstd
 
 
@@ -223,8 +246,11 @@ def rms_norm(x, weight=None, eps=1e-6, out=None, stream=None):
     y = torch.empty_like(x) if out is None else out
     if weight is not None and (weight.numel() != N or weight.dtype != x.dtype or not weight.is_contiguous()):
         raise ValueError("weight must be contiguous, of x's dtype, with N entries")
-    _check(nt_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(weight), _ptr(y),
-                           _stream(stream)), "nt_rmsnorm_rows")
+    dt = dtype_code(x)
+    wsb = nt_norm_workspace_bytes(NT_OP_RMSNORM, M, N, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+    _check(nt_rmsnorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(weight), _ptr(y), _ptr(ws), wsb,
+                              _stream(stream)), "nt_rmsnorm_rows_ws")
     return y
 
 

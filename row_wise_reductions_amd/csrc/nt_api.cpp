@@ -103,6 +103,17 @@ const Shape kSplitCoop16 = {4, 8};
 const Shape kSplitWide = {4, 4};
 // Looped norm kernel: 512 threads, tiles of 4 chunks per lane.
 const Shape kLooped = {8, 4};
+// Split norm chunk shapes, largest first: the first that gives the call at
+// least kNormSplitGrid workgroups is used (8 per CU on 256 CUs).
+const Shape kNormSplit[] = {{8, 4}, {8, 1}, {4, 1}};
+constexpr int64_t kNormSplitGrid = 2048;
+// Rows below which the split is used.  The looped kernel gives each row one
+// workgroup, so it fills the 256 CUs from 256 rows on; measured on MI355X
+// (rows of 64 KiB to 2 MiB), the split is 2-7x faster below 64 rows, even at
+// 256, and from there on 0-8% faster for RMSNorm but up to 8% slower for
+// LayerNorm, whose finalize kernel holds the parameters as well.
+constexpr int64_t kNormSplitRowsLN = 256;
+constexpr int64_t kNormSplitRowsRMS = 2048;
 
 int elem_bytes(nt_dtype dt) { return dt == NT_F32 ? 4 : 2; }
 int elems_per_chunk(nt_dtype dt) { return 16 / elem_bytes(dt); }
@@ -169,6 +180,17 @@ int64_t row_chunks(int64_t N, nt_dtype dt, bool aligned) {
     return (N + vec - 1 + vec - 1) / vec;
 }
 
+// Rows below which a norm too wide for one pass is split over workgroups
+// (given a workspace); NT_NORM_SPLIT_ROWS overrides (tuning).
+int64_t norm_split_rows(nt_op op) {
+    const char *s = std::getenv("NT_NORM_SPLIT_ROWS");
+    if (s && *s) {
+        const long long v = std::atoll(s);
+        if (v >= 0) return v;
+    }
+    return op == NT_OP_LAYERNORM ? kNormSplitRowsLN : kNormSplitRowsRMS;
+}
+
 // Persistent norm kernels: NT_PERSISTENT=0 never, "always" wherever the
 // kernel is built (tuning), else where it pays (persistent_pays).
 int persistent_mode() {
@@ -215,7 +237,7 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
 }
 
 nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true,
-                    bool res = false, bool causal = false) {
+                    bool res = false, bool causal = false, bool norm_split = false) {
     std::memset(p, 0, sizeof *p);
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
@@ -262,6 +284,27 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
             pick.K * elems_per_chunk(dt) <= 32 && persistent_built(op, dt, res, pick) &&
             (persistent_mode() == 2 || (persistent_mode() == 1 && persistent_pays(op, dt, res, pick, nch))))
             p->persistent = 1;
+        return NT_OK;
+    }
+    if (op != NT_OP_SOFTMAX && norm_split && !res && M < norm_split_rows(op)) {
+        // few wide rows: each row cut into chunks, one workgroup each
+        Shape s = kNormSplit[0];
+        int64_t P = 0;
+        for (const Shape &c : kNormSplit) {
+            s = c;
+            const int64_t per = (int64_t)64 * c.W * c.K;
+            P = (nch + per - 1) / per;
+            if (M * P >= kNormSplitGrid) break;
+        }
+        if (P > INT32_MAX || (M > 0 && P > (((int64_t)1 << 31) / (64 * s.W)) / M)) return NT_ERR_SHAPE;
+        p->split = 3;
+        p->waves_per_row = s.W;
+        p->chunks_per_lane = s.K;
+        p->rows_per_block = 1;
+        p->threads_per_block = 64 * s.W;
+        p->row_chunks = P;
+        p->grid = M * P;
+        p->workspace_bytes = M * P * 16 + M * 8;     // (s1, s2) per chunk, then a pivot per row
         return NT_OK;
     }
     if (op != NT_OP_SOFTMAX) {
@@ -341,11 +384,22 @@ hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hi
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_norm_split(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
+    const bool al = p.aligned != 0;
+    switch (dt) {
+    case NT_F32: return ntk::launch_norm_split_f32(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_F16: return ntk::launch_norm_split_f16(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_BF16: return ntk::launch_norm_split_bf16(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 void debug_print(const char *what, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p) {
     std::fprintf(stderr,
                  "[nt] %s M=%lld N=%lld dt=%d: path %s W=%d K=%d rows/block=%d threads=%d aligned=%d"
                  " persistent=%d cooperative=%d grid=%lld chunks/row=%lld ws=%lld\n",
-                 what, (long long)M, (long long)N, (int)dt, p.split == 1 ? "split" : p.split == 2 ? "looped" : "single-pass", p.waves_per_row,
+                 what, (long long)M, (long long)N, (int)dt,
+                 p.split == 1 ? "split" : p.split == 2 ? "looped" : p.split == 3 ? "split norm" : "single-pass", p.waves_per_row,
                  p.chunks_per_lane, p.rows_per_block, p.threads_per_block, p.aligned, p.persistent, p.cooperative, (long long)p.grid,
                  (long long)p.row_chunks, (long long)p.workspace_bytes);
 }
@@ -362,6 +416,7 @@ nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, con
     const int kop = (op == NT_OP_SOFTMAX && a.queries > 0) ? (int)ntk::OP_SOFTMAX_CAUSAL : (int)op;
     hipError_t e = p.split == 1   ? launch_split(dt, p, a, s)
                    : p.split == 2 ? launch_looped(dt, kop, p, a, s)
+                   : p.split == 3 ? launch_norm_split(dt, kop, p, a, s)
                                   : launch_resident(dt, kop, p, a, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -407,17 +462,18 @@ const char *nt_status_string(nt_status s) {
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt, int aligned16, nt_plan *out) {
     if (!out) return NT_ERR_NULL;
     if (op != NT_OP_SOFTMAX && op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM && op != NT_OP_ADD_LAYERNORM &&
-        op != NT_OP_ADD_RMSNORM && op != NT_OP_SOFTMAX_CAUSAL)
+        op != NT_OP_ADD_RMSNORM && op != NT_OP_SOFTMAX_CAUSAL && op != NT_OP_LAYERNORM_WS && op != NT_OP_RMSNORM_WS)
         return NT_ERR_SHAPE;
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
     const bool al = aligned16 && (N * elem_bytes(dt)) % 16 == 0;
     const bool res = op == NT_OP_ADD_LAYERNORM || op == NT_OP_ADD_RMSNORM;
-    const nt_op base = op == NT_OP_ADD_LAYERNORM   ? NT_OP_LAYERNORM
-                       : op == NT_OP_ADD_RMSNORM   ? NT_OP_RMSNORM
-                       : op == NT_OP_SOFTMAX_CAUSAL ? NT_OP_SOFTMAX
-                                                    : op;
-    return make_plan(base, M, N, dt, al, out, true, res, op == NT_OP_SOFTMAX_CAUSAL);
+    const bool ws = op == NT_OP_LAYERNORM_WS || op == NT_OP_RMSNORM_WS;
+    const nt_op base = (op == NT_OP_ADD_LAYERNORM || op == NT_OP_LAYERNORM_WS) ? NT_OP_LAYERNORM
+                       : (op == NT_OP_ADD_RMSNORM || op == NT_OP_RMSNORM_WS) ? NT_OP_RMSNORM
+                       : op == NT_OP_SOFTMAX_CAUSAL                         ? NT_OP_SOFTMAX
+                                                                             : op;
+    return make_plan(base, M, N, dt, al, out, true, res, op == NT_OP_SOFTMAX_CAUSAL, ws);
 }
 
 size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt) {
@@ -496,8 +552,23 @@ nt_status nt_softmax_causal_rows(int64_t M, int64_t N, nt_dtype dt, float scale,
     return softmax_launch(M, N, dt, x, y, workspace, workspace_bytes, stream, a);
 }
 
-nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,
-                            const void *beta, void *y, float *mean, float *rstd, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Workspace of a split-norm plan, or an error status before anything is
+// launched; a NULL workspace selected the plain plan already.
+nt_status attach_workspace(const nt_plan &p, void *ws, size_t wsb, ntk::RowArgs &a) {
+    if (p.split != 3) return NT_OK;
+    if (wsb < (size_t)p.workspace_bytes) return NT_ERR_WORKSPACE;
+    if (!aligned_to(ws, 8)) return NT_ERR_ALIGN;
+    a.P = (int32_t)p.row_chunks;
+    a.wsd = static_cast<double *>(ws);
+    return NT_OK;
+}
+
+nt_status layernorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,
+                         const void *beta, void *y, float *mean, float *rstd, void *ws, size_t wsb, void *stream) {
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
     if (!valid_eps(eps)) return NT_ERR_EPS;
@@ -509,9 +580,12 @@ nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const 
         return NT_ERR_ALIGN;
     const bool al = all_aligned16(N, dt, x, y, gamma, beta);
     nt_plan p;
-    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p, gamma != nullptr && beta != nullptr);
+    st = make_plan(NT_OP_LAYERNORM, M, N, dt, al, &p, gamma != nullptr && beta != nullptr, false, false,
+                   ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
+    st = attach_workspace(p, ws, wsb, a);
+    if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
     a.p0 = static_cast<const char *>(gamma);
@@ -526,8 +600,8 @@ nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const 
     return run(NT_OP_LAYERNORM, M, N, dt, p, a, stream);
 }
 
-nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *weight, void *y,
-                          void *stream) {
+nt_status rmsnorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *weight, void *y,
+                       void *ws, size_t wsb, void *stream) {
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
     if (!valid_eps(eps)) return NT_ERR_EPS;
@@ -536,9 +610,11 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const vo
     if (weight && !aligned_to(weight, (uintptr_t)elem_bytes(dt))) return NT_ERR_ALIGN;
     const bool al = all_aligned16(N, dt, x, y, weight, nullptr);
     nt_plan p;
-    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr);
+    st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr, false, false, ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
+    st = attach_workspace(p, ws, wsb, a);
+    if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
     a.p0 = static_cast<const char *>(weight);
@@ -548,6 +624,44 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const vo
     a.inv_nd = 1.0 / (double)N;
     a.eps = eps;
     return run(NT_OP_RMSNORM, M, N, dt, p, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+nt_status nt_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,
+                            const void *beta, void *y, float *mean, float *rstd, void *stream) {
+    return layernorm_impl(M, N, dt, eps, x, gamma, beta, y, mean, rstd, nullptr, 0, stream);
+}
+
+nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *weight, void *y,
+                          void *stream) {
+    return rmsnorm_impl(M, N, dt, eps, x, weight, y, nullptr, 0, stream);
+}
+
+size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt) {
+    if ((op != NT_OP_LAYERNORM && op != NT_OP_RMSNORM) || !valid_dtype(dt) || !valid_shape(M, N)) return 0;
+    size_t need = 0;
+    for (const bool al : {true, false}) {      // the larger of the two alignments' plans
+        nt_plan p;
+        if (make_plan((nt_op)op, M, N, dt, al && (N * elem_bytes(dt)) % 16 == 0, &p, true, false, false, true) ==
+                NT_OK &&
+            (size_t)p.workspace_bytes > need)
+            need = (size_t)p.workspace_bytes;
+    }
+    return need;
+}
+
+nt_status nt_layernorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *gamma,
+                               const void *beta, void *y, float *mean, float *rstd, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return layernorm_impl(M, N, dt, eps, x, gamma, beta, y, mean, rstd, workspace, workspace_bytes, stream);
+}
+
+nt_status nt_rmsnorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps, const void *x, const void *weight,
+                             void *y, void *workspace, size_t workspace_bytes, void *stream) {
+    return rmsnorm_impl(M, N, dt, eps, x, weight, y, workspace, workspace_bytes, stream);
 }
 
 // Checks of the fused add + norm entry points beyond common_checks: the

@@ -70,6 +70,7 @@ struct RowArgs {
     float *mean;         // LayerNorm statistics outputs; may be null
     float *rstd;
     float2 *ws;          // split softmax: (max, denominator) per (row, chunk)
+    double *wsd;         // split norm: (sum(x - p), sum((x - p)^2)) per (row, chunk)
     double inv_nd;       // 1/N in fp64
     int64_t M;
     int32_t N;
@@ -1198,6 +1199,134 @@ row_looped(RowArgs a) {
                 store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), tl * TILE);
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split norm, for a few rows too wide for one pass: workgroup b handles chunk
+// j = b mod P of row r = b / P (64*W*K 16-byte pieces, as in the split
+// softmax), so the row's chunks run on many CUs instead of one.  The partial
+// kernel writes each chunk's (sum(x - p), sum((x - p)^2)) in fp64 around the
+// row's first element p (RMSNorm: p = 0) to the workspace; the finalize
+// kernel sums the row's P pairs in a fixed order (lane l takes pairs l,
+// l + 64, ..., then the wave's fixed reduction), so every workgroup of the
+// row derives the same statistics, and writes its chunk's outputs, reading
+// the chunk again (usually from the Infinity Cache).  Workspace: M*P pairs,
+// then the M pivots (the finalize kernel takes p from there: in place,
+// workgroup 0 of the row overwrites the row's first element).
+// ---------------------------------------------------------------------------
+
+template <int OP, int DT, int W, int K, bool AL>
+__global__ void __launch_bounds__(64 * W)
+norm_split_partial(RowArgs a) {
+    static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "split norm");
+    using I = dt_info<DT>;
+    constexpr int VEC = I::VEC, TPR = 64 * W;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N, P = a.P;
+    const int64_t row = blockIdx.x / P;
+    const int64_t j = blockIdx.x - row * P;
+    const char *xr = a.x + row * (int64_t)N * I::E;
+    const RowGeom<DT, AL> geo(xr, N);
+    __shared__ double2 red[W];
+
+    const int64_t cbase = j * (int64_t)(TPR * K);
+    uint32_t padw = 0;
+    if constexpr (OP == OP_LAYERNORM) padw = pivot_word<DT>(xr);
+    const double pv = (double)elem_of_word<DT>(padw);
+    uint4 raw[K];
+    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, cbase);
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v[VEC];
+        unpack<DT>(raw[k], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const double d = (double)v[i] - pv;          // padding gives 0
+            if constexpr (OP == OP_LAYERNORM) s1 += d;
+            s2 = __builtin_fma(d, d, s2);
+        }
+    }
+    const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red, wv, lane);
+    if (t == 0) {
+        double *w = a.wsd + 2 * (row * P + j);
+        w[0] = st.x;
+        w[1] = st.y;
+        if (j == 0) a.wsd[2 * a.M * P + row] = pv;
+    }
+}
+
+template <int OP, int DT, int W, int K, bool AL>
+__global__ void __launch_bounds__(64 * W)
+norm_split_finalize(RowArgs a) {
+    static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "split norm");
+    using I = dt_info<DT>;
+    constexpr int VEC = I::VEC, TPR = 64 * W;
+    const int t = threadIdx.x, lane = t & 63;
+    const int32_t N = a.N, P = a.P;
+    const int64_t row = blockIdx.x / P;
+    const int64_t j = blockIdx.x - row * P;
+    const int64_t rowbytes = (int64_t)N * I::E;
+    const char *xr = a.x + row * rowbytes;
+    char *yr = a.y + row * rowbytes;
+    const RowGeom<DT, AL> geo(xr, N);
+    bool yvec = true;
+    if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+    const bool has_p0 = a.p0 != nullptr, has_p1 = a.p1 != nullptr;
+
+    // the loads of this chunk first, then the row's pairs
+    const int64_t cbase = j * (int64_t)(TPR * K);
+    const double *w = a.wsd + 2 * row * P;
+    const double pv = OP == OP_LAYERNORM ? a.wsd[2 * a.M * P + row] : 0.0;
+    uint4 raw[K], g4[K], b4[(OP == OP_LAYERNORM) ? K : 1];
+    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
+    if (has_p0) load_params<DT, AL, K, TPR>(g4, geo, a.p0, t, N, cbase);
+    if constexpr (OP == OP_LAYERNORM) {
+        if (has_p1) load_params<DT, AL, K, TPR>(b4, geo, a.p1, t, N, cbase);
+    }
+    double s1 = 0.0, s2 = 0.0;
+    for (int q = lane; q < P; q += 64) {
+        s1 += w[2 * q];
+        s2 += w[2 * q + 1];
+    }
+    const double2 st = wave_allreduce(double2{s1, s2}, SumOp());
+    double m1 = 0.0, scale;
+    if constexpr (OP == OP_LAYERNORM) {
+        m1 = st.x * a.inv_nd;
+        const double var = __builtin_fmax(st.y * a.inv_nd - m1 * m1, 0.0);
+        scale = rsqrt_f64(var + (double)a.eps);
+        if (j == 0 && t == 0) {
+            if (a.mean) a.mean[row] = (float)(pv + m1);
+            if (a.rstd) a.rstd[row] = (float)scale;
+        }
+    } else {
+        scale = rsqrt_f64(st.y * a.inv_nd + (double)a.eps);
+    }
+    const float scale_f = (float)scale;
+    const double nm = -m1 * scale;                  // as in the single-pass kernels
+
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, 0u, cbase);     // padding is not stored
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v[VEC], g[VEC], b[VEC];
+        unpack<DT>(raw[k], v);
+        if (has_p0) unpack<DT>(g4[k], g);
+        if constexpr (OP == OP_LAYERNORM) {
+            if (has_p1) unpack<DT>(b4[k], b);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float gi = has_p0 ? g[i] : 1.0f;
+            if constexpr (OP == OP_LAYERNORM) {
+                const double d = (double)v[i] - pv;
+                v[i] = (float)__builtin_fma(__builtin_fma(d, scale, nm), (double)gi, has_p1 ? (double)b[i] : 0.0);
+            } else {
+                v[i] = (v[i] * scale_f) * gi;
+            }
+        }
+        store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
     }
 }
 

@@ -1,0 +1,196 @@
+"""GPU parity of the norms with a workspace (nt_layernorm_rows_ws,
+nt_rmsnorm_rows_ws): a few rows too wide for one pass, each cut into chunks
+on many workgroups.  Against the oracle at the norms' bar (fp32: relative
+1e-5; fp16/bf16: 1 ulp of the oracle's float64 result rounded once; mean and
+rstd relative 1e-5), aligned and misaligned, with and without parameters, in
+place, with a workspace full of garbage, bitwise repeatable, and with a NULL
+workspace bitwise equal to the plain entry points."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from gpu_util import check_output, check_stats, empty_like_dev, oracle_for, to_dev, to_host_bits
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import torch  # noqa: E402
+
+import row_wise_reductions_amd as nt  # noqa: E402
+
+DT_CODE = {"f32": nt.NT_F32, "f16": nt.NT_F16, "bf16": nt.NT_BF16}
+OP_CODE = {"layernorm": nt.NT_OP_LAYERNORM, "rmsnorm": nt.NT_OP_RMSNORM}
+WS_CODE = {"layernorm": nt.NT_OP_LAYERNORM_WS, "rmsnorm": nt.NT_OP_RMSNORM_WS}
+EPS = {"layernorm": 1e-5, "rmsnorm": 1e-6}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_bits(seed, M, N, dt, scale=1.0, loc=0.0):
+    rng = np.random.default_rng(seed)
+    return workloads.encode(rng.standard_normal((M, N)) * scale + loc, dt)
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def run_ws(op, x_t, dt, p0=None, p1=None, y_t=None, ws=None, wsb=None, plain=False):
+    """Launch one norm through the C ABI on the current stream and wait:
+    the workspace entry point (ws=None allocates the size the library asks
+    for; ws=False passes NULL), or with plain=True the entry point without
+    a workspace."""
+    M, N = x_t.shape
+    code = DT_CODE[dt]
+    y = y_t if y_t is not None else empty_like_dev((M, N), dt)
+    s = torch.cuda.current_stream().cuda_stream
+    if ws is None:
+        need = nt.nt_norm_workspace_bytes(OP_CODE[op], M, N, code)
+        ws = torch.empty(max(need, 8), dtype=torch.uint8, device="cuda")
+        wsb = need
+    wp = None if ws is False else ws.data_ptr()
+    wsb = 0 if ws is False else (wsb if wsb is not None else ws.numel())
+    mean = rstd = None
+    if op == "layernorm":
+        mean = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        rstd = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        if plain:
+            rc = nt.nt_layernorm_rows(M, N, code, EPS[op], x_t.data_ptr(), _p(p0), _p(p1), y.data_ptr(),
+                                      mean.data_ptr(), rstd.data_ptr(), s)
+        else:
+            rc = nt.nt_layernorm_rows_ws(M, N, code, EPS[op], x_t.data_ptr(), _p(p0), _p(p1), y.data_ptr(),
+                                         mean.data_ptr(), rstd.data_ptr(), wp, wsb, s)
+    elif plain:
+        rc = nt.nt_rmsnorm_rows(M, N, code, EPS[op], x_t.data_ptr(), _p(p0), y.data_ptr(), s)
+    else:
+        rc = nt.nt_rmsnorm_rows_ws(M, N, code, EPS[op], x_t.data_ptr(), _p(p0), y.data_ptr(), wp, wsb, s)
+    assert rc == 0, f"{op}: status {rc} ({nt.nt_status_string(rc)})"
+    torch.cuda.synchronize()
+    return y, mean, rstd
+
+
+def params(op, N, dt, seed, with_params=True):
+    if not with_params:
+        return None, None
+    p0 = rand_bits(seed + 1, 1, N, dt, scale=0.3, loc=1.0)[0]
+    p1 = rand_bits(seed + 2, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
+    return p0, p1
+
+
+def check(op, y, mean, rstd, x, dt, p0, p1, what):
+    ref, rmean, rrstd = oracle_for(op, x, dt, EPS[op], p0, p1)
+    check_output(to_host_bits(y, dt), ref, dt, what)
+    if op == "layernorm":
+        check_stats(mean.cpu().numpy(), rmean, what + " mean")
+        check_stats(rstd.cpu().numpy(), rrstd, what + " rstd")
+
+
+CASES = [(1, 40000, "f32"), (3, 100003, "f32"), (2, 65536, "f16"), (7, 50001, "bf16"), (64, 262144, "bf16"),
+         (5, 1 << 20, "f16"), (16, 131072, "f32")]
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("M,N,dt", CASES)
+def test_split_norm_parity(op, M, N, dt):
+    """Every element against the oracle, rows shifted off the 16-byte grid
+    by 0 and 1 elements (x and y together, and y alone), with parameters
+    and, on the aligned rows, without (the identity fills)."""
+    seed = M * 1000003 + N
+    x = rand_bits(seed, M, N, dt, scale=2.0, loc=3.0)
+    for xo, yo, with_p in ((0, 0, True), (1, 1, True), (0, 1, True), (0, 0, False)):
+        plan = nt.nt_plan_launch(WS_CODE[op], M, N, DT_CODE[dt], xo == 0 and yo == 0)
+        assert plan["split"] == 3, plan
+        p0, p1 = params(op, N, dt, seed, with_p)
+        what = f"split {op} {dt} M={M} N={N} x_off={xo} y_off={yo} params={with_p} P={plan['row_chunks']}"
+        say("case", what)
+        x_t = to_dev(x, dt, xo)
+        y, mean, rstd = run_ws(op, x_t, dt, None if p0 is None else to_dev(p0, dt),
+                               None if p1 is None else to_dev(p1, dt), empty_like_dev((M, N), dt, yo))
+        check(op, y, mean, rstd, x, dt, p0, p1, what)
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_norm_in_place_garbage_workspace_repeatable(op, dt):
+    """y == x (the LayerNorm pivot, the row's first element, is read from
+    the workspace, not from x, which the row's first workgroup overwrites);
+    a workspace full of garbage; two calls bitwise equal."""
+    M, N = 6, 300007
+    x = rand_bits(77, M, N, dt, scale=1.5, loc=-2.0)
+    p0, p1 = params(op, N, dt, 77)
+    p0_t = to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    need = nt.nt_norm_workspace_bytes(OP_CODE[op], M, N, DT_CODE[dt])
+    assert need > 0
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    say(f"case in-place split {op} {dt} M={M} N={N}")
+    x_t = to_dev(x, dt)
+    y, mean, rstd = run_ws(op, x_t, dt, p0_t, p1_t, y_t=x_t, ws=ws)
+    check(op, x_t, mean, rstd, x, dt, p0, p1, f"in-place split {op} {dt}")
+    say(f"case repeat split {op} {dt} M={M} N={N}")
+    x_t = to_dev(x, dt)
+    a, am, ar = run_ws(op, x_t, dt, p0_t, p1_t, ws=ws)
+    ws.random_(0, 256)
+    b, bm, br = run_ws(op, x_t, dt, p0_t, p1_t, ws=ws)
+    assert np.array_equal(to_host_bits(a, dt), to_host_bits(b, dt))
+    if op == "layernorm":
+        assert torch.equal(am, bm) and torch.equal(ar, br)
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+def test_null_workspace_is_the_plain_plan(op):
+    """NULL workspace: the looped one-workgroup-per-row kernel, bitwise equal
+    to the plain entry point; both within the bar of the split result."""
+    M, N, dt = 4, 70001, "bf16"
+    x = rand_bits(5, M, N, dt, scale=2.0)
+    p0, p1 = params(op, N, dt, 5)
+    x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    say(f"case null-workspace {op} {dt} M={M} N={N}")
+    a, am, ar = run_ws(op, x_t, dt, p0_t, p1_t, ws=False)
+    b, bm, br = run_ws(op, x_t, dt, p0_t, p1_t, plain=True)
+    assert np.array_equal(to_host_bits(a, dt), to_host_bits(b, dt))
+    if op == "layernorm":
+        assert torch.equal(am, bm) and torch.equal(ar, br)
+    check(op, a, am, ar, x, dt, p0, p1, f"null-workspace {op}")
+
+
+def test_split_norm_rejects_small_workspace():
+    M, N, dt = 4, 70001, "f32"
+    need = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, M, N, nt.NT_F32)
+    x_t = to_dev(rand_bits(1, M, N, dt), dt)
+    y = empty_like_dev((M, N), dt)
+    ws = torch.empty(need + 8, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert nt.nt_rmsnorm_rows_ws(M, N, nt.NT_F32, 1e-6, x_t.data_ptr(), None, y.data_ptr(), ws.data_ptr(),
+                                 need - 8, s) == 6      # NT_ERR_WORKSPACE
+    assert nt.nt_rmsnorm_rows_ws(M, N, nt.NT_F32, 1e-6, x_t.data_ptr(), None, y.data_ptr(), ws.data_ptr() + 4,
+                                 need, s) == 5          # NT_ERR_ALIGN (in bounds had it launched)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()                 # nothing launched
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+def test_torch_wrappers_use_the_split(op):
+    M, N, dt = 8, 200000, "bf16"
+    x = rand_bits(11, M, N, dt, scale=2.0, loc=1.0)
+    p0, p1 = params(op, N, dt, 11)
+    assert nt.nt_norm_workspace_bytes(OP_CODE[op], M, N, DT_CODE[dt]) > 0
+    x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)
+    say(f"case torch wrapper split {op} {dt} M={M} N={N}")
+    if op == "layernorm":
+        y, mean, rstd = nt.layer_norm(x_t, p0_t, to_dev(p1, dt), eps=EPS[op])
+    else:
+        y, mean, rstd = nt.rms_norm(x_t, p0_t, eps=EPS[op]), None, None
+    torch.cuda.synchronize()
+    check(op, y, mean, rstd, x, dt, p0, p1, f"torch wrapper split {op}")

@@ -103,6 +103,18 @@ def test_status_strings():
                                       None, None, None), 8),
     (lambda: nt.nt_add_layernorm_rows(4, 8, F32, float("nan"), FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 128,
                                       None, None, None), 4),
+    # norms with a workspace: the plain checks, then the workspace's size and alignment
+    (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F32, -1.0, FAKE, None, None, FAKE, None, None, FAKE, 1 << 20,
+                                     None), 4),
+    (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F32, 1e-5, FAKE, None, None, FAKE, None, None, FAKE, 64, None), 6),
+    (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F32, 1e-5, FAKE, None, None, FAKE, None, None, FAKE + 4, 1 << 20,
+                                     None), 5),
+    (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F16, 1e-5, FAKE, FAKE + 1, None, FAKE, None, None, FAKE, 1 << 20,
+                                     None), 5),
+    (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, FAKE, None, FAKE, FAKE, 0, None), 6),
+    (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, FAKE, None, FAKE, FAKE + 2, 1 << 20, None), 5),
+    (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, None, None, FAKE, FAKE, 1 << 20, None), 1),
+    (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, 7, 1e-6, FAKE, None, FAKE, FAKE, 1 << 20, None), 3),
 ])
 def test_validation_before_launch(call, code):
     # every case here must fail validation; on a machine with a GPU a library
@@ -130,6 +142,8 @@ def test_empty_is_noop():
     assert nt.nt_add_layernorm_rows(0, 8, F32, 1e-5, None, None, None, None, None, None, None, None, None) == 0
     # a bad eps is still an error for an empty call
     assert nt.nt_rmsnorm_rows(0, 8, F32, -1.0, None, None, None, None) == 4
+    assert nt.nt_layernorm_rows_ws(0, 1 << 20, F32, 1e-5, None, None, None, None, None, None, None, 0, None) == 0
+    assert nt.nt_rmsnorm_rows_ws(0, 1 << 20, F32, 1e-6, None, None, None, None, 0, None) == 0
 
 
 def test_workspace_bytes():
@@ -299,3 +313,57 @@ def test_causal_softmax_plans():
     # part-filled 16-bit rows of 257..511 chunks: 4 waves x 2 chunks
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 8, 3000, BF16, True)
     assert (p["waves_per_row"], p["chunks_per_lane"]) == (4, 2)
+
+
+def test_norm_workspace_bytes():
+    LN, RMS = nt.NT_OP_LAYERNORM, nt.NT_OP_RMSNORM
+    # rows that fit one pass, or enough rows to fill the GPU: no workspace
+    assert nt.nt_norm_workspace_bytes(LN, 4, 8192, BF16) == 0
+    assert nt.nt_norm_workspace_bytes(RMS, 4, 30000, F32) == 0
+    # (a 32768-wide fp32 row fits when aligned, not with a misaligned head)
+    assert nt.nt_norm_workspace_bytes(RMS, 4, 32768, F32) > 0
+    assert nt.nt_norm_workspace_bytes(LN, 4096, 1 << 20, BF16) == 0
+    # 64 fp32 rows of 1 MiB: 32 KiB chunks (8 waves x 4 chunks) -> 32 per row,
+    # 33 for a misaligned head; 16 bytes per chunk and 8 per row
+    assert nt.nt_norm_workspace_bytes(LN, 64, 262144, F32) == 64 * 33 * 16 + 64 * 8
+    # 16 bf16 rows of 2 MiB: 8 KiB chunks fill the grid -> 256 per row (+1)
+    assert nt.nt_norm_workspace_bytes(RMS, 16, 1 << 20, BF16) == 16 * 257 * 16 + 16 * 8
+    # other ops and invalid arguments
+    for bad in ((nt.NT_OP_SOFTMAX, 4, 1 << 20, F32), (LN, -1, 1 << 20, F32), (LN, 4, 0, F32), (RMS, 4, 1 << 20, 5)):
+        assert nt.nt_norm_workspace_bytes(*bad) == 0
+
+
+def test_split_norm_plans():
+    for op, base in ((nt.NT_OP_LAYERNORM_WS, nt.NT_OP_LAYERNORM), (nt.NT_OP_RMSNORM_WS, nt.NT_OP_RMSNORM)):
+        for dt, e in ((F32, 4), (F16, 2), (BF16, 2)):
+            for M, N in ((1, 40000), (3, 100003), (64, 262144), (16, 1 << 20), (1000, 65536), (255, 20000)):
+                for al in (True, False):
+                    p = nt.nt_plan_launch(op, M, N, dt, al)
+                    plain = nt.nt_plan_launch(base, M, N, dt, al)
+                    # one pass, or enough rows to fill the GPU: the workspace changes nothing
+                    # (LayerNorm splits below 256 rows, RMSNorm below 2048)
+                    if plain["split"] == 0 or M >= (256 if base == nt.NT_OP_LAYERNORM else 2048):
+                        assert p == plain
+                        continue
+                    assert p["split"] == 3 and plain["split"] == 2, (op, dt, M, N, al)
+                    per = 64 * p["waves_per_row"] * p["chunks_per_lane"]
+                    aligned = al and (N * e) % 16 == 0
+                    nch = N * e // 16 if aligned else (N + 2 * (16 // e) - 2) // (16 // e)
+                    assert p["row_chunks"] == -(-nch // per) and p["grid"] == M * p["row_chunks"]
+                    assert (p["waves_per_row"], p["chunks_per_lane"]) in ((8, 4), (8, 1), (4, 1))
+                    # the largest chunk that still gives 2048 workgroups, else the smallest
+                    assert p["grid"] >= 2048 or (p["waves_per_row"], p["chunks_per_lane"]) == (4, 1)
+                    assert p["workspace_bytes"] == M * p["row_chunks"] * 16 + M * 8
+                    assert p["workspace_bytes"] <= nt.nt_norm_workspace_bytes(base, M, N, dt)
+        # many rows fill the GPU without the split
+        assert nt.nt_plan_launch(op, 4096, 1 << 20, BF16, True)["split"] == 2
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 256, 1 << 20, BF16, True)["split"] == 2
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 2047, 1 << 20, BF16, True)["split"] == 3
+
+
+def test_split_norm_rows_switch(monkeypatch):
+    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "0")
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 64, 262144, F32, True)["split"] == 2
+    assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 64, 262144, F32) == 0
+    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 4096, 262144, F32, True)["split"] == 3

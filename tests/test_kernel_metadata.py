@@ -142,6 +142,9 @@ def _shapes(kernels):
         m = re.search(r"softmax_coopILi(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", name)
         if m:
             have.add(("coop",) + tuple(int(g) for g in m.groups()))
+        m = re.search(r"norm_split_(partial|finalize)ILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("n" + m.group(1),) + tuple(int(g) for g in m.groups()[1:]))
     return have
 
 
@@ -149,9 +152,9 @@ def test_every_planned_shape_is_built(kernels):
     """Every launch the planner can choose (fused add + norm included) has an
     instantiated kernel: (op, type, W, K, aligned, residual)."""
     have = _shapes(kernels)
-    for op in (0, 1, 2, 3, 4, 5):
+    for op in (0, 1, 2, 3, 4, 5, 6, 7):
         # public op -> (kernel op, residual, causal)
-        base, res, causal = {3: (1, 1, 0), 4: (2, 1, 0), 5: (3, 0, 1)}.get(op, (op, 0, 0))
+        base, res, causal = {3: (1, 1, 0), 4: (2, 1, 0), 5: (3, 0, 1), 6: (1, 0, 0), 7: (2, 0, 0)}.get(op, (op, 0, 0))
         for dt in (0, 1, 2):
             for N in (1, 7, 64, 255, 781, 1000, 4096, 4097, 8192, 16384, 30000, 32768, 65536, 100000, 262144):
                 for al in (True, False):
@@ -167,6 +170,9 @@ def test_every_planned_shape_is_built(kernels):
                         assert ("finalize", dt, W, K, A, causal) in have, (op, dt, N, al, p)
                     elif p["split"] == 2:
                         assert ("loop", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
+                    elif p["split"] == 3:
+                        assert ("npartial", base, dt, W, K, A) in have, (op, dt, N, al, p)
+                        assert ("nfinalize", base, dt, W, K, A) in have, (op, dt, N, al, p)
                     else:
                         assert ("res", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
                         if p["persistent"]:
