@@ -561,7 +561,8 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
             for op, opc in (("layernorm", nt.NT_OP_LAYERNORM), ("rmsnorm", nt.NT_OP_RMSNORM)):
                 wop = nt.NT_OP_LAYERNORM_WS if op == "layernorm" else nt.NT_OP_RMSNORM_WS
                 p = nt.nt_plan_launch(wop, M, N, code, True)
-                r[op + "_plan"] = "split" if p["split"] == 3 else "looped"
+                r[op + "_plan"] = ({0: "single pass", 2: "looped"}.get(p["split"]) or
+                                   ("split, one pass" if p["cooperative"] else "split, two kernels"))
                 os.environ["NT_NORM_SPLIT_ROWS"] = str(1 << 40)
                 try:
                     wsb = nt.nt_norm_workspace_bytes(opc, M, N, code)
@@ -575,8 +576,11 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                             M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), ws.data_ptr(),
                             wsb, sh))
                     ms_split = timed(split, R)
+                    os.environ["NT_COOP"] = "0"
+                    ms_split2 = timed(split, R)
                 finally:
                     del os.environ["NT_NORM_SPLIT_ROWS"]
+                    os.environ.pop("NT_COOP", None)
                 if op == "layernorm":
                     looped = lambda i: ok(nt.nt_layernorm_rows(  # noqa: E731
                         M, N, code, 1e-5, xs[i].data_ptr(), g.data_ptr(), b.data_ptr(), ys[i].data_ptr(),
@@ -588,7 +592,8 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                         M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), sh))
                     theirs = lambda i: F.rms_norm(xs[i], (N,), g, 1e-6)  # noqa: E731
                     gb = 2 * n * e + N * e
-                for k, ms in (("split", ms_split), ("looped", timed(looped, R)), ("torch", timed(theirs, R))):
+                for k, ms in (("split", ms_split), ("split2", ms_split2), ("looped", timed(looped, R)),
+                              ("torch", timed(theirs, R))):
                     r[f"{op}_{k}_us"] = round(ms * 1e3, 1)
                     r[f"{op}_{k}_GBps"] = round(gb / (ms * 1e-3) / 1e9, 1)
             rows.append(r)
@@ -600,15 +605,17 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                  f"    python3 bench.py --sweep-wide-norms --steps {steps} --warmup {warmup} --sweep-md {md_path}", "",
                  "GB/s = algorithmic bytes (rows in and out, parameter vectors, LayerNorm's mean and rstd) / median "
                  "event-timed launch, inputs rotating through a 1 GiB pool.  split: nt_*_rows_ws with the split "
-                 "forced at every row count (two kernels, the row's chunks on many workgroups); looped: the plain "
-                 "entry point (one workgroup per row, the row streamed twice); torch: F.layer_norm / F.rms_norm on "
-                 "the same buffers.  plan: what nt_*_rows_ws picks by itself.", "",
-                 "| type | N | M | LN plan | LN split | LN looped | LN torch | RMS plan | RMS split | RMS looped | "
-                 "RMS torch |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+                 "forced at every row count, the row's chunks on many workgroups, in one pass where the row has at "
+                 "most 128 chunks (1p) else two kernels; 2k: the same with NT_COOP=0 (two kernels, x read twice); "
+                 "looped: the plain entry point (one workgroup per row, the row streamed twice); torch: "
+                 "F.layer_norm / F.rms_norm on the same buffers.  plan: what nt_*_rows_ws picks by itself.", "",
+                 "| type | N | M | LN plan | LN split | LN 2k | LN looped | LN torch | RMS plan | RMS split | RMS 2k | "
+                 "RMS looped | RMS torch |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for r in rows:
             lines.append(f"| {r['dt']} | {r['N']} | {r['M']} | {r['layernorm_plan']} | {r['layernorm_split_GBps']} | "
-                         f"{r['layernorm_looped_GBps']} | {r['layernorm_torch_GBps']} | {r['rmsnorm_plan']} | "
-                         f"{r['rmsnorm_split_GBps']} | {r['rmsnorm_looped_GBps']} | {r['rmsnorm_torch_GBps']} |")
+                         f"{r['layernorm_split2_GBps']} | {r['layernorm_looped_GBps']} | {r['layernorm_torch_GBps']} | "
+                         f"{r['rmsnorm_plan']} | {r['rmsnorm_split_GBps']} | {r['rmsnorm_split2_GBps']} | "
+                         f"{r['rmsnorm_looped_GBps']} | {r['rmsnorm_torch_GBps']} |")
         lines.append("")
         with open(md_path, "w") as f:
             f.write("\n".join(lines))

@@ -160,22 +160,29 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
 
 /*
  * The norms with a workspace, for a few rows too wide for one pass.  There
- * the plain entry points stream each row with one workgroup, so M rows keep
- * at most M compute units busy.  With a workspace the row is cut into
- * chunks, one workgroup each: a first kernel writes every chunk's partial
- * sums (LayerNorm: sum(x - p) and sum((x - p)^2) around the row's first
- * element p, RMSNorm: sum(x^2); in fp64) to the workspace, a second combines
- * a row's partial sums in a fixed order and writes the chunk's outputs,
- * reading x a second time.  The statistics are those of the definitions
- * above, summed in another order than the one-workgroup kernels' (results
- * within the same tolerances, not necessarily bitwise equal to them;
- * repeated calls are bitwise equal).  This is the split softmax's scheme
- * ("How Flash Attention Uses Triton") applied to the norms' sums.
+ * the plain entry points stream each row twice with one workgroup, so M
+ * rows keep at most M compute units busy.  With a workspace the row is cut
+ * into chunks, one workgroup each, and every chunk's partial sums
+ * (LayerNorm: sum(x - p) and sum((x - p)^2) around the row's first element
+ * p, RMSNorm: sum(x^2); in fp64) go through the workspace.  Up to 128 chunks
+ * per row this is one pass: the row's workgroups exchange their sums as
+ * tagged records, each keeping its chunk in registers, and a record that
+ * does not arrive within a bounded wait is recomputed from x by the waiting
+ * workgroup (so the result never depends on scheduling).  Beyond that, in
+ * place (y == x) or while the stream captures a graph, two kernels: the
+ * first writes the sums, the second combines them and writes the outputs,
+ * reading x a second time.  Both forms combine a row's sums in the same
+ * fixed order and give the same bits.  The statistics are those of the
+ * definitions above, summed in another order than the one-workgroup
+ * kernels' (results within the same tolerances, not necessarily bitwise
+ * equal to them; repeated calls are bitwise equal).  This is the split
+ * softmax's scheme ("How Flash Attention Uses Triton") applied to the
+ * norms' sums.
  *
- * nt_norm_workspace_bytes(op, M, N, dt): bytes the split needs (16 per row
- * chunk, 8 per row) for op NT_OP_LAYERNORM or NT_OP_RMSNORM, 0 when the plain plan is
- * used (rows that fit one pass, or enough rows to fill the GPU) or for
- * invalid arguments.
+ * nt_norm_workspace_bytes(op, M, N, dt): bytes the split needs (32 per row
+ * chunk, 8 per row) for op NT_OP_LAYERNORM or NT_OP_RMSNORM, 0 when the
+ * plain plan is used (rows that fit one pass, or enough rows to fill the
+ * GPU) or for invalid arguments.
  *
  * nt_layernorm_rows_ws / nt_rmsnorm_rows_ws take the plain entry points'
  * arguments, with their conventions and checks, plus `workspace` and
@@ -183,7 +190,8 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  * 8-byte aligned (NT_ERR_ALIGN) and hold nt_norm_workspace_bytes(op, M, N, dt)
  * bytes (NT_ERR_WORKSPACE).  Contents need not be initialized; two calls in
  * flight at once must not share a workspace, which must not overlap x, y or
- * the parameters.  In place (y == x) is allowed.
+ * the parameters.  In place (y == x) is allowed.  NT_COOP=0 in the
+ * environment selects the two kernels throughout.
  */
 size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt);
 

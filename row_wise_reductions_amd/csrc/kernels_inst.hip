@@ -209,8 +209,16 @@ hipError_t split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t
 }
 
 template <int OP, int W, int K, bool AL>
-hipError_t norm_split_go(const RowArgs &a, hipStream_t s) {
+hipError_t norm_split_go(bool coop, const RowArgs &a, hipStream_t s) {
     const uint32_t grid = (uint32_t)(a.M * a.P);
+    if (coop) {
+        // the one-pass form is planned for 8 x 4 chunks only, not for 16-bit LayerNorm
+        if constexpr (W == 8 && K == 4 && !(OP == OP_LAYERNORM && DT != DT_F32)) {
+            hipLaunchKernelGGL((norm_coop<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL((norm_split_partial<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -218,20 +226,21 @@ hipError_t norm_split_go(const RowArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The split norm's chunk shapes: 8 waves x 4 chunks (32 KiB), 8 x 1, 4 x 1.
+// The split norm's chunk shapes: 8 waves x 4 chunks (32 KiB), 8 x 1, 4 x 1 (two kernels); 8 x 4 in one pass.
 template <int OP>
-hipError_t norm_split(int W, int K, bool al, const RowArgs &a, hipStream_t s) {
+hipError_t norm_split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k) \
-    if (W == w && K == k) return al ? norm_split_go<OP, w, k, true>(a, s) : norm_split_go<OP, w, k, false>(a, s);
+    if (W == w && K == k) \
+        return al ? norm_split_go<OP, w, k, true>(coop, a, s) : norm_split_go<OP, w, k, false>(coop, a, s);
     NTK_CASE(8, 4) NTK_CASE(8, 1) NTK_CASE(4, 1)
 #undef NTK_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t norm_split_any(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s) {
+hipError_t norm_split_any(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     switch (op) {
-    case OP_LAYERNORM: return norm_split<OP_LAYERNORM>(W, K, al, a, s);
-    case OP_RMSNORM: return norm_split<OP_RMSNORM>(W, K, al, a, s);
+    case OP_LAYERNORM: return norm_split<OP_LAYERNORM>(W, K, al, coop, a, s);
+    case OP_RMSNORM: return norm_split<OP_RMSNORM>(W, K, al, coop, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -269,8 +278,8 @@ hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, in
 hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s) {
     return persistent_any(op, W, K, a, s);
 }
-hipError_t launch_norm_split_f32(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s) {
-    return norm_split_any(op, W, K, al, a, s);
+hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return norm_split_any(op, W, K, al, coop, a, s);
 }
 #elif NTK_DT == 1
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
@@ -285,8 +294,8 @@ hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, in
 hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
     return persistent_any(op, W, K, a, s);
 }
-hipError_t launch_norm_split_f16(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s) {
-    return norm_split_any(op, W, K, al, a, s);
+hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return norm_split_any(op, W, K, al, coop, a, s);
 }
 #else
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
@@ -301,8 +310,8 @@ hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, i
 hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
     return persistent_any(op, W, K, a, s);
 }
-hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s) {
-    return norm_split_any(op, W, K, al, a, s);
+hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+    return norm_split_any(op, W, K, al, coop, a, s);
 }
 #endif
 

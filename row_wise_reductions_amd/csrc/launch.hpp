@@ -38,8 +38,8 @@ hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a,
 // Launch the split norm (a few rows too wide for one pass): the partial
 // kernel, then the finalize kernel, one workgroup per (row, chunk), a.P
 // chunks per row, a.wsd holding 2 doubles per (row, chunk).
-hipError_t launch_norm_split_f32(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s);
-hipError_t launch_norm_split_f16(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s);
-hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, const RowArgs &a, hipStream_t s);
+hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 
 }  // namespace ntk

@@ -107,6 +107,7 @@ const Shape kLooped = {8, 4};
 // least kNormSplitGrid workgroups is used (8 per CU on 256 CUs).
 const Shape kNormSplit[] = {{8, 4}, {8, 1}, {4, 1}};
 constexpr int64_t kNormSplitGrid = 2048;
+constexpr int64_t kNormCoopPMax = 16;
 // Rows below which the split is used.  The looped kernel gives each row one
 // workgroup, so it fills the 256 CUs from 256 rows on; measured on MI355X
 // (rows of 64 KiB to 2 MiB), the split is 2-7x faster below 64 rows, even at
@@ -170,6 +171,18 @@ uint32_t next_tag() {
         return (uint32_t)rd();
     }()};
     return counter.fetch_add(1, std::memory_order_relaxed);
+}
+
+// Is `stream` capturing a graph?  A replay would reuse the call's record
+// tag, and could take the previous replay's records for its own.
+nt_status stream_capturing(void *stream, bool *capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return NT_ERR_HIP;
+    }
+    *capturing = cs != hipStreamCaptureStatusNone;
+    return NT_OK;
 }
 
 // Chunks a row can touch: N*e/16 when aligned, else up to one more for the
@@ -236,6 +249,43 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
     return true;
 }
 
+// The split norm's plan for M rows of nch chunks (norms with a workspace, rows
+// too wide for one pass): false for the plain (looped) plan.
+//   One pass (cooperative), at any row count, where the row has at most
+//   kNormCoopPMax chunks of 8 waves x 4 (32 KiB), those give at least
+//   kNormSplitGrid workgroups, and the kernel keeps 4 waves per SIMD (not
+//   16-bit LayerNorm, whose 8 x 4 form holds about 200 registers).
+//   Else, below norm_split_rows(op) rows, two kernels, with the largest chunk
+//   that gives kNormSplitGrid workgroups.
+// Measured on MI355X (rows of 64 KiB to 2 MiB, 4 to 2048 rows): the one pass
+// reads x once and beats the looped kernel by 8-35% there, but its
+// workgroups wait for the slowest of the row's chunks, which costs more than
+// the second read saves once a row has 32 chunks or more, or when few rows
+// leave the re-read in cache; the two kernels are 2-7x faster than the
+// looped kernel below 64 rows.
+bool split_norm_plan(nt_op op, nt_dtype dt, int64_t M, int64_t nch, bool coop, Shape *out, int64_t *P,
+                     bool *cooperative) {
+    auto chunks = [nch](const Shape &c) { return (nch + 64 * c.W * c.K - 1) / (64 * c.W * c.K); };
+    const Shape big = kNormSplit[0];
+    if (coop && !(op == NT_OP_LAYERNORM && dt != NT_F32) && chunks(big) <= kNormCoopPMax &&
+        M * chunks(big) >= kNormSplitGrid) {
+        *out = big;
+        *P = chunks(big);
+        *cooperative = true;
+        return true;
+    }
+    if (M >= norm_split_rows(op)) return false;
+    Shape s = big;
+    for (const Shape &c : kNormSplit) {
+        s = c;
+        if (M * chunks(c) >= kNormSplitGrid) break;
+    }
+    *out = s;
+    *P = chunks(s);
+    *cooperative = false;
+    return true;
+}
+
 nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, nt_plan *p, bool params = true,
                     bool res = false, bool causal = false, bool norm_split = false) {
     std::memset(p, 0, sizeof *p);
@@ -286,25 +336,26 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
             p->persistent = 1;
         return NT_OK;
     }
-    if (op != NT_OP_SOFTMAX && norm_split && !res && M < norm_split_rows(op)) {
-        // few wide rows: each row cut into chunks, one workgroup each
-        Shape s = kNormSplit[0];
-        int64_t P = 0;
-        for (const Shape &c : kNormSplit) {
-            s = c;
-            const int64_t per = (int64_t)64 * c.W * c.K;
-            P = (nch + per - 1) / per;
-            if (M * P >= kNormSplitGrid) break;
-        }
-        if (P > INT32_MAX || (M > 0 && P > (((int64_t)1 << 31) / (64 * s.W)) / M)) return NT_ERR_SHAPE;
+    Shape ns;
+    int64_t nP;
+    bool ncoop;
+    // (one workgroup per (row, chunk), no striding: else the looped plan)
+    if (op != NT_OP_SOFTMAX && norm_split && !res && split_norm_plan(op, dt, M, nch, coop_enabled(), &ns, &nP, &ncoop) &&
+        nP <= (((int64_t)1 << 31) / (64 * ns.W)) / M) {
+        // few wide rows, or wide rows of few chunks: each row cut into
+        // chunks, one workgroup each
         p->split = 3;
-        p->waves_per_row = s.W;
-        p->chunks_per_lane = s.K;
+        p->waves_per_row = ns.W;
+        p->chunks_per_lane = ns.K;
         p->rows_per_block = 1;
-        p->threads_per_block = 64 * s.W;
-        p->row_chunks = P;
-        p->grid = M * P;
-        p->workspace_bytes = M * P * 16 + M * 8;     // (s1, s2) per chunk, then a pivot per row
+        p->threads_per_block = 64 * ns.W;
+        p->row_chunks = nP;
+        p->grid = M * nP;
+        p->cooperative = ncoop ? 1 : 0;
+        // four tagged 64-bit words per chunk (the cooperative records; the
+        // two kernels use half of that for their (s1, s2) pairs), then a
+        // pivot per row
+        p->workspace_bytes = M * nP * 32 + M * 8;
         return NT_OK;
     }
     if (op != NT_OP_SOFTMAX) {
@@ -385,11 +436,11 @@ hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hi
 }
 
 hipError_t launch_norm_split(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
-    const bool al = p.aligned != 0;
+    const bool al = p.aligned != 0, coop = p.cooperative != 0;
     switch (dt) {
-    case NT_F32: return ntk::launch_norm_split_f32(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
-    case NT_F16: return ntk::launch_norm_split_f16(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
-    case NT_BF16: return ntk::launch_norm_split_bf16(op, p.waves_per_row, p.chunks_per_lane, al, a, s);
+    case NT_F32: return ntk::launch_norm_split_f32(op, p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
+    case NT_F16: return ntk::launch_norm_split_f16(op, p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
+    case NT_BF16: return ntk::launch_norm_split_bf16(op, p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -514,12 +565,10 @@ static nt_status softmax_launch(int64_t M, int64_t N, nt_dtype dt, const void *x
         // a captured graph would replay this call's tag, and a replay could
         // take the previous replay's records for its own
         if (p.cooperative) {
-            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-            if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) {
-                (void)hipGetLastError();
-                return NT_ERR_HIP;
-            }
-            if (cs != hipStreamCaptureStatusNone) p.cooperative = 0;
+            bool cap = false;
+            const nt_status cst = stream_capturing(stream, &cap);
+            if (cst != NT_OK) return cst;
+            if (cap) p.cooperative = 0;
         }
         if (p.cooperative) {
             a.tag = next_tag();
@@ -558,12 +607,27 @@ namespace {
 
 // Workspace of a split-norm plan, or an error status before anything is
 // launched; a NULL workspace selected the plain plan already.
-nt_status attach_workspace(const nt_plan &p, void *ws, size_t wsb, ntk::RowArgs &a) {
+// The split norm's workspace checks, and the choice between its one-pass
+// (cooperative) and two-kernel forms: in place, or under graph capture,
+// the two kernels.
+nt_status attach_workspace(nt_plan &p, void *ws, size_t wsb, const void *x, const void *y, void *stream,
+                           ntk::RowArgs &a) {
     if (p.split != 3) return NT_OK;
     if (wsb < (size_t)p.workspace_bytes) return NT_ERR_WORKSPACE;
     if (!aligned_to(ws, 8)) return NT_ERR_ALIGN;
     a.P = (int32_t)p.row_chunks;
     a.wsd = static_cast<double *>(ws);
+    if (x == y) p.cooperative = 0;
+    if (p.cooperative) {
+        bool cap = false;
+        const nt_status st = stream_capturing(stream, &cap);
+        if (st != NT_OK) return st;
+        if (cap) p.cooperative = 0;
+    }
+    if (p.cooperative) {
+        a.tag = next_tag();
+        a.spin = coop_spin();
+    }
     return NT_OK;
 }
 
@@ -584,7 +648,7 @@ nt_status layernorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const voi
                    ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
-    st = attach_workspace(p, ws, wsb, a);
+    st = attach_workspace(p, ws, wsb, x, y, stream, a);
     if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
@@ -613,7 +677,7 @@ nt_status rmsnorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const void 
     st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr, false, false, ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
-    st = attach_workspace(p, ws, wsb, a);
+    st = attach_workspace(p, ws, wsb, x, y, stream, a);
     if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
@@ -645,10 +709,19 @@ size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt) {
     size_t need = 0;
     for (const bool al : {true, false}) {      // the larger of the two alignments' plans
         nt_plan p;
-        if (make_plan((nt_op)op, M, N, dt, al && (N * elem_bytes(dt)) % 16 == 0, &p, true, false, false, true) ==
-                NT_OK &&
-            (size_t)p.workspace_bytes > need)
-            need = (size_t)p.workspace_bytes;
+        if (make_plan((nt_op)op, M, N, dt, al && (N * elem_bytes(dt)) % 16 == 0, &p, true, false, false, false) !=
+                NT_OK ||
+            p.split != 2)
+            continue;          // rows that fit one pass need nothing
+        // and of the two forms' plans, so the size does not depend on NT_COOP
+        for (const bool coop : {true, false}) {
+            Shape s;
+            int64_t P;
+            bool c;
+            if (split_norm_plan((nt_op)op, dt, M, row_chunks(N, dt, p.aligned != 0), coop, &s, &P, &c) &&
+                P <= (((int64_t)1 << 31) / (64 * s.W)) / M && (size_t)(M * P * 32 + M * 8) > need)
+                need = (size_t)(M * P * 32 + M * 8);
+        }
     }
     return need;
 }

@@ -1216,12 +1216,59 @@ row_looped(RowArgs a) {
 // workgroup 0 of the row overwrites the row's first element).
 // ---------------------------------------------------------------------------
 
+// (sum(x - p), sum((x - p)^2)) of chunk `qbase` of a row, in registers,
+// reduced over the workgroup (`slot`: W entries of LDS, see group_allreduce).
+template <int OP, int DT, int W, int K>
+__device__ __forceinline__ double2 norm_chunk_sums(const uint4 (&raw)[K], double pv, double2 *slot, int wv,
+                                                   int lane) {
+    constexpr int VEC = dt_info<DT>::VEC;
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v[VEC];
+        unpack<DT>(raw[k], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const double d = (double)v[i] - pv;          // padding gives 0
+            if constexpr (OP == OP_LAYERNORM) s1 += d;
+            s2 = __builtin_fma(d, d, s2);
+        }
+    }
+    return group_allreduce<W>(double2{s1, s2}, SumOp(), slot, wv, lane);
+}
+
+// The same sums of a chunk that is not in registers, one 16-byte slice per
+// lane at a time: slice k holds exactly slot k of a whole-chunk load and the
+// additions run in the same order, so the pair is bitwise norm_chunk_sums'.
+template <int OP, int DT, int W, int K, bool AL>
+__device__ __forceinline__ double2 norm_chunk_sums_reload(const RowGeom<DT, AL> &geo, const char *xr, int t,
+                                                          int32_t N, uint32_t padw, double pv, int64_t qbase,
+                                                          double2 *slot, int wv, int lane) {
+    constexpr int VEC = dt_info<DT>::VEC, TPR = 64 * W;
+    double s1 = 0.0, s2 = 0.0;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+        uint4 r[1];
+        load_row<DT, AL, 1, TPR>(r, geo, t, N, qbase + (int64_t)k * TPR);
+        finish_row<DT, AL, 1, TPR>(r, geo, xr, t, N, padw, qbase + (int64_t)k * TPR);
+        float v[VEC];
+        unpack<DT>(r[0], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const double d = (double)v[i] - pv;
+            if constexpr (OP == OP_LAYERNORM) s1 += d;
+            s2 = __builtin_fma(d, d, s2);
+        }
+    }
+    return group_allreduce<W>(double2{s1, s2}, SumOp(), slot, wv, lane);
+}
+
 template <int OP, int DT, int W, int K, bool AL>
 __global__ void __launch_bounds__(64 * W)
 norm_split_partial(RowArgs a) {
     static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "split norm");
     using I = dt_info<DT>;
-    constexpr int VEC = I::VEC, TPR = 64 * W;
+    constexpr int TPR = 64 * W;
     const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
     const int32_t N = a.N, P = a.P;
     const int64_t row = blockIdx.x / P;
@@ -1237,19 +1284,7 @@ norm_split_partial(RowArgs a) {
     uint4 raw[K];
     load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
     finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, cbase);
-    double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        float v[VEC];
-        unpack<DT>(raw[k], v);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const double d = (double)v[i] - pv;          // padding gives 0
-            if constexpr (OP == OP_LAYERNORM) s1 += d;
-            s2 = __builtin_fma(d, d, s2);
-        }
-    }
-    const double2 st = group_allreduce<W>(double2{s1, s2}, SumOp(), red, wv, lane);
+    const double2 st = norm_chunk_sums<OP, DT, W, K>(raw, pv, red, wv, lane);
     if (t == 0) {
         double *w = a.wsd + 2 * (row * P + j);
         w[0] = st.x;
@@ -1622,6 +1657,165 @@ softmax_coop(RowArgs a) {
     float c, inv;
     merge_pairs(static_cast<const float2 *>(qs), P, lane, c, inv, s2);
     softmax_chunk_out<DT, W, K, AL>(raw, geo, yr, t, N, yvec, cbase, c, inv, s2);
+}
+
+// ---------------------------------------------------------------------------
+// Cooperative split norm: the split norm's chunks and arithmetic in ONE
+// pass, so x is read once.  The record exchange is the cooperative softmax's
+// (tagged 64-bit words, written and read as relaxed device-scope atomics, a
+// bounded poll by wave 0, then recomputation of whatever did not arrive),
+// with fp64 sums: a record is four words {tag, low or high half of s1 or
+// s2}.  The row's sums are combined in the finalize kernel's order, so both
+// forms give the same bits.  x must not alias y (a recomputed chunk may
+// already hold outputs), and the parameters are loaded with the chunk.
+// ---------------------------------------------------------------------------
+
+template <int OP, int DT, int W, int K, bool AL>
+__global__ void __launch_bounds__(64 * W)
+norm_coop(RowArgs a) {
+    static_assert(OP == OP_LAYERNORM || OP == OP_RMSNORM, "split norm");
+    using I = dt_info<DT>;
+    constexpr int VEC = I::VEC, TPR = 64 * W, NB = COOP_PMAX / 64;
+    constexpr int NW = OP == OP_LAYERNORM ? 4 : 2;      // record words: s1 (LayerNorm) and s2, two halves each
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N, P = a.P;
+    const int64_t row = blockIdx.x / P;
+    const int j = (int)(blockIdx.x - row * P);
+    const int64_t rowbytes = (int64_t)N * I::E;
+    const char *xr = a.x + row * rowbytes;
+    char *yr = a.y + row * rowbytes;
+    const RowGeom<DT, AL> geo(xr, N);
+    bool yvec = true;
+    if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+    const bool has_p0 = a.p0 != nullptr, has_p1 = a.p1 != nullptr;
+    __shared__ double2 red[2][W];
+    __shared__ double2 qs[COOP_PMAX];
+    __shared__ uint64_t miss[NB];
+
+    const int64_t cbase = (int64_t)j * (TPR * K);
+    uint32_t padw = 0;
+    if constexpr (OP == OP_LAYERNORM) padw = pivot_word<DT>(xr);
+    const double pv = (double)elem_of_word<DT>(padw);
+    uint4 raw[K], g4[K], b4[(OP == OP_LAYERNORM) ? K : 1];
+    load_row<DT, AL, K, TPR>(raw, geo, t, N, cbase);
+    if (has_p0) load_params<DT, AL, K, TPR>(g4, geo, a.p0, t, N, cbase);
+    if constexpr (OP == OP_LAYERNORM) {
+        if (has_p1) load_params<DT, AL, K, TPR>(b4, geo, a.p1, t, N, cbase);
+    }
+    finish_row<DT, AL, K, TPR>(raw, geo, xr, t, N, padw, cbase);
+    const double2 mine = norm_chunk_sums<OP, DT, W, K>(raw, pv, red[0], wv, lane);
+
+    uint64_t *rec = reinterpret_cast<uint64_t *>(a.wsd) + row * P * NW;
+    const uint64_t tg = (uint64_t)a.tag << 32;
+    if (t == 0) {
+        const uint64_t b1 = (uint64_t)__double_as_longlong(mine.x), b2 = (uint64_t)__double_as_longlong(mine.y);
+        uint64_t *r = rec + (int64_t)NW * j;
+        __hip_atomic_store(r, tg | (b2 & 0xffffffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(r + 1, tg | (b2 >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (NW == 4) {
+            __hip_atomic_store(r + 2, tg | (b1 & 0xffffffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(r + 3, tg | (b1 >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        qs[j] = mine;
+    }
+    if (wv == 0) {
+        // bit b of `pending`: this lane's record b*64 + lane is still missing
+        uint32_t pending = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int p = b * 64 + lane;
+            if (p < P && p != j) pending |= 1u << b;
+        }
+        for (int it = 0;; ++it) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (pending >> b & 1) {
+                    const uint64_t *r = rec + (int64_t)NW * (b * 64 + lane);
+                    uint64_t w[NW];
+                    bool ok = true;
+#pragma unroll
+                    for (int q = 0; q < NW; ++q) {
+                        w[q] = __hip_atomic_load(r + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = ok && (w[q] >> 32) == a.tag;
+                    }
+                    if (ok) {
+                        const double s2 = __longlong_as_double((long long)((w[0] & 0xffffffffu) | (w[1] << 32)));
+                        double s1 = 0.0;
+                        if constexpr (NW == 4)
+                            s1 = __longlong_as_double((long long)((w[2] & 0xffffffffu) | (w[3] << 32)));
+                        qs[b * 64 + lane] = double2{s1, s2};
+                        pending &= ~(1u << b);
+                    }
+                }
+            }
+            if (__ballot(pending != 0) == 0 || it >= a.spin) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint64_t m = __ballot((pending >> b) & 1);
+            if (lane == 0) miss[b] = m;
+        }
+    }
+    __syncthreads();
+    // records that did not arrive: recompute them here (uniform loop; the
+    // reductions alternate between the two LDS slots)
+    int par = 1;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        uint64_t m = miss[b];
+        while (m) {
+            const int q = b * 64 + __builtin_ctzll(m);
+            m &= m - 1;
+            const double2 e = norm_chunk_sums_reload<OP, DT, W, K, AL>(geo, xr, t, N, padw, pv,
+                                                                       (int64_t)q * (TPR * K), red[par], wv, lane);
+            par ^= 1;
+            if (t == 0) qs[q] = e;
+        }
+    }
+    __syncthreads();
+
+    // the row's sums in the finalize kernel's order: lane l takes l, l + 64, ...
+    double s1 = 0.0, s2 = 0.0;
+    for (int q = lane; q < P; q += 64) {
+        s1 += qs[q].x;
+        s2 += qs[q].y;
+    }
+    const double2 st = wave_allreduce(double2{s1, s2}, SumOp());
+    double m1 = 0.0, scale;
+    if constexpr (OP == OP_LAYERNORM) {
+        m1 = st.x * a.inv_nd;
+        const double var = __builtin_fmax(st.y * a.inv_nd - m1 * m1, 0.0);
+        scale = rsqrt_f64(var + (double)a.eps);
+        if (j == 0 && t == 0) {
+            if (a.mean) a.mean[row] = (float)(pv + m1);
+            if (a.rstd) a.rstd[row] = (float)scale;
+        }
+    } else {
+        scale = rsqrt_f64(st.y * a.inv_nd + (double)a.eps);
+    }
+    const float scale_f = (float)scale;
+    const double nm = -m1 * scale;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float v[VEC], g[VEC], b[VEC];
+        unpack<DT>(raw[k], v);
+        if (has_p0) unpack<DT>(g4[k], g);
+        if constexpr (OP == OP_LAYERNORM) {
+            if (has_p1) unpack<DT>(b4[k], b);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const float gi = has_p0 ? g[i] : 1.0f;
+            if constexpr (OP == OP_LAYERNORM) {
+                const double d = (double)v[i] - pv;
+                v[i] = (float)__builtin_fma(__builtin_fma(d, scale, nm), (double)gi, has_p1 ? (double)b[i] : 0.0);
+            } else {
+                v[i] = (v[i] * scale_f) * gi;
+            }
+        }
+        store_slice<DT, AL, TPR>(geo, yr, k, t, N, yvec, pack<DT>(v), cbase);
+    }
 }
 
 }  // namespace ntk

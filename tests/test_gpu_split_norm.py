@@ -194,3 +194,73 @@ def test_torch_wrappers_use_the_split(op):
         y, mean, rstd = nt.rms_norm(x_t, p0_t, eps=EPS[op]), None, None
     torch.cuda.synchronize()
     check(op, y, mean, rstd, x, dt, p0, p1, f"torch wrapper split {op}")
+
+
+@pytest.mark.parametrize("op,M,N,dt,al", [("rmsnorm", 256, 65536, "f32", True), ("layernorm", 256, 65536, "f32", True),
+                                          ("rmsnorm", 128, 262144, "bf16", True), ("rmsnorm", 512, 65536, "f16", True),
+                                          ("rmsnorm", 410, 40003, "f32", False),
+                                          ("layernorm", 410, 40003, "f32", False)])
+def test_cooperative_split_norm_bitwise(op, M, N, dt, al, monkeypatch):
+    """The one-pass form (records exchanged between a row's workgroups) passes
+    the oracle and gives the two-kernel form's bits, also when every other
+    chunk's record is recomputed by the waiting workgroup (no wait at all)."""
+    code = DT_CODE[dt]
+    xo = 0 if al else 1
+    p = nt.nt_plan_launch(WS_CODE[op], M, N, code, al)
+    assert p["split"] == 3 and p["cooperative"] == 1, p
+    seed = 7 * M + N
+    x = rand_bits(seed, M, N, dt, scale=2.0, loc=1.0)
+    p0, p1 = params(op, N, dt, seed)
+    x_t, p0_t = to_dev(x, dt, xo), to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    say(f"case coop split {op} {dt} M={M} N={N} aligned={al} P={p['row_chunks']}")
+    a, am, ar = run_ws(op, x_t, dt, p0_t, p1_t)
+    check(op, a, am, ar, x, dt, p0, p1, f"coop split {op} {dt} M={M} N={N}")
+    outs = []
+    for env, val in (("NT_COOP_SPIN", "0"), ("NT_COOP", "0")):
+        monkeypatch.setenv(env, val)
+        if env == "NT_COOP":
+            # the two kernels at this row count
+            monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+            q = nt.nt_plan_launch(WS_CODE[op], M, N, code, al)
+            assert q["split"] == 3 and q["cooperative"] == 0, q
+        say(f"case coop split {op} {dt} M={M} N={N} {env}={val}")
+        outs.append((env, run_ws(op, x_t, dt, p0_t, p1_t),
+                     (q["waves_per_row"], q["chunks_per_lane"]) == (8, 4) if env == "NT_COOP" else True))
+        monkeypatch.delenv(env)
+        monkeypatch.delenv("NT_NORM_SPLIT_ROWS", raising=False)
+    ref = to_host_bits(a, dt)
+    for env, (y, ym, yr), same_chunks in outs:
+        if same_chunks:
+            # same chunks (records recomputed, or the two kernels): bitwise
+            assert np.array_equal(to_host_bits(y, dt), ref), env
+            if op == "layernorm":
+                assert torch.equal(ym, am) and torch.equal(yr, ar), env
+        else:
+            # the two kernels on other chunks: the oracle's bar
+            check(op, y, ym, yr, x, dt, p0, p1, f"two-kernel split {op} {dt} M={M} N={N}")
+
+
+def test_cooperative_split_norm_on_concurrent_streams():
+    """Two calls in flight at once on two streams, each with its own
+    workspace: records are per workspace and tagged per call."""
+    M, N, dt = 128, 262144, "bf16"
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, M, N, nt.NT_BF16, True)["cooperative"] == 1
+    xs = [rand_bits(40 + i, M, N, dt, scale=2.0) for i in range(2)]
+    w = rand_bits(43, 1, N, dt, scale=0.3, loc=1.0)[0]
+    w_t = to_dev(w, dt)
+    need = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, M, N, nt.NT_BF16)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    x_ts = [to_dev(x, dt) for x in xs]
+    ys = [empty_like_dev((M, N), dt) for _ in range(2)]
+    wss = [torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    say(f"case coop split on two streams M={M} N={N}")
+    for _ in range(3):
+        for i in range(2):
+            rc = nt.nt_rmsnorm_rows_ws(M, N, nt.NT_BF16, EPS["rmsnorm"], x_ts[i].data_ptr(), w_t.data_ptr(),
+                                       ys[i].data_ptr(), wss[i].data_ptr(), need, streams[i].cuda_stream)
+            assert rc == 0
+    torch.cuda.synchronize()
+    for i in range(2):
+        check("rmsnorm", ys[i], None, None, xs[i], dt, w, None, f"two streams, stream {i}")

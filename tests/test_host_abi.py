@@ -324,38 +324,54 @@ def test_norm_workspace_bytes():
     assert nt.nt_norm_workspace_bytes(RMS, 4, 32768, F32) > 0
     assert nt.nt_norm_workspace_bytes(LN, 4096, 1 << 20, BF16) == 0
     # 64 fp32 rows of 1 MiB: 32 KiB chunks (8 waves x 4 chunks) -> 32 per row,
-    # 33 for a misaligned head; 16 bytes per chunk and 8 per row
-    assert nt.nt_norm_workspace_bytes(LN, 64, 262144, F32) == 64 * 33 * 16 + 64 * 8
+    # 33 for a misaligned head; 32 bytes per chunk (four tagged words) and 8 per row
+    assert nt.nt_norm_workspace_bytes(LN, 64, 262144, F32) == 64 * 33 * 32 + 64 * 8
     # 16 bf16 rows of 2 MiB: 8 KiB chunks fill the grid -> 256 per row (+1)
-    assert nt.nt_norm_workspace_bytes(RMS, 16, 1 << 20, BF16) == 16 * 257 * 16 + 16 * 8
+    assert nt.nt_norm_workspace_bytes(RMS, 16, 1 << 20, BF16) == 16 * 257 * 32 + 16 * 8
     # other ops and invalid arguments
     for bad in ((nt.NT_OP_SOFTMAX, 4, 1 << 20, F32), (LN, -1, 1 << 20, F32), (LN, 4, 0, F32), (RMS, 4, 1 << 20, 5)):
         assert nt.nt_norm_workspace_bytes(*bad) == 0
 
 
+def _split_norm_plan(base, dt, M, nch, coop=True):
+    """The split norm's expected plan: ((W, K), one_pass), or None for the
+    looped plan.  One pass with 8 waves x 4 chunks per lane at any row count
+    when the row has at most 16 such chunks, the call at least 2048
+    workgroups, and the op is not 16-bit LayerNorm; else two kernels below
+    256 (LayerNorm) or 2048 (RMSNorm) rows, with the largest chunk of 8x4,
+    8x1, 4x1 giving at least 2048 workgroups (else 4x1)."""
+    shapes = ((8, 4), (8, 1), (4, 1))
+    P = lambda s: -(-nch // (64 * s[0] * s[1]))  # noqa: E731
+    ln = base == nt.NT_OP_LAYERNORM
+    if coop and not (ln and dt != F32) and P((8, 4)) <= 16 and M * P((8, 4)) >= 2048:
+        return (8, 4), True
+    if M >= (256 if ln else 2048):
+        return None
+    return next((s for s in shapes if M * P(s) >= 2048), shapes[-1]), False
+
+
 def test_split_norm_plans():
     for op, base in ((nt.NT_OP_LAYERNORM_WS, nt.NT_OP_LAYERNORM), (nt.NT_OP_RMSNORM_WS, nt.NT_OP_RMSNORM)):
         for dt, e in ((F32, 4), (F16, 2), (BF16, 2)):
-            for M, N in ((1, 40000), (3, 100003), (64, 262144), (16, 1 << 20), (1000, 65536), (255, 20000)):
+            for M, N in ((1, 40000), (3, 100003), (64, 262144), (16, 1 << 20), (1000, 65536), (255, 20000),
+                         (4096, 65536), (300, 262144), (5000, 40003)):
                 for al in (True, False):
                     p = nt.nt_plan_launch(op, M, N, dt, al)
                     plain = nt.nt_plan_launch(base, M, N, dt, al)
-                    # one pass, or enough rows to fill the GPU: the workspace changes nothing
-                    # (LayerNorm splits below 256 rows, RMSNorm below 2048)
-                    if plain["split"] == 0 or M >= (256 if base == nt.NT_OP_LAYERNORM else 2048):
-                        assert p == plain
-                        continue
-                    assert p["split"] == 3 and plain["split"] == 2, (op, dt, M, N, al)
-                    per = 64 * p["waves_per_row"] * p["chunks_per_lane"]
                     aligned = al and (N * e) % 16 == 0
                     nch = N * e // 16 if aligned else (N + 2 * (16 // e) - 2) // (16 // e)
+                    want = _split_norm_plan(base, dt, M, nch) if plain["split"] == 2 else None
+                    if want is None:          # one pass, or the looped plan: the workspace changes nothing
+                        assert p == plain, (op, dt, M, N, al)
+                        continue
+                    assert p["split"] == 3, (op, dt, M, N, al, p)
+                    assert ((p["waves_per_row"], p["chunks_per_lane"]), bool(p["cooperative"])) == want, \
+                        (op, dt, M, N, al, p)
+                    per = 64 * p["waves_per_row"] * p["chunks_per_lane"]
                     assert p["row_chunks"] == -(-nch // per) and p["grid"] == M * p["row_chunks"]
-                    assert (p["waves_per_row"], p["chunks_per_lane"]) in ((8, 4), (8, 1), (4, 1))
-                    # the largest chunk that still gives 2048 workgroups, else the smallest
-                    assert p["grid"] >= 2048 or (p["waves_per_row"], p["chunks_per_lane"]) == (4, 1)
-                    assert p["workspace_bytes"] == M * p["row_chunks"] * 16 + M * 8
+                    assert p["workspace_bytes"] == M * p["row_chunks"] * 32 + M * 8
                     assert p["workspace_bytes"] <= nt.nt_norm_workspace_bytes(base, M, N, dt)
-        # many rows fill the GPU without the split
+        # many rows of many chunks: looped
         assert nt.nt_plan_launch(op, 4096, 1 << 20, BF16, True)["split"] == 2
     assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 256, 1 << 20, BF16, True)["split"] == 2
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 2047, 1 << 20, BF16, True)["split"] == 3
@@ -367,3 +383,28 @@ def test_split_norm_rows_switch(monkeypatch):
     assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 64, 262144, F32) == 0
     monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 4096, 262144, F32, True)["split"] == 3
+
+
+def test_split_norm_cooperative_switch(monkeypatch):
+    # 128 bf16 rows of 512 KiB: 16 chunks of 32 KiB per row in one pass
+    p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 128, 262144, BF16, True)
+    assert (p["split"], p["cooperative"], p["row_chunks"], p["grid"]) == (3, 1, 16, 2048)
+    # not for 16-bit LayerNorm: two kernels, same chunks
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 128, 262144, BF16, True)
+    assert (p["split"], p["cooperative"], p["row_chunks"]) == (3, 0, 16)
+    # one pass at any row count where it applies; fp32 LayerNorm included
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 65536, 65536, F32, True)
+    assert (p["split"], p["cooperative"], p["row_chunks"]) == (3, 1, 8)
+    monkeypatch.setenv("NT_COOP", "0")
+    p2 = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 128, 262144, BF16, True)
+    assert (p2["split"], p2["cooperative"], p2["row_chunks"]) == (3, 0, 16)
+    p3 = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 64, 65536, F32, True)      # 2048 workgroups need 8 KiB chunks
+    assert (p3["split"], p3["cooperative"], p3["row_chunks"]) == (3, 0, 32)
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 65536, 65536, F32, True)["split"] == 2
+    # the documented size covers both forms and both alignments (9 chunks
+    # of 32 KiB with a misaligned head)
+    need = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32)
+    assert need == 256 * 9 * 32 + 256 * 8
+    monkeypatch.delenv("NT_COOP")
+    assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32) == need
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 256, 65536, F32, True)["row_chunks"] == 8

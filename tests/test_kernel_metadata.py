@@ -145,6 +145,9 @@ def _shapes(kernels):
         m = re.search(r"norm_split_(partial|finalize)ILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
         if m:
             have.add(("n" + m.group(1),) + tuple(int(g) for g in m.groups()[1:]))
+        m = re.search(r"norm_coopILi(\d)ELi(\d)ELi(\d+)ELi(\d+)ELb(\d)", name)
+        if m:
+            have.add(("ncoop",) + tuple(int(g) for g in m.groups()))
     return have
 
 
@@ -173,6 +176,8 @@ def test_every_planned_shape_is_built(kernels):
                     elif p["split"] == 3:
                         assert ("npartial", base, dt, W, K, A) in have, (op, dt, N, al, p)
                         assert ("nfinalize", base, dt, W, K, A) in have, (op, dt, N, al, p)
+                        if p["cooperative"]:
+                            assert ("ncoop", base, dt, W, K, A) in have, (op, dt, N, al, p)
                     else:
                         assert ("res", base, dt, W, K, A, res) in have, (op, dt, N, al, p)
                         if p["persistent"]:
