@@ -605,8 +605,9 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                  f"    python3 bench.py --sweep-wide-norms --steps {steps} --warmup {warmup} --sweep-md {md_path}", "",
                  "GB/s = algorithmic bytes (rows in and out, parameter vectors, LayerNorm's mean and rstd) / median "
                  "event-timed launch, inputs rotating through a 1 GiB pool.  split: nt_*_rows_ws with the split "
-                 "forced at every row count, the row's chunks on many workgroups, in one pass where the row has at "
-                 "most 128 chunks (1p) else two kernels; 2k: the same with NT_COOP=0 (two kernels, x read twice); "
+                 "forced at every row count, the row's chunks on many workgroups: in one pass where the planner allows "
+                 "it (at most 16 chunks of 32 KiB per row, at least 2048 workgroups, not 16-bit LayerNorm), else two "
+                 "kernels; 2k: the same with NT_COOP=0 (two kernels, x read twice); "
                  "looped: the plain entry point (one workgroup per row, the row streamed twice); torch: "
                  "F.layer_norm / F.rms_norm on the same buffers.  plan: what nt_*_rows_ws picks by itself.", "",
                  "| type | N | M | LN plan | LN split | LN 2k | LN looped | LN torch | RMS plan | RMS split | RMS 2k | "
