@@ -11,17 +11,17 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
 
   python -m row_wise_reductions_amd.rocprof_summary traffic --fetch DIR --write DIR \\
          --calib-fetch DIR --calib-write DIR --cmds FILE --md FILE.md --json FILE.json
+      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc FETCH_SIZE`
+      and `--pmc WRITE_SIZE` runs of bench.py and of `bench.py --calibrate`.
+      Counter values (KiB per dispatch) are scaled by what the same counter
+      reads for the calibration copy of known size (1 GiB read + 1 GiB
+      written), giving HBM bytes per call of each workload.
 
   python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR [--valu DIR] --cmds FILE --md FILE.md
       DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`,
       `--pmc MeanOccupancyPerActiveCU` and `--pmc VALUBusy` runs of bench.py; beside them, each
       kernel's registers, LDS and static occupancy limit from the built code
       object (codeobj.py).
-      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc FETCH_SIZE`
-      and `--pmc WRITE_SIZE` runs of bench.py and of `bench.py --calibrate`.
-      Counter values (KiB per dispatch) are scaled by what the same counter
-      reads for the calibration copy of known size (1 GiB read + 1 GiB
-      written), giving HBM bytes per call of each workload.
 """
 from __future__ import annotations
 
