@@ -264,3 +264,57 @@ def test_cooperative_split_norm_on_concurrent_streams():
     torch.cuda.synchronize()
     for i in range(2):
         check("rmsnorm", ys[i], None, None, xs[i], dt, w, None, f"two streams, stream {i}")
+
+
+def test_split_norm_graph_capture_and_replay():
+    """Split norms captured into a HIP graph and replayed with new inputs
+    copied in (eagerly) between replays: every replay matches the oracle.
+    Under capture the one-pass form is not used (a replay would reuse the
+    call's record tag): the shape that runs in one pass eagerly is captured
+    as two kernels."""
+    M, N = 128, 262144
+    xs = [rand_bits(70 + i, M, N, "bf16", scale=2.0 + i, loc=0.5) for i in range(3)]
+    w = rand_bits(73, 1, N, "bf16", scale=0.3, loc=1.0)[0]
+    lx = [rand_bits(80 + i, 4, 100003, "f32", scale=1.0 + i, loc=-1.0) for i in range(3)]
+    g_ = rand_bits(83, 1, 100003, "f32", scale=0.3, loc=1.0)[0]
+    b_ = rand_bits(84, 1, 100003, "f32", scale=0.3)[0]
+    assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, M, N, nt.NT_BF16, True)["cooperative"] == 1
+    x_t, w_t, y_t = to_dev(xs[0], "bf16"), to_dev(w, "bf16"), empty_like_dev((M, N), "bf16")
+    lx_t, g_t, b_t = to_dev(lx[0], "f32"), to_dev(g_, "f32"), to_dev(b_, "f32")
+    ly_t = empty_like_dev((4, 100003), "f32")
+    mean = torch.empty(4, device="cuda")
+    rstd = torch.empty(4, device="cuda")
+    wsb = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, M, N, nt.NT_BF16)
+    lwsb = nt.nt_norm_workspace_bytes(nt.NT_OP_LAYERNORM, 4, 100003, nt.NT_F32)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    lws = torch.empty(lwsb, dtype=torch.uint8, device="cuda")
+
+    def calls(stream):
+        assert nt.nt_rmsnorm_rows_ws(M, N, nt.NT_BF16, EPS["rmsnorm"], x_t.data_ptr(), w_t.data_ptr(),
+                                     y_t.data_ptr(), ws.data_ptr(), wsb, stream) == 0
+        assert nt.nt_layernorm_rows_ws(4, 100003, nt.NT_F32, EPS["layernorm"], lx_t.data_ptr(), g_t.data_ptr(),
+                                       b_t.data_ptr(), ly_t.data_ptr(), mean.data_ptr(), rstd.data_ptr(),
+                                       lws.data_ptr(), lwsb, stream) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = to_host_bits(y_t, "bf16")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(torch.cuda.current_stream().cuda_stream)
+    for i in (1, 0, 2, 2, 1):
+        say(f"case split-norm graph replay inputs {i}")
+        x_t.copy_(to_dev(xs[i], "bf16"))
+        lx_t.copy_(to_dev(lx[i], "f32"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check("rmsnorm", y_t, None, None, xs[i], "bf16", w, None, f"graph split rmsnorm {i}")
+        check("layernorm", ly_t, mean, rstd, lx[i], "f32", g_, b_, f"graph split layernorm {i}")
+        if i == 0:
+            # the captured two kernels on the eager call's chunks: the eager one-pass bits
+            assert np.array_equal(to_host_bits(y_t, "bf16"), eager)

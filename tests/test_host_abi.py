@@ -389,9 +389,10 @@ def test_split_norm_cooperative_switch(monkeypatch):
     # 128 bf16 rows of 512 KiB: 16 chunks of 32 KiB per row in one pass
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 128, 262144, BF16, True)
     assert (p["split"], p["cooperative"], p["row_chunks"], p["grid"]) == (3, 1, 16, 2048)
-    # not for 16-bit LayerNorm: two kernels, same chunks
+    # not for 16-bit LayerNorm: two kernels (same chunks) at few rows, the looped kernel at many
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 128, 262144, BF16, True)
     assert (p["split"], p["cooperative"], p["row_chunks"]) == (3, 0, 16)
+    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 4096, 131072, F16, True)["split"] == 2
     # one pass at any row count where it applies; fp32 LayerNorm included
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 65536, 65536, F32, True)
     assert (p["split"], p["cooperative"], p["row_chunks"]) == (3, 1, 8)
