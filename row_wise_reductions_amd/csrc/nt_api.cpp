@@ -265,6 +265,7 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
 // looped kernel below 64 rows.
 bool split_norm_plan(nt_op op, nt_dtype dt, int64_t M, int64_t nch, bool coop, Shape *out, int64_t *P,
                      bool *cooperative) {
+    if (M <= 0) return false;                            // nothing to split (callers divide by M)
     auto chunks = [nch](const Shape &c) { return (nch + 64 * c.W * c.K - 1) / (64 * c.W * c.K); };
     const Shape big = kNormSplit[0];
     if (coop && !(op == NT_OP_LAYERNORM && dt != NT_F32) && chunks(big) <= kNormCoopPMax &&

@@ -331,6 +331,12 @@ def test_norm_workspace_bytes():
     # other ops and invalid arguments
     for bad in ((nt.NT_OP_SOFTMAX, 4, 1 << 20, F32), (LN, -1, 1 << 20, F32), (LN, 4, 0, F32), (RMS, 4, 1 << 20, 5)):
         assert nt.nt_norm_workspace_bytes(*bad) == 0
+    # no rows: nothing to split (a regression: the grid check divided by M)
+    for op in (LN, RMS):
+        for dt in (F32, F16, BF16):
+            assert nt.nt_norm_workspace_bytes(op, 0, 1 << 20, dt) == 0
+            ws_op = nt.NT_OP_LAYERNORM_WS if op == LN else nt.NT_OP_RMSNORM_WS
+            assert nt.nt_plan_launch(ws_op, 0, 1 << 20, dt, True) == nt.nt_plan_launch(op, 0, 1 << 20, dt, True)
 
 
 def _split_norm_plan(base, dt, M, nch, coop=True):
@@ -409,3 +415,35 @@ def test_split_norm_cooperative_switch(monkeypatch):
     monkeypatch.delenv("NT_COOP")
     assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32) == need
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 256, 65536, F32, True)["row_chunks"] == 8
+
+
+def test_planner_survives_extreme_arguments():
+    """The host-only calls (plans, workspace sizes) over every op, type and
+    extreme sizes, in a child process so that a crash (a division by zero, an
+    overflow trap) fails this test instead of the test run: each returns a
+    plan, an error status or a size, never a signal."""
+    import subprocess
+    import sys
+    code = r'''
+import row_wise_reductions_amd as nt
+Ms = (0, 1, 2, 255, 256, 2047, 2048, 4096, 1 << 20, (1 << 31) - 1, 1 << 31, 1 << 40)
+Ns = (1, 7, 781, 8192, 16385, 32769, 1 << 20, (1 << 31) - 1, 1 << 31)
+n = 0
+for op in range(8):
+    for M in Ms:
+        for N in Ns:
+            for dt in (0, 1, 2, 3):
+                for al in (True, False):
+                    try:
+                        nt.nt_plan_launch(op, M, N, dt, al)
+                    except nt.NtError:
+                        pass
+                    n += 1
+                if op < 3:
+                    nt.nt_softmax_workspace_bytes(M, N, dt)
+                    nt.nt_norm_workspace_bytes(op, M, N, dt)
+print("ok", n)
+'''
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout[-500:], r.stderr[-2000:])
