@@ -10,9 +10,15 @@
  *
  * Everything is computed in IEEE double precision from the exact input bits:
  * inputs stored as fp32, fp16 or bf16 are decoded exactly to double by this
- * file's own decoders, every sum runs in element index order, and results are
- * returned as doubles.  Rounding a result to the output storage type is done
- * once, by the caller's comparator, never here.
+ * file's own decoders, every row sum runs in element index order with
+ * Neumaier's compensation (or_acc below), and results are returned as
+ * doubles.  Rounding a result to the output storage type is done once, by the
+ * caller's comparator, never here.  The compensation matters for long rows of
+ * 16-bit inputs: their few distinct values make the rounding errors of a
+ * plain running sum add up in one direction (2^28 bf16 values: about 1e-9
+ * relative in LayerNorm's sum of squares), which a LayerNorm output that
+ * nearly cancels (y = (x - mean) * rstd * gamma + beta close to 0) magnifies
+ * beyond one unit in the last place of a bf16 result.
  *
  * Sources (cited by page title and section):
  *  - softmax: "Portable Triton Kernels" (Hugging Face kernel-builder
@@ -89,6 +95,34 @@ static double or_load(int dtype, const void *base, int64_t idx)
     return NAN;
 }
 
+/*
+ * Compensated running sum (Neumaier's refinement of Kahan summation): the
+ * rounding error of every addition is recovered exactly (two-sum) and
+ * accumulated apart, and added back once at the end, so the error of the sum
+ * stays about one rounding of the result instead of growing with the number
+ * of terms.  Once the running sum is not finite it is returned as it is (the
+ * plain sum's inf or NaN).  Needs strict IEEE evaluation (no reassociation,
+ * no contraction), which the build flags ask for.
+ */
+typedef struct { double s, c; } or_acc;
+
+static void or_acc_add(or_acc *a, double v)
+{
+    double t = a->s + v;
+    if (isfinite(t)) {
+        if (fabs(a->s) >= fabs(v))
+            a->c += (a->s - t) + v;
+        else
+            a->c += (v - t) + a->s;
+    }
+    a->s = t;
+}
+
+static double or_acc_sum(const or_acc *a)
+{
+    return isfinite(a->s) ? a->s + a->c : a->s;
+}
+
 static int or_check(int64_t M, int64_t N, int dtype)
 {
     if (M < 0 || N <= 0) return 1;
@@ -122,15 +156,16 @@ int or_softmax(int64_t M, int64_t N, int dtype, const void *x, double *y)
             if (isnan(v) || isnan(m)) m = NAN;
             else if (v > m) m = v;
         }
-        double s = 0.0;
+        or_acc acc = {0.0, 0.0};
         for (int64_t j = 0; j < N; ++j) {
             double v = or_load(dtype, x, base + j);
             /* exp(-inf - m) is exactly 0 for finite m; for m = -inf the
              * difference is NaN, which is the all-masked row's result. */
             double e = exp(v - m);
             yr[j] = e;
-            s += e;
+            or_acc_add(&acc, e);
         }
+        const double s = or_acc_sum(&acc);
         for (int64_t j = 0; j < N; ++j)
             yr[j] = yr[j] / s;
     }
@@ -148,16 +183,16 @@ int or_layernorm(int64_t M, int64_t N, int dtype, float eps, const void *x,
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < M; ++r) {
         int64_t base = r * N;
-        double s1 = 0.0;
+        or_acc a1 = {0.0, 0.0};
         for (int64_t j = 0; j < N; ++j)
-            s1 += or_load(dtype, x, base + j);
-        double mu = s1 / (double)N;
-        double s2 = 0.0;
+            or_acc_add(&a1, or_load(dtype, x, base + j));
+        double mu = or_acc_sum(&a1) / (double)N;
+        or_acc a2 = {0.0, 0.0};
         for (int64_t j = 0; j < N; ++j) {
             double d = or_load(dtype, x, base + j) - mu;
-            s2 += d * d;
+            or_acc_add(&a2, d * d);
         }
-        double var = s2 / (double)N;
+        double var = or_acc_sum(&a2) / (double)N;
         double rs = 1.0 / sqrt(var + deps);
         for (int64_t j = 0; j < N; ++j) {
             double g = gamma ? or_load(dtype, gamma, j) : 1.0;
@@ -180,12 +215,12 @@ int or_rmsnorm(int64_t M, int64_t N, int dtype, float eps, const void *x,
     #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < M; ++r) {
         int64_t base = r * N;
-        double ss = 0.0;
+        or_acc acc = {0.0, 0.0};
         for (int64_t j = 0; j < N; ++j) {
             double v = or_load(dtype, x, base + j);
-            ss += v * v;
+            or_acc_add(&acc, v * v);
         }
-        double inv = 1.0 / sqrt(ss / (double)N + deps);
+        double inv = 1.0 / sqrt(or_acc_sum(&acc) / (double)N + deps);
         for (int64_t j = 0; j < N; ++j) {
             double wv = w ? or_load(dtype, w, j) : 1.0;
             y[base + j] = or_load(dtype, x, base + j) * inv * wv;
@@ -248,11 +283,12 @@ int or_softmax_causal(int64_t M, int64_t N, int dtype, float scale, int64_t quer
             if (isnan(v) || isnan(m)) m = NAN;
             else if (v > m) m = v;
         }
-        double s = 0.0;
+        or_acc acc = {0.0, 0.0};
         for (int64_t k = 0; k < vis; ++k) {
             double v = sc * or_load(dtype, x, base + k);
-            s += (v == -INFINITY) ? 0.0 : exp(v - m);
+            or_acc_add(&acc, (v == -INFINITY) ? 0.0 : exp(v - m));
         }
+        const double s = or_acc_sum(&acc);
         for (int64_t k = 0; k < vis; ++k) {
             double v = sc * or_load(dtype, x, base + k);
             y[base + k] = ((v == -INFINITY) ? 0.0 : exp(v - m)) / s;

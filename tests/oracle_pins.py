@@ -274,6 +274,39 @@ def pin_layernorm_affine_invariance(lib):
     assert _rel(rs2, rs / 4.0) < 1e-12
 
 
+def pin_layernorm_long_periodic_row(lib):
+    """A long row that repeats (0, 1, 1) in bf16 (3 * 2^22 elements) has mean
+    exactly 2/3 and biased variance exactly 2/9, so rstd = 1/sqrt(2/9 + eps)
+    and y = (x - 2/3) * rstd.  A plain running sum of its squared deviations
+    drifts by about 1e-10 relative (its few distinct terms round the same
+    way again and again); the oracle's sums must stay within a few
+    roundings."""
+    reps = 1 << 22
+    x = np.tile(np.array([0x0000, 0x3F80, 0x3F80], dtype=np.uint16), reps).reshape(1, 3 * reps)
+    y, mu, rs = oracle.layernorm(x, "bf16", 1e-5, lib=lib)
+    want = 1.0 / math.sqrt(2.0 / 9.0 + F32_EPS5)
+    assert _rel(mu, [2.0 / 3.0]) < 1e-15
+    assert _rel(rs, [want]) < 1e-13
+    assert _rel(y[0, :3], [-2.0 / 3.0 * want, 1.0 / 3.0 * want, 1.0 / 3.0 * want]) < 1e-13
+
+
+def pin_rmsnorm_long_periodic_row(lib):
+    """RMSNorm of a long row repeating (a, a, b) with a = fp32(0.1), b =
+    fp32(0.3) (3 * 2^22 elements): the mean square is exactly (2a^2 + b^2)/3
+    (computed here in rationals), so y = x / sqrt(that + eps).  The squares
+    carry bits below the last place of the running sum, and a plain running
+    sum drifts by about 5e-11 relative; the oracle's stays within a few
+    roundings."""
+    from fractions import Fraction
+    reps = 1 << 22
+    a, b = np.float32(0.1), np.float32(0.3)
+    x = np.tile(np.array([a, a, b], dtype=np.float32), reps).reshape(1, 3 * reps)
+    y = oracle.rmsnorm(x, "f32", 1e-6, lib=lib)
+    ms = float((2 * Fraction(float(a)) ** 2 + Fraction(float(b)) ** 2) / 3)
+    inv = 1.0 / math.sqrt(ms + float(np.float32(1e-6)))
+    assert _rel(y[0, :3], [float(a) * inv, float(a) * inv, float(b) * inv]) < 1e-14
+
+
 def pin_layernorm_constant_row(lib):
     """A constant row has variance 0: rstd = 1/sqrt(eps) and y = beta."""
     beta = np.array([0.5, -0.25, 2.0], dtype=np.float32)

@@ -318,3 +318,33 @@ def test_split_norm_graph_capture_and_replay():
         if i == 0:
             # the captured two kernels on the eager call's chunks: the eager one-pass bits
             assert np.array_equal(to_host_bits(y_t, "bf16"), eager)
+
+
+def test_split_layernorm_rows_past_2gib_offsets():
+    """Five bf16 rows of 2^28 + 5 elements (512 MiB each, the last one
+    starting beyond 2^31 bytes; misaligned rows): the split LayerNorm (two
+    kernels, 16385 chunks per row) against the oracle on every element,
+    compared in column blocks, with mean and rstd.  Inputs drawn in float32
+    and rounded once to bf16 to keep the host side small."""
+    import oracle
+    M, N = 5, (1 << 28) + 5
+    rng = np.random.default_rng(N)
+    x = workloads.to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32) * np.float32(2.0) + np.float32(1.0))
+    g = workloads.to_bf16_bits(np.float32(1.0) + np.float32(0.3) * rng.standard_normal(N, dtype=np.float32))
+    b = workloads.to_bf16_bits(np.float32(0.3) * rng.standard_normal(N, dtype=np.float32))
+    assert (M - 1) * N * 2 > (1 << 31)
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, M, N, nt.NT_BF16, False)
+    assert p["split"] == 3 and p["cooperative"] == 0 and p["row_chunks"] > 16384, p
+    say(f"case 2GiB-offset split layernorm bf16 M={M} N={N} P={p['row_chunks']}")
+    x_t, g_t, b_t = to_dev(x, "bf16"), to_dev(g, "bf16"), to_dev(b, "bf16")
+    y, mean, rstd = run_ws("layernorm", x_t, "bf16", g_t, b_t)
+    del x_t
+    yb = to_host_bits(y, "bf16")
+    del y
+    ref, rmean, rrstd = oracle.layernorm(x, "bf16", EPS["layernorm"], gamma=g, beta=b)
+    check_stats(mean.cpu().numpy(), rmean, "2GiB-offset split layernorm mean")
+    check_stats(rstd.cpu().numpy(), rrstd, "2GiB-offset split layernorm rstd")
+    blk = 1 << 25
+    for r in range(M):
+        for j0 in range(0, N, blk):
+            check_output(yb[r, j0:j0 + blk], ref[r, j0:j0 + blk], "bf16", f"2GiB-offset split layernorm row {r} col {j0}")

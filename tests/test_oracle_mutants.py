@@ -14,20 +14,24 @@ from oracle_pins import ALL_PINS
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
-    "ln_unbiased_variance": ("double var = s2 / (double)N;", "double var = s2 / (double)(N - 1);"),
+    "ln_unbiased_variance": ("double var = or_acc_sum(&a2) / (double)N;",
+                             "double var = or_acc_sum(&a2) / (double)(N - 1);"),
     "ln_eps_outside_sqrt": ("double rs = 1.0 / sqrt(var + deps);", "double rs = 1.0 / sqrt(var) + deps;"),
-    "ln_mean_wrong_count": ("double mu = s1 / (double)N;", "double mu = s1 / (double)(N + 1);"),
+    "ln_mean_wrong_count": ("double mu = or_acc_sum(&a1) / (double)N;",
+                            "double mu = or_acc_sum(&a1) / (double)(N + 1);"),
     "ln_gamma_beta_swapped": ("- mu) * rs * g + b;", "- mu) * rs * b + g;"),
     "ln_gamma_reversed": ("or_load(dtype, gamma, j)", "or_load(dtype, gamma, N - 1 - j)"),
     "ln_beta_dropped": ("double b = beta ? or_load(dtype, beta, j) : 0.0;", "double b = 0.0;"),
-    "rms_no_mean": ("1.0 / sqrt(ss / (double)N + deps);", "1.0 / sqrt(ss + deps);"),
+    "rms_no_mean": ("1.0 / sqrt(or_acc_sum(&acc) / (double)N + deps);", "1.0 / sqrt(or_acc_sum(&acc) + deps);"),
     "rms_weight_first_only": ("or_load(dtype, w, j)", "or_load(dtype, w, 0)"),
-    "rms_eps_dropped": ("sqrt(ss / (double)N + deps)", "sqrt(ss / (double)N)"),
+    "rms_eps_dropped": ("sqrt(or_acc_sum(&acc) / (double)N + deps)", "sqrt(or_acc_sum(&acc) / (double)N)"),
     "softmax_no_shift": ("double e = exp(v - m);", "double e = exp(v);"),
-    "softmax_dropped_term": ("s += e;", "s += (j > 0) ? e : 0.0;"),
+    "softmax_dropped_term": ("or_acc_add(&acc, e);", "or_acc_add(&acc, (j > 0) ? e : 0.0);"),
+    "sum_compensation_dropped": ("    return isfinite(a->s) ? a->s + a->c : a->s;", "    return a->s;"),
+    "sum_compensation_wrong_branch": ("        if (fabs(a->s) >= fabs(v))", "        if (fabs(a->s) < fabs(v))"),
     "softmax_exp2": ("double e = exp(v - m);", "double e = exp2(v - m);"),
     "softmax_multiply": ("yr[j] = yr[j] / s;", "yr[j] = yr[j] * s;"),
-    "softmax_max_is_min": ("else if (v > m) m = v;\n        }\n        double s", "else if (v < m || m == -INFINITY) m = v;\n        }\n        double s"),
+    "softmax_max_is_min": ("else if (v > m) m = v;\n        }\n        or_acc acc", "else if (v < m || m == -INFINITY) m = v;\n        }\n        or_acc acc"),
     "f16_bias_off_by_one": ("expo - 25", "expo - 24"),
     "f16_subnormal_scale": ("ldexp((double)mant, -24)", "ldexp((double)mant, -25)"),
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
