@@ -348,3 +348,38 @@ def test_split_layernorm_rows_past_2gib_offsets():
     for r in range(M):
         for j0 in range(0, N, blk):
             check_output(yb[r, j0:j0 + blk], ref[r, j0:j0 + blk], "bf16", f"2GiB-offset split layernorm row {r} col {j0}")
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "layernorm"])
+def test_cooperative_split_norm_large_grid(op, monkeypatch):
+    """8192 fp32 rows of 65536 elements in one pass: 65536 workgroups, far
+    more than are resident at once, so rows straddle dispatch waves and some
+    workgroups wait on siblings that start later.  Sampled rows against the
+    oracle; every output bitwise equal to the two-kernel form on the same
+    chunks."""
+    M, N, dt = 8192, 65536, "f32"
+    p = nt.nt_plan_launch(WS_CODE[op], M, N, nt.NT_F32, True)
+    assert p["split"] == 3 and p["cooperative"] == 1 and p["grid"] == M * 8, p
+    rng = np.random.default_rng(M + N)
+    x = (rng.standard_normal((M, N), dtype=np.float32) * np.float32(1.5) + np.float32(0.25))
+    p0, p1 = params(op, N, dt, 99)
+    x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)
+    p1_t = None if p1 is None else to_dev(p1, dt)
+    say(f"case coop split large grid {op} {dt} M={M} N={N} grid={p['grid']}")
+    a, am, ar = run_ws(op, x_t, dt, p0_t, p1_t)
+    rows = np.unique(np.concatenate([np.random.default_rng(5).choice(M, 48, replace=False), [0, 1, M - 1]]))
+    ab = to_host_bits(a, dt)
+    ref, rmean, rrstd = oracle_for(op, x[rows], dt, EPS[op], p0, p1)
+    check_output(ab[rows], ref, dt, f"coop large grid {op}")
+    if op == "layernorm":
+        check_stats(am.cpu().numpy()[rows], rmean, "coop large grid mean")
+        check_stats(ar.cpu().numpy()[rows], rrstd, "coop large grid rstd")
+    monkeypatch.setenv("NT_COOP", "0")
+    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+    q = nt.nt_plan_launch(WS_CODE[op], M, N, nt.NT_F32, True)
+    assert (q["split"], q["cooperative"], q["row_chunks"], q["chunks_per_lane"]) == (3, 0, 8, 4), q
+    say(f"case two-kernel split large grid {op} {dt} M={M} N={N}")
+    b, bm, br = run_ws(op, x_t, dt, p0_t, p1_t)
+    assert np.array_equal(to_host_bits(b, dt), ab)
+    if op == "layernorm":
+        assert torch.equal(am, bm) and torch.equal(ar, br)
