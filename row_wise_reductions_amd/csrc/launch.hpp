@@ -35,9 +35,11 @@ hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, 
 hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 
-// Launch the split norm (a few rows too wide for one pass): the partial
-// kernel, then the finalize kernel, one workgroup per (row, chunk), a.P
-// chunks per row, a.wsd holding 2 doubles per (row, chunk).
+// Launch the split norm (rows too wide for one pass, cut into a.P chunks of
+// 64*W*K 16-byte pieces, one workgroup per (row, chunk)): with `coop` the
+// one-pass kernel (a.wsd holds four tagged 64-bit words per (row, chunk);
+// a.tag, a.spin set), else the partial kernel, then the finalize kernel
+// (a.wsd holds 2 doubles per (row, chunk), then a pivot per row).
 hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
 hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);

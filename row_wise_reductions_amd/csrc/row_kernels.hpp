@@ -35,6 +35,10 @@
 //                         exchange (max, denominator) records
 //   softmax_split_partial / softmax_split_finalize
 //                         the same split softmax in two kernels
+//   norm_coop             split LayerNorm / RMSNorm in one pass: the
+//                         workgroups of a row exchange fp64 sum records
+//   norm_split_partial / norm_split_finalize
+//                         the same split norm in two kernels
 #pragma once
 
 #include <hip/hip_runtime.h>
