@@ -27,16 +27,16 @@ hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
 }
 
 // Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
-// arithmetic needs twice the registers) except 32 at 8 waves (rows of up to
-// 16384 elements in one pass; 512-thread workgroups leave a wave 256
-// registers; the persistent fp32 form would spill and is not built), RMSNorm
+// arithmetic needs twice the registers) except 32 at 5 to 8 waves (rows of up
+// to 16384 elements in one pass; 320- to 512-thread workgroups leave a wave
+// 256 registers; the persistent fp32 form would spill and is not built), RMSNorm
 // and softmax 64, and a fused residual add (which also
 // holds the residual's words) 32.  Wider shapes would spill registers and are
 // not built.
 template <int OP, int K, bool RES = false, int W = 0>
 constexpr bool shape_built() {
     constexpr int V = K * dt_info<DT>::VEC;
-    return OP == OP_LAYERNORM ? (V <= 16 || (W == 8 && V == 32)) : V <= (RES ? 32 : 64);
+    return OP == OP_LAYERNORM ? (V <= 16 || (W >= 5 && W <= 8 && V == 32)) : V <= (RES ? 32 : 64);
 }
 
 // Norms with every parameter vector present take the specialised PR kernel;
@@ -69,6 +69,14 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
     NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4) NTK_CASE(8, 8) NTK_CASE(8, 16)
     NTK_CASE(16, 1) NTK_CASE(16, 2)
+    // LayerNorm's shapes between powers of two: 16-bit 7 x 2 and 5..7 x 4,
+    // fp32 12 x 4 (768 threads: a wave keeps up to 170 registers)
+    if constexpr (OP == OP_LAYERNORM && !kWide) {
+        NTK_CASE(7, 2) NTK_CASE(5, 4) NTK_CASE(6, 4) NTK_CASE(7, 4)
+    }
+    if constexpr (OP == OP_LAYERNORM && kWide) {
+        NTK_CASE(12, 4)
+    }
 #undef NTK_CASE
     return hipErrorInvalidValue;
 }
@@ -133,6 +141,9 @@ hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
     NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4) NTK_CASE(8, 8) NTK_CASE(8, 16)
+    if constexpr (OP == OP_LAYERNORM && !kWide) {
+        NTK_CASE(7, 2) NTK_CASE(5, 4) NTK_CASE(6, 4) NTK_CASE(7, 4)
+    }
 #undef NTK_CASE
     return hipErrorInvalidValue;
 }

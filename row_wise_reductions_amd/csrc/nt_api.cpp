@@ -37,6 +37,7 @@ namespace {
 
 struct Shape {
     int W, K;
+    int cap = 0;     // menu entries: most chunks per row it is chosen for (0: its capacity, 64*W*K)
 };
 
 // Single-pass shapes in order of capacity (64*W*K chunks of 16 bytes).  None
@@ -62,14 +63,21 @@ struct Menu {
 // x 1 chunk for rows of 129..256 chunks (3% over one wave x 4 at large M),
 // 8 x 1 for 257..512 (6% over 1 x 8), fp32 16 x 2 for 1025..2048.  LayerNorm,
 // whose fp64 statistics lengthen each row's compute, prefers fewer waves:
-// f16 2 x 2 for 129..256 chunks, fp32 2 x 4 for 257..512 (2-5%).  The fused
-// residual add + norm entries have menus of their own (below).
+// f16 2 x 2 for 129..256 chunks, fp32 2 x 4 for 257..512 (2-5%); and it
+// takes 5-7 waves (12 for fp32 with 4 chunks) where a power of two would
+// leave lanes idle: 16-bit 7 x 2 for 513..896 chunks (1-3% over 8 x 2),
+// 5 x 4 to 1216 chunks, 6 x 4 to 1408, 7 x 4 from 1473 to 1792 (2-5% over
+// 8 x 4; near the top of its capacity 5 x 4 and 6 x 4 fell 2-7% behind
+// 8 x 4, hence the caps), fp32 12 x 4 for 2049..3072 (2-8% over 8 x 8; two
+// M = 4096 sweeps of the pages' widths).  The fused residual add + norm
+// entries have menus of their own (below).
 const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
 const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
 const Shape kRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kLn16[] = {{1, 1}, {1, 2}, {2, 2}, {4, 2}, {8, 2}, {8, 4}};
+const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}, {12, 4}, {8, 8}};
+const Shape kLn16[] = {{1, 1},       {1, 2},       {2, 2},       {4, 2}, {7, 2}, {8, 2},
+                       {5, 4, 1216}, {6, 4, 1408}, {8, 4, 1472}, {7, 4}, {8, 4}};
 // Fused residual add + norm (two input and two output streams per row): more
 // waves per row than the plain norms at the same width.  16-bit RMSNorm rows
 // of 1025..2048 chunks take 16 waves x 2 (7% over 8 x 4); f16 LayerNorm rows
@@ -305,11 +313,13 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         } else if (full_row_shape(op, dt, nch, causal, &o)) {
             pick = o;
         } else {
-            for (int i = 0; i < menu.n; ++i)
-                if ((int64_t)64 * menu.s[i].W * menu.s[i].K >= nch && shape_fits(op, dt, res, menu.s[i])) {
-                    pick = menu.s[i];
+            for (int i = 0; i < menu.n; ++i) {
+                const Shape &c = menu.s[i];
+                if ((c.cap ? c.cap : (int64_t)64 * c.W * c.K) >= nch && shape_fits(op, dt, res, c)) {
+                    pick = {c.W, c.K};
                     break;
                 }
+            }
         }
     }
     if (pick.W) {

@@ -620,3 +620,38 @@ def test_errors_before_launch():
     assert nt.nt_layernorm_rows(M, N, nt.NT_F32, float("nan"), p, None, None, p, None, None, None) == 4
     assert nt.nt_layernorm_rows(-1, N, nt.NT_F32, 1e-5, p, None, None, p, None, None, None) == 2
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt,N,shape", [("f16", 4104, (7, 2)), ("bf16", 7168, (7, 2)), ("f16", 8200, (5, 4)),
+                                        ("bf16", 9728, (5, 4)), ("bf16", 9736, (6, 4)), ("f16", 11264, (6, 4)),
+                                        ("bf16", 11520, (8, 4)), ("bf16", 11784, (7, 4)), ("f16", 14336, (7, 4)),
+                                        ("f32", 8200, (12, 4)), ("f32", 12288, (12, 4))])
+def test_layernorm_between_power_of_two_shapes(dt, N, shape, monkeypatch):
+    """LayerNorm's shapes of 5-7 waves (16-bit) and 12 waves (fp32): the
+    persistent kernel (aligned rows, parameters present; a grid smaller than
+    the row count) against the oracle and bitwise against the one-row-per-
+    workgroup kernel, and the resident kernel on misaligned rows and
+    without parameters (the identity fills)."""
+    code = DT_CODE[dt]
+    M = 300
+    p = nt.nt_plan_launch(1, M, N, code, True)
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"]) == (0, *shape), p
+    x = rand_bits(N + 7, M, N, dt, scale=2.0, loc=-1.0)
+    g = rand_bits(N + 8, 1, N, dt, scale=0.3, loc=1.0)[0]
+    b = rand_bits(N + 9, 1, N, dt, scale=0.3)[0]
+    x_t, g_t, b_t = to_dev(x, dt), to_dev(g, dt), to_dev(b, dt)
+    monkeypatch.setenv("NT_PERSIST_GRID", "37")
+    say(f"case layernorm {dt} {M}x{N} shape {shape} persistent={p['persistent']}")
+    y1, m1, r1 = run_op("layernorm", x_t, dt, 1e-5, g_t, b_t)
+    ref, rmean, rrstd = oracle_for("layernorm", x, dt, 1e-5, g, b)
+    check_output(to_host_bits(y1, dt), ref, dt, f"layernorm {dt} {shape}")
+    check_stats(m1.cpu().numpy(), rmean, "mean")
+    check_stats(r1.cpu().numpy(), rrstd, "rstd")
+    monkeypatch.setenv("NT_PERSISTENT", "0")
+    y2, m2, r2 = run_op("layernorm", x_t, dt, 1e-5, g_t, b_t)
+    assert np.array_equal(to_host_bits(y1, dt), to_host_bits(y2, dt))
+    assert torch.equal(m1, m2) and torch.equal(r1, r2)
+    monkeypatch.delenv("NT_PERSISTENT")
+    for off in (1, 3):
+        parity_case("layernorm", x, dt, 1e-5, g, b, x_off=off, y_off=off, what=f"misaligned {dt} {shape} off={off}")
+    parity_case("layernorm", x, dt, 1e-5, None, None, what=f"no params {dt} {shape}")

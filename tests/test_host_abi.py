@@ -208,11 +208,20 @@ def test_wide_rows_take_the_streaming_paths():
     # 16-bit row, 64 KiB of fp32 row in one pass
     assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16384, BF16, True)["split"] == 0
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, BF16, True)      # 1025 whole chunks
-    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 8, 4, 1)
-    assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8193, BF16, True)["waves_per_row"] == 8
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 5, 4, 1)
+    # 16-bit: 7 x 2 to 896 chunks, 8 x 2 to 1024, then 5 x 4 to 1216 chunks, 6 x 4 to 1408,
+    # 8 x 4 to 1472, 7 x 4 to 1792, 8 x 4
+    for N, shape in ((4104, (7, 2)), (7168, (7, 2)), (7176, (8, 2)), (8192, (8, 2)), (9728, (5, 4)),
+                     (9736, (6, 4)), (11264, (6, 4)), (11272, (8, 4)), (11776, (8, 4)), (11784, (7, 4)),
+                     (14336, (7, 4)), (14344, (8, 4)), (16384, (8, 4))):
+        p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, N, F16, True)
+        assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, *shape, 1), (N, p)
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16385, BF16, True)
     assert p["split"] == 2 and p["grid"] == 1 and p["threads_per_block"] == 512
-    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, F32, True)       # fp32 8 x 8: one row per workgroup
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, F32, True)       # fp32 12 x 4: one row per workgroup
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 12, 4, 0)
+    assert p["threads_per_block"] == 768
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 12296, F32, True)      # past 12 x 4: 8 x 8
     assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 8, 8, 0)
     assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16384, F32, True)["split"] == 0
     assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16385, F32, True)["split"] == 2
