@@ -70,9 +70,19 @@
 extern "C" {
 #endif
 
-typedef enum { NT_F32 = 0, NT_F16 = 1, NT_BF16 = 2 } nt_dtype;
+/* The enumerations are int-sized in C.  Compiled as C++ they get int as a
+ * fixed underlying type, so that any int a caller passes (an unknown dtype
+ * or op code) is a valid value of the parameter and is rejected with a
+ * status, not undefined behaviour; the ABI is the same. */
+#ifdef __cplusplus
+#define NT_ENUM enum : int
+#else
+#define NT_ENUM enum
+#endif
 
-typedef enum {
+typedef NT_ENUM { NT_F32 = 0, NT_F16 = 1, NT_BF16 = 2 } nt_dtype;
+
+typedef NT_ENUM {
     NT_OK = 0,
     NT_ERR_NULL = 1,       /* a required pointer is NULL                       */
     NT_ERR_SHAPE = 2,      /* M < 0, N <= 0, N > INT32_MAX, or M*N overflows   */
@@ -247,7 +257,7 @@ const char *nt_status_string(nt_status s);
  * every pointer is 16-byte aligned (`aligned16` != 0) or not, with every
  * parameter vector present.
  */
-typedef enum {
+typedef NT_ENUM {
     NT_OP_SOFTMAX = 0,
     NT_OP_LAYERNORM = 1,
     NT_OP_RMSNORM = 2,
@@ -283,6 +293,8 @@ typedef struct {
 
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt,
                          int aligned16, nt_plan *out);
+
+#undef NT_ENUM
 
 #ifdef __cplusplus
 }

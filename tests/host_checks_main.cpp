@@ -1,0 +1,105 @@
+// Host-side checks of the library's planning and argument validation, built
+// with AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+// (tests/test_host_sanitizers.py).  The kernel launchers are replaced by
+// stubs that abort: every call made here must be answered by the host code
+// alone (a plan, a size or an error status), so reaching a launcher is a
+// failure, and so is any overflow, division by zero or out-of-bounds access
+// the sanitizers see.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "launch.hpp"
+#include "nt.h"
+
+namespace ntk {
+#define NT_STUB                                              \
+    {                                                        \
+        std::fprintf(stderr, "a kernel launcher was reached\n"); \
+        std::abort();                                        \
+    }
+hipError_t launch_resident_f32(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_resident_f16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_resident_bf16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_looped_f32(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_looped_f16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_looped_bf16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
+hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_split_f32(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_split_f16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_split_bf16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_norm_split_f32(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_norm_split_f16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_norm_split_bf16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+#undef NT_STUB
+}  // namespace ntk
+
+static int failures = 0;
+
+static void expect_error(nt_status s, const char *what) {
+    if (s == NT_OK) {
+        std::fprintf(stderr, "expected an error: %s\n", what);
+        ++failures;
+    }
+}
+
+int main() {
+    // plans and workspace sizes over every op, type and extreme sizes
+    const int64_t Ms[] = {0, 1, 2, 255, 256, 2047, 2048, 4096, 1 << 20, (1LL << 31) - 1, 1LL << 31, 1LL << 40,
+                          INT64_MAX};
+    const int64_t Ns[] = {-1, 0, 1, 7, 781, 8192, 16385, 32769, 1 << 20, (1LL << 31) - 1, 1LL << 31, INT64_MAX};
+    long plans = 0;
+    for (int op = -1; op <= 8; ++op)
+        for (int64_t M : Ms)
+            for (int64_t N : Ns)
+                for (int dt = -1; dt <= 3; ++dt) {
+                    for (int al = 0; al <= 1; ++al) {
+                        nt_plan p;
+                        if (nt_plan_launch((nt_op)op, M, N, (nt_dtype)dt, al, &p) == NT_OK) ++plans;
+                    }
+                    (void)nt_softmax_workspace_bytes(M, N, (nt_dtype)dt);
+                    (void)nt_norm_workspace_bytes(op, M, N, (nt_dtype)dt);
+                }
+    expect_error(nt_plan_launch(NT_OP_SOFTMAX, 4, 8, NT_F32, 1, nullptr), "plan into NULL");
+
+    // argument errors are answered before anything is launched
+    char buf[256];
+    void *P = buf + 64;  // a 16-byte aligned address never dereferenced on the host
+    void *odd = buf + 65;
+    const int64_t wide = 1 << 20;
+    expect_error(nt_softmax_rows(4, 8, (nt_dtype)7, P, P, nullptr, 0, nullptr), "softmax bad dtype");
+    expect_error(nt_softmax_rows(-1, 8, NT_F32, P, P, nullptr, 0, nullptr), "softmax M < 0");
+    expect_error(nt_softmax_rows(4, 0, NT_F32, P, P, nullptr, 0, nullptr), "softmax N = 0");
+    expect_error(nt_softmax_rows(1LL << 40, 1 << 30, NT_F32, P, P, nullptr, 0, nullptr), "softmax M*N too big");
+    expect_error(nt_softmax_rows(4, 8, NT_F32, nullptr, P, nullptr, 0, nullptr), "softmax x NULL");
+    expect_error(nt_softmax_rows(4, 8, NT_F16, P, odd, nullptr, 0, nullptr), "softmax y misaligned");
+    expect_error(nt_softmax_rows(4, wide, NT_F32, P, P, nullptr, wide, nullptr), "softmax workspace NULL");
+    expect_error(nt_softmax_rows(4, wide, NT_F32, P, P, P, 8, nullptr), "softmax workspace small");
+    expect_error(nt_softmax_causal_rows(4, 8, NT_F32, 0.0f, 4, 0, P, P, nullptr, 0, nullptr), "causal scale 0");
+    expect_error(nt_softmax_causal_rows(4, 8, NT_F32, 1.0f, 0, 0, P, P, nullptr, 0, nullptr), "causal queries 0");
+    expect_error(nt_softmax_causal_rows(4, 8, NT_F32, 1.0f, 4, -1, P, P, nullptr, 0, nullptr), "causal offset < 0");
+    expect_error(nt_layernorm_rows(4, 8, NT_F32, -1.0f, P, nullptr, nullptr, P, nullptr, nullptr, nullptr),
+                 "layernorm eps < 0");
+    expect_error(nt_layernorm_rows(4, 8, NT_F16, 1e-5f, P, odd, nullptr, P, nullptr, nullptr, nullptr),
+                 "layernorm gamma misaligned");
+    expect_error(nt_rmsnorm_rows(4, 8, NT_BF16, 1e-6f, nullptr, nullptr, P, nullptr), "rmsnorm x NULL");
+    expect_error(nt_rmsnorm_rows(4, 1LL << 31, NT_BF16, 1e-6f, P, nullptr, P, nullptr), "rmsnorm N too big");
+    expect_error(nt_layernorm_rows_ws(4, wide, NT_F32, 1e-5f, P, nullptr, nullptr, P, nullptr, nullptr, P, 64,
+                                      nullptr),
+                 "layernorm_ws workspace small");
+    expect_error(nt_rmsnorm_rows_ws(4, wide, NT_BF16, 1e-6f, P, nullptr, P, odd, wide, nullptr),
+                 "rmsnorm_ws workspace misaligned");
+    expect_error(nt_add_rmsnorm_rows(4, 8, NT_BF16, 1e-6f, P, nullptr, nullptr, P, P, nullptr),
+                 "add_rmsnorm residual NULL");
+    expect_error(nt_add_rmsnorm_rows(4, 8, NT_BF16, 1e-6f, P, buf + 96, nullptr, buf + 128, buf + 128, nullptr),
+                 "add_rmsnorm h == y");
+    expect_error(nt_add_layernorm_rows(4, 8, NT_F32, 1e-5f, P, buf + 100, nullptr, nullptr, buf + 128, buf + 160,
+                                       nullptr, nullptr, nullptr),
+                 "add_layernorm residual out of x's phase");
+    for (int s = -1; s <= 12; ++s) (void)nt_status_string((nt_status)s);
+
+    std::printf("ok %ld plans, %d failures\n", plans, failures);
+    return failures ? 1 : 0;
+}
