@@ -622,6 +622,62 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
             f.write("\n".join(lines))
 
 
+WIDE_TRAFFIC = ("f32", 2048, 65536)      # 512 MiB in, 512 MiB out: twice the Infinity Cache
+
+
+def wide_norm_traffic(torch, steps):
+    """The three forms of a wide-row RMSNorm on one large matrix (fp32
+    2048 x 65536, every parameter present), `steps` launches each, inputs
+    alternating between two 512 MiB buffers so no launch finds its rows in
+    the Infinity Cache: the one-pass split norm (norm_coop), the two-kernel
+    split norm (norm_split_partial + norm_split_finalize: NT_COOP=0) and the
+    looped kernel (row_looped: the plain entry point).  Meant to run under
+    rocprofv3, whose counters then tell how often each form reads x; prints
+    each form's median event-timed launch."""
+    import row_wise_reductions_amd as nt
+    dt, M, N = WIDE_TRAFFIC
+    code = nt.NT_F32
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    xs = [torch.randn(M, N, device="cuda", generator=gen) for _ in range(2)]
+    y = torch.empty_like(xs[0])
+    w = torch.randn(N, device="cuda", generator=gen) * 0.3 + 1
+    sh = torch.cuda.current_stream().cuda_stream
+    wsb = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, M, N, code)
+    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(nt.nt_status_string(rc))
+
+    forms = (("one pass", {}, True), ("two kernels", {"NT_COOP": "0", "NT_NORM_SPLIT_ROWS": str(1 << 40)}, True),
+             ("looped", {}, False))
+    out = {}
+    for name, env, with_ws in forms:
+        os.environ.update(env)
+        try:
+            p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS if with_ws else nt.NT_OP_RMSNORM, M, N, code, True)
+            evs = []
+            for i in range(steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                if with_ws:
+                    ok(nt.nt_rmsnorm_rows_ws(M, N, code, 1e-6, xs[i % 2].data_ptr(), w.data_ptr(), y.data_ptr(),
+                                             ws.data_ptr(), wsb, sh))
+                else:
+                    ok(nt.nt_rmsnorm_rows(M, N, code, 1e-6, xs[i % 2].data_ptr(), w.data_ptr(), y.data_ptr(), sh))
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+        finally:
+            for k in env:
+                del os.environ[k]
+        out[name] = {"plan": {k: p[k] for k in ("split", "cooperative", "waves_per_row", "chunks_per_lane",
+                                               "row_chunks")},
+                     "median_us": round(statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3, 2)}
+    print(json.dumps({"wide_norm_traffic": f"RMSNorm {dt} {M}x{N}", "algorithmic_bytes": 2 * M * N * 4 + N * 4,
+                      "forms": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -641,6 +697,8 @@ def main():
                     help="fp32 softmax / RMSNorm over the pages' benchmark widths (M=4096, N=128 i), vs torch")
     ap.add_argument("--sweep-wide-norms", dest="sweep_wide_norms", action="store_true",
                     help="LayerNorm / RMSNorm on rows of 64 KiB to 2 MiB: split vs looped vs torch")
+    ap.add_argument("--wide-norm-traffic", dest="wide_norm_traffic", action="store_true",
+                    help="the three forms of a wide-row RMSNorm, for rocprofv3 counters (x read once or twice)")
     ap.add_argument("--sweep-md", default=None, help="with a sweep: also write a markdown summary here")
     ap.add_argument("--copy-at-sizes", action="store_true",
                     help="time the plain streaming copy at each workload's byte count instead")
@@ -669,6 +727,9 @@ def main():
         return
     if args.sweep_wide_norms:
         wide_norm_sweep(torch, args.steps, args.warmup, args.sweep_md)
+        return
+    if args.wide_norm_traffic:
+        wide_norm_traffic(torch, args.steps)
         return
     if args.copy_at_sizes:
         names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]

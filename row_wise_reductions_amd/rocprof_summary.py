@@ -17,6 +17,12 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
       reads for the calibration copy of known size (1 GiB read + 1 GiB
       written), giving HBM bytes per call of each workload.
 
+  python -m row_wise_reductions_amd.rocprof_summary kernels --fetch DIR --write DIR --calib-fetch DIR \\
+         --calib-write DIR --trace DIR --groups "name=kernel+kernel;..." --bytes B --title T --cmds FILE --md FILE.md
+      HBM bytes (scaled as above) and average durations per group of named
+      kernels in a run that launches them directly (bench.py
+      --wide-norm-traffic), beside the work's algorithmic bytes B.
+
   python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR [--valu DIR] --cmds FILE --md FILE.md
       DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`,
       `--pmc MeanOccupancyPerActiveCU` and `--pmc VALUBusy` runs of bench.py; beside them, each
@@ -187,6 +193,50 @@ def traffic(args):
     print("\n".join(lines))
 
 
+def kernels(args):
+    fetch, write = _counter_means(args.fetch, "FETCH_SIZE"), _counter_means(args.write, "WRITE_SIZE")
+    cf, _ = _lookup(_counter_means(args.calib_fetch, "FETCH_SIZE"), CALIB_KERNEL)
+    cw, _ = _lookup(_counter_means(args.calib_write, "WRITE_SIZE"), CALIB_KERNEL)
+    if not cf or not cw:
+        raise SystemExit("calibration copy kernel not found in the counter output")
+    f_fac, w_fac = (CALIB_BYTES / 1024.0) / cf, (CALIB_BYTES / 1024.0) / cw
+    trace = _rows(os.path.join(args.trace, "**", "*kernel_stats.csv"))
+    with open(args.cmds) as fh:
+        cmds = fh.read().strip().splitlines()
+    lines = [f"# {args.title}", "", "Commands (each counter in a run of its own, from the repository root on the GPU "
+             "host):", ""] + [f"    {c}" for c in cmds] + [
+             "", f"Counter values scaled by what they read for the 1 GiB calibration copy: {f_fac:.4f} (FETCH_SIZE), "
+             f"{w_fac:.4f} (WRITE_SIZE).  Algorithmic bytes per call: {args.bytes}.", "",
+             "| form | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / call (scaled) | "
+             "avg duration (us) |", "|---|---|---|---|---|---|---|"]
+    summary = []
+    for group in args.groups.split(";"):
+        name, ks = group.split("=")
+        total, dur = 0.0, 0.0
+        for i, k in enumerate(ks.split("+")):
+            fv, n = _lookup(fetch, k)
+            wv, _ = _lookup(write, k)
+            hit = [r for r in trace if _match(r["Name"], k)]
+            avg = float(hit[0]["AverageNs"]) / 1000.0 if hit else float("nan")
+            if fv is None or wv is None:
+                lines.append(f"| {name if i == 0 else ''} | `{k}` | not found | | | | |")
+                continue
+            b = (fv * f_fac + wv * w_fac) * 1024.0
+            total += b
+            dur += avg
+            lines.append(f"| {name if i == 0 else ''} | `{k}` | {n} | {fv:.1f} | {wv:.1f} | {b:.0f} | {avg:.2f} |")
+        summary.append((name, total, dur))
+    lines += ["", "| form | HBM bytes / call | HBM / algorithmic | kernel time (us) | algorithmic GB/s |",
+              "|---|---|---|---|---|"]
+    for name, total, dur in summary:
+        lines.append(f"| {name} | {total:.0f} | {total / args.bytes:.3f} | {dur:.2f} | "
+                     f"{args.bytes / (dur * 1e-6) / 1e9:.1f} |")
+    lines.append("")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def occupancy(args):
     import tempfile
 
@@ -252,6 +302,14 @@ def main():
     t.add_argument("--cmds", required=True)
     t.add_argument("--md", required=True)
     t.add_argument("--json", required=True)
+    k = sub.add_parser("kernels")
+    for key in ("fetch", "write", "calib_fetch", "calib_write", "trace"):
+        k.add_argument("--" + key.replace("_", "-"), dest=key, required=True)
+    k.add_argument("--groups", required=True, help='"name=kernel+kernel;name=kernel"')
+    k.add_argument("--bytes", type=int, required=True, help="algorithmic bytes per call")
+    k.add_argument("--title", required=True)
+    k.add_argument("--cmds", required=True)
+    k.add_argument("--md", required=True)
     o = sub.add_parser("occupancy")
     o.add_argument("--occ", required=True)
     o.add_argument("--active", required=True)
@@ -259,7 +317,7 @@ def main():
     o.add_argument("--cmds", required=True)
     o.add_argument("--md", required=True)
     a = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "occupancy": occupancy}[a.mode](a)
+    {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -60,3 +60,44 @@ def test_cpu_baseline_fields():
 
 def test_cpu_baseline_sees_planted_error():
     assert bench.cpu_baseline(_jobs(plant=True), np)["gpu_parity_on_sample"] is False
+
+
+def test_kernels_summary_groups_and_scales(tmp_path):
+    """rocprof_summary's per-kernel mode on synthetic counter files: the
+    calibration copy fixes the scale factors, a group's bytes are the sum of
+    its kernels', and the ratio is to the algorithmic bytes given."""
+    import csv
+    from row_wise_reductions_amd import rocprof_summary as rs
+
+    def counters(d, counter, rows):
+        d.mkdir(parents=True)
+        with open(d / "x_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for name, v in rows:
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+    kib = 1 << 20          # 1 GiB in KiB
+    counters(tmp_path / "cf", "FETCH_SIZE", [(rs.CALIB_KERNEL, kib / 2)])      # fetch counts half: factor 2
+    counters(tmp_path / "cw", "WRITE_SIZE", [(rs.CALIB_KERNEL, kib)])          # factor 1
+    counters(tmp_path / "f", "FETCH_SIZE", [("ntk::alpha<1>", 100.0), ("ntk::alpha<1>", 300.0), ("ntk::beta<2>", 50.0)])
+    counters(tmp_path / "w", "WRITE_SIZE", [("ntk::alpha<1>", 10.0), ("ntk::beta<2>", 400.0)])
+    (tmp_path / "t").mkdir()
+    with open(tmp_path / "t" / "x_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs"])
+        w.writeheader()
+        w.writerow({"Name": "ntk::alpha<1>", "Calls": 2, "AverageNs": 1000})
+        w.writerow({"Name": "ntk::beta<2>", "Calls": 1, "AverageNs": 3000})
+    cmds = tmp_path / "cmds.txt"
+    cmds.write_text("cmd one\ncmd two\n")
+    md = tmp_path / "out.md"
+    args = types.SimpleNamespace(fetch=str(tmp_path / "f"), write=str(tmp_path / "w"), calib_fetch=str(tmp_path / "cf"),
+                                 calib_write=str(tmp_path / "cw"), trace=str(tmp_path / "t"),
+                                 groups="both=alpha+beta;first=alpha", bytes=2048 * 1024, title="T",
+                                 cmds=str(cmds), md=str(md))
+    rs.kernels(args)
+    text = md.read_text()
+    # alpha: fetch mean 200 KiB x 2 + write 10 KiB = 410 KiB; beta: 50 x 2 + 400 = 500 KiB
+    assert "| both | 931840 | 0.444 | 4.00 |" in text
+    assert "| first | 419840 | 0.200 | 1.00 |" in text
+    assert "    cmd one" in text
