@@ -505,6 +505,27 @@ def op_sweep(torch, dt, steps, warmup, md_path=None):
             f.write("\n".join(lines))
 
 
+class _env:
+    """Temporary environment settings (the planner reads them per call);
+    previous values, or their absence, are restored on exit."""
+
+    def __init__(self, **kv):
+        self.kv, self.saved = kv, {}
+
+    def __enter__(self):
+        for k, v in self.kv.items():
+            self.saved[k] = os.environ.get(k)
+            os.environ[k] = v
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 WIDE_NORM_CASES = (("bf16", 32768), ("bf16", 262144), ("bf16", 1 << 20), ("f32", 65536), ("f32", 262144))
 WIDE_NORM_M = (4, 16, 64, 256, 1024, 2048)
 
@@ -563,8 +584,7 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                 p = nt.nt_plan_launch(wop, M, N, code, True)
                 r[op + "_plan"] = ({0: "single pass", 2: "looped"}.get(p["split"]) or
                                    ("split, one pass" if p["cooperative"] else "split, two kernels"))
-                os.environ["NT_NORM_SPLIT_ROWS"] = str(1 << 40)
-                try:
+                with _env(NT_NORM_SPLIT_ROWS=str(1 << 40)):
                     wsb = nt.nt_norm_workspace_bytes(opc, M, N, code)
                     ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
                     if op == "layernorm":
@@ -576,11 +596,8 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                             M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), ws.data_ptr(),
                             wsb, sh))
                     ms_split = timed(split, R)
-                    os.environ["NT_COOP"] = "0"
-                    ms_split2 = timed(split, R)
-                finally:
-                    del os.environ["NT_NORM_SPLIT_ROWS"]
-                    os.environ.pop("NT_COOP", None)
+                    with _env(NT_COOP="0"):
+                        ms_split2 = timed(split, R)
                 if op == "layernorm":
                     looped = lambda i: ok(nt.nt_layernorm_rows(  # noqa: E731
                         M, N, code, 1e-5, xs[i].data_ptr(), g.data_ptr(), b.data_ptr(), ys[i].data_ptr(),
@@ -653,8 +670,7 @@ def wide_norm_traffic(torch, steps):
              ("looped", {}, False))
     out = {}
     for name, env, with_ws in forms:
-        os.environ.update(env)
-        try:
+        with _env(**env):
             p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS if with_ws else nt.NT_OP_RMSNORM, M, N, code, True)
             evs = []
             for i in range(steps):
@@ -668,9 +684,6 @@ def wide_norm_traffic(torch, steps):
                 b.record()
                 evs.append((a, b))
             torch.cuda.synchronize()
-        finally:
-            for k in env:
-                del os.environ[k]
         out[name] = {"plan": {k: p[k] for k in ("split", "cooperative", "waves_per_row", "chunks_per_lane",
                                                "row_chunks")},
                      "median_us": round(statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3, 2)}

@@ -101,3 +101,12 @@ def test_kernels_summary_groups_and_scales(tmp_path):
     assert "| both | 931840 | 0.444 | 4.00 |" in text
     assert "| first | 419840 | 0.200 | 1.00 |" in text
     assert "    cmd one" in text
+
+
+def test_env_helper_restores(monkeypatch):
+    monkeypatch.setenv("NT_COOP", "7")
+    monkeypatch.delenv("NT_NORM_SPLIT_ROWS", raising=False)
+    import os
+    with bench._env(NT_COOP="0", NT_NORM_SPLIT_ROWS="5"):
+        assert os.environ["NT_COOP"] == "0" and os.environ["NT_NORM_SPLIT_ROWS"] == "5"
+    assert os.environ["NT_COOP"] == "7" and "NT_NORM_SPLIT_ROWS" not in os.environ
