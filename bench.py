@@ -659,8 +659,6 @@ def wide_norm_traffic(torch, steps):
     y = torch.empty_like(xs[0])
     w = torch.randn(N, device="cuda", generator=gen) * 0.3 + 1
     sh = torch.cuda.current_stream().cuda_stream
-    wsb = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, M, N, code)
-    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
 
     def ok(rc):
         if rc != 0:
@@ -672,6 +670,8 @@ def wide_norm_traffic(torch, steps):
     for name, env, with_ws in forms:
         with _env(**env):
             p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS if with_ws else nt.NT_OP_RMSNORM, M, N, code, True)
+            wsb = int(p["workspace_bytes"])          # this form's own workspace (the two use other chunks)
+            ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
             evs = []
             for i in range(steps):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

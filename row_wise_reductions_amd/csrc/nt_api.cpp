@@ -260,9 +260,10 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
 // The split norm's plan for M rows of nch chunks (norms with a workspace, rows
 // too wide for one pass): false for the plain (looped) plan.
 //   One pass (cooperative), at any row count, where the row has at most
-//   kNormCoopPMax chunks of 8 waves x 4 (32 KiB), those give at least
-//   kNormSplitGrid workgroups, and the kernel keeps 4 waves per SIMD (not
-//   16-bit LayerNorm, whose 8 x 4 form holds about 200 registers).
+//   kNormCoopPMax chunks of 8 waves x 4 (32 KiB; fp32 RMSNorm first tries
+//   8 x 8, 64 KiB), those give at least kNormSplitGrid workgroups, and the
+//   kernel keeps 4 waves per SIMD (not 16-bit LayerNorm, whose 8 x 4 form
+//   holds about 200 registers).
 //   Else, below norm_split_rows(op) rows, two kernels, with the largest chunk
 //   that gives kNormSplitGrid workgroups.
 // Measured on MI355X (rows of 64 KiB to 2 MiB, 4 to 2048 rows): the one pass
@@ -276,12 +277,22 @@ bool split_norm_plan(nt_op op, nt_dtype dt, int64_t M, int64_t nch, bool coop, S
     if (M <= 0) return false;                            // nothing to split (callers divide by M)
     auto chunks = [nch](const Shape &c) { return (nch + 64 * c.W * c.K - 1) / (64 * c.W * c.K); };
     const Shape big = kNormSplit[0];
-    if (coop && !(op == NT_OP_LAYERNORM && dt != NT_F32) && chunks(big) <= kNormCoopPMax &&
-        M * chunks(big) >= kNormSplitGrid) {
-        *out = big;
-        *P = chunks(big);
-        *cooperative = true;
-        return true;
+    if (coop && !(op == NT_OP_LAYERNORM && dt != NT_F32)) {
+        // fp32 RMSNorm first tries 64 KiB chunks (8 x 8, 110 VGPRs, still two
+        // workgroups per CU): half the chunks per row wait on each other, and
+        // rows up to 262144 elements qualify (11% faster at 2048 x 65536,
+        // 27-41% on 262144-wide rows, which the 8 x 4 form left to the looped
+        // kernel); 16-bit 8 x 8 holds 174 VGPRs and was not faster
+        const Shape cands[2] = {{8, 8}, big};
+        for (int i = (op == NT_OP_RMSNORM && dt == NT_F32) ? 0 : 1; i < 2; ++i) {
+            const Shape &c = cands[i];
+            if (chunks(c) <= kNormCoopPMax && M * chunks(c) >= kNormSplitGrid) {
+                *out = c;
+                *P = chunks(c);
+                *cooperative = true;
+                return true;
+            }
+        }
     }
     if (M >= norm_split_rows(op)) return false;
     Shape s = big;
@@ -513,7 +524,7 @@ const char *nt_status_string(nt_status s) {
     case NT_ERR_DTYPE: return "unknown element type";
     case NT_ERR_EPS: return "eps must be finite and >= 0";
     case NT_ERR_ALIGN: return "pointer not aligned to its element size";
-    case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes()";
+    case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes() / nt_norm_workspace_bytes()";
     case NT_ERR_HIP: return "HIP launch error";
     case NT_ERR_ALIAS: return "h and y must be different buffers";
     case NT_ERR_SCALE: return "scale must be finite and > 0";
