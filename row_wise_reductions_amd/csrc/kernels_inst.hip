@@ -224,9 +224,9 @@ hipError_t norm_split_go(bool coop, const RowArgs &a, hipStream_t s) {
     const uint32_t grid = (uint32_t)(a.M * a.P);
     if (coop) {
         // the one-pass form is planned for 8 x 4 chunks, not for 16-bit
-        // LayerNorm, and for fp32 RMSNorm also 8 x 8
+        // LayerNorm, and in fp32 also 8 x 8
         if constexpr ((W == 8 && K == 4 && !(OP == OP_LAYERNORM && DT != DT_F32)) ||
-                      (OP == OP_RMSNORM && DT == DT_F32 && W == 8 && K == 8)) {
+                      (DT == DT_F32 && W == 8 && K == 8)) {
             hipLaunchKernelGGL((norm_coop<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
             return hipGetLastError();
         }
@@ -240,14 +240,14 @@ hipError_t norm_split_go(bool coop, const RowArgs &a, hipStream_t s) {
 }
 
 // The split norm's chunk shapes: 8 waves x 4 chunks (32 KiB), 8 x 1, 4 x 1 (two kernels); 8 x 4 in one pass,
-// and fp32 RMSNorm 8 x 8 (64 KiB) in one pass or, in place or under capture, in two kernels.
+// and fp32 8 x 8 (64 KiB) in one pass or, in place or under capture, in two kernels.
 template <int OP>
 hipError_t norm_split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k) \
     if (W == w && K == k) \
         return al ? norm_split_go<OP, w, k, true>(coop, a, s) : norm_split_go<OP, w, k, false>(coop, a, s);
     NTK_CASE(8, 4) NTK_CASE(8, 1) NTK_CASE(4, 1)
-    if constexpr (OP == OP_RMSNORM && DT == DT_F32) {
+    if constexpr (DT == DT_F32) {
         NTK_CASE(8, 8)     // the one-pass plan's chunks, in two kernels in place or under capture
     }
 #undef NTK_CASE

@@ -260,8 +260,9 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
 // The split norm's plan for M rows of nch chunks (norms with a workspace, rows
 // too wide for one pass): false for the plain (looped) plan.
 //   One pass (cooperative), at any row count, where the row has at most
-//   kNormCoopPMax chunks of 8 waves x 4 (32 KiB; fp32 RMSNorm first tries
-//   8 x 8, 64 KiB), those give at least kNormSplitGrid workgroups, and the
+//   kNormCoopPMax chunks of 8 waves x 4 (32 KiB; fp32 also 8 x 8, 64 KiB:
+//   RMSNorm first, LayerNorm second), those give at least kNormSplitGrid
+//   workgroups, and the
 //   kernel keeps 4 waves per SIMD (not 16-bit LayerNorm, whose 8 x 4 form
 //   holds about 200 registers).
 //   Else, below norm_split_rows(op) rows, two kernels, with the largest chunk
@@ -282,9 +283,15 @@ bool split_norm_plan(nt_op op, nt_dtype dt, int64_t M, int64_t nch, bool coop, S
         // workgroups per CU): half the chunks per row wait on each other, and
         // rows up to 262144 elements qualify (11% faster at 2048 x 65536,
         // 27-41% on 262144-wide rows, which the 8 x 4 form left to the looped
-        // kernel); 16-bit 8 x 8 holds 174 VGPRs and was not faster
-        const Shape cands[2] = {{8, 8}, big};
-        for (int i = (op == NT_OP_RMSNORM && dt == NT_F32) ? 0 : 1; i < 2; ++i) {
+        // kernel); 16-bit 8 x 8 holds 174 VGPRs and was not faster.  fp32
+        // LayerNorm's 8 x 8 (206 VGPRs, one workgroup per CU) was 5% slower
+        // than its 8 x 4 but 3-9% faster than the looped kernel: it comes
+        // second, for rows of 17 to 16 x 2 chunks of 32 KiB.
+        const Shape big8 = {8, 8};
+        const Shape rms32[2] = {big8, big}, ln32[2] = {big, big8}, one[1] = {big};
+        const Shape *cands = dt != NT_F32 ? one : op == NT_OP_RMSNORM ? rms32 : ln32;
+        const int nc = dt != NT_F32 ? 1 : 2;
+        for (int i = 0; i < nc; ++i) {
             const Shape &c = cands[i];
             if (chunks(c) <= kNormCoopPMax && M * chunks(c) >= kNormSplitGrid) {
                 *out = c;

@@ -201,7 +201,8 @@ def test_torch_wrappers_use_the_split(op):
                                           ("rmsnorm", 410, 40003, "f32", False),
                                           ("layernorm", 410, 40003, "f32", False),
                                           ("rmsnorm", 128, 262144, "f32", True),
-                                          ("rmsnorm", 300, 100003, "f32", False)])
+                                          ("rmsnorm", 300, 100003, "f32", False),
+                                          ("layernorm", 128, 262144, "f32", True)])
 def test_cooperative_split_norm_bitwise(op, M, N, dt, al, monkeypatch):
     """The one-pass form (records exchanged between a row's workgroups) passes
     the oracle and gives the two-kernel form's bits, also when every other

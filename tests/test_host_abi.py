@@ -350,8 +350,8 @@ def test_norm_workspace_bytes():
 
 def _split_norm_plan(base, dt, M, nch, coop=True):
     """The split norm's expected plan: ((W, K), one_pass), or None for the
-    looped plan.  One pass with 8 waves x 4 chunks per lane (fp32 RMSNorm:
-    8 x 8 first) at any row count when the row has at most 16 such chunks,
+    looped plan.  One pass with 8 waves x 4 chunks per lane (fp32 also 8 x 8:
+    RMSNorm first, LayerNorm second) at any row count when the row has at most 16 such chunks,
     the call at least 2048 workgroups, and the op is not 16-bit LayerNorm;
     else two kernels below
     256 (LayerNorm) or 2048 (RMSNorm) rows, with the largest chunk of 8x4,
@@ -360,8 +360,8 @@ def _split_norm_plan(base, dt, M, nch, coop=True):
     P = lambda s: -(-nch // (64 * s[0] * s[1]))  # noqa: E731
     ln = base == nt.NT_OP_LAYERNORM
     if coop and not (ln and dt != F32):
-        # fp32 RMSNorm tries 8 x 8 (64 KiB chunks) first
-        for one in ([(8, 8)] if (not ln and dt == F32) else []) + [(8, 4)]:
+        # fp32: 8 x 8 (64 KiB chunks) too, RMSNorm first, LayerNorm second
+        for one in ([(8, 8), (8, 4)] if (not ln and dt == F32) else [(8, 4), (8, 8)] if dt == F32 else [(8, 4)]):
             if P(one) <= 16 and M * P(one) >= 2048:
                 return one, True
     if M >= (256 if ln else 2048):
