@@ -655,3 +655,36 @@ def test_layernorm_between_power_of_two_shapes(dt, N, shape, monkeypatch):
     for off in (1, 3):
         parity_case("layernorm", x, dt, 1e-5, g, b, x_off=off, y_off=off, what=f"misaligned {dt} {shape} off={off}")
     parity_case("layernorm", x, dt, 1e-5, None, None, what=f"no params {dt} {shape}")
+
+
+def test_torch_wrappers_check_outputs_devices_and_stream():
+    """The torch conveniences refuse outputs that do not match x (the
+    kernels write M*N elements of x's type) and tensors on another device,
+    and enqueue on the current stream: inside a torch.cuda.stream context
+    the work goes to that stream (checked by ordering against a long
+    preceding fill on the same stream)."""
+    x = to_dev(rand_bits(3, 8, 1024, "f32"), "f32")
+    w = torch.ones(1024, device="cuda")
+    for bad in (torch.empty(8, 1023, device="cuda"), torch.empty(8, 1024, device="cuda", dtype=torch.float16),
+                torch.empty(1024, 8, device="cuda").t(), torch.empty(8, 1024)):
+        with pytest.raises(ValueError):
+            nt.softmax(x, out=bad)
+        with pytest.raises(ValueError):
+            nt.rms_norm(x, w, out=bad)
+    with pytest.raises(ValueError):
+        nt.rms_norm(x, torch.ones(1024))                      # weight in host memory
+    with pytest.raises(ValueError):
+        nt.layer_norm(x, w, torch.zeros(1024))                # beta in host memory
+    with pytest.raises(ValueError):
+        nt.add_rms_norm(x, torch.zeros(8, 1024))              # residual in host memory
+    say("case wrappers on a side stream")
+    s = torch.cuda.Stream()
+    big = torch.empty(1 << 27, device="cuda")
+    xs = x.clone()
+    with torch.cuda.stream(s):
+        big.fill_(1.0)                                        # keeps the side stream busy for a while
+        xs.mul_(2.0)
+        y = nt.softmax(xs)                                    # must see the doubled input
+    s.synchronize()
+    ref = oracle.softmax(to_host_bits(x, "f32").view(np.float32) * np.float32(2.0), "f32")
+    check_output(to_host_bits(y, "f32"), ref, "f32", "softmax on the current side stream")

@@ -460,3 +460,16 @@ print("ok", n)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout[-500:], r.stderr[-2000:])
+
+
+def test_torch_wrappers_reject_host_tensors():
+    """The torch conveniences pass raw addresses to the library: a tensor
+    in host memory is refused before any call."""
+    import torch
+    x = torch.zeros(4, 8)
+    for call in (lambda: nt.softmax(x), lambda: nt.softmax_causal(x), lambda: nt.layer_norm(x),
+                 lambda: nt.rms_norm(x), lambda: nt.add_layer_norm(x, x), lambda: nt.add_rms_norm(x, x)):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
+    with pytest.raises(TypeError):
+        nt.dtype_code(torch.zeros(2, dtype=torch.float64))
