@@ -49,8 +49,10 @@
  *  Errors     argument errors are returned synchronously, before anything is
  *             enqueued.  A failed launch returns NT_ERR_HIP (the HIP error is
  *             read and cleared with hipGetLastError).
- *  Aliasing   y == x (in place) is allowed.  Any other overlap between y and
- *             an input, the stats or the workspace is undefined.
+ *  Aliasing   y == x (in place) is allowed.  y partly overlapping x, and a
+ *             workspace overlapping x or y, return NT_ERR_ALIAS (checked from
+ *             the addresses and sizes, before anything is enqueued).  Any
+ *             overlap of y with the parameters or the stats is undefined.
  *  Numerics   inputs are widened to fp32 and reduced in fp32 (LayerNorm keeps
  *             its two row sums and its per-element affine step in fp64); the
  *             result is rounded to `dt` once, round-to-nearest-even.  The
@@ -92,7 +94,7 @@ typedef NT_ENUM {
     NT_ERR_WORKSPACE = 6,  /* workspace smaller than nt_softmax_workspace_bytes
                               (or nt_norm_workspace_bytes)                    */
     NT_ERR_HIP = 7,        /* the HIP runtime reported a launch error          */
-    NT_ERR_ALIAS = 8,      /* fused add + norm: h and y are the same buffer    */
+    NT_ERR_ALIAS = 8,      /* an output overlaps a buffer it may not overlap   */
     NT_ERR_SCALE = 9       /* causal softmax: scale is not finite and > 0      */
 } nt_status;
 
@@ -101,7 +103,8 @@ typedef NT_ENUM {
  * row fits on chip (single pass), else 16 bytes per (row, row chunk) for the
  * per-chunk running max and denominator of the split online path.  Returns 0
  * for invalid arguments.  The contents need not be initialized and are
- * overwritten; two calls in flight at once must not share a workspace.
+ * overwritten; two calls in flight at once must not share a workspace, and a
+ * workspace overlapping x or y is NT_ERR_ALIAS.
  */
 size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
 
@@ -199,8 +202,9 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  * `workspace_bytes`: NULL runs the plain plan; otherwise workspace must be
  * 8-byte aligned (NT_ERR_ALIGN) and hold nt_norm_workspace_bytes(op, M, N, dt)
  * bytes (NT_ERR_WORKSPACE).  Contents need not be initialized; two calls in
- * flight at once must not share a workspace, which must not overlap x, y or
- * the parameters.  In place (y == x) is allowed.  NT_COOP=0 in the
+ * flight at once must not share a workspace; a workspace overlapping x or y
+ * is NT_ERR_ALIAS (overlapping the parameters is undefined).  In place
+ * (y == x) is allowed.  NT_COOP=0 in the
  * environment selects the two kernels throughout.
  */
 size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt);
@@ -234,8 +238,8 @@ nt_status nt_rmsnorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps,
  * gamma, beta, weight, mean and rstd as in the plain norms.  residual and h
  * must be non-NULL (NT_ERR_NULL) and lie at the same address modulo 16 as x
  * (NT_ERR_ALIGN); y may have any element-aligned address.  h may be x or
- * residual (in place); y may be x or residual; y == h is NT_ERR_ALIAS.
- * Any other overlap is undefined.
+ * residual (in place); y may be x or residual; any other overlap of h or y
+ * with x, the residual or each other (y == h included) is NT_ERR_ALIAS.
  */
 nt_status nt_add_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
                                 const void *x, const void *residual,

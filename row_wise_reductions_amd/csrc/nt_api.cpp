@@ -507,6 +507,17 @@ nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, con
 }
 
 // Checks shared by every entry point, in the documented order.
+// Do the byte ranges [a, a + na) and [b, b + nb) overlap?  (Addresses and
+// sizes here stay far below 2^63, so the sums do not wrap.)
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uint64_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+uint64_t matrix_bytes(int64_t M, int64_t N, int dt) {
+    return (uint64_t)M * (uint64_t)N * (uint64_t)elem_bytes((nt_dtype)dt);
+}
+
 nt_status common_checks(int64_t M, int64_t N, int dt, const void *x, const void *y) {
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;
     if (!valid_shape(M, N)) return NT_ERR_SHAPE;
@@ -514,6 +525,17 @@ nt_status common_checks(int64_t M, int64_t N, int dt, const void *x, const void 
     if (!x || !y) return NT_ERR_NULL;
     const uintptr_t e = (uintptr_t)elem_bytes((nt_dtype)dt);
     if (!aligned_to(x, e) || !aligned_to(y, e)) return NT_ERR_ALIGN;
+    // in place (y == x) is fine; a partial overlap would read outputs as inputs
+    const uint64_t b = matrix_bytes(M, N, dt);
+    if (x != y && overlaps(x, b, y, b)) return NT_ERR_ALIAS;
+    return NT_OK;
+}
+
+// A workspace must not overlap x or y.
+nt_status workspace_apart(int64_t M, int64_t N, int dt, const void *x, const void *y, const void *ws,
+                          size_t wsb) {
+    const uint64_t b = matrix_bytes(M, N, dt);
+    if (ws && (overlaps(ws, wsb, x, b) || overlaps(ws, wsb, y, b))) return NT_ERR_ALIAS;
     return NT_OK;
 }
 
@@ -533,7 +555,7 @@ const char *nt_status_string(nt_status s) {
     case NT_ERR_ALIGN: return "pointer not aligned to its element size";
     case NT_ERR_WORKSPACE: return "workspace smaller than nt_softmax_workspace_bytes() / nt_norm_workspace_bytes()";
     case NT_ERR_HIP: return "HIP launch error";
-    case NT_ERR_ALIAS: return "h and y must be different buffers";
+    case NT_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case NT_ERR_SCALE: return "scale must be finite and > 0";
     }
     return "unknown status";
@@ -586,6 +608,7 @@ static nt_status softmax_launch(int64_t M, int64_t N, nt_dtype dt, const void *x
         // The documented requirement (sized for misaligned rows) is enforced,
         // not the possibly smaller need of this particular call.
         if (workspace_bytes < nt_softmax_workspace_bytes(M, N, dt)) return NT_ERR_WORKSPACE;
+        if (workspace_apart(M, N, dt, x, y, workspace, workspace_bytes) != NT_OK) return NT_ERR_ALIAS;
         a.ws = static_cast<float2 *>(workspace);
         a.P = (int32_t)p.row_chunks;
         // in place, a chunk recomputed by another workgroup could already
@@ -639,11 +662,12 @@ namespace {
 // The split norm's workspace checks, and the choice between its one-pass
 // (cooperative) and two-kernel forms: in place, or under graph capture,
 // the two kernels.
-nt_status attach_workspace(nt_plan &p, void *ws, size_t wsb, const void *x, const void *y, void *stream,
-                           ntk::RowArgs &a) {
+nt_status attach_workspace(nt_plan &p, void *ws, size_t wsb, int64_t M, int64_t N, nt_dtype dt, const void *x,
+                           const void *y, void *stream, ntk::RowArgs &a) {
     if (p.split != 3) return NT_OK;
     if (wsb < (size_t)p.workspace_bytes) return NT_ERR_WORKSPACE;
     if (!aligned_to(ws, 8)) return NT_ERR_ALIGN;
+    if (workspace_apart(M, N, dt, x, y, ws, wsb) != NT_OK) return NT_ERR_ALIAS;
     a.P = (int32_t)p.row_chunks;
     a.wsd = static_cast<double *>(ws);
     if (x == y) p.cooperative = 0;
@@ -677,7 +701,7 @@ nt_status layernorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const voi
                    ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
-    st = attach_workspace(p, ws, wsb, x, y, stream, a);
+    st = attach_workspace(p, ws, wsb, M, N, dt, x, y, stream, a);
     if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
@@ -706,7 +730,7 @@ nt_status rmsnorm_impl(int64_t M, int64_t N, nt_dtype dt, float eps, const void 
     st = make_plan(NT_OP_RMSNORM, M, N, dt, al, &p, weight != nullptr, false, false, ws != nullptr);
     if (st != NT_OK) return st;
     ntk::RowArgs a{};
-    st = attach_workspace(p, ws, wsb, x, y, stream, a);
+    st = attach_workspace(p, ws, wsb, M, N, dt, x, y, stream, a);
     if (st != NT_OK) return st;
     a.x = static_cast<const char *>(x);
     a.y = static_cast<char *>(y);
@@ -768,13 +792,19 @@ nt_status nt_rmsnorm_rows_ws(int64_t M, int64_t N, nt_dtype dt, float eps, const
 
 // Checks of the fused add + norm entry points beyond common_checks: the
 // residual and h present, element-aligned and in x's 16-byte phase, y != h.
-static nt_status residual_checks(nt_dtype dt, const void *x, const void *residual, const void *h,
-                                 const void *y) {
+static nt_status residual_checks(int64_t M, int64_t N, nt_dtype dt, const void *x, const void *residual,
+                                 const void *h, const void *y) {
     if (!residual || !h) return NT_ERR_NULL;
     const uintptr_t e = (uintptr_t)elem_bytes(dt);
     if (!aligned_to(residual, e) || !aligned_to(h, e)) return NT_ERR_ALIGN;
     if ((((uintptr_t)residual ^ (uintptr_t)x) & 15) || (((uintptr_t)h ^ (uintptr_t)x) & 15)) return NT_ERR_ALIGN;
-    if (h == y) return NT_ERR_ALIAS;
+    // h and y may each be x or the residual exactly; no other overlap
+    const uint64_t b = matrix_bytes(M, N, dt);
+    if (overlaps(h, b, y, b)) return NT_ERR_ALIAS;
+    for (const void *in : {x, residual}) {
+        if (h != in && overlaps(h, b, in, b)) return NT_ERR_ALIAS;
+        if (y != in && overlaps(y, b, in, b)) return NT_ERR_ALIAS;
+    }
     return NT_OK;
 }
 
@@ -786,7 +816,7 @@ nt_status nt_add_layernorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, co
     if (!valid_eps(eps)) return NT_ERR_EPS;
     nt_status st = common_checks(M, N, dt, x, y);
     if (st != NT_OK || M == 0) return st;
-    st = residual_checks(dt, x, residual, h, y);
+    st = residual_checks(M, N, dt, x, residual, h, y);
     if (st != NT_OK) return st;
     const uintptr_t e = (uintptr_t)elem_bytes(dt);
     if ((gamma && !aligned_to(gamma, e)) || (beta && !aligned_to(beta, e)) || (mean && !aligned_to(mean, 4)) ||
@@ -820,7 +850,7 @@ nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, cons
     if (!valid_eps(eps)) return NT_ERR_EPS;
     nt_status st = common_checks(M, N, dt, x, y);
     if (st != NT_OK || M == 0) return st;
-    st = residual_checks(dt, x, residual, h, y);
+    st = residual_checks(M, N, dt, x, residual, h, y);
     if (st != NT_OK) return st;
     if (weight && !aligned_to(weight, (uintptr_t)elem_bytes(dt))) return NT_ERR_ALIGN;
     const bool al = all_aligned16(N, dt, x, y, weight, nullptr) && aligned_to(residual, 16) && aligned_to(h, 16);

@@ -80,28 +80,28 @@ def test_status_strings():
     (lambda: nt.nt_softmax_causal_rows(4, 1 << 20, F32, 1.0, 4, 0, FAKE, FAKE, None, 1 << 20, None), 1),
     (lambda: nt.nt_softmax_causal_rows(4, 1 << 20, F32, 1.0, 4, 0, FAKE, FAKE, FAKE, 8, None), 6),
     # fused add + norm: residual and h required, in x's 16-byte phase, h != y
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, None, None, FAKE + 64, FAKE + 128, None), 1),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, None, FAKE + 128, None), 1),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, None, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 1),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 33, None, FAKE + 64, FAKE + 128, None), 5),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 34, None, FAKE + 64, FAKE + 128, None), 5),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 66, FAKE + 128, None), 5),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, FAKE + 1, FAKE + 64, FAKE + 128, None), 5),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 64, None), 8),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, -1.0, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 4),
-    (lambda: nt.nt_add_rmsnorm_rows(4, 8, 5, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 3),
-    (lambda: nt.nt_add_rmsnorm_rows(-2, 8, BF16, 1e-6, FAKE, FAKE + 32, None, FAKE + 64, FAKE + 128, None), 2),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, None, None, None, FAKE + 64, FAKE + 128,
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, None, None, FAKE + 512, FAKE + 768, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, None, None, FAKE + 768, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, None, FAKE + 256, None, FAKE + 512, FAKE + 768, None), 1),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 257, None, FAKE + 512, FAKE + 768, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 258, None, FAKE + 512, FAKE + 768, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, None, FAKE + 514, FAKE + 768, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, FAKE + 1, FAKE + 512, FAKE + 768, None), 5),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, None, FAKE + 512, FAKE + 512, None), 8),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, -1.0, FAKE, FAKE + 256, None, FAKE + 512, FAKE + 768, None), 4),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, 5, 1e-6, FAKE, FAKE + 256, None, FAKE + 512, FAKE + 768, None), 3),
+    (lambda: nt.nt_add_rmsnorm_rows(-2, 8, BF16, 1e-6, FAKE, FAKE + 256, None, FAKE + 512, FAKE + 768, None), 2),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, None, None, None, FAKE + 512, FAKE + 768,
                                       None, None, None), 1),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 36, None, None, FAKE + 64, FAKE + 128,
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 260, None, None, FAKE + 512, FAKE + 768,
                                       None, None, None), 5),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, FAKE + 2, None, FAKE + 64, FAKE + 128,
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 256, FAKE + 2, None, FAKE + 512, FAKE + 768,
                                       None, None, None), 5),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 128,
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 256, None, None, FAKE + 512, FAKE + 768,
                                       FAKE + 2, None, None), 5),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 64,
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 256, None, None, FAKE + 512, FAKE + 512,
                                       None, None, None), 8),
-    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, float("nan"), FAKE, FAKE + 32, None, None, FAKE + 64, FAKE + 128,
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, float("nan"), FAKE, FAKE + 256, None, None, FAKE + 512, FAKE + 768,
                                       None, None, None), 4),
     # norms with a workspace: the plain checks, then the workspace's size and alignment
     (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F32, -1.0, FAKE, None, None, FAKE, None, None, FAKE, 1 << 20,
@@ -115,6 +115,19 @@ def test_status_strings():
     (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, FAKE, None, FAKE, FAKE + 2, 1 << 20, None), 5),
     (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, None, None, FAKE, FAKE, 1 << 20, None), 1),
     (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, 7, 1e-6, FAKE, None, FAKE, FAKE, 1 << 20, None), 3),
+    # overlaps: y partly over x, a workspace over x or y, h or y partly over an input
+    (lambda: nt.nt_softmax_rows(4, 8, F32, FAKE, FAKE + 16, None, 0, None), 8),
+    (lambda: nt.nt_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE + 62, None, FAKE, None), 8),
+    (lambda: nt.nt_layernorm_rows(4, 8, F32, 1e-5, FAKE, None, None, FAKE + 124, None, None, None), 8),
+    (lambda: nt.nt_softmax_rows(4, 1 << 20, F32, FAKE, FAKE + (1 << 25), FAKE + 64, 1 << 20, None), 8),
+    (lambda: nt.nt_softmax_rows(4, 1 << 20, F32, FAKE, FAKE + (1 << 25), FAKE + (1 << 25) + 64, 1 << 20, None), 8),
+    (lambda: nt.nt_rmsnorm_rows_ws(4, 1 << 20, BF16, 1e-6, FAKE, None, FAKE, FAKE + 8, 1 << 20, None), 8),
+    (lambda: nt.nt_layernorm_rows_ws(4, 1 << 20, F32, 1e-5, FAKE, None, None, FAKE + (1 << 25), None, None,
+                                     FAKE + (1 << 25) - 8, 1 << 20, None), 8),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, None, FAKE + 272, FAKE + 512, None), 8),
+    (lambda: nt.nt_add_rmsnorm_rows(4, 8, BF16, 1e-6, FAKE, FAKE + 256, None, FAKE + 512, FAKE + 40, None), 8),
+    (lambda: nt.nt_add_layernorm_rows(4, 8, F32, 1e-5, FAKE, FAKE + 256, None, None, FAKE + 512, FAKE + 544,
+                                      None, None, None), 8),
 ])
 def test_validation_before_launch(call, code):
     # every case here must fail validation; on a machine with a GPU a library
