@@ -68,14 +68,15 @@ struct Menu {
 // leave lanes idle: 16-bit 7 x 2 for 513..896 chunks (1-3% over 8 x 2),
 // 5 x 4 to 1216 chunks, 6 x 4 to 1408, 7 x 4 from 1473 to 1792 (2-5% over
 // 8 x 4; near the top of its capacity 5 x 4 and 6 x 4 fell 2-7% behind
-// 8 x 4, hence the caps), fp32 12 x 4 for 2049..3072 (2-8% over 8 x 8; two
-// M = 4096 sweeps of the pages' widths).  The fused residual add + norm
+// 8 x 4, hence the caps), fp32 4 x 4 for 513..640 chunks (1-8% over 8 x 2),
+// 12 x 4 for 2049..3072 (2-8% over 8 x 8; two M = 4096 sweeps of the
+// pages' widths).  The fused residual add + norm
 // entries have menus of their own (below).
 const Shape kSoftmax32[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}, {8, 16}};
 const Shape kSoftmax16[] = {{1, 1}, {1, 2}, {1, 4}, {4, 2}, {8, 2}, {8, 4}, {8, 8}};
 const Shape kRms32[] = {{1, 1}, {1, 2}, {1, 4}, {8, 1}, {8, 2}, {16, 2}, {8, 8}, {8, 16}};
 const Shape kRms16[] = {{1, 1}, {1, 2}, {4, 1}, {8, 1}, {8, 2}, {8, 4}, {8, 8}};
-const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {8, 2}, {8, 4}, {12, 4}, {8, 8}};
+const Shape kLn32[] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {4, 4, 640}, {8, 2}, {8, 4}, {12, 4}, {8, 8}};
 const Shape kLn16[] = {{1, 1},       {1, 2},       {2, 2},       {4, 2}, {7, 2}, {8, 2},
                        {5, 4, 1216}, {6, 4, 1408}, {8, 4, 1472}, {7, 4}, {8, 4}};
 // Fused residual add + norm (two input and two output streams per row): more

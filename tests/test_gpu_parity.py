@@ -625,7 +625,7 @@ def test_errors_before_launch():
 @pytest.mark.parametrize("dt,N,shape", [("f16", 4104, (7, 2)), ("bf16", 7168, (7, 2)), ("f16", 8200, (5, 4)),
                                         ("bf16", 9728, (5, 4)), ("bf16", 9736, (6, 4)), ("f16", 11264, (6, 4)),
                                         ("bf16", 11520, (8, 4)), ("bf16", 11784, (7, 4)), ("f16", 14336, (7, 4)),
-                                        ("f32", 8200, (12, 4)), ("f32", 12288, (12, 4))])
+                                        ("f32", 8200, (12, 4)), ("f32", 12288, (12, 4)), ("f32", 2304, (4, 4))])
 def test_layernorm_between_power_of_two_shapes(dt, N, shape, monkeypatch):
     """LayerNorm's shapes of 5-7 waves (16-bit) and 12 waves (fp32): the
     persistent kernel (aligned rows, parameters present; a grid smaller than

@@ -234,6 +234,9 @@ def test_wide_rows_take_the_streaming_paths():
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 8200, F32, True)       # fp32 12 x 4: one row per workgroup
     assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 12, 4, 0)
     assert p["threads_per_block"] == 768
+    for N, shape in ((2048, (2, 4)), (2052, (4, 4)), (2560, (4, 4)), (2564, (8, 2))):   # fp32 4 x 4 to 640 chunks
+        p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, N, F32, True)
+        assert (p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (*shape, 1), (N, p)
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 12296, F32, True)      # past 12 x 4: 8 x 8
     assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["persistent"]) == (0, 8, 8, 0)
     assert nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 1, 16384, F32, True)["split"] == 0
