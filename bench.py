@@ -120,16 +120,18 @@ class Job:
             raise RuntimeError(f"{w.name}: {nt.nt_status_string(rc)}")
 
 
-def cpu_baseline(jobs, np, stride=1, check_every=16):
+def cpu_baseline(jobs, np, stride=1, check_every=1):
     """The oracle (as it stands) on every `stride`-th row of each workload
     (by default all rows: about 6 core-seconds per pass over the suite), on
     this host's cores: 1 warm-up and 3 timed runs, median.  The GPU output
-    of the timed run is checked against the oracle on every
-    `check_every`-th sampled row."""
+    of the last launch is checked against the oracle on every
+    `check_every`-th of those rows (by default every row; compared on
+    blocks in a thread pool)."""
     import oracle
     from oracle import compare
     total_bytes, total_t, ok = 0, 0.0, True
     parts = []
+    checked_rows = 0
     for j in jobs:
         w, data = j.w, j.data
         rows = np.arange(0, w.M, stride)
@@ -157,18 +159,20 @@ def cpu_baseline(jobs, np, stride=1, check_every=16):
         total_bytes += b
         total_t += t
         parts.append(f"{w.name}: {len(rows)} of {w.M} rows")
-        # parity of the timed GPU output on a subset of the same rows
-        sub = np.arange(0, len(rows), check_every)
-        y = j.y[0].cpu()
+        # parity of the GPU output on the same rows (every check_every-th)
+        y = j.y[0].cpu()             # every buffer set holds the same input
+        refs = ref[::check_every]
+        checked_rows += refs.shape[0]
         if w.dt == "f32":
-            gb = y.numpy()[rows[sub]].view(np.uint32)
-            good = compare.max_rel_err(compare.bits_to_f64(gb, "f32"), ref[sub]) <= 1e-5
+            gb = y.numpy()[::stride][::check_every].view(np.uint32)
+            rel, quanta = compare.f32_errors_threaded(gb, refs)
+            good = rel <= 1e-5 and quanta <= 1.0
         else:
             import torch
-            gb = y.view(torch.int16).numpy()[rows[sub]].view(np.uint16)
-            good = int(compare.ulp_distance(gb, ref[sub], w.dt).max()) <= 1
+            gb = y.view(torch.int16).numpy()[::stride][::check_every].view(np.uint16)
+            good = compare.max_ulp_distance(gb, refs, w.dt) <= 1
         ok = ok and good
-        del ref
+        del ref, refs, gb, y
     threads = oracle.num_threads()
     # one thread on the small softmax workload (every row), then back
     single = None
@@ -194,7 +198,7 @@ def cpu_baseline(jobs, np, stride=1, check_every=16):
                        f" of each workload ({'; '.join(parts)}); median of 3 timed runs after 1 warm-up; "
                        f"fp64 C with OpenMP over rows on {threads} threads"),
             "seconds": round(total_t, 3), "core_seconds": round(total_t * threads, 2),
-            "gpu_parity_on_sample": bool(ok)}
+            "gpu_parity_on_sample": bool(ok), "gpu_parity_rows_checked": int(checked_rows)}
 
 
 def warm_up(step, count, min_ms, torch):
@@ -248,85 +252,106 @@ def traffic_for(kernel_name, launches_bytes):
 def _ntcal():
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "row_wise_reductions_amd", "libntcal.so"))
-    lib.ntcal_copy_policy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
-    lib.ntcal_copy_policy.restype = ctypes.c_int
+    lib.ntcal_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.ntcal_stream.restype = ctypes.c_int
     return lib
 
 
+# Reference streams of libntcal.so: (name, kind, chunks per lane, sc1).
+# kind 0 copy (read + write), 1 read only, 2 fill (write only).
+CALIB_VARIANTS = [(f"{('copy', 'read', 'fill')[kind]} K={k}" + (" nt sc1" if sc1 else (" nt" if kind != 1 else "")),
+                   kind, k, sc1)
+                  for kind in (0, 1, 2) for k in (1, 2, 4, 8) for sc1 in ((0, 1) if kind != 1 else (0,))]
+NEVER = 0x9E3779B9          # the read stream stores its fold only if it equals this
+
+
+def _timed_median(fn, steps, warmup, torch, min_ms=200.0):
+    warm_up(lambda: fn(0), warmup, min_ms, torch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
 def calibrate_copy(torch, steps, warmup, nbytes=1 << 30):
-    """Attainable-bandwidth reference: the plain streaming copy kernels of
-    libntcal.so (read nbytes, write nbytes), rotating 4 buffer pairs, with
-    non-temporal stores (ntcal, the counter calibration) and with the
-    device-scope streaming stores of the row kernels (ntcal_sc1); torch's own
-    copy_ is timed beside them."""
+    """Attainable-bandwidth references at 1 GiB, rotating 4 buffer pairs:
+    libntcal.so's copy, read-only and write-only streams with 1, 2, 4 and 8
+    16-byte chunks per lane in flight, with non-temporal stores and with the
+    device-scope streaming stores (nt sc1) of the row kernels; torch's own
+    copy_ beside them.  GB/s counts the bytes each moves (copy: read +
+    written).  Event-timed medians; under rocprofv3 --kernel-trace the same
+    launches give kernel durations."""
     lib = _ntcal()
     n = nbytes // 4
     src = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(4)]
     dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
     sh = torch.cuda.current_stream().cuda_stream
-    out = {"calibration": "plain streaming copy (ntcal_copy_kernel), 4 KiB per workgroup, non-temporal; "
-                          "ntcal_sc1: the same with device-scope streaming stores",
-           "bytes_read": nbytes, "bytes_written": nbytes}
-    for name, fn in (("ntcal", lambda i: lib.ntcal_copy_policy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(),
-                                                               nbytes, 0, sh)),
-                     ("ntcal_sc1", lambda i: lib.ntcal_copy_policy(dst[i % 4].data_ptr(), src[i % 4].data_ptr(),
-                                                                   nbytes, 1, sh)),
-                     ("torch_copy", lambda i: dst[i % 4].copy_(src[i % 4]))):
-        cnt = [0]
-
-        def one():
-            rc = fn(cnt[0])
-            cnt[0] += 1
-            assert not isinstance(rc, int) or rc == 0, rc
-        warm_up(one, warmup, 200.0, torch)
-        durs = []
-        for i in range(steps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn(i)
-            b.record()
-            b.synchronize()
-            durs.append(a.elapsed_time(b))
-        ms = statistics.median(durs)
-        out[f"{name}_median_ms"] = round(ms, 5)
-        out[f"{name}_GBps"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    out = {"calibration": "libntcal.so reference streams at 1 GiB: copy (read + write), read only, fill (write "
+                          "only); K 16-byte chunks per lane in flight; stores non-temporal (nt) or device-scope "
+                          "streaming (nt sc1)",
+           "bytes": nbytes, "variants": []}
+    for name, kind, k, sc1 in CALIB_VARIANTS:
+        def one(i, kind=kind, k=k, sc1=sc1):
+            rc = lib.ntcal_stream(kind, k, sc1, dst[i % 4].data_ptr(), src[i % 4].data_ptr(), nbytes,
+                                  0x3F800000 if kind == 2 else NEVER, sh)
+            assert rc == 0, rc
+        ms = _timed_median(one, steps, warmup, torch)
+        moved = (2 if kind == 0 else 1) * nbytes
+        out["variants"].append({"name": name, "kind": kind, "K": k, "sc1": sc1, "median_ms": round(ms, 5),
+                                "GBps": round(moved / (ms * 1e-3) / 1e9, 1)})
+        log(f"[calibrate] {name}: {out['variants'][-1]['GBps']} GB/s")
+    ms = _timed_median(lambda i: dst[i % 4].copy_(src[i % 4]), steps, warmup, torch)
+    out["torch_copy_median_ms"] = round(ms, 5)
+    out["torch_copy_GBps"] = round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+    best = max((v for v in out["variants"] if v["kind"] == 0), key=lambda v: v["GBps"])
+    out["best_copy"] = best["name"]
+    out["best_copy_GBps"] = best["GBps"]
     print(json.dumps(out), flush=True)
 
 
-def copy_at_sizes(torch, steps, warmup, workloads):
-    """The plain streaming copy of libntcal.so moving each workload's bytes
-    (read M*N*e, write M*N*e), rotating buffer sets of >= 1 GiB so the
-    Infinity Cache cannot serve them: what a kernel that only streams its
-    rows could reach at that size (launch and ramp included), with each
-    store policy.  Event-timed like the breakdown pass; median of `steps`
-    launches."""
+COPY_AT_SIZES = [("copy K=1 nt", 0, 1, 0), ("copy K=1 nt sc1", 0, 1, 1), ("copy K=2 nt sc1", 0, 2, 1),
+                 ("copy K=4 nt sc1", 0, 4, 1)]
+
+
+def copy_at_sizes(torch, steps, warmup, wls):
+    """Each workload's own kernel and reference copies of its bytes (read
+    M*N*e, write M*N*e; libntcal.so, 1, 2 and 4 chunks per lane), launched in
+    the same run, rotating buffer sets of >= 1 GiB so the Infinity Cache
+    cannot serve them: under rocprofv3 --kernel-trace both get kernel
+    durations on the same clock (the copies are told apart by their grid
+    sizes).  Also event-timed here; median of `steps` launches."""
+    import numpy as np
+
+    import row_wise_reductions_amd as nt
     lib = _ntcal()
     sh = torch.cuda.current_stream().cuda_stream
-    out = {"copy_at_sizes": "plain streaming copy (ntcal_copy_kernel) of each workload's read bytes", "workloads": []}
-    for w in workloads:
+    out = {"copy_at_sizes": "each workload's kernel, and libntcal.so copies of its read bytes", "workloads": []}
+    for w in wls:
         nb = w.M * w.N * w.elem_bytes // 16 * 16
         R = max(1, -(-(1 << 30) // (2 * nb)))
+        row = {"workload": w.name, "bytes_read": nb, "bytes_written": nb, "buffer_sets": R,
+               "algorithmic_bytes": w.algorithmic_bytes()}
+        data = w.make()
+        job = Job(w, data, R, torch, np, nt)
+        ms = _timed_median(lambda i: job.launch(sh), steps, warmup, torch)
+        row["kernel_median_ms"] = round(ms, 5)
+        row["kernel_GBps"] = round(w.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1)
+        del job, data
         src = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
         dst = [torch.empty(nb // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
-        row = {"workload": w.name, "bytes_read": nb, "bytes_written": nb, "buffer_sets": R}
-        for pol, tag in ((0, ""), (1, "sc1_")):
-            cnt = [0]
-
-            def one():
-                i = cnt[0]
-                cnt[0] += 1
-                assert lib.ntcal_copy_policy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, pol, sh) == 0
-            warm_up(one, warmup, 200.0, torch)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(steps)]
-            for i, (a, b) in enumerate(evs):
-                a.record()
-                lib.ntcal_copy_policy(dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, pol, sh)
-                b.record()
-            torch.cuda.synchronize()
-            ms = statistics.median(a.elapsed_time(b) for a, b in evs)
-            row[f"{tag}median_ms"] = round(ms, 5)
-            row[f"{tag}GBps"] = round(2 * nb / (ms * 1e-3) / 1e9, 1)
+        row["copies"] = []
+        for name, kind, k, sc1 in COPY_AT_SIZES:
+            def one(i, k=k, sc1=sc1):
+                assert lib.ntcal_stream(0, k, sc1, dst[i % R].data_ptr(), src[i % R].data_ptr(), nb, 0, sh) == 0
+            ms = _timed_median(one, steps, warmup, torch)
+            row["copies"].append({"name": name, "K": k, "sc1": sc1, "grid": -(-(nb // 16) // (256 * k)),
+                                  "median_ms": round(ms, 5), "GBps": round(2 * nb / (ms * 1e-3) / 1e9, 1)})
+        log(f"[copy at sizes] {w.name}: kernel {row['kernel_median_ms']} ms, copies " +
+            ", ".join(f"{c['name']} {c['median_ms']}" for c in row["copies"]))
         out["workloads"].append(row)
         del src, dst
         torch.cuda.empty_cache()
@@ -505,27 +530,6 @@ def op_sweep(torch, dt, steps, warmup, md_path=None):
             f.write("\n".join(lines))
 
 
-class _env:
-    """Temporary environment settings (the planner reads them per call);
-    previous values, or their absence, are restored on exit."""
-
-    def __init__(self, **kv):
-        self.kv, self.saved = kv, {}
-
-    def __enter__(self):
-        for k, v in self.kv.items():
-            self.saved[k] = os.environ.get(k)
-            os.environ[k] = v
-        return self
-
-    def __exit__(self, *exc):
-        for k, v in self.saved.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
 WIDE_NORM_CASES = (("bf16", 32768), ("bf16", 262144), ("bf16", 1 << 20), ("f32", 65536), ("f32", 262144))
 WIDE_NORM_M = (4, 16, 64, 256, 1024, 2048)
 
@@ -584,7 +588,7 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                 p = nt.nt_plan_launch(wop, M, N, code, True)
                 r[op + "_plan"] = ({0: "single pass", 2: "looped"}.get(p["split"]) or
                                    ("split, one pass" if p["cooperative"] else "split, two kernels"))
-                with _env(NT_NORM_SPLIT_ROWS=str(1 << 40)):
+                with nt.override(NT_NORM_SPLIT_ROWS=str(1 << 40)):
                     wsb = nt.nt_norm_workspace_bytes(opc, M, N, code)
                     ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")
                     if op == "layernorm":
@@ -596,7 +600,7 @@ def wide_norm_sweep(torch, steps, warmup, md_path=None):
                             M, N, code, 1e-6, xs[i].data_ptr(), g.data_ptr(), ys[i].data_ptr(), ws.data_ptr(),
                             wsb, sh))
                     ms_split = timed(split, R)
-                    with _env(NT_COOP="0"):
+                    with nt.override(NT_COOP="0"):
                         ms_split2 = timed(split, R)
                 if op == "layernorm":
                     looped = lambda i: ok(nt.nt_layernorm_rows(  # noqa: E731
@@ -668,7 +672,7 @@ def wide_norm_traffic(torch, steps):
              ("looped", {}, False))
     out = {}
     for name, env, with_ws in forms:
-        with _env(**env):
+        with nt.override(**env):
             p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS if with_ws else nt.NT_OP_RMSNORM, M, N, code, True)
             wsb = int(p["workspace_bytes"])          # this form's own workspace (the two use other chunks)
             ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device="cuda")

@@ -47,8 +47,11 @@
  *             results are valid once the stream reaches that point, and the
  *             inputs must stay alive until then.
  *  Errors     argument errors are returned synchronously, before anything is
- *             enqueued.  A failed launch returns NT_ERR_HIP (the HIP error is
- *             read and cleared with hipGetLastError).
+ *             enqueued.  A failed launch returns NT_ERR_HIP: the status is
+ *             the one the launch call itself returned; the library neither
+ *             reads nor clears the thread's last HIP error, so an error left
+ *             by an earlier, unrelated HIP call is not reported as this
+ *             call's and stays for its owner to read.
  *  Aliasing   y == x (in place) is allowed.  y partly overlapping x, and a
  *             workspace overlapping x or y, return NT_ERR_ALIAS (checked from
  *             the addresses and sizes, before anything is enqueued).  Any
@@ -58,9 +61,15 @@
  *             result is rounded to `dt` once, round-to-nearest-even.  The
  *             reduction order is fixed, so results are bitwise repeatable
  *             for a given shape, type and device.
- *  Threads    every entry point is thread-safe; the library's only global
- *             state is a read-only device-property cache and an atomic call
- *             counter that tags the split path's workspace records.
+ *  Threads    every entry point is thread-safe.  Global state: a cache of
+ *             per-device properties (compute units, each kernel's occupancy;
+ *             filled on first use, then read-only), an atomic call counter
+ *             that tags the split path's workspace records, the tuning
+ *             overrides of nt_set_override (atomics, read once from the
+ *             environment at load), and the device scratch array of
+ *             nt_softmax_rows_noalloc.  The per-call path reads the
+ *             environment never and queries device attributes only on the
+ *             first call on each device.
  */
 #ifndef NT_H
 #define NT_H
@@ -95,7 +104,8 @@ typedef NT_ENUM {
                               (or nt_norm_workspace_bytes)                    */
     NT_ERR_HIP = 7,        /* the HIP runtime reported a launch error          */
     NT_ERR_ALIAS = 8,      /* an output overlaps a buffer it may not overlap   */
-    NT_ERR_SCALE = 9       /* causal softmax: scale is not finite and > 0      */
+    NT_ERR_SCALE = 9,      /* causal softmax: scale is not finite and > 0      */
+    NT_ERR_OVERRIDE = 10   /* nt_set_override: unknown name or malformed value */
 } nt_status;
 
 /*
@@ -204,8 +214,8 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  * bytes (NT_ERR_WORKSPACE).  Contents need not be initialized; two calls in
  * flight at once must not share a workspace; a workspace overlapping x or y
  * is NT_ERR_ALIAS (overlapping the parameters is undefined).  In place
- * (y == x) is allowed.  NT_COOP=0 in the
- * environment selects the two kernels throughout.
+ * (y == x) is allowed.  The override NT_COOP=0 (nt_set_override) selects
+ * the two kernels throughout.
  */
 size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt);
 
@@ -251,6 +261,30 @@ nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
                               const void *x, const void *residual,
                               const void *weight, void *h, void *y,
                               void *stream);
+
+/*
+ * Tuning overrides, for tests and launch-shape sweeps (not needed in normal
+ * use).  `name` is one of the NT_* settings below, each read once from the
+ * environment variable of the same name when the library is loaded; `value`
+ * is its new value, or NULL to restore the value read at load.  Returns
+ * NT_ERR_OVERRIDE for an unknown name or a malformed value (nothing
+ * changes), NT_ERR_NULL for a NULL name.  The settings are process-wide and
+ * apply to calls planned after the change; change them only while no other
+ * thread is calling the library.
+ *   NT_FORCE_PATH      "split" (softmax: the split path at any width) or
+ *                      "looped" (norms: the looped kernel at any width)
+ *   NT_FORCE_SHAPE     "W,K": single-pass shape, ignored where it does not
+ *                      fit the row or is not built
+ *   NT_SPLIT_SHAPE     "W,K": chunk shape of the split softmax
+ *   NT_COOP            "0": the two-kernel split forms throughout
+ *   NT_COOP_SPIN       polls (0..65536, default 1024) of a cooperative
+ *                      kernel before it recomputes a missing record
+ *   NT_PERSISTENT      "0" never, "1" where it pays (default), "always"
+ *   NT_PERSIST_GRID    workgroups of the persistent norm kernel (> 0)
+ *   NT_NORM_SPLIT_ROWS rows below which a wide norm row is split (>= 0)
+ *   NT_DEBUG           "1": print each plan to stderr
+ */
+nt_status nt_set_override(const char *name, const char *value);
 
 /* Static, human-readable name of a status code. */
 const char *nt_status_string(nt_status s);

@@ -7,7 +7,8 @@ integers, ``stream`` as a ``hipStream_t`` handle) and return the status code.
 ``softmax``, ``softmax_causal``, ``layer_norm``, ``rms_norm``,
 ``add_layer_norm`` and ``add_rms_norm`` are conveniences over torch
 tensors on an AMD GPU: they check contiguity, allocate outputs (and the
-split-path workspace) with torch, and launch on torch's current stream.
+split-path workspace) with torch, and launch on torch's current stream, or
+on the `stream` given (then the allocations belong to that stream).
 
 There is no fallback: if ``libnt.so`` is missing or the call fails, an
 exception is raised.
@@ -27,11 +28,11 @@ NT_OP_LAYERNORM_WS = 6
 NT_OP_RMSNORM_WS = 7
 STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4: "NT_ERR_EPS",
           5: "NT_ERR_ALIGN", 6: "NT_ERR_WORKSPACE", 7: "NT_ERR_HIP", 8: "NT_ERR_ALIAS",
-          9: "NT_ERR_SCALE"}
+          9: "NT_ERR_SCALE", 10: "NT_ERR_OVERRIDE"}
 EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows",
             "nt_rmsnorm_rows", "nt_norm_workspace_bytes", "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws",
             "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
-            "nt_status_string", "nt_plan_launch")
+            "nt_status_string", "nt_plan_launch", "nt_set_override")
 
 
 class NtError(RuntimeError):
@@ -80,7 +81,8 @@ def lib():
     L.nt_status_string.argtypes = [i32]
     L.nt_status_string.restype = ctypes.c_char_p
     L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
-    for f in ("nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
+    L.nt_set_override.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
+    for f in ("nt_set_override", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
               "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws", "nt_add_layernorm_rows",
               "nt_add_rmsnorm_rows", "nt_plan_launch"):
         getattr(L, f).restype = i32
@@ -144,6 +146,43 @@ def nt_plan_launch(op: int, M: int, N: int, dt: int, aligned16: bool = True) -> 
     return p.as_dict()
 
 
+def nt_set_override(name: str, value) -> int:
+    return int(lib().nt_set_override(name.encode(), None if value is None else str(value).encode()))
+
+
+# The overrides this module has set (name -> value; absent = the value the
+# library read from the environment at load).
+_overrides = {}
+
+
+def set_override(name: str, value) -> None:
+    """Set one tuning override (value None: back to the load-time value)."""
+    _check(nt_set_override(name, value), f"nt_set_override({name!r}, {value!r})")
+    if value is None:
+        _overrides.pop(name, None)
+    else:
+        _overrides[name] = str(value)
+
+
+class override:
+    """Context manager: tuning overrides (NT_COOP="0", NT_FORCE_SHAPE="4,2",
+    ...) for the calls made inside it; the previous settings are restored on
+    exit.  Process-wide: not for use while other threads call the library."""
+
+    def __init__(self, **kv):
+        self.kv, self.saved = kv, {}
+
+    def __enter__(self):
+        for k, v in self.kv.items():
+            self.saved[k] = _overrides.get(k)
+            set_override(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            set_override(k, v)
+
+
 def status_string(code: int) -> str:
     try:
         return nt_status_string(code)
@@ -188,6 +227,33 @@ def _stream(stream, x=None):
     return torch.cuda.current_stream().cuda_stream
 
 
+class _alloc_on:
+    """Allocations made inside belong to the stream the kernels run on.  With
+    an explicit `stream` (a torch stream or a raw hipStream_t handle) torch's
+    caching allocator is told so (torch.cuda.stream): a buffer created here
+    and dropped on return -- the split path's workspace -- is then not handed
+    to another stream's allocation while these kernels may still use it, and
+    is not a block that a kernel still running on the current stream uses.
+    Without one, the current stream is the launch stream already."""
+
+    def __init__(self, stream, x):
+        self.ctx = None
+        if stream is not None:
+            torch = _torch()
+            if not isinstance(stream, torch.cuda.Stream):
+                stream = torch.cuda.ExternalStream(int(stream), device=x.device)
+            self.ctx = torch.cuda.stream(stream)
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+
+
 def _rows(x):
     if not x.is_contiguous():
         raise ValueError("x must be contiguous (rows of stride N)")
@@ -228,11 +294,12 @@ def softmax(x, out=None, stream=None):
     torch = _torch()
     M, N = _rows(x)
     _on_device(x)
-    y = _out_like(x, out)
     dt = dtype_code(x)
-    wsb = nt_softmax_workspace_bytes(M, N, dt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
-    _check(nt_softmax_rows(M, N, dt, _ptr(x), _ptr(y), _ptr(ws), wsb, _stream(stream, x)), "nt_softmax_rows")
+    with _alloc_on(stream, x):
+        y = _out_like(x, out)
+        wsb = nt_softmax_workspace_bytes(M, N, dt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+        _check(nt_softmax_rows(M, N, dt, _ptr(x), _ptr(y), _ptr(ws), wsb, _stream(stream, x)), "nt_softmax_rows")
     return y
 
 
@@ -245,12 +312,13 @@ def softmax_causal(x, scale=1.0, queries=None, offset=0, out=None, stream=None):
     if queries is None:
         queries = x.shape[-2] if x.dim() >= 2 else 1
     _on_device(x)
-    y = _out_like(x, out)
     dt = dtype_code(x)
-    wsb = nt_softmax_workspace_bytes(M, N, dt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
-    _check(nt_softmax_causal_rows(M, N, dt, float(scale), int(queries), int(offset), _ptr(x), _ptr(y), _ptr(ws),
-                                  wsb, _stream(stream, x)), "nt_softmax_causal_rows")
+    with _alloc_on(stream, x):
+        y = _out_like(x, out)
+        wsb = nt_softmax_workspace_bytes(M, N, dt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+        _check(nt_softmax_causal_rows(M, N, dt, float(scale), int(queries), int(offset), _ptr(x), _ptr(y),
+                                      _ptr(ws), wsb, _stream(stream, x)), "nt_softmax_causal_rows")
     return y
 
 
@@ -259,18 +327,19 @@ def layer_norm(x, gamma=None, beta=None, eps=1e-5, out=None, stream=None):
     torch = _torch()
     M, N = _rows(x)
     _on_device(x, gamma, beta)
-    y = _out_like(x, out)
-    lead = x.shape[:-1]
-    mean = torch.empty(lead, dtype=torch.float32, device=x.device)
-    rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
     for p in (gamma, beta):
         if p is not None and (p.numel() != N or p.dtype != x.dtype or not p.is_contiguous()):
             raise ValueError("gamma/beta must be contiguous, of x's dtype, with N entries")
     dt = dtype_code(x)
-    wsb = nt_norm_workspace_bytes(NT_OP_LAYERNORM, M, N, dt)     # a few rows too wide for one pass
-    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
-    _check(nt_layernorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean),
-                                _ptr(rstd), _ptr(ws), wsb, _stream(stream, x)), "nt_layernorm_rows_ws")
+    lead = x.shape[:-1]
+    with _alloc_on(stream, x):
+        y = _out_like(x, out)
+        mean = torch.empty(lead, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
+        wsb = nt_norm_workspace_bytes(NT_OP_LAYERNORM, M, N, dt)     # a few rows too wide for one pass
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+        _check(nt_layernorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean),
+                                    _ptr(rstd), _ptr(ws), wsb, _stream(stream, x)), "nt_layernorm_rows_ws")
     return y, mean, rstd
 
 
@@ -279,14 +348,15 @@ def rms_norm(x, weight=None, eps=1e-6, out=None, stream=None):
     torch = _torch()
     M, N = _rows(x)
     _on_device(x, weight)
-    y = _out_like(x, out)
     if weight is not None and (weight.numel() != N or weight.dtype != x.dtype or not weight.is_contiguous()):
         raise ValueError("weight must be contiguous, of x's dtype, with N entries")
     dt = dtype_code(x)
-    wsb = nt_norm_workspace_bytes(NT_OP_RMSNORM, M, N, dt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
-    _check(nt_rmsnorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(weight), _ptr(y), _ptr(ws), wsb,
-                              _stream(stream, x)), "nt_rmsnorm_rows_ws")
+    with _alloc_on(stream, x):
+        y = _out_like(x, out)
+        wsb = nt_norm_workspace_bytes(NT_OP_RMSNORM, M, N, dt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device) if wsb else None
+        _check(nt_rmsnorm_rows_ws(M, N, dt, float(eps), _ptr(x), _ptr(weight), _ptr(y), _ptr(ws), wsb,
+                                  _stream(stream, x)), "nt_rmsnorm_rows_ws")
     return y
 
 
@@ -302,17 +372,18 @@ def add_layer_norm(x, residual, gamma=None, beta=None, eps=1e-5, h_out=None, out
     M, N = _rows(x)
     _same_rows(x, residual)
     _on_device(x, residual, gamma, beta)
-    h = _out_like(x, h_out, "h_out")
-    y = _out_like(x, out)
-    lead = x.shape[:-1]
-    mean = torch.empty(lead, dtype=torch.float32, device=x.device)
-    rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
     for p in (gamma, beta):
         if p is not None and (p.numel() != N or p.dtype != x.dtype or not p.is_contiguous()):
             raise ValueError("gamma/beta must be contiguous, of x's dtype, with N entries")
-    _check(nt_add_layernorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(gamma),
-                                 _ptr(beta), _ptr(h), _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream, x)),
-           "nt_add_layernorm_rows")
+    lead = x.shape[:-1]
+    with _alloc_on(stream, x):
+        h = _out_like(x, h_out, "h_out")
+        y = _out_like(x, out)
+        mean = torch.empty(lead, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
+        _check(nt_add_layernorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(gamma),
+                                     _ptr(beta), _ptr(h), _ptr(y), _ptr(mean), _ptr(rstd), _stream(stream, x)),
+               "nt_add_layernorm_rows")
     return h, y, mean, rstd
 
 
@@ -322,10 +393,11 @@ def add_rms_norm(x, residual, weight=None, eps=1e-6, h_out=None, out=None, strea
     M, N = _rows(x)
     _same_rows(x, residual)
     _on_device(x, residual, weight)
-    h = _out_like(x, h_out, "h_out")
-    y = _out_like(x, out)
     if weight is not None and (weight.numel() != N or weight.dtype != x.dtype or not weight.is_contiguous()):
         raise ValueError("weight must be contiguous, of x's dtype, with N entries")
-    _check(nt_add_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(weight), _ptr(h),
-                               _ptr(y), _stream(stream, x)), "nt_add_rmsnorm_rows")
+    with _alloc_on(stream, x):
+        h = _out_like(x, h_out, "h_out")
+        y = _out_like(x, out)
+        _check(nt_add_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(weight),
+                                   _ptr(h), _ptr(y), _stream(stream, x)), "nt_add_rmsnorm_rows")
     return h, y

@@ -1,7 +1,6 @@
 // Instantiation of the row kernels for one element type, selected at build
 // time with -DNTK_DT=0 (fp32), 1 (fp16) or 2 (bf16).
 #include <atomic>
-#include <cstdlib>
 
 #include "launch.hpp"
 
@@ -16,14 +15,19 @@ constexpr int DT = NTK_DT;
 // fp32 holds 4 values per chunk, 16-bit types 8.
 constexpr bool kWide = dt_info<DT>::VEC == 4;
 
+// Launch a row kernel; the status is the one the launch call returns (the
+// thread's last-error state is neither read nor cleared).
+hipError_t launch_k(void (*k)(RowArgs), int64_t grid, int threads, hipStream_t s, RowArgs a) {
+    void *args[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), dim3((uint32_t)grid), dim3((uint32_t)threads), args, 0,
+                           s);
+}
+
 template <int OP, int W, int K, bool PR, bool RES>
 hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     constexpr int T = GroupShape<W>::THREADS;
-    if (al)
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, true, PR, RES>), dim3((uint32_t)grid), dim3(T), 0, s, a);
-    else
-        hipLaunchKernelGGL((row_resident<OP, DT, W, K, false, PR, RES>), dim3((uint32_t)grid), dim3(T), 0, s, a);
-    return hipGetLastError();
+    return al ? launch_k(row_resident<OP, DT, W, K, true, PR, RES>, grid, T, s, a)
+              : launch_k(row_resident<OP, DT, W, K, false, PR, RES>, grid, T, s, a);
 }
 
 // Values a lane holds for one row: LayerNorm keeps at most 16 (its fp64
@@ -36,7 +40,8 @@ hipError_t go_pr(bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
 template <int OP, int K, bool RES = false, int W = 0>
 constexpr bool shape_built() {
     constexpr int V = K * dt_info<DT>::VEC;
-    return OP == OP_LAYERNORM ? (V <= 16 || (W >= 5 && W <= 8 && V == 32)) : V <= (RES ? 32 : 64);
+    // LayerNorm is never planned with more than 12 waves per row
+    return OP == OP_LAYERNORM ? ((V <= 16 || (W >= 5 && W <= 8 && V == 32)) && W <= 12) : V <= (RES ? 32 : 64);
 }
 
 // Norms with every parameter vector present take the specialised PR kernel;
@@ -82,10 +87,11 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
 }
 
 // Persistent norm kernel: as many workgroups as fit on the device at once
-// (occupancy x compute units, the occupancy cached per instantiation), or
-// NT_PERSIST_GRID when set; never more than there are rows.
+// (occupancy x `cus` compute units, the occupancy cached per instantiation),
+// or `grid_override` when > 0 (the NT_PERSIST_GRID tuning override); never
+// more than there are rows.
 template <int OP, int W, int K, bool RES>
-hipError_t persist_go(const RowArgs &a, hipStream_t s) {
+hipError_t persist_go(const RowArgs &a, hipStream_t s, int cus, int64_t grid_override) {
     static std::atomic<int> per_cu{0};
     int pc = per_cu.load(std::memory_order_relaxed);
     if (pc == 0) {
@@ -96,24 +102,15 @@ hipError_t persist_go(const RowArgs &a, hipStream_t s) {
         per_cu.store(n, std::memory_order_relaxed);
         pc = n;
     }
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        cus = 256;
     // RMSNorm: half the resident workgroups per CU (rounded up) streams 2%
     // faster than all of them on 8192- and 16384-wide bf16 rows; LayerNorm,
     // whose rows take longer to reduce, is fastest with every slot filled.
     // The grid stays a multiple of the CU count: uneven grids leave some CUs
     // a row more than others (7-10% slower).
     if constexpr (OP == OP_RMSNORM) pc = (pc + 1) / 2;
-    int64_t grid = (int64_t)pc * cus;
-    if (const char *e = std::getenv("NT_PERSIST_GRID")) {
-        const long long v = std::atoll(e);
-        if (v > 0) grid = v;
-    }
+    int64_t grid = grid_override > 0 ? grid_override : (int64_t)pc * cus;
     if (grid > a.M) grid = a.M;
-    hipLaunchKernelGGL((row_norm_persistent<OP, DT, W, K, RES>), dim3((uint32_t)grid), dim3(64 * W), 0, s, a);
-    return hipGetLastError();
+    return launch_k(row_norm_persistent<OP, DT, W, K, RES>, grid, 64 * W, s, a);
 }
 
 // The persistent kernel is planned for LayerNorm (plain, and fused with the
@@ -121,22 +118,22 @@ hipError_t persist_go(const RowArgs &a, hipStream_t s) {
 // chunks; other norms stream faster one row per workgroup, and their
 // persistent forms are not built.
 template <int OP, int W, int K>
-hipError_t persist_pick(const RowArgs &a, hipStream_t s) {
+hipError_t persist_pick(const RowArgs &a, hipStream_t s, int cus, int64_t go) {
     if (a.r) {
-        if constexpr (OP == OP_LAYERNORM) return persist_go<OP, W, K, true>(a, s);
+        if constexpr (OP == OP_LAYERNORM) return persist_go<OP, W, K, true>(a, s, cus, go);
         return hipErrorInvalidValue;
     }
-    if constexpr (OP == OP_LAYERNORM || !kWide || (W == 8 && K == 8)) return persist_go<OP, W, K, false>(a, s);
+    if constexpr (OP == OP_LAYERNORM || !kWide || (W == 8 && K == 8)) return persist_go<OP, W, K, false>(a, s, cus, go);
     return hipErrorInvalidValue;
 }
 
 template <int OP>
-hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
+hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s, int cus, int64_t go) {
 #define NTK_CASE(w, k)                                                   \
     if (W == w && K == k) {                                              \
         if constexpr (shape_built<OP, k, false, w>() && k * dt_info<DT>::VEC <= 32 &&                       \
                       !(OP == OP_LAYERNORM && kWide && k * dt_info<DT>::VEC > 16))                        \
-            return persist_pick<OP, w, k>(a, s);                                                          \
+            return persist_pick<OP, w, k>(a, s, cus, go);                                                 \
         return hipErrorInvalidValue;                                     \
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
@@ -148,10 +145,10 @@ hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s) {
+hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus, int64_t go) {
     switch (op) {
-    case OP_LAYERNORM: return persistent<OP_LAYERNORM>(W, K, a, s);
-    case OP_RMSNORM: return persistent<OP_RMSNORM>(W, K, a, s);
+    case OP_LAYERNORM: return persistent<OP_LAYERNORM>(W, K, a, s, cus, go);
+    case OP_RMSNORM: return persistent<OP_RMSNORM>(W, K, a, s, cus, go);
     }
     return hipErrorInvalidValue;
 }
@@ -159,35 +156,22 @@ hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s)
 template <int OP>
 hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     if (W == 8 && K == 4) {
-        const dim3 g((uint32_t)grid), b(512);
-        if (a.r) {
-            if (al)
-                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true, true>), g, b, 0, s, a);
-            else
-                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false, true>), g, b, 0, s, a);
-        } else {
-            if (al)
-                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, true, false>), g, b, 0, s, a);
-            else
-                hipLaunchKernelGGL((row_looped<OP, DT, 8, 4, false, false>), g, b, 0, s, a);
-        }
-        return hipGetLastError();
+        if (a.r)
+            return al ? launch_k(row_looped<OP, DT, 8, 4, true, true>, grid, 512, s, a)
+                      : launch_k(row_looped<OP, DT, 8, 4, false, true>, grid, 512, s, a);
+        return al ? launch_k(row_looped<OP, DT, 8, 4, true, false>, grid, 512, s, a)
+                  : launch_k(row_looped<OP, DT, 8, 4, false, false>, grid, 512, s, a);
     }
     return hipErrorInvalidValue;
 }
 
 template <int W, int K, bool AL, bool CAUSAL>
 hipError_t split_al(bool coop, const RowArgs &a, hipStream_t s) {
-    const uint32_t grid = (uint32_t)(a.M * a.P);
-    if (coop) {
-        hipLaunchKernelGGL((softmax_coop<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((softmax_split_partial<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
-    hipError_t e = hipGetLastError();
+    const int64_t grid = a.M * a.P;
+    if (coop) return launch_k(softmax_coop<DT, W, K, AL, CAUSAL>, grid, 64 * W, s, a);
+    const hipError_t e = launch_k(softmax_split_partial<DT, W, K, AL, CAUSAL>, grid, 64 * W, s, a);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((softmax_split_finalize<DT, W, K, AL, CAUSAL>), dim3(grid), dim3(64 * W), 0, s, a);
-    return hipGetLastError();
+    return launch_k(softmax_split_finalize<DT, W, K, AL, CAUSAL>, grid, 64 * W, s, a);
 }
 
 // The causal split kernels are built for the planner's split shapes only:
@@ -221,22 +205,18 @@ hipError_t split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t
 
 template <int OP, int W, int K, bool AL>
 hipError_t norm_split_go(bool coop, const RowArgs &a, hipStream_t s) {
-    const uint32_t grid = (uint32_t)(a.M * a.P);
+    const int64_t grid = a.M * a.P;
     if (coop) {
         // the one-pass form is planned for 8 x 4 chunks, not for 16-bit
         // LayerNorm, and in fp32 also 8 x 8
         if constexpr ((W == 8 && K == 4 && !(OP == OP_LAYERNORM && DT != DT_F32)) ||
-                      (DT == DT_F32 && W == 8 && K == 8)) {
-            hipLaunchKernelGGL((norm_coop<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
-            return hipGetLastError();
-        }
+                      (DT == DT_F32 && W == 8 && K == 8))
+            return launch_k(norm_coop<OP, DT, W, K, AL>, grid, 64 * W, s, a);
         return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((norm_split_partial<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_k(norm_split_partial<OP, DT, W, K, AL>, grid, 64 * W, s, a);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((norm_split_finalize<OP, DT, W, K, AL>), dim3(grid), dim3(64 * W), 0, s, a);
-    return hipGetLastError();
+    return launch_k(norm_split_finalize<OP, DT, W, K, AL>, grid, 64 * W, s, a);
 }
 
 // The split norm's chunk shapes: 8 waves x 4 chunks (32 KiB), 8 x 1, 4 x 1 (two kernels); 8 x 4 in one pass,
@@ -292,8 +272,9 @@ hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, 
 hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s) {
-    return persistent_any(op, W, K, a, s);
+hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
+                                 int64_t grid_override) {
+    return persistent_any(op, W, K, a, s, cus, grid_override);
 }
 hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);
@@ -308,8 +289,9 @@ hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, 
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
-    return persistent_any(op, W, K, a, s);
+hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
+                                 int64_t grid_override) {
+    return persistent_any(op, W, K, a, s, cus, grid_override);
 }
 hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);
@@ -324,8 +306,9 @@ hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a,
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s) {
-    return persistent_any(op, W, K, a, s);
+hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
+                                 int64_t grid_override) {
+    return persistent_any(op, W, K, a, s, cus, grid_override);
 }
 hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);

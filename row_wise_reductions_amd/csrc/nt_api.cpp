@@ -138,37 +138,120 @@ bool valid_shape(int64_t M, int64_t N) {
 
 bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Optional "W,K" override from the environment (tuning and tests only).
-bool env_shape(const char *name, Shape *out) {
-    const char *s = std::getenv(name);
-    if (!s || !*s) return false;
-    int w = 0, k = 0;
-    if (std::sscanf(s, "%d,%d", &w, &k) != 2 || w <= 0 || k <= 0) return false;
-    *out = {w, k};
+// ---------------------------------------------------------------------------
+// Tuning overrides (tests and launch-shape sweeps).  Each is read once from
+// the NT_* environment variable of the same name when the library is loaded;
+// nt_set_override() changes it afterwards.  The per-call path only reads
+// these atomics.  Shapes are packed as (W << 32) | K, 0 = none.
+// ---------------------------------------------------------------------------
+enum TuneKey {
+    T_FORCE_PATH,       // NT_FORCE_PATH: 0 none, 1 "split" (softmax), 2 "looped" (norms)
+    T_FORCE_SHAPE,      // NT_FORCE_SHAPE "W,K": single-pass shape (ignored if it does not fit the row)
+    T_SPLIT_SHAPE,      // NT_SPLIT_SHAPE "W,K": split softmax chunk shape
+    T_COOP,             // NT_COOP: "0" selects the two-kernel split forms
+    T_COOP_SPIN,        // NT_COOP_SPIN: polls before a missing record is recomputed (0..65536)
+    T_PERSISTENT,       // NT_PERSISTENT: "0" never, "always" wherever built, "1" where it pays
+    T_PERSIST_GRID,     // NT_PERSIST_GRID: workgroups of the persistent norm kernel (> 0)
+    T_NORM_SPLIT_ROWS,  // NT_NORM_SPLIT_ROWS: rows below which a wide norm is split (>= 0)
+    T_DEBUG,            // NT_DEBUG: print each plan to stderr
+    T_COUNT
+};
+const char *const kTuneNames[T_COUNT] = {"NT_FORCE_PATH",   "NT_FORCE_SHAPE",     "NT_SPLIT_SHAPE",
+                                         "NT_COOP",         "NT_COOP_SPIN",       "NT_PERSISTENT",
+                                         "NT_PERSIST_GRID", "NT_NORM_SPLIT_ROWS", "NT_DEBUG"};
+constexpr int64_t kTuneDefault[T_COUNT] = {0, 0, 0, 1, 1024, 1, 0, -1, 0};
+std::atomic<int64_t> g_tune[T_COUNT];
+int64_t g_tune_loaded[T_COUNT];      // the values read at load (what a reset restores)
+
+// Parse a setting (NULL or "" gives the default); false for a malformed
+// value, which the environment reader replaces by the default and the
+// setter refuses.
+bool parse_tune(int key, const char *s, int64_t *out) {
+    if (!s || !*s) {
+        *out = kTuneDefault[key];
+        return true;
+    }
+    switch (key) {
+    case T_FORCE_PATH:
+        if (std::strcmp(s, "split") == 0) *out = 1;
+        else if (std::strcmp(s, "looped") == 0) *out = 2;
+        else return false;
+        return true;
+    case T_FORCE_SHAPE:
+    case T_SPLIT_SHAPE: {
+        int w = 0, k = 0;
+        char tail = 0;
+        if (std::sscanf(s, "%d,%d%c", &w, &k, &tail) != 2 || w <= 0 || k <= 0) return false;
+        *out = ((int64_t)w << 32) | (int64_t)k;
+        return true;
+    }
+    case T_COOP:
+    case T_DEBUG:
+        *out = std::strcmp(s, "0") == 0 ? 0 : 1;
+        return true;
+    case T_PERSISTENT:
+        if (std::strcmp(s, "0") == 0) *out = 0;
+        else if (std::strcmp(s, "1") == 0) *out = 1;
+        else if (std::strcmp(s, "always") == 0) *out = 2;
+        else return false;
+        return true;
+    default: {
+        char *end = nullptr;
+        const long long v = std::strtoll(s, &end, 10);
+        if (end == s || *end) return false;
+        if (key == T_COOP_SPIN && (v < 0 || v > 65536)) return false;
+        if (key == T_PERSIST_GRID && v <= 0) return false;
+        if (key == T_NORM_SPLIT_ROWS && v < 0) return false;
+        *out = (int64_t)v;
+        return true;
+    }
+    }
+}
+
+// Runs once, when the library is loaded.
+struct TuneInit {
+    TuneInit() {
+        for (int k = 0; k < T_COUNT; ++k) {
+            int64_t v = kTuneDefault[k];
+            if (!parse_tune(k, std::getenv(kTuneNames[k]), &v)) v = kTuneDefault[k];
+            g_tune_loaded[k] = v;
+            g_tune[k].store(v, std::memory_order_relaxed);
+        }
+    }
+} g_tune_init;
+
+int64_t tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
+
+bool tune_shape(TuneKey k, Shape *out) {
+    const int64_t v = tune(k);
+    if (v == 0) return false;
+    *out = {(int)(v >> 32), (int)(v & 0xffffffff)};
     return true;
 }
 
-bool debug_on() {
-    const char *s = std::getenv("NT_DEBUG");
-    return s && *s && std::strcmp(s, "0") != 0;
-}
+bool debug_on() { return tune(T_DEBUG) != 0; }
 
-// Cooperative split softmax (one pass over x) unless NT_COOP=0.
-bool coop_enabled() {
-    const char *s = std::getenv("NT_COOP");
-    return !(s && std::strcmp(s, "0") == 0);
-}
+// Cooperative split forms (one pass over x) unless NT_COOP=0.
+bool coop_enabled() { return tune(T_COOP) != 0; }
 
-// Polls of the cooperative kernel before it recomputes a missing chunk's
-// record itself (NT_COOP_SPIN overrides; 0 recomputes every chunk that has
-// not arrived at the first look, which tests use).
-int32_t coop_spin() {
-    const char *s = std::getenv("NT_COOP_SPIN");
-    if (s && *s) {
-        const long v = std::strtol(s, nullptr, 10);
-        if (v >= 0 && v <= 65536) return (int32_t)v;
+// Polls of the cooperative kernels before they recompute a missing chunk's
+// record themselves (0 recomputes every record not there at the first look,
+// which tests use).
+int32_t coop_spin() { return (int32_t)tune(T_COOP_SPIN); }
+
+// Compute units of each device, queried on the first call made on it.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        g_cus[dev].store(c, std::memory_order_relaxed);
     }
-    return 1024;
+    return c;
 }
 
 // Tag of the cooperative kernel's workspace records: unique per call within
@@ -186,10 +269,7 @@ uint32_t next_tag() {
 // tag, and could take the previous replay's records for its own.
 nt_status stream_capturing(void *stream, bool *capturing) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) {
-        (void)hipGetLastError();
-        return NT_ERR_HIP;
-    }
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) return NT_ERR_HIP;
     *capturing = cs != hipStreamCaptureStatusNone;
     return NT_OK;
 }
@@ -205,22 +285,14 @@ int64_t row_chunks(int64_t N, nt_dtype dt, bool aligned) {
 // Rows below which a norm too wide for one pass is split over workgroups
 // (given a workspace); NT_NORM_SPLIT_ROWS overrides (tuning).
 int64_t norm_split_rows(nt_op op) {
-    const char *s = std::getenv("NT_NORM_SPLIT_ROWS");
-    if (s && *s) {
-        const long long v = std::atoll(s);
-        if (v >= 0) return v;
-    }
+    const int64_t v = tune(T_NORM_SPLIT_ROWS);
+    if (v >= 0) return v;
     return op == NT_OP_LAYERNORM ? kNormSplitRowsLN : kNormSplitRowsRMS;
 }
 
 // Persistent norm kernels: NT_PERSISTENT=0 never, "always" wherever the
 // kernel is built (tuning), else where it pays (persistent_pays).
-int persistent_mode() {
-    const char *s = std::getenv("NT_PERSISTENT");
-    if (s && std::strcmp(s, "0") == 0) return 0;
-    if (s && std::strcmp(s, "always") == 0) return 2;
-    return 1;
-}
+int persistent_mode() { return (int)tune(T_PERSISTENT); }
 
 // Whether persistent workgroups beat one workgroup per row, from sweeps with
 // both forced on every planned shape and row fill (M = 4096 and 256 MiB
@@ -247,7 +319,9 @@ bool persistent_pays(nt_op op, nt_dtype dt, bool res, Shape sh, int64_t nch) {
 
 // `res`: the fused residual add + norm, whose lanes also hold the residual's
 // words (at most 32 values per lane for RMSNorm; LayerNorm is capped at 16).
+// LayerNorm is built with at most 12 waves per row.
 bool shape_fits(nt_op op, nt_dtype dt, bool res, Shape sh) {
+    if (op == NT_OP_LAYERNORM && sh.W > 12) return false;      // not built
     return !(res && op == NT_OP_RMSNORM && sh.K * elems_per_chunk(dt) > 32);
 }
 
@@ -320,14 +394,14 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     p->aligned = aligned ? 1 : 0;
     const int64_t nch = row_chunks(N, dt, aligned);
     const Menu menu = menu_for(op, dt, res);
-    const char *force = std::getenv("NT_FORCE_PATH");
-    const bool force_split = op == NT_OP_SOFTMAX && force && std::strcmp(force, "split") == 0;
-    const bool force_loop = op != NT_OP_SOFTMAX && force && std::strcmp(force, "looped") == 0;
+    const int64_t force = tune(T_FORCE_PATH);
+    const bool force_split = op == NT_OP_SOFTMAX && force == 1;
+    const bool force_loop = op != NT_OP_SOFTMAX && force == 2;
 
     Shape pick = {0, 0};
     if (!force_split && !force_loop) {
         Shape o;
-        if (env_shape("NT_FORCE_SHAPE", &o) && (int64_t)64 * o.W * o.K >= nch && shape_fits(op, dt, res, o)) {
+        if (tune_shape(T_FORCE_SHAPE, &o) && (int64_t)64 * o.W * o.K >= nch && shape_fits(op, dt, res, o)) {
             pick = o;
         } else if (full_row_shape(op, dt, nch, causal, &o)) {
             pick = o;
@@ -402,7 +476,7 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     Shape s = dt == NT_F32 ? kSplitCoop32 : kSplitCoop16;
     if ((nch + 64 * s.W * s.K - 1) / (64 * s.W * s.K) > ntk::COOP_PMAX) s = kSplitWide;
     Shape o;
-    if (env_shape("NT_SPLIT_SHAPE", &o)) s = o;
+    if (tune_shape(T_SPLIT_SHAPE, &o)) s = o;
     const int64_t per = (int64_t)64 * s.W * s.K;
     const int64_t P = (nch + per - 1) / per;
     // one workgroup per (row, chunk), no striding: the grid must fit the packet
@@ -431,10 +505,12 @@ bool all_aligned16(int64_t N, nt_dtype dt, const void *x, const void *y, const v
 hipError_t launch_resident(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
     const bool al = p.aligned != 0;
     if (p.persistent) {
+        const int cus = device_cus();
+        const int64_t pg = tune(T_PERSIST_GRID);
         switch (dt) {
-        case NT_F32: return ntk::launch_persistent_f32(op, p.waves_per_row, p.chunks_per_lane, a, s);
-        case NT_F16: return ntk::launch_persistent_f16(op, p.waves_per_row, p.chunks_per_lane, a, s);
-        case NT_BF16: return ntk::launch_persistent_bf16(op, p.waves_per_row, p.chunks_per_lane, a, s);
+        case NT_F32: return ntk::launch_persistent_f32(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
+        case NT_F16: return ntk::launch_persistent_f16(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
+        case NT_BF16: return ntk::launch_persistent_bf16(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
         }
     }
     switch (dt) {
@@ -500,7 +576,6 @@ nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, con
                    : p.split == 3 ? launch_norm_split(dt, kop, p, a, s)
                                   : launch_resident(dt, kop, p, a, s);
     if (e != hipSuccess) {
-        (void)hipGetLastError();
         if (debug_on()) std::fprintf(stderr, "[nt] launch failed: %s\n", hipGetErrorString(e));
         return NT_ERR_HIP;
     }
@@ -558,8 +633,21 @@ const char *nt_status_string(nt_status s) {
     case NT_ERR_HIP: return "HIP launch error";
     case NT_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case NT_ERR_SCALE: return "scale must be finite and > 0";
+    case NT_ERR_OVERRIDE: return "unknown override name or malformed value";
     }
     return "unknown status";
+}
+
+nt_status nt_set_override(const char *name, const char *value) {
+    if (!name) return NT_ERR_NULL;
+    for (int k = 0; k < T_COUNT; ++k) {
+        if (std::strcmp(name, kTuneNames[k]) != 0) continue;
+        int64_t v = g_tune_loaded[k];
+        if (value && !parse_tune(k, value, &v)) return NT_ERR_OVERRIDE;
+        g_tune[k].store(v, std::memory_order_relaxed);
+        return NT_OK;
+    }
+    return NT_ERR_OVERRIDE;
 }
 
 nt_status nt_plan_launch(nt_op op, int64_t M, int64_t N, nt_dtype dt, int aligned16, nt_plan *out) {

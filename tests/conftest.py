@@ -24,3 +24,25 @@ def gpu_available() -> bool:
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+@pytest.fixture
+def ntenv():
+    """The library's tuning overrides (nt_set_override) with monkeypatch's
+    setenv / delenv interface; every one touched is restored when the test
+    ends."""
+    import row_wise_reductions_amd as nt
+    touched = set()
+
+    class _Overrides:
+        def setenv(self, name, value):
+            touched.add(name)
+            nt.set_override(name, value)
+
+        def delenv(self, name, raising=True):
+            touched.add(name)
+            nt.set_override(name, None)
+
+    yield _Overrides()
+    for name in touched:
+        nt.set_override(name, None)

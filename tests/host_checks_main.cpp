@@ -24,9 +24,9 @@ hipError_t launch_resident_bf16(int, int, int, bool, const RowArgs &, int64_t, h
 hipError_t launch_looped_f32(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
 hipError_t launch_looped_f16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
 hipError_t launch_looped_bf16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_STUB
-hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t) NT_STUB
-hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t) NT_STUB
-hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_STUB
+hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_STUB
+hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_STUB
 hipError_t launch_split_f32(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
 hipError_t launch_split_f16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
 hipError_t launch_split_bf16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
@@ -99,6 +99,19 @@ int main() {
                                        nullptr, nullptr, nullptr),
                  "add_layernorm residual out of x's phase");
     for (int s = -1; s <= 12; ++s) (void)nt_status_string((nt_status)s);
+    // tuning overrides: unknown names and malformed values change nothing
+    expect_error(nt_set_override(nullptr, "1"), "override NULL name");
+    expect_error(nt_set_override("NT_NOPE", "1"), "override unknown name");
+    expect_error(nt_set_override("NT_FORCE_SHAPE", "4,x"), "override malformed shape");
+    expect_error(nt_set_override("NT_FORCE_SHAPE", "4,2,1"), "override shape with a tail");
+    expect_error(nt_set_override("NT_COOP_SPIN", "65537"), "override spin out of range");
+    expect_error(nt_set_override("NT_PERSIST_GRID", "0"), "override grid 0");
+    expect_error(nt_set_override("NT_PERSISTENT", "sometimes"), "override persistent mode");
+    expect_error(nt_set_override("NT_FORCE_PATH", "both"), "override path");
+    if (nt_set_override("NT_FORCE_SHAPE", "4,4") != NT_OK || nt_set_override("NT_FORCE_SHAPE", nullptr) != NT_OK) {
+        std::fprintf(stderr, "override set/reset failed\n");
+        ++failures;
+    }
 
     std::printf("ok %ld plans, %d failures\n", plans, failures);
     return failures ? 1 : 0;

@@ -33,7 +33,7 @@ def _job(name, op, dt, M, N, data, y_bits, eps=0.0):
     return types.SimpleNamespace(w=w, data=data, y=[y], bytes=bytes_)
 
 
-def _jobs(plant=False):
+def _jobs(plant=False, row=16):
     rng = np.random.default_rng(5)
     x1 = workloads.encode(rng.standard_normal((64, 781)), "f32")
     y1 = compare.round_to(oracle.softmax(x1, "f32"), "f32")
@@ -42,7 +42,7 @@ def _jobs(plant=False):
     y2 = compare.round_to(oracle.rmsnorm(x2, "bf16", 1e-6, weight=w2), "bf16")
     if plant:                                       # a wrong element on a checked row
         y2 = y2.copy()
-        y2[16, 7] ^= np.uint16(0x0040)
+        y2[row, 7] ^= np.uint16(0x0040)
     return [_job("small_softmax", "softmax", "f32", 64, 781, {"x": x1}, y1),
             _job("small_rmsnorm", "rmsnorm", "bf16", 32, 512, {"x": x2, "weight": w2}, y2, eps=1e-6)]
 
@@ -60,6 +60,10 @@ def test_cpu_baseline_fields():
 
 def test_cpu_baseline_sees_planted_error():
     assert bench.cpu_baseline(_jobs(plant=True), np)["gpu_parity_on_sample"] is False
+    # every row is checked, not a sample of them
+    for row in (1, 5, 31):
+        r = bench.cpu_baseline(_jobs(plant=True, row=row), np)
+        assert r["gpu_parity_on_sample"] is False and r["gpu_parity_rows_checked"] == 64 + 32
 
 
 def test_kernels_summary_groups_and_scales(tmp_path):
@@ -103,10 +107,20 @@ def test_kernels_summary_groups_and_scales(tmp_path):
     assert "    cmd one" in text
 
 
-def test_env_helper_restores(monkeypatch):
-    monkeypatch.setenv("NT_COOP", "7")
-    monkeypatch.delenv("NT_NORM_SPLIT_ROWS", raising=False)
-    import os
-    with bench._env(NT_COOP="0", NT_NORM_SPLIT_ROWS="5"):
-        assert os.environ["NT_COOP"] == "0" and os.environ["NT_NORM_SPLIT_ROWS"] == "5"
-    assert os.environ["NT_COOP"] == "7" and "NT_NORM_SPLIT_ROWS" not in os.environ
+def test_override_helper_restores():
+    """bench.py's tuning settings (nt.override) are restored on exit,
+    nested or not, and a bad setting changes nothing."""
+    import row_wise_reductions_amd as nt
+    plan = lambda: nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, nt.NT_F32, True)["cooperative"]  # noqa: E731
+    assert plan() == 1
+    with nt.override(NT_COOP="0", NT_NORM_SPLIT_ROWS="5"):
+        assert plan() == 0
+        with nt.override(NT_COOP="1"):
+            assert plan() == 1
+        assert plan() == 0
+    assert plan() == 1
+    with pytest.raises(nt.NtError):
+        nt.set_override("NT_NO_SUCH_SETTING", "1")
+    with pytest.raises(nt.NtError):
+        nt.set_override("NT_COOP_SPIN", "-3")
+    assert plan() == 1

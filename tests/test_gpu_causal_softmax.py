@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from gpu_util import check_output, empty_like_dev, to_dev, to_host_bits
+from gpu_util import check_output, empty_like_dev, row_blocks, to_dev, to_host_bits
 import oracle
 import workloads
 
@@ -77,7 +77,7 @@ def causal_case(x, dt, scale, Q, off, x_off=0, y_off=0, what=""):
 # ----------------------------------------------------------------------------
 
 def test_causal_workload_full_size():
-    """131072 x 4096 bf16 (32 heads x 4096 queries): parity on sampled rows,
+    """131072 x 4096 bf16 (32 heads x 4096 queries): parity on every row,
     q + 1 non-zeros per row, and agreement with the generic softmax of the
     same -inf-masked input (bitwise when both plan the same lane shape)."""
     w = workloads.BY_NAME["causal_entry_softmax_bf16"]
@@ -102,17 +102,16 @@ def test_causal_workload_full_size():
         a = compare.ordinal(to_host_bits(y, w.dt), w.dt)
         b = compare.ordinal(to_host_bits(y_gen, w.dt), w.dt)
         assert int(np.abs(a - b).max()) <= 1, "causal entry and generic softmax differ by more than 1 ulp"
-    rng = np.random.default_rng(17)
-    rows = np.unique(np.concatenate([rng.choice(w.M, 4096, replace=False), [0, 1, Q - 1, Q, w.M - 1]]))
-    yb = to_host_bits(y, w.dt)[rows]
-    # a sampled row keeps its query through the offset: one row, queries = 1
-    # (so q = 0) and offset = its query index
-    ref = np.zeros(yb.shape, dtype=np.float64)
-    for i, r in enumerate(rows):
-        q = r % Q
-        ref[i] = oracle.softmax_causal(np.ascontiguousarray(d["x"][r:r + 1]), w.dt, 1.0, 1, q)[0]
-    check_output(yb, ref, w.dt, "causal entry")
-    assert np.array_equal(((yb & 0x7FFF) != 0).sum(axis=1), rows % Q + 1)
+    # every row against the oracle, in blocks of whole heads (row r0 of a
+    # block is query 0, so the block's own row index gives each query)
+    yb_all = to_host_bits(y, w.dt)
+    del y, y_gen, x_t
+    for r0, r1 in row_blocks(w.M, w.N, align=Q):
+        say(f"workload causal entry: rows {r0}..{r1 - 1}")
+        ref = oracle.softmax_causal(np.ascontiguousarray(d["x"][r0:r1]), w.dt, w.extra["scale"], Q, w.extra["offset"])
+        yb = yb_all[r0:r1]
+        check_output(yb, ref, w.dt, f"causal entry rows {r0}..{r1 - 1}")
+        assert np.array_equal(((yb & 0x7FFF) != 0).sum(axis=1), np.arange(r0, r1) % Q + 1)
 
 
 # ----------------------------------------------------------------------------
@@ -151,7 +150,7 @@ def test_causal_masked_inputs_unused(dt, N):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [65536, 262147, (1 << 21) + 8])
-def test_causal_split_forms_bitwise(dt, N, monkeypatch):
+def test_causal_split_forms_bitwise(dt, N, ntenv):
     """Cooperative kernel, its recompute-everything form and the two-kernel
     form agree bitwise on causal rows (chunks wholly past the visible prefix
     included)."""
@@ -162,9 +161,9 @@ def test_causal_split_forms_bitwise(dt, N, monkeypatch):
     outs = []
     for env in ({}, {"NT_COOP_SPIN": "0"}, {"NT_COOP": "0"}):
         for k in ("NT_COOP_SPIN", "NT_COOP"):
-            monkeypatch.delenv(k, raising=False)
+            ntenv.delenv(k, raising=False)
         for k, v in env.items():
-            monkeypatch.setenv(k, v)
+            ntenv.setenv(k, v)
         say(f"case causal split {dt} N={N} {env}")
         yb = to_host_bits(run_causal(x_t, dt, 0.3, Q, off), dt)
         check_output(yb, ref, dt, f"causal split {env}")

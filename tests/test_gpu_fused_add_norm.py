@@ -159,13 +159,13 @@ def test_fused_sweep(op, dt, N):
 
 @pytest.mark.parametrize("op", ["add_rmsnorm", "add_layernorm"])
 @pytest.mark.parametrize("path", ["default", "looped", "resident"])
-def test_fused_in_place(op, path, monkeypatch):
+def test_fused_in_place(op, path, ntenv):
     """h may be x or the residual, y may be x or the residual, on every path."""
     dt, M, N = "bf16", 40, 4096
     if path == "looped":
-        monkeypatch.setenv("NT_FORCE_PATH", "looped")
+        ntenv.setenv("NT_FORCE_PATH", "looped")
     if path == "resident":
-        monkeypatch.setenv("NT_PERSISTENT", "0")
+        ntenv.setenv("NT_PERSISTENT", "0")
     x = rand_bits(11, M, N, dt, scale=2.0)
     r = rand_bits(12, M, N, dt)
     p0, p1 = params(op, N, dt, 13)
@@ -182,7 +182,7 @@ def test_fused_in_place(op, path, monkeypatch):
 
 @pytest.mark.parametrize("op", ["add_layernorm"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-def test_fused_persistent_small_grids(op, dt, monkeypatch):
+def test_fused_persistent_small_grids(op, dt, ntenv):
     """The persistent fused kernel (fused add + LayerNorm rows of 1024 chunks
     or more) on grids far smaller than M is bitwise the one-row fused kernel."""
     M, N = 300, 8192
@@ -197,10 +197,10 @@ def test_fused_persistent_small_grids(op, dt, monkeypatch):
     for grid in ("3", "7", None):
         say(f"case fused persistent {op} {dt} grid={grid}")
         if grid:
-            monkeypatch.setenv("NT_PERSIST_GRID", grid)
+            ntenv.setenv("NT_PERSIST_GRID", grid)
         else:
-            monkeypatch.delenv("NT_PERSIST_GRID", raising=False)
-            monkeypatch.setenv("NT_PERSISTENT", "0")
+            ntenv.delenv("NT_PERSIST_GRID", raising=False)
+            ntenv.setenv("NT_PERSISTENT", "0")
         h, y, mean, rstd = run_fused(op, x_t, r_t, dt, EPS[op], p0_t, p1_t)
         check_fused(op, dt, h, y, mean, rstd, ref, f"fused persistent {op} {dt} grid={grid}")
         outs.append((to_host_bits(h, dt), to_host_bits(y, dt)))

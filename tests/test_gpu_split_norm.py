@@ -203,7 +203,7 @@ def test_torch_wrappers_use_the_split(op):
                                           ("rmsnorm", 128, 262144, "f32", True),
                                           ("rmsnorm", 300, 100003, "f32", False),
                                           ("layernorm", 128, 262144, "f32", True)])
-def test_cooperative_split_norm_bitwise(op, M, N, dt, al, monkeypatch):
+def test_cooperative_split_norm_bitwise(op, M, N, dt, al, ntenv):
     """The one-pass form (records exchanged between a row's workgroups) passes
     the oracle and gives the two-kernel form's bits, also when every other
     chunk's record is recomputed by the waiting workgroup (no wait at all)."""
@@ -221,18 +221,18 @@ def test_cooperative_split_norm_bitwise(op, M, N, dt, al, monkeypatch):
     check(op, a, am, ar, x, dt, p0, p1, f"coop split {op} {dt} M={M} N={N}")
     outs = []
     for env, val in (("NT_COOP_SPIN", "0"), ("NT_COOP", "0")):
-        monkeypatch.setenv(env, val)
+        ntenv.setenv(env, val)
         if env == "NT_COOP":
             # the two kernels at this row count
-            monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+            ntenv.setenv("NT_NORM_SPLIT_ROWS", "100000")
             q = nt.nt_plan_launch(WS_CODE[op], M, N, code, al)
             assert q["split"] == 3 and q["cooperative"] == 0, q
         say(f"case coop split {op} {dt} M={M} N={N} {env}={val}")
         outs.append((env, run_ws(op, x_t, dt, p0_t, p1_t),
                      (q["waves_per_row"], q["chunks_per_lane"], q["row_chunks"]) ==
                      (p["waves_per_row"], p["chunks_per_lane"], p["row_chunks"]) if env == "NT_COOP" else True))
-        monkeypatch.delenv(env)
-        monkeypatch.delenv("NT_NORM_SPLIT_ROWS", raising=False)
+        ntenv.delenv(env)
+        ntenv.delenv("NT_NORM_SPLIT_ROWS", raising=False)
     ref = to_host_bits(a, dt)
     for env, (y, ym, yr), same_chunks in outs:
         if same_chunks:
@@ -355,7 +355,7 @@ def test_split_layernorm_rows_past_2gib_offsets():
 
 
 @pytest.mark.parametrize("op", ["rmsnorm", "layernorm"])
-def test_cooperative_split_norm_large_grid(op, monkeypatch):
+def test_cooperative_split_norm_large_grid(op, ntenv):
     """8192 fp32 rows of 65536 elements in one pass: 65536 workgroups, far
     more than are resident at once, so rows straddle dispatch waves and some
     workgroups wait on siblings that start later.  Sampled rows against the
@@ -378,8 +378,8 @@ def test_cooperative_split_norm_large_grid(op, monkeypatch):
     if op == "layernorm":
         check_stats(am.cpu().numpy()[rows], rmean, "coop large grid mean")
         check_stats(ar.cpu().numpy()[rows], rrstd, "coop large grid rstd")
-    monkeypatch.setenv("NT_COOP", "0")
-    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+    ntenv.setenv("NT_COOP", "0")
+    ntenv.setenv("NT_NORM_SPLIT_ROWS", "100000")
     q = nt.nt_plan_launch(WS_CODE[op], M, N, nt.NT_F32, True)
     assert (q["split"], q["cooperative"]) == (3, 0), q
     say(f"case two-kernel split large grid {op} {dt} M={M} N={N} P={q['row_chunks']}")

@@ -199,8 +199,8 @@ def test_cooperative_split_limits():
     assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 2, 4096, F32, True)["cooperative"] == 0
 
 
-def test_cooperative_split_can_be_switched_off(monkeypatch):
-    monkeypatch.setenv("NT_COOP", "0")
+def test_cooperative_split_can_be_switched_off(ntenv):
+    ntenv.setenv("NT_COOP", "0")
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
     assert (p["split"], p["cooperative"]) == (1, 0)
 
@@ -259,15 +259,15 @@ def test_grid_fits_dispatch_packet():
         nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1 << 24, 1 << 20, F32, True)
 
 
-def test_env_overrides(monkeypatch):
-    monkeypatch.setenv("NT_FORCE_SHAPE", "4,4")
+def test_env_overrides(ntenv):
+    ntenv.setenv("NT_FORCE_SHAPE", "4,4")
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 8192, BF16, True)
     assert (p["waves_per_row"], p["chunks_per_lane"]) == (4, 4)
-    monkeypatch.setenv("NT_FORCE_SHAPE", "1,1")          # too small for the row: ignored
+    ntenv.setenv("NT_FORCE_SHAPE", "1,1")          # too small for the row: ignored
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 8192, BF16, True)
     assert 64 * p["waves_per_row"] * p["chunks_per_lane"] >= 1024
-    monkeypatch.delenv("NT_FORCE_SHAPE")
-    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    ntenv.delenv("NT_FORCE_SHAPE")
+    ntenv.setenv("NT_FORCE_PATH", "split")
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 16, 4096, F32, True)
     assert p["split"] == 1 and p["row_chunks"] == 1
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 4096, F32, True)["split"] == 0
@@ -412,15 +412,15 @@ def test_split_norm_plans():
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 2047, 1 << 20, BF16, True)["split"] == 3
 
 
-def test_split_norm_rows_switch(monkeypatch):
-    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "0")
+def test_split_norm_rows_switch(ntenv):
+    ntenv.setenv("NT_NORM_SPLIT_ROWS", "0")
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 64, 262144, F32, True)["split"] == 2
     assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 64, 262144, F32) == 0
-    monkeypatch.setenv("NT_NORM_SPLIT_ROWS", "100000")
+    ntenv.setenv("NT_NORM_SPLIT_ROWS", "100000")
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 4096, 262144, F32, True)["split"] == 3
 
 
-def test_split_norm_cooperative_switch(monkeypatch):
+def test_split_norm_cooperative_switch(ntenv):
     # 128 bf16 rows of 512 KiB: 16 chunks of 32 KiB per row in one pass
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 128, 262144, BF16, True)
     assert (p["split"], p["cooperative"], p["row_chunks"], p["grid"]) == (3, 1, 16, 2048)
@@ -431,7 +431,7 @@ def test_split_norm_cooperative_switch(monkeypatch):
     # one pass at any row count where it applies; fp32 LayerNorm included
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM_WS, 65536, 65536, F32, True)
     assert (p["split"], p["cooperative"], p["row_chunks"]) == (3, 1, 8)
-    monkeypatch.setenv("NT_COOP", "0")
+    ntenv.setenv("NT_COOP", "0")
     p2 = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 128, 262144, BF16, True)
     assert (p2["split"], p2["cooperative"], p2["row_chunks"]) == (3, 0, 16)
     p3 = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 64, 65536, F32, True)      # 2048 workgroups need 8 KiB chunks
@@ -441,7 +441,7 @@ def test_split_norm_cooperative_switch(monkeypatch):
     # of 32 KiB with a misaligned head)
     need = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32)
     assert need == 256 * 9 * 32 + 256 * 8
-    monkeypatch.delenv("NT_COOP")
+    ntenv.delenv("NT_COOP")
     assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32) == need
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 256, 65536, F32, True)["row_chunks"] == 8
 

@@ -42,6 +42,21 @@ def test_library_host_code_under_sanitizers(tmp_path):
     assert r.stdout.startswith("ok ") and "0 failures" in r.stdout, r.stdout
 
 
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_per_call_path_is_quiet(tmp_path):
+    """After the first call on a device, no call of any entry point reads the
+    environment or queries a device attribute: the host code is linked with
+    counting stand-ins for getenv and the HIP property queries, and with
+    launchers that succeed without launching (tests/percall_checks_main.cpp)."""
+    exe = str(tmp_path / "percall_checks")
+    _run([HIPCC, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-Wno-unused-command-line-argument",
+          f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+          os.path.join(CSRC, "nt_api.cpp"), os.path.join(ROOT, "tests", "percall_checks_main.cpp"), "-o", exe],
+         timeout=600)
+    r = _run([exe], env=dict(os.environ, NT_COOP="1", NT_DEBUG="0"), timeout=120)
+    assert "ok, 0 failures" in r.stdout and "getenv 0," in r.stdout, r.stdout
+
+
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 def test_oracle_under_sanitizers(tmp_path):
     exe = str(tmp_path / "oracle_checks")
