@@ -13,6 +13,11 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   distance in units in the last place.
 * ``max_rel_err`` is the fp32 criterion: max |y - y_ref| / |y_ref| with exact
   zeros required where the reference is exactly zero.
+* ``f32_errors`` splits the fp32 criterion at the bottom of the normal range:
+  where the reference rounded once to fp32 is a normal number, the relative
+  error; below 2^-126, where fp32 has a fixed quantum of 2^-149 and no
+  relative bound is attainable, the distance from the correctly rounded
+  value in units of that quantum.
 """
 from __future__ import annotations
 
@@ -132,3 +137,59 @@ def max_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
     if not np.any(nz):
         return 0.0
     return float(np.max(np.abs(y[nz] - ref[nz]) / np.abs(ref[nz])))
+
+
+F32_MIN_NORMAL = 2.0 ** -126
+F32_SUB_QUANTUM = 2.0 ** -149
+
+
+def f32_errors(gpu_bits: np.ndarray, ref: np.ndarray):
+    """(relative error over the outputs whose reference rounds to a normal
+    fp32, distance in 2^-149 quanta from RNE_f32(reference) over the others).
+
+    Exact zeros are required where the reference is exactly zero (relative
+    error inf otherwise); NaN must match NaN (inf otherwise)."""
+    y = bits_to_f64(gpu_bits, "f32")
+    ref = np.asarray(ref, dtype=np.float64)
+    r32 = round_to_value(ref, "f32")
+    sub = np.isfinite(ref) & (np.abs(r32) < F32_MIN_NORMAL) & (ref != 0)
+    rel = max_rel_err(y[~sub], ref[~sub])
+    if not np.any(sub):
+        return rel, 0.0
+    quanta = float(np.max(np.abs(y[sub] - r32[sub]) / F32_SUB_QUANTUM))
+    return rel, quanta
+
+
+def _parts(n: int, threads: int):
+    step = max(1, -(-n // threads))
+    return [(i, min(n, i + step)) for i in range(0, n, step)]
+
+
+def _threads(threads):
+    import os
+    return max(1, min(16, threads or os.cpu_count() or 1))
+
+
+def max_ulp_distance(gpu_bits: np.ndarray, ref64: np.ndarray, dt, threads=None) -> int:
+    """max over all elements of ulp_distance, computed on row blocks in a
+    thread pool (numpy releases the GIL): the same numbers, faster."""
+    from concurrent.futures import ThreadPoolExecutor
+    g = np.asarray(gpu_bits).reshape(-1)
+    r = np.asarray(ref64).reshape(-1)
+    if g.size == 0:
+        return 0
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return max(ex.map(lambda ab: int(ulp_distance(g[ab[0]:ab[1]], r[ab[0]:ab[1]], dt).max()),
+                          _parts(g.size, 4 * _threads(threads))))
+
+
+def f32_errors_threaded(gpu_bits: np.ndarray, ref: np.ndarray, threads=None):
+    """f32_errors on blocks in a thread pool: (max relative error, max quanta)."""
+    from concurrent.futures import ThreadPoolExecutor
+    g = np.asarray(gpu_bits).reshape(-1)
+    r = np.asarray(ref).reshape(-1)
+    if g.size == 0:
+        return 0.0, 0.0
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        res = list(ex.map(lambda ab: f32_errors(g[ab[0]:ab[1]], r[ab[0]:ab[1]]), _parts(g.size, 4 * _threads(threads))))
+    return max(a for a, _ in res), max(b for _, b in res)

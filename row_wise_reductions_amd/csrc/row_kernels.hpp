@@ -125,12 +125,6 @@ __device__ __forceinline__ uint4 ld16(const char *p) {
 __device__ __forceinline__ void st16(char *p, uint4 v) {
     *reinterpret_cast<uint4 *>(p) = v;
 }
-// Wait until this wave's own stores have completed (they may be issued by
-// st16_nt, which the compiler's wait counting does not see).
-__device__ __forceinline__ void wait_own_stores() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Streaming (non-temporal) 16-byte load and store for row data that is
 // touched once: they keep single-use lines from displacing reused ones
 // (the parameter vectors) and measurably raise read+write HBM throughput.
@@ -142,18 +136,32 @@ __device__ __forceinline__ uint4 ld16_nt(const char *p) {
     return ld16(p);
 #endif
 }
+// Wait until this wave's own stores have completed: s_waitcnt vmcnt(0)
+// (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Cache-policy operand of the buffer store for "nt sc1": bit 1 streaming
+// (non-temporal), bit 4 device scope (the store writes through the XCD's L2).
+constexpr int CPOL_NT_SC1 = (1 << 1) | (1 << 4);
+
 __device__ __forceinline__ void st16_nt(char *p, uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
 #if NTK_NT_STORES && NTK_STORE_SC1
-    // The compiler does not see this store, so it neither counts it for
-    // s_waitcnt nor keeps its hazards.  A VALU must not overwrite the data
-    // registers of a store wider than 64 bits within 2 wait states of it on
-    // gfx950 (1 is not enough: stores then write the new values); s_nop 1
-    // gives the 2.  A kernel that reads back what it stored waits on vmcnt
-    // itself (wait_own_stores).
-    const u32x4 t = {v.x, v.y, v.z, v.w};
-    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(p), "v"(t) : "memory");
+    // A raw buffer store, which the compiler sees (it keeps the store's
+    // hazards and wait counts itself).  The buffer's base is the first
+    // active lane's address less 1 MiB, a wave-uniform value, and each
+    // lane's offset its distance from that base: exact for every lane within
+    // 1 MiB below to 4 GiB - 1 MiB above the first active one (the lanes of a
+    // wave store at most 64 consecutive 16-byte chunks here).  The range
+    // check is effectively off (2^32 - 1 bytes).
+    const uint64_t pa = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+    const uint64_t base = ((((uint64_t)hi) << 32) | lo) - (1ull << 20);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, (int)0xFFFFFFFFu, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(t, rs, (int)(uint32_t)(pa - base), 0, CPOL_NT_SC1);
 #elif NTK_NT_STORES
-    const u32x4 t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
 #else
     st16(p, v);
@@ -668,6 +676,18 @@ __device__ __forceinline__ void softmax_finish(uint4 (&raw)[K], const RowGeom<DT
 // Per-row scalar helpers
 // ---------------------------------------------------------------------------
 
+// Exponent offset of every softmax kernel.  Each term is taken as
+// 2^(x*s2 - c) with c = m*s2 - EXP_SHIFT rounded once (m the row's or the
+// chunk's max, s2 = log2(e) or scale*log2(e)), so the largest term is about
+// 2^EXP_SHIFT.  v_exp_f32 flushes results below 2^-126 to zero; with the
+// offset, every term down to 2^-150 of the largest (the smallest that can
+// still round to a non-zero fp32 output, the sum being >= the largest term)
+// is a normal float, and the output multiply by 1/sum rounds it once into
+// the subnormal range.  Shift invariance makes any c exact in real
+// arithmetic; the sum stays far from overflow (at most 2^24 * N).
+constexpr float EXP_SHIFT = 24.0f;
+__device__ __forceinline__ float exp_offset(float m, float s2) { return __builtin_fmaf(m, s2, -EXP_SHIFT); }
+
 // 1/x and 1/sqrt(x) in fp32 from the hardware approximations (v_rcp_f32,
 // v_rsq_f32: about 1 ulp), used once per row.
 __device__ __forceinline__ float rcp_approx(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -786,15 +806,14 @@ row_resident(RowArgs a) {
         for (int k = 0; k < K; ++k) unpack<DT>(raw[k], v[k]);
 
         if constexpr (SM) {
-            // ---- softmax.  With c = m*log2(e) rounded to fp32, every element
-            // is 2^(x*log2(e) - c): one fma (exact product, one rounding) and
-            // one v_exp_f32.  Shift invariance makes any shift exact, and c is
-            // within half an ulp of m*log2(e), so no term exceeds 2^(1e-7).
-            // The causal softmax of scale*x uses s2 = scale*log2(e) in place
-            // of log2(e) (scale > 0, so the max of x gives the max of scale*x).
+            // ---- softmax.  With c = exp_offset(m), every element is
+            // 2^(x*log2(e) - c): one fma (exact product, one rounding) and
+            // one v_exp_f32; shift invariance makes the offset exact.  The
+            // causal softmax of scale*x uses s2 = scale*log2(e) in place of
+            // log2(e) (scale > 0, so the max of x gives the max of scale*x).
             const float s2 = CAUSAL ? a.s2 : LOG2E;
             const float mx = group_allreduce<W>(lane_max(v), MaxOp(), red_f[par][0], wv, lane);
-            const float c = mx * s2;
+            const float c = exp_offset(mx, s2);
             // fp32 rows of 4 or 8 chunks per lane recompute each exponential
             // for the output instead of keeping them all (the same arguments,
             // so the same bits): their stores then leave one chunk at a time,
@@ -1402,11 +1421,7 @@ __device__ __forceinline__ float2 chunk_stats(const uint4 (&raw)[K], float (&red
         for (int i = 0; i < VEC; i += 2) lm = __builtin_fmaxf(lm, __builtin_fmaxf(v[i], v[i + 1]));
     }
     const float mx = group_allreduce<W>(lm, MaxOp(), red[0], wv, lane);
-    float cj;
-    {
-#pragma clang fp contract(off)
-        cj = mx * s2;
-    }
+    const float cj = exp_offset(mx, s2);
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -1445,11 +1460,7 @@ __device__ __forceinline__ float2 chunk_stats_reload(const RowGeom<DT, AL> &geo,
         for (int i = 0; i < VEC; i += 2) lm = __builtin_fmaxf(lm, __builtin_fmaxf(v[i], v[i + 1]));
     }
     const float mx = group_allreduce<W>(lm, MaxOp(), red[0], wv, lane);
-    float cj;
-    {
-#pragma clang fp contract(off)
-        cj = mx * s2;
-    }
+    const float cj = exp_offset(mx, s2);
     float s = 0.f;
 #pragma unroll 1
     for (int k = 0; k < K; ++k) {
@@ -1467,9 +1478,10 @@ __device__ __forceinline__ float2 chunk_stats_reload(const RowGeom<DT, AL> &geo,
 }
 
 // Merge of a row's P chunk pairs q[0..P) (global or LDS) by one wave, in a
-// fixed order: m = max_j m_j, l = sum_j l_j * 2^(c_j - c) with c = m*log2e
-// (the online-normalizer rescaling).  Returns c and 1/l.  Every wave that
-// calls it on the same pairs gets the same bits.
+// fixed order: m = max_j m_j, l = sum_j l_j * 2^(c_j - c) with
+// c = exp_offset(m) and c_j = exp_offset(m_j), the offsets the pairs were
+// computed with (the online-normalizer rescaling).  Returns c and 1/l.
+// Every wave that calls it on the same pairs gets the same bits.
 template <class Q>
 __device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, float &inv, float s2 = LOG2E) {
     float m = -__builtin_inff();
@@ -1478,10 +1490,10 @@ __device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, 
     float l = 0.f;
     {
 #pragma clang fp contract(off)
-        c = m * s2;
+        c = exp_offset(m, s2);
         for (int p = lane; p < P; p += 64) {
             const float2 e = q[p];
-            const float cj = e.x * s2;       // rounded exactly as in chunk_stats
+            const float cj = exp_offset(e.x, s2);       // as chunk_stats computed it
             l += (e.x == -__builtin_inff()) ? 0.f : e.y * __builtin_amdgcn_exp2f(cj - c);
         }
     }
@@ -1490,7 +1502,7 @@ __device__ __forceinline__ void merge_pairs(Q q, int32_t P, int lane, float &c, 
     inv = rcp_approx(l);
 }
 
-// Output of one chunk: y = 2^(x*log2e - c) * (1/l), rounded once to the type.
+// Output of one chunk: y = 2^(x*s2 - c) * (1/l), rounded once to the type.
 template <int DT, int W, int K, bool AL>
 __device__ __forceinline__ void softmax_chunk_out(const uint4 (&raw)[K], const RowGeom<DT, AL> &geo, char *yr, int t,
                                                   int32_t N, bool yvec, int64_t cbase, float c, float inv,

@@ -23,6 +23,13 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
       kernels in a run that launches them directly (bench.py
       --wide-norm-traffic), beside the work's algorithmic bytes B.
 
+  python -m row_wise_reductions_amd.rocprof_summary calib --big DIR --sizes DIR --cmds FILE --md FILE.md
+      DIRs hold *_kernel_trace.csv from `rocprofv3 --kernel-trace` runs of
+      `bench.py --calibrate` (reference streams at 1 GiB) and `bench.py
+      --copy-at-sizes` (each workload's kernel beside copies of its bytes):
+      median kernel durations per (kernel, grid), all on the kernel-trace
+      clock.
+
   python -m row_wise_reductions_amd.rocprof_summary occupancy --occ DIR --active DIR [--valu DIR] --cmds FILE --md FILE.md
       DIRs hold *_counter_collection.csv from `rocprofv3 --pmc OccupancyPercent`,
       `--pmc MeanOccupancyPerActiveCU` and `--pmc VALUBusy` runs of bench.py; beside them, each
@@ -289,6 +296,89 @@ def occupancy(args):
     print("\n".join(lines))
 
 
+def _trace(pattern):
+    """(kernel name, grid work-items, duration ns) of every dispatch in the
+    kernel-trace CSV files matching `pattern`."""
+    out = []
+    for r in _rows(pattern):
+        name = r.get("Kernel_Name") or r.get("Name") or ""
+        gk = next((k for k in ("Grid_Size_X", "Grid_Size", "Grid_SizeX") if k in r), None)
+        grid = int(float(r[gk])) if gk else 0
+        out.append((name, grid, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def _median_us(ds):
+    return statistics.median(ds) / 1000.0 if ds else None
+
+
+def calib(args):
+    import bench
+    import workloads
+    big = _trace(os.path.join(args.big, "**", "*kernel_trace.csv"))
+    sizes = _trace(os.path.join(args.sizes, "**", "*kernel_trace.csv"))
+    with open(args.cmds) as f:
+        cmds = [c.strip() for c in f if c.strip()]
+    kname = {0: "ntcal_copy_kernel", 1: "ntcal_read_kernel", 2: "ntcal_fill_kernel"}
+    lines = ["# Reference streams and the row kernels on one clock (rocprofv3 kernel trace)", "",
+             "Commands (repository root, GPU host):", ""] + [f"    {c}" for c in cmds] + [
+             "", "Kernel durations from the rocprofv3 kernel trace (end - start of each dispatch), median over the "
+             "launches; GB/s counts the bytes each kernel must move (a copy: read + written).", "",
+             "## Reference streams at 1 GiB", "",
+             "| stream | kernel | dispatches | median (us) | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|"]
+    nb = 1 << 30
+    best = {}
+    for name, kind, k, sc1 in bench.CALIB_VARIANTS:
+        key = f"{kname[kind]}<{k}" + (f", {sc1}>" if kind != 1 else ">")
+        ds = [d for n, g, d in big if key in n]
+        med = _median_us(ds)
+        if med is None:
+            continue
+        gbs = (2 if kind == 0 else 1) * nb / (med * 1e-6) / 1e9
+        best[kind] = max(best.get(kind, (0, "")), (gbs, name))
+        lines.append(f"| {name} | `{key}>` | {len(ds)} | {med:.2f} | {gbs:.1f} | {gbs / 80:.1f}% |"
+                     .replace(">>`", ">`"))
+    lines.append("")
+    for kind, label in ((0, "copy (read + write)"), (1, "read only"), (2, "write only")):
+        if kind in best:
+            lines.append(f"Best {label}: {best[kind][1]}, {best[kind][0]:.1f} GB/s ({best[kind][0] / 80:.1f}% of "
+                         f"peak).  ")
+    lines += ["", "## Each workload's kernel beside copies of its bytes", "",
+              "The copies read and write the workload's M x N x e bytes (the parameter vectors and statistics "
+              "aside); inputs rotate through buffer sets of at least 1 GiB.", "",
+              "| workload | algorithmic bytes | kernel median (us) | GB/s | copy K=1 nt (us) | copy K=1 nt sc1 (us) | "
+              "copy K=2 nt sc1 (us) | copy K=4 nt sc1 (us) | kernel / fastest copy |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for w in workloads.WORKLOADS:
+        ks = kernels_of(w)
+        kmed = 0.0
+        for k in ks:
+            m = _median_us([d for n, g, d in sizes if _match(n, k)])
+            if m is None:
+                kmed = None
+                break
+            kmed += m
+        n16 = w.M * w.N * w.elem_bytes // 16
+        cols, fastest = [], None
+        for name, kind, k, sc1 in bench.COPY_AT_SIZES:
+            grid = -(-n16 // (256 * k))
+            key = f"ntcal_copy_kernel<{k}, {sc1}>"
+            m = _median_us([d for n, g, d in sizes if key in n and g in (grid, grid * 256)])
+            cols.append("" if m is None else f"{m:.2f}")
+            if m is not None:
+                fastest = m if fastest is None else min(fastest, m)
+        if kmed is None:
+            continue
+        gbs = w.algorithmic_bytes() / (kmed * 1e-6) / 1e9
+        ratio = "" if fastest is None else f"{kmed / fastest:.3f}"
+        lines.append(f"| {w.name} | {w.algorithmic_bytes()} | {kmed:.2f} | {gbs:.1f} | " + " | ".join(cols) +
+                     f" | {ratio} |")
+    lines.append("")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -310,6 +400,11 @@ def main():
     k.add_argument("--title", required=True)
     k.add_argument("--cmds", required=True)
     k.add_argument("--md", required=True)
+    c = sub.add_parser("calib")
+    c.add_argument("--big", required=True)
+    c.add_argument("--sizes", required=True)
+    c.add_argument("--cmds", required=True)
+    c.add_argument("--md", required=True)
     o = sub.add_parser("occupancy")
     o.add_argument("--occ", required=True)
     o.add_argument("--active", required=True)
@@ -317,7 +412,7 @@ def main():
     o.add_argument("--cmds", required=True)
     o.add_argument("--md", required=True)
     a = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels}[a.mode](a)
+    {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels, "calib": calib}[a.mode](a)
 
 
 if __name__ == "__main__":

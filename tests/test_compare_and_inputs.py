@@ -124,3 +124,27 @@ def test_algorithmic_bytes():
     assert b["rmsnorm_bf16_16384x8192"] == 2 * 16384 * 8192 * 2 + 8192 * 2
     assert b["causal_softmax_bf16"] == 2 * 131072 * 4096 * 2
     assert b["vocab_softmax_f32"] == 2 * 64 * 262144 * 4
+
+
+def test_f32_errors_reading_below_the_normal_range():
+    """The fp32 bar: relative 1e-5 where the reference rounds to a normal
+    fp32, one 2^-149 quantum from the correctly rounded value below 2^-126."""
+    q = 2.0 ** -149
+
+    def bits(v):
+        return np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32)
+
+    ref = np.array([1.0, 2.0 ** -140, 3.25 * q, 0.4 * q, 0.0, 2.0 ** -126])
+    good = bits([1.0 + 5e-6, 2.0 ** -140 + q, 3.0 * q, 0.0, 0.0, 2.0 ** -126 - q])
+    rel, quanta = compare.f32_errors(good, ref)
+    assert rel <= 1e-5 and quanta <= 1.0, (rel, quanta)
+    # a flushed subnormal (2^-140 is 512 quanta) fails
+    assert compare.f32_errors(bits([1.0, 0.0, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] == 512.0
+    # two quanta off fails; a non-zero result where the reference is exactly 0 fails
+    assert compare.f32_errors(bits([1.0, 2.0 ** -140 + 2 * q, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] == 2.0
+    assert compare.f32_errors(bits([1.0, 2.0 ** -140, 3 * q, 0.0, q, 2.0 ** -126]), ref)[0] == float("inf")
+    # the normal range keeps the relative bar
+    assert compare.f32_errors(bits([1.0 + 3e-5, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[0] > 1e-5
+    # NaN where the reference is finite fails either part
+    assert compare.f32_errors(bits([np.nan, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[0] == float("inf")
+    assert not compare.f32_errors(bits([1.0, np.nan, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] <= 1.0

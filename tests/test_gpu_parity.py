@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from gpu_util import (check_output, check_stats, empty_like_dev, oracle_for, tdt, to_dev,
+from gpu_util import (check_output, check_stats, empty_like_dev, oracle_for, row_blocks, tdt, to_dev,
                       to_host_bits)
 import oracle
 import workloads
@@ -84,14 +84,8 @@ def parity_case(op, x_bits, dt, eps=0.0, p0=None, p1=None, x_off=0, y_off=0, wha
 
 
 # ----------------------------------------------------------------------------
-# the five workloads at full size (sampled rows for the two largest)
+# the five workloads at full size, every row
 # ----------------------------------------------------------------------------
-
-def _sample_rows(M, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = rng.choice(M, size=min(n, M), replace=False)
-    return np.unique(np.concatenate([rows, [0, 1, M - 1]]))
-
 
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
 def test_workload_full_size(name):
@@ -106,22 +100,29 @@ def test_workload_full_size(name):
     p1_t = None if p1 is None else to_dev(p1, w.dt)
     say(f"workload {name}: launching")
     y, mean, rstd = run_op(w.op, x_t, w.dt, w.eps, p0_t, p1_t)
-    big = w.M * w.N > 40_000_000
-    rows = _sample_rows(w.M, 4096, 7) if big else np.arange(w.M)
-    ref, rmean, rrstd = oracle_for(w.op, np.ascontiguousarray(x[rows]), w.dt, w.eps, p0, p1)
-    yb = to_host_bits(y, w.dt)[rows]
-    check_output(yb, ref, w.dt, name)
-    if w.op == "layernorm":
-        check_stats(mean.cpu().numpy()[rows], rmean, name + " mean")
-        check_stats(rstd.cpu().numpy()[rows], rrstd, name + " rstd")
-    if name == "causal_softmax_bf16":
-        # row with query q has exactly q+1 non-zero outputs; masked entries are exact 0
-        q = rows % w.extra["queries"]
-        nz = (yb & 0x7FFF) != 0
-        assert np.array_equal(nz.sum(axis=1), q + 1)
+    yb_all = to_host_bits(y, w.dt)
+    mean_h = None if mean is None else mean.cpu().numpy()
+    rstd_h = None if rstd is None else rstd.cpu().numpy()
+    del y, x_t
+    # every row, against the oracle, in blocks of rows
+    Q = w.extra.get("queries", 1) if w.extra else 1
+    for r0, r1 in row_blocks(w.M, w.N, align=Q):
+        say(f"workload {name}: rows {r0}..{r1 - 1}")
+        ref, rmean, rrstd = oracle_for(w.op, np.ascontiguousarray(x[r0:r1]), w.dt, w.eps, p0, p1)
+        yb = yb_all[r0:r1]
+        check_output(yb, ref, w.dt, f"{name} rows {r0}..{r1 - 1}")
+        del ref
+        if w.op == "layernorm":
+            check_stats(mean_h[r0:r1], rmean, name + " mean")
+            check_stats(rstd_h[r0:r1], rrstd, name + " rstd")
+        if name == "causal_softmax_bf16":
+            # row with query q has exactly q+1 non-zero outputs; masked entries are exact 0
+            q = np.arange(r0, r1) % w.extra["queries"]
+            nz = (yb & 0x7FFF) != 0
+            assert np.array_equal(nz.sum(axis=1), q + 1)
     if name == "vocab_softmax_f32":
         # the 8 spikes of a row are bit-identical and carry almost all the mass
-        yv = yb.view(np.float32)
+        yv = yb_all.view(np.float32)
         for r in range(w.M):
             s = yv[r, data["spikes"][r]]
             assert np.all(s == s[0]) and abs(float(s[0]) - 0.125) < 1e-6
@@ -185,9 +186,9 @@ def test_correctness_shapes_from_pages():
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [4096, 65536, 100003])
-def test_split_path_forced(dt, N, monkeypatch):
+def test_split_path_forced(dt, N, ntenv):
     """The split online path on rows that would fit on chip, and odd widths."""
-    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    ntenv.setenv("NT_FORCE_PATH", "split")
     x = rand_bits(N, 7, N, dt, scale=3.0)
     x[2, :] = -np.inf if dt == "f32" else workloads.NEG_INF_BITS[dt]
     x[2, N // 3] = x[3, 0]                       # row 2: one finite entry
@@ -209,7 +210,7 @@ def softmax_with_ws(x_t, dt, ws, y_t=None):
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [65536, 100003, 262144, 2097152])
-def test_cooperative_split_bitwise(dt, N, monkeypatch):
+def test_cooperative_split_bitwise(dt, N, ntenv):
     """The one-kernel cooperative split (x read once), the same kernel with
     every record that has not arrived at the first look recomputed by the
     waiting workgroup (NT_COOP_SPIN=0), and the two-kernel split give
@@ -223,7 +224,7 @@ def test_cooperative_split_bitwise(dt, N, monkeypatch):
     for r in range(M):
         x[r, rng.choice(N, 8, replace=False)] = spike
     x[3, : N // 2] = -np.inf if dt == "f32" else workloads.NEG_INF_BITS[dt]   # masked first half
-    monkeypatch.setenv("NT_FORCE_PATH", "split")
+    ntenv.setenv("NT_FORCE_PATH", "split")
     ref, _, _ = oracle_for("softmax", x, dt)
     for off in (0, 1):
         al = off == 0 and (N * (4 if dt == "f32" else 2)) % 16 == 0
@@ -235,12 +236,12 @@ def test_cooperative_split_bitwise(dt, N, monkeypatch):
         ws = torch.empty(nt.nt_softmax_workspace_bytes(M, N, code), dtype=torch.uint8, device="cuda")
         y_coop = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
         check_output(y_coop, ref, dt, f"coop {dt} N={N} off={off}")
-        monkeypatch.setenv("NT_COOP_SPIN", "0")
+        ntenv.setenv("NT_COOP_SPIN", "0")
         y_rec = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
-        monkeypatch.delenv("NT_COOP_SPIN")
-        monkeypatch.setenv("NT_COOP", "0")
+        ntenv.delenv("NT_COOP_SPIN")
+        ntenv.setenv("NT_COOP", "0")
         y_two = to_host_bits(softmax_with_ws(x_t, dt, ws, empty_like_dev((M, N), dt, off)), dt)
-        monkeypatch.delenv("NT_COOP")
+        ntenv.delenv("NT_COOP")
         assert np.array_equal(y_coop, y_rec), "recomputed records differ from published ones"
         assert np.array_equal(y_coop, y_two), "cooperative and two-kernel split differ"
 
@@ -280,10 +281,10 @@ def test_split_in_place(dt):
 @pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [1000, 4096, 100003])
-def test_looped_path_forced(op, dt, N, monkeypatch):
+def test_looped_path_forced(op, dt, N, ntenv):
     """The looped one-workgroup-per-row norm kernel on rows that would fit on
     chip, and on odd widths, aligned and misaligned."""
-    monkeypatch.setenv("NT_FORCE_PATH", "looped")
+    ntenv.setenv("NT_FORCE_PATH", "looped")
     x = rand_bits(N + 1, 6, N, dt, scale=2.0, loc=3.0)
     p0 = rand_bits(N + 2, 1, N, dt, scale=0.3, loc=1.0)[0]
     p1 = rand_bits(N + 3, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
@@ -294,7 +295,7 @@ def test_looped_path_forced(op, dt, N, monkeypatch):
 @pytest.mark.parametrize("op,dt", [("layernorm", "f32"), ("layernorm", "f16"), ("layernorm", "bf16"),
                                    ("rmsnorm", "f32"), ("rmsnorm", "f16"), ("rmsnorm", "bf16")])
 @pytest.mark.parametrize("N,M,grid", [(4096, 37, 0), (8192, 300, 7), (4096, 5, 2), (8192, 64, 3)])
-def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
+def test_persistent_norms(op, dt, N, M, grid, ntenv):
     """Persistent norm kernel (parameters held across rows, next row prefetched):
     parity with the oracle and bitwise equality with the one-row-per-group
     kernel, including grids much smaller than the row count.  (fp32 RMSNorm
@@ -307,7 +308,7 @@ def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
     p0 = rand_bits(N + 1, 1, N, dt, scale=0.3, loc=1.0)[0]
     p1 = rand_bits(N + 2, 1, N, dt, scale=0.3)[0] if op == "layernorm" else None
     if grid:
-        monkeypatch.setenv("NT_PERSIST_GRID", str(grid))
+        ntenv.setenv("NT_PERSIST_GRID", str(grid))
     x_t, p0_t = to_dev(x, dt), to_dev(p0, dt)
     p1_t = None if p1 is None else to_dev(p1, dt)
     say(f"case persistent {op} {dt} {M}x{N} grid={grid}")
@@ -317,7 +318,7 @@ def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
     if op == "layernorm":
         check_stats(m1.cpu().numpy(), rmean, "persistent mean")
         check_stats(r1.cpu().numpy(), rrstd, "persistent rstd")
-    monkeypatch.setenv("NT_PERSISTENT", "0")
+    ntenv.setenv("NT_PERSISTENT", "0")
     y2, m2, r2 = run_op(op, x_t, dt, 1e-5, p0_t, p1_t)
     assert np.array_equal(to_host_bits(y1, dt), to_host_bits(y2, dt))
     if op == "layernorm":
@@ -325,7 +326,7 @@ def test_persistent_norms(op, dt, N, M, grid, monkeypatch):
 
 
 @pytest.mark.parametrize("fused,M,N", [(False, 16384, 4096), (True, 13107, 5120)])
-def test_persistent_layernorm_bitwise_at_size(fused, M, N, monkeypatch):
+def test_persistent_layernorm_bitwise_at_size(fused, M, N, ntenv):
     """fp32 LayerNorm over many rows: the persistent and one-row kernels
     evaluate the same expression per element, so y, mean and rstd agree
     bitwise on every row (a differently rounded epilogue shows up at this
@@ -341,7 +342,7 @@ def test_persistent_layernorm_bitwise_at_size(fused, M, N, monkeypatch):
     outs = []
     for mode in (None, "0"):
         if mode:
-            monkeypatch.setenv("NT_PERSISTENT", mode)
+            ntenv.setenv("NT_PERSISTENT", mode)
         assert nt.nt_plan_launch(opc, M, N, nt.NT_F32, True)["persistent"] == (0 if mode else 1)
         say(f"case LN f32 bitwise fused={fused} {M}x{N} persistent={'off' if mode else 'on'}")
         y, mean, rstd = torch.empty_like(x), torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
@@ -626,7 +627,7 @@ def test_errors_before_launch():
                                         ("bf16", 9728, (5, 4)), ("bf16", 9736, (6, 4)), ("f16", 11264, (6, 4)),
                                         ("bf16", 11520, (8, 4)), ("bf16", 11784, (7, 4)), ("f16", 14336, (7, 4)),
                                         ("f32", 8200, (12, 4)), ("f32", 12288, (12, 4)), ("f32", 2304, (4, 4))])
-def test_layernorm_between_power_of_two_shapes(dt, N, shape, monkeypatch):
+def test_layernorm_between_power_of_two_shapes(dt, N, shape, ntenv):
     """LayerNorm's shapes of 5-7 waves (16-bit) and 12 waves (fp32): the
     persistent kernel (aligned rows, parameters present; a grid smaller than
     the row count) against the oracle and bitwise against the one-row-per-
@@ -640,18 +641,18 @@ def test_layernorm_between_power_of_two_shapes(dt, N, shape, monkeypatch):
     g = rand_bits(N + 8, 1, N, dt, scale=0.3, loc=1.0)[0]
     b = rand_bits(N + 9, 1, N, dt, scale=0.3)[0]
     x_t, g_t, b_t = to_dev(x, dt), to_dev(g, dt), to_dev(b, dt)
-    monkeypatch.setenv("NT_PERSIST_GRID", "37")
+    ntenv.setenv("NT_PERSIST_GRID", "37")
     say(f"case layernorm {dt} {M}x{N} shape {shape} persistent={p['persistent']}")
     y1, m1, r1 = run_op("layernorm", x_t, dt, 1e-5, g_t, b_t)
     ref, rmean, rrstd = oracle_for("layernorm", x, dt, 1e-5, g, b)
     check_output(to_host_bits(y1, dt), ref, dt, f"layernorm {dt} {shape}")
     check_stats(m1.cpu().numpy(), rmean, "mean")
     check_stats(r1.cpu().numpy(), rrstd, "rstd")
-    monkeypatch.setenv("NT_PERSISTENT", "0")
+    ntenv.setenv("NT_PERSISTENT", "0")
     y2, m2, r2 = run_op("layernorm", x_t, dt, 1e-5, g_t, b_t)
     assert np.array_equal(to_host_bits(y1, dt), to_host_bits(y2, dt))
     assert torch.equal(m1, m2) and torch.equal(r1, r2)
-    monkeypatch.delenv("NT_PERSISTENT")
+    ntenv.delenv("NT_PERSISTENT")
     for off in (1, 3):
         parity_case("layernorm", x, dt, 1e-5, g, b, x_off=off, y_off=off, what=f"misaligned {dt} {shape} off={off}")
     parity_case("layernorm", x, dt, 1e-5, None, None, what=f"no params {dt} {shape}")
@@ -688,3 +689,60 @@ def test_torch_wrappers_check_outputs_devices_and_stream():
     s.synchronize()
     ref = oracle.softmax(to_host_bits(x, "f32").view(np.float32) * np.float32(2.0), "f32")
     check_output(to_host_bits(y, "f32"), ref, "f32", "softmax on the current side stream")
+
+
+def test_explicit_stream_allocations_belong_to_it():
+    """With stream= given, the torch conveniences allocate on that stream:
+    a block they free (the split path's workspace) goes back to that
+    stream's pool, so the current stream's next allocation cannot be handed
+    the same memory while the side stream's kernels may still use it."""
+    s = torch.cuda.Stream()
+    x = torch.zeros(8, 64, device="cuda")
+    nbytes = 3 << 20
+    with nt._alloc_on(s, x):
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pa = a.data_ptr()
+    del a
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")       # current stream
+    assert b.data_ptr() != pa
+    with nt._alloc_on(s.cuda_stream, x):                            # a raw handle works the same
+        c = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pc = c.data_ptr()
+    del c
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert d.data_ptr() != pc
+    torch.cuda.synchronize()
+
+
+def test_explicit_stream_split_paths():
+    """nt.softmax on the split path (64 x 262144 fp32: a workspace) and
+    nt.rms_norm on a wide-row workspace shape, launched on a busy side
+    stream, while the current stream allocates and fills buffers of the
+    workspaces' sizes: the results match the oracle."""
+    s = torch.cuda.Stream()
+    xs = rand_bits(31, 64, 262144, "f32", scale=2.0)
+    xr = rand_bits(32, 16, 1 << 20, "bf16")
+    w = rand_bits(33, 1, 1 << 20, "bf16", scale=0.3, loc=1.0)[0]
+    xs_t, xr_t, w_t = to_dev(xs, "f32"), to_dev(xr, "bf16"), to_dev(w, "bf16")
+    wsb_s = nt.nt_softmax_workspace_bytes(64, 262144, nt.NT_F32)
+    wsb_r = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 16, 1 << 20, nt.NT_BF16)
+    assert wsb_s > 0 and wsb_r > 0
+    big = torch.empty(1 << 28, device="cuda")
+    torch.cuda.synchronize()
+    say("case explicit side stream: softmax split + rms_norm split")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        big.fill_(1.0)                                # the side stream is busy for a while
+    y = nt.softmax(xs_t, stream=s)
+    yr = nt.rms_norm(xr_t, w_t, eps=1e-6, stream=s)
+    junk = []
+    for i in range(8):                                # current stream: reuse whatever is free
+        for n in (wsb_s, wsb_r):
+            t = torch.empty(n, dtype=torch.uint8, device="cuda")
+            t.fill_(0xA5 + i)
+            junk.append(t)
+    s.synchronize()
+    torch.cuda.synchronize()
+    check_output(to_host_bits(y, "f32"), oracle.softmax(xs, "f32"), "f32", "softmax on an explicit stream")
+    check_output(to_host_bits(yr, "bf16"), oracle.rmsnorm(xr, "bf16", 1e-6, weight=w), "bf16",
+                 "rms_norm on an explicit stream")
