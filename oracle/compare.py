@@ -13,11 +13,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   distance in units in the last place.
 * ``max_rel_err`` is the fp32 criterion: max |y - y_ref| / |y_ref| with exact
   zeros required where the reference is exactly zero.
-* ``f32_errors`` splits the fp32 criterion at the bottom of the normal range:
-  where the reference rounded once to fp32 is a normal number, the relative
-  error; below 2^-126, where fp32 has a fixed quantum of 2^-149 and no
-  relative bound is attainable, the distance from the correctly rounded
-  value in units of that quantum.
+* ``f32_errors`` extends the fp32 criterion below the normal range: the
+  relative error everywhere, and below 2^-126, where fp32 has a fixed
+  quantum of 2^-149 and the relative bar becomes finer than the format can
+  resolve, one quantum from the correctly rounded value as well.
 """
 from __future__ import annotations
 
@@ -143,9 +142,13 @@ F32_MIN_NORMAL = 2.0 ** -126
 F32_SUB_QUANTUM = 2.0 ** -149
 
 
-def f32_errors(gpu_bits: np.ndarray, ref: np.ndarray):
+def f32_errors(gpu_bits: np.ndarray, ref: np.ndarray, rel_bar: float = 1e-5):
     """(relative error over the outputs whose reference rounds to a normal
-    fp32, distance in 2^-149 quanta from RNE_f32(reference) over the others).
+    fp32; distance in 2^-149 quanta from RNE_f32(reference) over the outputs
+    below 2^-126 whose relative error exceeds `rel_bar`).  Below 2^-126 fp32
+    has a fixed quantum, so there the relative bar holds where it can (near
+    the top of that range one quantum is far finer than it) and one quantum
+    from the correctly rounded value is granted where it cannot.
 
     Exact zeros are required where the reference is exactly zero (relative
     error inf otherwise); NaN must match NaN (inf otherwise)."""
@@ -156,8 +159,13 @@ def f32_errors(gpu_bits: np.ndarray, ref: np.ndarray):
     rel = max_rel_err(y[~sub], ref[~sub])
     if not np.any(sub):
         return rel, 0.0
-    quanta = float(np.max(np.abs(y[sub] - r32[sub]) / F32_SUB_QUANTUM))
-    return rel, quanta
+    ys, rs, r32s = y[sub], ref[sub], r32[sub]
+    with np.errstate(invalid="ignore"):
+        beyond = ~(np.abs(ys - rs) <= rel_bar * np.abs(rs))       # NaN counts as beyond
+    if not np.any(beyond):
+        return rel, 0.0
+    quanta = float(np.max(np.abs(ys[beyond] - r32s[beyond]) / F32_SUB_QUANTUM))
+    return rel, quanta if np.isfinite(quanta) else float("inf")
 
 
 def _parts(n: int, threads: int):

@@ -51,16 +51,16 @@ def to_host_bits(t, dt: str) -> np.ndarray:
 
 def check_output(gpu_bits: np.ndarray, ref64: np.ndarray, dt: str, what: str = ""):
     """The parity bar: fp32 -> max relative error <= 1e-5 (exact zeros where the
-    oracle is exactly zero), and within 2^-149 of the correctly rounded value
-    where that is below 2^-126; fp16/bf16 -> at most 1 ulp from the oracle
+    oracle is exactly zero), or, below 2^-126, within 2^-149 of the correctly
+    rounded value; fp16/bf16 -> at most 1 ulp from the oracle
     rounded once to the output type (subnormals included: ulps are counted
     on the ordered representable values).  Large arrays are compared on
     blocks in a thread pool (the same numbers)."""
     big = gpu_bits.size > (1 << 22)
     if dt == "f32":
-        # relative 1e-5 where the result is a normal fp32; below 2^-126 (no
-        # relative bound is attainable there) within one subnormal quantum,
-        # 2^-149, of the correctly rounded value
+        # relative 1e-5; below 2^-126, where fp32's fixed quantum (2^-149)
+        # can be coarser than that, one quantum from the correctly rounded
+        # value is granted as well
         err, quanta = (compare.f32_errors_threaded if big else compare.f32_errors)(gpu_bits, ref64)
         assert err <= 1e-5, f"{what}: max rel err {err:.3e} > 1e-5"
         assert quanta <= 1.0, f"{what}: {quanta} subnormal quanta from the correctly rounded value"

@@ -127,24 +127,31 @@ def test_algorithmic_bytes():
 
 
 def test_f32_errors_reading_below_the_normal_range():
-    """The fp32 bar: relative 1e-5 where the reference rounds to a normal
-    fp32, one 2^-149 quantum from the correctly rounded value below 2^-126."""
+    """The fp32 bar: relative 1e-5; below 2^-126 also one 2^-149 quantum
+    from the correctly rounded value (where the relative bar is finer than
+    the format)."""
     q = 2.0 ** -149
 
     def bits(v):
         return np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32)
 
-    ref = np.array([1.0, 2.0 ** -140, 3.25 * q, 0.4 * q, 0.0, 2.0 ** -126])
-    good = bits([1.0 + 5e-6, 2.0 ** -140 + q, 3.0 * q, 0.0, 0.0, 2.0 ** -126 - q])
+    ref = np.array([1.0, 2.0 ** -140, 3.25 * q, 0.4 * q, 0.0, 2.0 ** -126, 2.0 ** -127])
+    near_top = 2.0 ** -127 * (1 + 8e-6)         # relative 8e-6 near the top: 2^22 * 8e-6 = 33 quanta
+    good = bits([1.0 + 5e-6, 2.0 ** -140 + q, 3.0 * q, 0.0, 0.0, 2.0 ** -126 - q, near_top])
     rel, quanta = compare.f32_errors(good, ref)
     assert rel <= 1e-5 and quanta <= 1.0, (rel, quanta)
+    # relative 2e-5 near the top of the subnormal range is beyond both
+    assert compare.f32_errors(bits([1.0, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127 * (1 + 2e-5)]),
+                              ref)[1] > 1.0
     # a flushed subnormal (2^-140 is 512 quanta) fails
-    assert compare.f32_errors(bits([1.0, 0.0, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] == 512.0
-    # two quanta off fails; a non-zero result where the reference is exactly 0 fails
-    assert compare.f32_errors(bits([1.0, 2.0 ** -140 + 2 * q, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] == 2.0
-    assert compare.f32_errors(bits([1.0, 2.0 ** -140, 3 * q, 0.0, q, 2.0 ** -126]), ref)[0] == float("inf")
+    assert compare.f32_errors(bits([1.0, 0.0, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]), ref)[1] == 512.0
+    # two quanta off at 2^-140 (relative 2^-8) fails; non-zero where the reference is exactly 0 fails
+    assert compare.f32_errors(bits([1.0, 2.0 ** -140 + 2 * q, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]),
+                              ref)[1] == 2.0
+    assert compare.f32_errors(bits([1.0, 2.0 ** -140, 3 * q, 0.0, q, 2.0 ** -126, 2.0 ** -127]), ref)[0] == float("inf")
     # the normal range keeps the relative bar
-    assert compare.f32_errors(bits([1.0 + 3e-5, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[0] > 1e-5
+    assert compare.f32_errors(bits([1.0 + 3e-5, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]), ref)[0] > 1e-5
     # NaN where the reference is finite fails either part
-    assert compare.f32_errors(bits([np.nan, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[0] == float("inf")
-    assert not compare.f32_errors(bits([1.0, np.nan, 3 * q, 0.0, 0.0, 2.0 ** -126]), ref)[1] <= 1.0
+    assert compare.f32_errors(bits([np.nan, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]),
+                              ref)[0] == float("inf")
+    assert not compare.f32_errors(bits([1.0, np.nan, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]), ref)[1] <= 1.0
