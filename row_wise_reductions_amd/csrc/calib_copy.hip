@@ -19,12 +19,16 @@
 namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte store of lane t's k-th chunk of the tile at `tile`: device-scope
+// streaming (the row kernels' st16_nt_at, wave-uniform tile base) or plain
+// non-temporal.
 template <int SC1>
-__device__ __forceinline__ void store16(u32x4 *p, u32x4 v) {
+__device__ __forceinline__ void store16(u32x4 *tile, int k, int t, u32x4 v) {
     if constexpr (SC1)
-        ntk::st16_nt(reinterpret_cast<char *>(p), make_uint4(v.x, v.y, v.z, v.w));
+        ntk::st16_nt_at(reinterpret_cast<const char *>(tile), (uint32_t)(k * 256 * 16), (uint32_t)(t * 16),
+                        make_uint4(v.x, v.y, v.z, v.w));
     else
-        __builtin_nontemporal_store(v, p);
+        __builtin_nontemporal_store(v, tile + k * 256 + t);
 }
 
 template <int K, int SC1>
@@ -37,10 +41,11 @@ __global__ void __launch_bounds__(256) ntcal_copy_kernel(const u32x4 *__restrict
         const int64_t i = base + (int64_t)k * 256;
         v[k] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
     }
+    u32x4 *tile = dst + (int64_t)blockIdx.x * 256 * K;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) store16<SC1>(dst + i, v[k]);
+        if (i < n16) store16<SC1>(tile, k, threadIdx.x, v[k]);
     }
 }
 
@@ -64,10 +69,11 @@ template <int K, int SC1>
 __global__ void __launch_bounds__(256) ntcal_fill_kernel(u32x4 *__restrict__ dst, int64_t n16, uint32_t val) {
     const int64_t base = (int64_t)blockIdx.x * 256 * K + threadIdx.x;
     const u32x4 v = {val, val, val, val};
+    u32x4 *tile = dst + (int64_t)blockIdx.x * 256 * K;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t i = base + (int64_t)k * 256;
-        if (i < n16) store16<SC1>(dst + i, v);
+        if (i < n16) store16<SC1>(tile, k, threadIdx.x, v);
     }
 }
 

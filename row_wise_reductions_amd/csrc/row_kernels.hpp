@@ -144,27 +144,29 @@ __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0
 // (non-temporal), bit 4 device scope (the store writes through the XCD's L2).
 constexpr int CPOL_NT_SC1 = (1 << 1) | (1 << 4);
 
-__device__ __forceinline__ void st16_nt(char *p, uint4 v) {
+// Streaming store of one 16-byte chunk to base + soff + voff.  `base` is the
+// same for every lane of the wave (a row's or a chunk's start), `soff` a
+// wave-uniform byte offset and `voff` the lane's own one; soff + voff must
+// stay below 2^32 - 16.  With device-scope streaming stores this is a raw
+// buffer store, which the compiler sees (it keeps the store's hazards and
+// wait counts itself): the buffer resource is built from `base` in scalar
+// registers (readfirstlane, which folds away when the compiler already
+// knows the value is uniform), `soff` goes to the scalar offset and only
+// `voff` is per lane, so the address costs no vector instruction per store.
+// The range check is effectively off (2^32 - 1 bytes).
+__device__ __forceinline__ void st16_nt_at(const char *base, uint32_t soff, uint32_t voff, uint4 v) {
     const u32x4 t = {v.x, v.y, v.z, v.w};
 #if NTK_NT_STORES && NTK_STORE_SC1
-    // A raw buffer store, which the compiler sees (it keeps the store's
-    // hazards and wait counts itself).  The buffer's base is the first
-    // active lane's address less 1 MiB, a wave-uniform value, and each
-    // lane's offset its distance from that base: exact for every lane within
-    // 1 MiB below to 4 GiB - 1 MiB above the first active one (the lanes of a
-    // wave store at most 64 consecutive 16-byte chunks here).  The range
-    // check is effectively off (2^32 - 1 bytes).
-    const uint64_t pa = (uint64_t)(uintptr_t)p;
+    const uint64_t pa = (uint64_t)(uintptr_t)base;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
-    const uint64_t base = ((((uint64_t)hi) << 32) | lo) - (1ull << 20);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, (int)0xFFFFFFFFu, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(t, rs, (int)(uint32_t)(pa - base), 0, CPOL_NT_SC1);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>((((uint64_t)hi) << 32) | lo), 0, (int)0xFFFFFFFFu, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(t, rs, (int)voff, (int)soff, CPOL_NT_SC1);
 #elif NTK_NT_STORES
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(const_cast<char *>(base) + soff + voff));
 #else
-    st16(p, v);
+    st16(const_cast<char *>(base) + soff + voff, v);
 #endif
 }
 
@@ -419,17 +421,20 @@ __device__ __forceinline__ uint4 load_param(const RowGeom<DT, AL> &g, const char
     }
 }
 
-// Store chunk c of a row.  `yvec` tells whether y shares x's 16-byte phase
+// Store chunk c = cbase + k*TPR + t of a row (the k-th slice of lane t,
+// from chunk cbase on).  `yvec` tells whether y shares x's 16-byte phase
 // (then whole chunks are stored as vectors).
-template <int DT, bool AL>
-__device__ __forceinline__ void store_chunk(const RowGeom<DT, AL> &g, char *yr, int64_t c, int32_t N,
-                                            bool yvec, uint4 v) {
+template <int DT, bool AL, int TPR>
+__device__ __forceinline__ void store_chunk(const RowGeom<DT, AL> &g, char *yr, int64_t cbase, int k, int t,
+                                            int32_t N, bool yvec, uint4 v) {
+    const int64_t c = cbase + (int64_t)k * TPR + t;
     if (c < g.nch) {
         if constexpr (AL) {
-            st16_nt(yr + c * 16, v);
+            st16_nt_at(yr + cbase * 16, (uint32_t)(k * TPR * 16), (uint32_t)(t * 16), v);
         } else {
             if (yvec && g.full(c, N))
-                st16_nt(yr - (int64_t)g.head * dt_info<DT>::E + c * 16, v);
+                st16_nt_at(yr - (int64_t)g.head * dt_info<DT>::E + cbase * 16, (uint32_t)(k * TPR * 16),
+                           (uint32_t)(t * 16), v);
             else
                 scatter<DT>(yr, g.col0(c), N, v);
         }
@@ -512,11 +517,10 @@ __device__ __forceinline__ void load_params(uint4 (&out)[K], const RowGeom<DT, A
 template <int DT, bool AL, int TPR>
 __device__ __forceinline__ void store_slice(const RowGeom<DT, AL> &g, char *yr, int k, int t, int32_t N, bool yvec,
                                             uint4 v, int64_t cbase = 0) {
-    const int64_t c = cbase + (int64_t)k * TPR + t;
     if (AL && cbase + ((int64_t)k + 1) * TPR <= g.nch)
-        st16_nt(yr + c * 16, v);
+        st16_nt_at(yr + cbase * 16, (uint32_t)(k * TPR * 16), (uint32_t)(t * 16), v);   // whole slice
     else
-        store_chunk<DT, AL>(g, yr, c, N, yvec, v);
+        store_chunk<DT, AL, TPR>(g, yr, cbase, k, t, N, yvec, v);
 }
 
 // Is element i of chunk c a column of the row?

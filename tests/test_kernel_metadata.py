@@ -66,8 +66,11 @@ def _store_hazards(code_object, need=2):
     """16-byte device-scope streaming stores (`nt sc1`, global or buffer
     form) followed, within `need` wait states in straight-line order, by a
     VALU writing one of their data registers (s_nop N counts N + 1, any other
-    instruction 1).  gfx950 needs 2: with 1 the store writes the new register
-    values.  Returns (stores, hazards)."""
+    instruction 1).  gfx950 needs 2 after a global store of more than 64
+    bits (with 1 the store writes the new register values) and after a
+    buffer store with a constant scalar offset; a buffer store whose scalar
+    offset is an SGPR has no such hazard (the compiler's hazard rules for
+    gfx940-class targets).  Returns (stores, hazards)."""
     asm = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(code_object)], check=True,
                          capture_output=True, text=True).stdout.splitlines()
     ins, fn = [], None
@@ -83,6 +86,11 @@ def _store_hazards(code_object, need=2):
         if op not in STREAM_STORES or "nt sc1" not in args:
             continue
         stores += 1
+        # a buffer store whose scalar offset is an SGPR reads its data at
+        # issue: the data hazard exists only with a constant offset
+        ops = [a.strip() for a in args.split(",")]
+        if op.startswith("buffer") and len(ops) > 3 and ops[3].split()[0].startswith("s"):
+            continue
         data = _vregs(args.split(",")[0 if op.startswith("buffer") else 1].strip())
         ws = 0
         for f2, op2, a2 in ins[j + 1:j + 1 + 2 * need]:
