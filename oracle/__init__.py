@@ -62,9 +62,12 @@ def load(path: str = _LIB_PATH):
     lib.or_softmax_online.argtypes = [i64, i64, i32, i64, vp, dp]
     lib.or_add.argtypes = [i64, i32, vp, vp, dp]
     lib.or_softmax_causal.argtypes = [i64, i64, i32, ctypes.c_float, i64, i64, vp, dp]
+    lib.or_attention.argtypes = [i64, i64, i64, i64, i32, ctypes.c_float, i32, i64, vp, vp, vp, i64, vp, dp]
+    lib.or_attention_online.argtypes = [i64, i64, i64, i64, i32, ctypes.c_float, i32, i64, i64, vp, vp, vp, dp]
     lib.or_num_threads.argtypes = []
     for f in ("or_decode", "or_softmax", "or_layernorm", "or_rmsnorm",
-              "or_softmax_online", "or_add", "or_softmax_causal", "or_num_threads"):
+              "or_softmax_online", "or_add", "or_softmax_causal", "or_attention", "or_attention_online",
+              "or_num_threads"):
         getattr(lib, f).restype = ctypes.c_int
     lib.or_set_num_threads.argtypes = [ctypes.c_int]
     lib.or_set_num_threads.restype = None
@@ -198,6 +201,46 @@ def add_layernorm(x: np.ndarray, r: np.ndarray, dt, eps: float, gamma=None, beta
     (h as stored values, y, mean, rstd), the last three in float64."""
     h = _stored(add(x, r, dt, lib=lib), dt)
     return (h,) + tuple(layernorm(h, dt, eps, gamma=gamma, beta=beta, lib=lib))
+
+
+def _qkv(q, k, v, code):
+    qb, kb, vb = (_as_bits(a, code) for a in (q, k, v))
+    if qb.ndim != 3 or kb.ndim != 3 or vb.ndim != 3:
+        raise ValueError("q, k, v must be [heads, length, head_dim] arrays")
+    BH, Lq, D = qb.shape
+    if kb.shape[0] != BH or kb.shape[2] != D or vb.shape != kb.shape:
+        raise ValueError("k and v must be [heads, Lk, head_dim] like q")
+    return qb, kb, vb, BH, Lq, kb.shape[1], D
+
+
+def attention(q, k, v, dt, scale: float, causal: bool = False, offset: int = 0, rows=None, lib=None):
+    """Attention forward, plain definition: softmax(scale Q K^T) V per head,
+    keys j <= i + offset only when causal.  q [BH, Lq, D], k and v
+    [BH, Lk, D] (stored values).  Returns float64 [BH, Lq, D], or [len(rows),
+    D] for the rows b*Lq + i listed in `rows`."""
+    code = dtype_code(dt)
+    qb, kb, vb, BH, Lq, Lk, D = _qkv(q, k, v, code)
+    if rows is None:
+        o = np.empty((BH, Lq, D), dtype=np.float64)
+        _check((lib or load()).or_attention(BH, Lq, Lk, D, code, float(scale), int(bool(causal)), int(offset),
+                                            _ptr(qb), _ptr(kb), _ptr(vb), BH * Lq, None, _ptr(o)))
+        return o
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.empty((r.size, D), dtype=np.float64)
+    _check((lib or load()).or_attention(BH, Lq, Lk, D, code, float(scale), int(bool(causal)), int(offset),
+                                        _ptr(qb), _ptr(kb), _ptr(vb), r.size, _ptr(r), _ptr(o)))
+    return o
+
+
+def attention_online(q, k, v, dt, scale: float, block: int, causal: bool = False, offset: int = 0, lib=None):
+    """The page's tiled form of the attention forward (blocks of `block`
+    keys, running max and rescaled accumulator).  float64 [BH, Lq, D]."""
+    code = dtype_code(dt)
+    qb, kb, vb, BH, Lq, Lk, D = _qkv(q, k, v, code)
+    o = np.empty((BH, Lq, D), dtype=np.float64)
+    _check((lib or load()).or_attention_online(BH, Lq, Lk, D, code, float(scale), int(bool(causal)), int(offset),
+                                               int(block), _ptr(qb), _ptr(kb), _ptr(vb), _ptr(o)))
+    return o
 
 
 def num_threads() -> int:

@@ -8,8 +8,10 @@ bfloat16, not through the C decoders.
 
 Definitions follow the same passages as ``oracle.c``: the softmax of
 "Portable Triton Kernels" ("Safe Softmax Pattern"), its RMSNorm ("Reference
-Kernel: RMSNorm") and the plain LayerNorm reading (biased variance, eps inside
-the square root).  Use only for rows of at most a few thousand elements.
+Kernel: RMSNorm"), the plain LayerNorm reading (biased variance, eps inside
+the square root) and the attention forward of "Triton: Block-Level GPU
+Programming Without CUDA" ("How Flash Attention Uses Triton").  Use only for
+rows of at most a few thousand elements.
 """
 from __future__ import annotations
 
@@ -49,3 +51,14 @@ def rmsnorm_row(xs, eps, weight=None):
     inv = 1.0 / math.sqrt(ms + eps)
     w = weight if weight is not None else [1.0] * n
     return [v * inv * w[j] for j, v in enumerate(xs)]
+
+
+def attention_row(qrow, K, V, scale, visible):
+    """One query row of softmax(scale Q K^T) V over the first `visible` keys:
+    scores by math.fsum of the products, weights exp(s - max), output sums
+    by math.fsum, divided by the fsum of the weights."""
+    s = [scale * math.fsum(a * b for a, b in zip(qrow, K[j])) for j in range(visible)]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    tot = math.fsum(w)
+    return [math.fsum(w[j] * V[j][c] for j in range(visible)) / tot for c in range(len(V[0]))]

@@ -43,7 +43,10 @@
  *  - online softmax: "Triton: Block-Level GPU Programming Without CUDA",
  *    section "How Flash Attention Uses Triton" (running max m and
  *    denominator l rescaled by alpha = exp(m_prev - m_new) per block; the
- *    Milakov & Gimelshein online normalizer).  Only the (m, l) part is used.
+ *    Milakov & Gimelshein online normalizer), for the rows' (m, l).
+ *  - attention forward (or_attention, or_attention_online): the same
+ *    section's loop over key/value tiles, whose result is
+ *    softmax(scale Q K^T) V with an optional causal mask.
  *
  * Special cases (readings where the pages are silent):
  *  - x_j = -inf gives exp(x_j - m) = 0 exactly (the masked-load identity of
@@ -55,6 +58,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* The oracle's own storage-type codes. */
@@ -341,6 +345,126 @@ int or_softmax_online(int64_t M, int64_t N, int dtype, int64_t block,
             y[base + j] = exp(or_load(dtype, x, base + j) - m_prev) / l_prev;
     }
     return 0;
+}
+
+/*
+ * Attention forward, plain definition.  BH independent heads; q is
+ * [BH, Lq, D], k and v are [BH, Lk, D], row-major, one storage type.  For
+ * head b and query i the visible keys are j < Lk, and when `causal` only
+ * j <= i + offset (offset 0: square causal attention, the diagonal kept;
+ * Lk - Lq aligns the last query with the last key).  With
+ *   s_j = scale * sum_c q[b,i,c] k[b,j,c]      over the visible keys,
+ *   m = max_j s_j,  w_j = exp(s_j - m),
+ *   o[b,i,c] = sum_j w_j v[b,j,c] / sum_j w_j.
+ * "Triton: Block-Level GPU Programming Without CUDA", section "How Flash
+ * Attention Uses Triton", prints the tiled loop that computes this without
+ * materializing the scores (Q K^T tile, running max, rescale of the
+ * accumulator, P V tile); in real arithmetic the loop's result is this
+ * softmax(scale Q K^T) V, which is written out here with every sum
+ * compensated and in index order.  The page's loop applies no scale; scale
+ * (1/sqrt(D) in attention) is an argument and 1 gives the page's scores.
+ * `rows` lists the rows b*Lq + i to compute (NULL: all BH*Lq in order);
+ * o receives nrows rows of D doubles in that order.  A query with no
+ * visible key (only possible when Lk is 0) yields NaN.
+ */
+int or_attention(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, int dtype, float scale, int causal,
+                 int64_t offset, const void *q, const void *k, const void *v, int64_t nrows,
+                 const int64_t *rows, double *o)
+{
+    if (BH < 0 || Lq < 0 || Lk < 1 || D < 1 || offset < 0) return 1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return 2;
+    if (!rows) nrows = BH * Lq;
+    const double sc = (double)scale;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t n = 0; n < nrows; ++n) {
+        const int64_t row = rows ? rows[n] : n;
+        if (row < 0 || row >= BH * Lq) { bad = 1; continue; }
+        const int64_t b = row / Lq, i = row % Lq;
+        int64_t vis = Lk;
+        if (causal && i + offset + 1 < vis) vis = i + offset + 1;
+        double *s = (double *)malloc((size_t)vis * sizeof(double));
+        if (!s) { bad = 1; continue; }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < vis; ++j) {
+            or_acc dot = {0.0, 0.0};
+            for (int64_t c = 0; c < D; ++c)
+                or_acc_add(&dot, or_load(dtype, q, row * D + c) * or_load(dtype, k, (b * Lk + j) * D + c));
+            s[j] = sc * or_acc_sum(&dot);
+            if (s[j] > m) m = s[j];
+        }
+        or_acc l = {0.0, 0.0};
+        for (int64_t j = 0; j < vis; ++j) {
+            s[j] = exp(s[j] - m);
+            or_acc_add(&l, s[j]);
+        }
+        const double ls = or_acc_sum(&l);
+        for (int64_t c = 0; c < D; ++c) {
+            or_acc acc = {0.0, 0.0};
+            for (int64_t j = 0; j < vis; ++j)
+                or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));
+            o[n * D + c] = or_acc_sum(&acc) / ls;
+        }
+        free(s);
+    }
+    return bad ? 3 : 0;
+}
+
+/*
+ * Attention forward in the page's tiled order ("How Flash Attention Uses
+ * Triton"): per query row the visible keys are taken in consecutive blocks
+ * of `block`; per block, the block's scores s_j, then m_new = max(m_prev,
+ * max_j s_j), alpha = exp(m_prev - m_new), p_j = exp(s_j - m_new),
+ * acc = acc * alpha + sum_j p_j v_j, l = l * alpha + sum_j p_j, m_prev =
+ * m_new; finally o = acc / l.  Plain (uncompensated) sums in that order.  In
+ * real arithmetic it equals or_attention; it is kept as the page's own form
+ * of the algorithm and pinned against the plain definition.  Reading, as in
+ * or_softmax_online: alpha = 1 while the running max is still -inf.
+ */
+int or_attention_online(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, int dtype, float scale, int causal,
+                        int64_t offset, int64_t block, const void *q, const void *k, const void *v,
+                        double *o)
+{
+    if (BH < 0 || Lq < 0 || Lk < 1 || D < 1 || offset < 0 || block < 1) return 1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return 2;
+    const double sc = (double)scale;
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t row = 0; row < BH * Lq; ++row) {
+        const int64_t b = row / Lq, i = row % Lq;
+        int64_t vis = Lk;
+        if (causal && i + offset + 1 < vis) vis = i + offset + 1;
+        double *acc = (double *)calloc((size_t)D, sizeof(double));
+        double *s = (double *)malloc((size_t)block * sizeof(double));
+        if (!acc || !s) { free(acc); free(s); bad = 1; continue; }
+        double m_prev = -INFINITY, l_prev = 0.0;
+        for (int64_t j0 = 0; j0 < vis; j0 += block) {
+            const int64_t j1 = j0 + block < vis ? j0 + block : vis;
+            double bmax = -INFINITY;
+            for (int64_t j = j0; j < j1; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < D; ++c)
+                    dot += or_load(dtype, q, row * D + c) * or_load(dtype, k, (b * Lk + j) * D + c);
+                s[j - j0] = sc * dot;
+                if (s[j - j0] > bmax) bmax = s[j - j0];
+            }
+            const double m_new = bmax > m_prev ? bmax : m_prev;
+            const double alpha = (m_prev == -INFINITY) ? 1.0 : exp(m_prev - m_new);
+            double psum = 0.0;
+            for (int64_t c = 0; c < D; ++c) acc[c] *= alpha;
+            for (int64_t j = j0; j < j1; ++j) {
+                const double p = exp(s[j - j0] - m_new);
+                psum += p;
+                for (int64_t c = 0; c < D; ++c) acc[c] += p * or_load(dtype, v, (b * Lk + j) * D + c);
+            }
+            l_prev = l_prev * alpha + psum;
+            m_prev = m_new;
+        }
+        for (int64_t c = 0; c < D; ++c) o[row * D + c] = acc[c] / l_prev;
+        free(acc);
+        free(s);
+    }
+    return bad ? 3 : 0;
 }
 
 /* Sets the number of OpenMP threads later parallel regions use (n >= 1);

@@ -593,4 +593,161 @@ def pin_softmax_causal_brute(lib):
                 assert np.all(y[r, vis:] == 0.0)
 
 
+
+
+# ----------------------------------------------------------------------------
+# attention forward: softmax(scale Q K^T) V ("How Flash Attention Uses Triton")
+# ----------------------------------------------------------------------------
+
+def _qkv(seed, BH, Lq, Lk, D, dt, qk_scale=1.0):
+    q = _rng_rows(seed, BH * Lq, D, dt, qk_scale).reshape(BH, Lq, D)
+    k = _rng_rows(seed + 1, BH * Lk, D, dt, qk_scale).reshape(BH, Lk, D)
+    v = _rng_rows(seed + 2, BH * Lk, D, dt).reshape(BH, Lk, D)
+    return q, k, v
+
+
+def _dec(a, dt):
+    """Stored values -> float64 through numpy (f32, f16) or the bf16 shift."""
+    if dt == "f32":
+        return np.asarray(a, dtype=np.float64)
+    if dt == "f16":
+        return np.asarray(a).view(np.float16).astype(np.float64)
+    return (np.asarray(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_attention_single_visible_key(lib):
+    """One visible key gives that key's value row exactly: causal query 0
+    with offset 0, and every query of a head with one key."""
+    for dt in ("f32", "bf16"):
+        q, k, v = _qkv(11, 2, 6, 9, 16, dt)
+        o = oracle.attention(q, k, v, dt, 0.3, causal=True, offset=0, lib=lib)
+        assert np.array_equal(o[:, 0, :], _dec(v[:, 0, :], dt))
+        q1, k1, v1 = _qkv(12, 3, 4, 1, 8, dt)
+        o1 = oracle.attention(q1, k1, v1, dt, 1.0, lib=lib)
+        assert np.array_equal(o1, np.broadcast_to(_dec(v1, dt), (3, 4, 8)))
+
+
+def pin_attention_equal_scores_give_mean(lib):
+    """q = 0 makes every score 0: the output is the plain mean of the visible
+    value rows (all of them, or rows 0..i + offset when causal)."""
+    BH, Lq, Lk, D = 2, 7, 11, 8
+    _, k, v = _qkv(13, BH, Lq, Lk, D, "f32")
+    q = np.zeros((BH, Lq, D), dtype=np.float32)
+    vd = v.astype(np.float64)
+    o = oracle.attention(q, k, v, "f32", 2.0, lib=lib)
+    assert _rel(o, np.broadcast_to(vd.mean(axis=1, keepdims=True), o.shape)) < 1e-13
+    off = 2
+    oc = oracle.attention(q, k, v, "f32", 2.0, causal=True, offset=off, lib=lib)
+    for i in range(Lq):
+        want = vd[:, :min(Lk, i + off + 1), :].mean(axis=1)
+        assert np.max(np.abs(oc[:, i, :] - want)) <= 1e-14 * np.max(np.abs(vd)), i
+
+
+def pin_attention_two_keys_logistic(lib):
+    """Two keys: o = v0 / (1 + e^-(s0 - s1)) + v1 / (1 + e^(s0 - s1)), the
+    logistic form, with s_j = scale * q . k_j (values exact in fp32; the
+    key count differs from the head dimension, so a transposed K shows)."""
+    q = np.array([[[1.0, 2.0, 0.0, -1.0, 0.5]]], dtype=np.float32)
+    k = np.array([[[0.5, 0.0, 1.0, 0.0, 2.0], [0.0, 1.0, 0.0, 2.0, -1.0]]], dtype=np.float32)
+    v = np.array([[[1.0, -2.0, 3.0, 0.25, 8.0], [-4.0, 0.5, 1.0, 2.0, -1.0]]], dtype=np.float32)
+    scale = 0.75
+    s0 = scale * (0.5 + 1.0)          # q . k0 = 0.5 + 1
+    s1 = scale * (2.0 - 2.0 - 0.5)    # q . k1 = 2 - 2 - 0.5
+    a0 = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+    want = a0 * v[0, 0].astype(np.float64) + (1.0 - a0) * v[0, 1].astype(np.float64)
+    o = oracle.attention(q, k, v, "f32", scale, lib=lib)
+    assert np.max(np.abs(o[0, 0] - want)) < 1e-15 * 8, (o[0, 0], want)
+
+
+def pin_attention_large_scores(lib):
+    """Scores near 700-800 (exp would overflow without the max shift): one
+    key dominates by 100 in the exponent, so o equals its value row to
+    e^-100."""
+    D, Lk = 4, 5
+    q = np.array([[[10.0, 0.0, 0.0, 0.0]]], dtype=np.float32)
+    k = np.zeros((1, Lk, D), dtype=np.float32)
+    k[0, :, 0] = [70.0, 80.0, 60.0, 70.0, 65.0]      # scores 700, 800, 600, ...
+    v = _rng_rows(14, Lk, D, "f32").reshape(1, Lk, D)
+    o = oracle.attention(q, k, v, "f32", 1.0, lib=lib)
+    assert np.all(np.isfinite(o)) and np.max(np.abs(o[0, 0] - v[0, 1])) < 1e-40
+
+
+def pin_attention_value_affine(lib):
+    """The weights of a row sum to one: o(V + c) = o(V) + c and
+    o(a V) = a o(V) (values chosen so V + c and a V are exact in fp32)."""
+    q, k, v = _qkv(15, 2, 6, 10, 8, "f32")
+    v = (np.round(v * 64) / 64).astype(np.float32)
+    o = oracle.attention(q, k, v, "f32", 0.4, causal=True, offset=3, lib=lib)
+    o2 = oracle.attention(q, k, (v + np.float32(3.0)).astype(np.float32), "f32", 0.4, causal=True, offset=3, lib=lib)
+    o3 = oracle.attention(q, k, (v * np.float32(-2.0)).astype(np.float32), "f32", 0.4, causal=True, offset=3, lib=lib)
+    assert np.max(np.abs(o2 - (o + 3.0))) < 1e-14
+    assert np.max(np.abs(o3 - (-2.0 * o))) < 1e-14
+
+
+def pin_attention_key_permutation(lib):
+    """Without a mask, permuting the keys together with their value rows
+    leaves every output unchanged (up to the order of the sums)."""
+    q, k, v = _qkv(16, 2, 5, 13, 8, "f32")
+    perm = np.random.default_rng(17).permutation(13)
+    o = oracle.attention(q, k, v, "f32", 0.5, lib=lib)
+    op = oracle.attention(q, np.ascontiguousarray(k[:, perm]), np.ascontiguousarray(v[:, perm]), "f32", 0.5,
+                          lib=lib)
+    assert np.max(np.abs(o - op)) < 1e-14
+
+
+def pin_attention_torch(lib):
+    """PyTorch float64 CPU (matmul, masked_fill with -inf, softmax, matmul)
+    on the exactly decoded inputs: several shapes, scales, causal offsets and
+    storage types."""
+    import torch
+    for seed, (BH, Lq, Lk, D, causal, off, scale, dt) in enumerate(
+            [(2, 9, 9, 16, True, 0, 0.25, "bf16"), (3, 5, 17, 8, True, 12, 0.35, "f16"),
+             (1, 33, 20, 32, False, 0, 1.0 / math.sqrt(32), "f32"), (2, 16, 40, 64, True, 24, 0.125, "bf16")]):
+        q, k, v = _qkv(100 + seed, BH, Lq, Lk, D, dt)
+        qd, kd, vd = (torch.from_numpy(_dec(a, dt)) for a in (q, k, v))
+        s = float(np.float32(scale)) * (qd @ kd.transpose(1, 2))     # scale arrives as a C float
+        if causal:
+            mask = torch.arange(Lk)[None, :] > (torch.arange(Lq)[:, None] + off)
+            s = s.masked_fill(mask, float("-inf"))
+        want = (torch.softmax(s, dim=-1) @ vd).numpy()
+        o = oracle.attention(q, k, v, dt, scale, causal=causal, offset=off, lib=lib)
+        assert np.max(np.abs(o - want)) <= 1e-13 * np.max(np.abs(_dec(v, dt))), (seed, np.max(np.abs(o - want)))
+
+
+def pin_attention_brute(lib):
+    """The pure-Python definition (math.fsum sums, its own 16-bit decoding)
+    on tiny heads, causal and not."""
+    for dt, (BH, Lq, Lk, D, causal, off) in (("bf16", (2, 4, 6, 5, True, 1)), ("f16", (1, 3, 7, 4, False, 0)),
+                                             ("f32", (2, 5, 5, 3, True, 0))):
+        q, k, v = _qkv(200 + Lk, BH, Lq, Lk, D, dt)
+        o = oracle.attention(q, k, v, dt, 0.6, causal=causal, offset=off, lib=lib)
+        for b in range(BH):
+            K = [_decode_py(k[b, j], dt) for j in range(Lk)]
+            V = [_decode_py(v[b, j], dt) for j in range(Lk)]
+            for i in range(Lq):
+                vis = min(Lk, i + off + 1) if causal else Lk
+                want = brute.attention_row(_decode_py(q[b, i], dt), K, V, float(np.float32(0.6)), vis)
+                assert np.max(np.abs(o[b, i] - np.array(want))) < 1e-14, (dt, b, i)
+
+
+def pin_attention_online_matches_plain(lib):
+    """The page's tiled loop (running max, alpha rescale of the accumulator
+    and the denominator) equals the plain definition for every block size,
+    causal rows included (blocks cut through the diagonal)."""
+    q, k, v = _qkv(18, 2, 11, 23, 8, "bf16")
+    for causal, off in ((False, 0), (True, 0), (True, 7)):
+        o = oracle.attention(q, k, v, "bf16", 0.7, causal=causal, offset=off, lib=lib)
+        for block in (1, 2, 5, 16, 23, 40):
+            ob = oracle.attention_online(q, k, v, "bf16", 0.7, block, causal=causal, offset=off, lib=lib)
+            assert np.max(np.abs(ob - o)) < 1e-13, (causal, off, block)
+
+
+def pin_attention_rows_subset(lib):
+    """Computing a subset of rows gives those rows of the full result."""
+    q, k, v = _qkv(19, 3, 8, 12, 8, "f16")
+    o = oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, lib=lib).reshape(24, 8)
+    rows = [23, 0, 7, 8, 15, 16]
+    assert np.array_equal(oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, rows=rows, lib=lib), o[rows])
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -49,6 +49,26 @@ MUTANTS = {
                                       "for (int64_t k = vis; k < N; ++k) y[base + k] = 1.0 / (double)N;"),
     "add_residual_shifted": ("h[i] = or_load(dtype, x, i) + or_load(dtype, r, i);",
                              "h[i] = or_load(dtype, x, i) + or_load(dtype, r, i > 0 ? i - 1 : i);"),
+    "attn_no_scale": ("s[j] = sc * or_acc_sum(&dot);", "s[j] = or_acc_sum(&dot);"),
+    "attn_k_transposed": ("or_load(dtype, k, (b * Lk + j) * D + c)", "or_load(dtype, k, b * Lk * D + c * Lk + j)"),
+    "attn_mask_drops_diagonal": ("if (causal && i + offset + 1 < vis) vis = i + offset + 1;",
+                                 "if (causal && i + offset < vis) vis = i + offset;"),
+    "attn_mask_one_too_many": ("if (causal && i + offset + 1 < vis) vis = i + offset + 1;",
+                               "if (causal && i + offset + 2 < vis) vis = i + offset + 2;"),
+    "attn_mask_ignores_offset": ("if (causal && i + offset + 1 < vis) vis = i + offset + 1;",
+                                 "if (causal && i + 1 < vis) vis = i + 1;"),
+    "attn_no_max_shift": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "attn_value_first_column": ("or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));",
+                                "or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D));"),
+    "attn_value_of_query_head": ("or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));",
+                                 "or_acc_add(&acc, s[j] * or_load(dtype, v, j * D + c));"),
+    "attn_no_normalization": ("o[n * D + c] = or_acc_sum(&acc) / ls;", "o[n * D + c] = or_acc_sum(&acc);"),
+    "attn_online_no_acc_rescale": ("for (int64_t c = 0; c < D; ++c) acc[c] *= alpha;",
+                                   "for (int64_t c = 0; c < D; ++c) acc[c] *= 1.0;"),
+    "attn_online_no_l_rescale": ("            l_prev = l_prev * alpha + psum;\n            m_prev = m_new;\n        }\n"
+                                 "        for (int64_t c = 0; c < D; ++c) o[row * D + c]",
+                                 "            l_prev = l_prev + psum;\n            m_prev = m_new;\n        }\n"
+                                 "        for (int64_t c = 0; c < D; ++c) o[row * D + c]"),
 }
 
 
