@@ -139,6 +139,24 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
                           void *stream);
 
 /*
+ * nt_softmax_rows without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split path's records go to a device
+ * array inside the library, NT_NOALLOC_SCRATCH_BYTES (1 MiB) per device,
+ * which each device the library runs on holds until the process ends.  The
+ * result is bitwise that of nt_softmax_rows.  Shapes whose workspace
+ * (nt_softmax_workspace_bytes) exceeds the array return NT_ERR_WORKSPACE
+ * before anything is enqueued; rows that fit on chip need none.  The call
+ * allocates and frees nothing; the first call on a device looks the array's
+ * address up once (NT_ERR_HIP if that fails).  Every call on a device
+ * shares its array, so calls that overlap in time on one device (other
+ * streams, other threads) race and must not be made; calls ordered on one
+ * stream are fine.  Other arguments, checks and errors as nt_softmax_rows.
+ */
+#define NT_NOALLOC_SCRATCH_BYTES (1u << 20)
+nt_status nt_softmax_rows_noalloc(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *stream);
+
+/*
  * Causal, scaled softmax of attention-score rows.  Row r holds the scores of
  * query q = r mod `queries` (rows of several heads follow one another) against
  * N keys; key k is visible to it iff k <= q + offset (offset 0: square causal

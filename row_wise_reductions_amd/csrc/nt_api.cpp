@@ -727,6 +727,61 @@ nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt, const void *x, void
     return softmax_launch(M, N, dt, x, y, workspace, workspace_bytes, stream, a);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of nt_softmax_rows_noalloc: the split path's workspace (the per
+// (row, chunk) records) in a file-scope device array, for callers that
+// cannot allocate.  Each device holds its own copy; host code never uses
+// the array's name as an address: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept.  Calls
+// that overlap on one device share it and race; nothing in it has to start
+// at zero (the records carry a per-call tag, and the two-kernel form writes
+// every record before reading any).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[NT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The scratch array's address on the device `stream` belongs to.
+nt_status scratch_for(void *stream, void **out) {
+    int dev = 0;
+    if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev) != hipSuccess) return NT_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return NT_ERR_HIP;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return NT_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return NT_ERR_HIP;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || r != hipSuccess || !p) return NT_ERR_HIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return NT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nt_status nt_softmax_rows_noalloc(int64_t M, int64_t N, nt_dtype dt, const void *x, void *y, void *stream) {
+    nt_status st = common_checks(M, N, dt, x, y);
+    if (st != NT_OK || M == 0) return st;
+    const size_t need = nt_softmax_workspace_bytes(M, N, dt);
+    if (need > (size_t)NT_NOALLOC_SCRATCH_BYTES) return NT_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need) {
+        st = scratch_for(stream, &ws);
+        if (st != NT_OK) return st;
+    }
+    ntk::RowArgs a{};
+    return softmax_launch(M, N, dt, x, y, ws, need ? (size_t)NT_NOALLOC_SCRATCH_BYTES : 0, stream, a);
+}
+
 nt_status nt_softmax_causal_rows(int64_t M, int64_t N, nt_dtype dt, float scale, int64_t queries, int64_t offset,
                                  const void *x, void *y, void *workspace, size_t workspace_bytes, void *stream) {
     if (!valid_dtype(dt)) return NT_ERR_DTYPE;

@@ -21,7 +21,7 @@
 
 extern "C" char **environ;
 
-static std::atomic<long> g_getenv{0}, g_attr{0}, g_getdev{0}, g_capt{0}, g_launch{0};
+static std::atomic<long> g_getenv{0}, g_attr{0}, g_getdev{0}, g_capt{0}, g_launch{0}, g_symbol{0};
 
 extern "C" char *getenv(const char *name) {
     g_getenv.fetch_add(1);
@@ -39,6 +39,15 @@ hipError_t hipGetDevice(int *dev) {
 hipError_t hipDeviceGetAttribute(int *v, hipDeviceAttribute_t attr, int dev) {
     g_attr.fetch_add(1);
     *v = (attr == hipDeviceAttributeMultiprocessorCount && dev == 0) ? 256 : 0;
+    return hipSuccess;
+}
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *dev) {
+    *dev = 0;
+    return hipSuccess;
+}
+hipError_t hipGetSymbolAddress(void **p, const void *) {
+    g_symbol.fetch_add(1);
+    *p = reinterpret_cast<void *>((uintptr_t)1 << 46);      // a device address stand-in, never dereferenced
     return hipSuccess;
 }
 hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus *st) {
@@ -93,6 +102,7 @@ static void every_entry_point(char *base) {
     expect_ok(nt_softmax_rows(1024, 781, NT_F32, x, y, nullptr, 0, nullptr), "softmax single pass");
     expect_ok(nt_softmax_rows(64, 262144, NT_F32, x, y, ws, 1 << 20, nullptr), "softmax split, one pass");
     expect_ok(nt_softmax_rows(64, 262144, NT_F32, x, x, ws, 1 << 20, nullptr), "softmax split, two kernels");
+    expect_ok(nt_softmax_rows_noalloc(64, 262144, NT_F32, x, y, nullptr), "softmax split without a workspace");
     expect_ok(nt_softmax_causal_rows(131072, 4096, NT_BF16, 1.0f, 4096, 0, x, y, nullptr, 0, nullptr), "causal");
     expect_ok(nt_layernorm_rows(4096, 4096, NT_F16, 1e-5f, x, w, b, y, mean, rstd, nullptr), "layernorm persistent");
     expect_ok(nt_layernorm_rows(4096, 4095, NT_F16, 1e-5f, x, w, b, y, mean, rstd, nullptr), "layernorm one row");
@@ -115,7 +125,7 @@ int main() {
     char *base = reinterpret_cast<char *>(((uintptr_t)arena + 255) & ~(uintptr_t)255);
     // the first calls may fill the per-device cache (one attribute query)
     every_entry_point(base);
-    const long attr_first = g_attr.load();
+    const long attr_first = g_attr.load(), symbol_first = g_symbol.load();
     const long getenv0 = g_getenv.load(), attr0 = g_attr.load(), launch0 = g_launch.load();
     for (int i = 0; i < 100; ++i) {
         every_entry_point(base);
@@ -124,11 +134,14 @@ int main() {
     expect_ok(nt_set_override("NT_COOP", nullptr), "override reset");
     const long getenv_calls = g_getenv.load() - getenv0, attr_calls = g_attr.load() - attr0;
     const long launches = g_launch.load() - launch0;
-    std::printf("getenv %ld, device attribute queries %ld (first round %ld), launches %ld, capture queries %ld\n",
-                getenv_calls, attr_calls, attr_first, launches, g_capt.load());
+    std::printf("getenv %ld, device attribute queries %ld (first round %ld), symbol lookups %ld (first round %ld), "
+                "launches %ld, capture queries %ld\n",
+                getenv_calls, attr_calls, attr_first, g_symbol.load() - symbol_first, symbol_first, launches,
+                g_capt.load());
     if (getenv_calls != 0) ++failures;
     if (attr_calls != 0 || attr_first > 1) ++failures;
-    if (launches < 100 * 12) ++failures;
+    if (g_symbol.load() != 1) ++failures;
+    if (launches < 100 * 13) ++failures;
     std::printf("%s, %d failures\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;
 }

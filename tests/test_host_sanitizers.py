@@ -31,8 +31,9 @@ def _run(cmd, **kw):
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 def test_library_host_code_under_sanitizers(tmp_path):
     exe = str(tmp_path / "host_checks")
-    # host compilation only; each -fsanitize= applies to the host side
-    _run([HIPCC, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-g",
+    # each -fsanitize= applies to the host side only (the device side of
+    # nt_api.cpp is the no-alloc entry point's scratch array)
+    _run([HIPCC, "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1", "-g",
           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
           "-Xarch_host", "-fno-sanitize-recover=all", "-Wno-unused-command-line-argument",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
@@ -49,7 +50,7 @@ def test_per_call_path_is_quiet(tmp_path):
     counting stand-ins for getenv and the HIP property queries, and with
     launchers that succeed without launching (tests/percall_checks_main.cpp)."""
     exe = str(tmp_path / "percall_checks")
-    _run([HIPCC, "-x", "hip", "--offload-host-only", "-std=c++17", "-O1", "-Wno-unused-command-line-argument",
+    _run([HIPCC, "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1", "-Wno-unused-command-line-argument",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           os.path.join(CSRC, "nt_api.cpp"), os.path.join(ROOT, "tests", "percall_checks_main.cpp"), "-o", exe],
          timeout=600)
