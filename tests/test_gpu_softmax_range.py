@@ -1,9 +1,9 @@
 """GPU parity of the softmax on rows whose logits spread over 90 to 150:
 outputs run from the normal range down through the subnormals (fp32 and
 bf16 share the exponent range: subnormal below 2^-126, nothing below 2^-149 /
-2^-133) to exact zeros.  fp32 outputs meet the relative 1e-5 bar where they
-are normal and lie within one 2^-149 quantum of the correctly rounded value
-below that; 16-bit outputs within 1 ulp of it (subnormal ulps included).
+2^-133) to exact zeros.  fp32 outputs meet the relative 1e-5 bar, or, below
+2^-126, lie within one 2^-149 quantum of the correctly rounded value;
+16-bit outputs within 1 ulp of it (subnormal ulps included).
 Single pass, cooperative split, two-kernel split and the causal entry.
 """
 from __future__ import annotations
@@ -87,7 +87,8 @@ def test_split_wide_spread(dt, N, spread, form, ntenv):
     if form == "two kernels":
         ntenv.setenv("NT_COOP", "0")
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, DT_CODE[dt], True)
-    assert p["split"] == 1 and p["cooperative"] == (1 if form == "one pass" else 0), p
+    # (an in-place call switches to the two kernels when it is made; the plan cannot know)
+    assert p["split"] == 1 and p["cooperative"] == (0 if form == "two kernels" else 1), p
     say(f"case wide spread split ({form}) {dt} {M}x{N} spread {spread}: {tiny_share(ref, dt):.3f} below normal")
     x_t = to_dev(x, dt)
     y = run_softmax(x_t, dt, y=x_t if form == "in place" else None)
