@@ -62,7 +62,7 @@ def load(path: str = _LIB_PATH):
     lib.or_softmax_online.argtypes = [i64, i64, i32, i64, vp, dp]
     lib.or_add.argtypes = [i64, i32, vp, vp, dp]
     lib.or_softmax_causal.argtypes = [i64, i64, i32, ctypes.c_float, i64, i64, vp, dp]
-    lib.or_attention.argtypes = [i64, i64, i64, i64, i32, ctypes.c_float, i32, i64, vp, vp, vp, i64, vp, dp]
+    lib.or_attention.argtypes = [i64, i64, i64, i64, i32, ctypes.c_float, i32, i64, vp, vp, vp, i64, vp, dp, dp]
     lib.or_attention_online.argtypes = [i64, i64, i64, i64, i32, ctypes.c_float, i32, i64, i64, vp, vp, vp, dp]
     lib.or_num_threads.argtypes = []
     for f in ("or_decode", "or_softmax", "or_layernorm", "or_rmsnorm",
@@ -213,23 +213,25 @@ def _qkv(q, k, v, code):
     return qb, kb, vb, BH, Lq, kb.shape[1], D
 
 
-def attention(q, k, v, dt, scale: float, causal: bool = False, offset: int = 0, rows=None, lib=None):
+def attention(q, k, v, dt, scale: float, causal: bool = False, offset: int = 0, rows=None, lib=None,
+              with_abs: bool = False):
     """Attention forward, plain definition: softmax(scale Q K^T) V per head,
     keys j <= i + offset only when causal.  q [BH, Lq, D], k and v
     [BH, Lk, D] (stored values).  Returns float64 [BH, Lq, D], or [len(rows),
-    D] for the rows b*Lq + i listed in `rows`."""
+    D] for the rows b*Lq + i listed in `rows`; with `with_abs`, also the
+    same-shaped sum_j w_j |v_j| / sum_j w_j (the size of the summed terms)."""
     code = dtype_code(dt)
     qb, kb, vb, BH, Lq, Lk, D = _qkv(q, k, v, code)
     if rows is None:
-        o = np.empty((BH, Lq, D), dtype=np.float64)
-        _check((lib or load()).or_attention(BH, Lq, Lk, D, code, float(scale), int(bool(causal)), int(offset),
-                                            _ptr(qb), _ptr(kb), _ptr(vb), BH * Lq, None, _ptr(o)))
-        return o
-    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-    o = np.empty((r.size, D), dtype=np.float64)
+        r, n, shape = None, BH * Lq, (BH, Lq, D)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n, shape = r.size, (r.size, D)
+    o = np.empty(shape, dtype=np.float64)
+    oa = np.empty(shape, dtype=np.float64) if with_abs else None
     _check((lib or load()).or_attention(BH, Lq, Lk, D, code, float(scale), int(bool(causal)), int(offset),
-                                        _ptr(qb), _ptr(kb), _ptr(vb), r.size, _ptr(r), _ptr(o)))
-    return o
+                                        _ptr(qb), _ptr(kb), _ptr(vb), n, _ptr(r), _ptr(o), _ptr(oa)))
+    return (o, oa) if with_abs else o
 
 
 def attention_online(q, k, v, dt, scale: float, block: int, causal: bool = False, offset: int = 0, lib=None):

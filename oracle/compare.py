@@ -201,3 +201,32 @@ def f32_errors_threaded(gpu_bits: np.ndarray, ref: np.ndarray, threads=None):
     with ThreadPoolExecutor(_threads(threads)) as ex:
         res = list(ex.map(lambda ab: f32_errors(g[ab[0]:ab[1]], r[ab[0]:ab[1]]), _parts(g.size, 4 * _threads(threads))))
     return max(a for a, _ in res), max(b for _, b in res)
+
+
+def ulp_of(ref64: np.ndarray, dt) -> np.ndarray:
+    """Spacing of `dt` at RNE_dt(ref): 2^(e - p + 1) for the rounded value's
+    binade e (at least the subnormal quantum)."""
+    key = _fmt(dt)
+    p, emin, _ = _FORMATS[key]
+    r = np.abs(round_to_value(np.asarray(ref64, dtype=np.float64), key))
+    _, e2 = np.frexp(np.where(r > 0, r, 1.0))
+    e = np.maximum(e2.astype(np.int64) - 1, emin)
+    return np.ldexp(1.0, (e - (p - 1)).astype(np.int32))
+
+
+ATTN_REL = 2.0 ** -12
+
+
+def attention_errors(gpu_bits: np.ndarray, ref64: np.ndarray, abs64: np.ndarray, dt) -> float:
+    """max over outputs of |y - ref| / (ulp_dt(ref) + 2^-12 * A), A the size
+    of the summed terms (the oracle's sum_j w_j |v_j| / sum_j w_j): the
+    attention bar is met when this is <= 1.  NaN anywhere gives inf."""
+    y = bits_to_f64(gpu_bits, dt)
+    ref = np.asarray(ref64, dtype=np.float64)
+    bound = ulp_of(ref, dt) + ATTN_REL * np.asarray(abs64, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        q = np.abs(y - ref) / bound
+    if q.size == 0:
+        return 0.0
+    m = float(np.max(q))
+    return m if np.isfinite(m) and not np.isnan(q).any() else float("inf")

@@ -364,12 +364,14 @@ int or_softmax_online(int64_t M, int64_t N, int dtype, int64_t block,
  * compensated and in index order.  The page's loop applies no scale; scale
  * (1/sqrt(D) in attention) is an argument and 1 gives the page's scores.
  * `rows` lists the rows b*Lq + i to compute (NULL: all BH*Lq in order);
- * o receives nrows rows of D doubles in that order.  A query with no
- * visible key (only possible when Lk is 0) yields NaN.
+ * o receives nrows rows of D doubles in that order.  `oabs` (NULL: not
+ * computed) receives, in the same layout, sum_j w_j |v[b,j,c]| / sum_j w_j:
+ * the size of the terms each output sums, the scale of the error a finite-
+ * precision evaluation of the sums can make.
  */
 int or_attention(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, int dtype, float scale, int causal,
                  int64_t offset, const void *q, const void *k, const void *v, int64_t nrows,
-                 const int64_t *rows, double *o)
+                 const int64_t *rows, double *o, double *oabs)
 {
     if (BH < 0 || Lq < 0 || Lk < 1 || D < 1 || offset < 0) return 1;
     if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return 2;
@@ -400,10 +402,14 @@ int or_attention(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, int dtype, float
         }
         const double ls = or_acc_sum(&l);
         for (int64_t c = 0; c < D; ++c) {
-            or_acc acc = {0.0, 0.0};
-            for (int64_t j = 0; j < vis; ++j)
-                or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));
+            or_acc acc = {0.0, 0.0}, aab = {0.0, 0.0};
+            for (int64_t j = 0; j < vis; ++j) {
+                const double vj = or_load(dtype, v, (b * Lk + j) * D + c);
+                or_acc_add(&acc, s[j] * vj);
+                if (oabs) or_acc_add(&aab, s[j] * fabs(vj));
+            }
             o[n * D + c] = or_acc_sum(&acc) / ls;
+            if (oabs) oabs[n * D + c] = or_acc_sum(&aab) / ls;
         }
         free(s);
     }

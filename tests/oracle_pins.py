@@ -742,12 +742,26 @@ def pin_attention_online_matches_plain(lib):
             assert np.max(np.abs(ob - o)) < 1e-13, (causal, off, block)
 
 
+def pin_attention_abs_scale(lib):
+    """The size of the summed terms, sum_j w_j |v_j| / sum_j w_j, is the
+    output of the same weights on |V|: it equals o(|V|), bounds |o(V)|, and
+    equals o(V) where V is non-negative."""
+    q, k, v = _qkv(21, 2, 9, 14, 8, "f32")
+    o, oa = oracle.attention(q, k, v, "f32", 0.5, causal=True, offset=2, lib=lib, with_abs=True)
+    o_abs = oracle.attention(q, k, np.abs(v), "f32", 0.5, causal=True, offset=2, lib=lib)
+    assert np.max(np.abs(oa - o_abs)) < 1e-15 and np.all(np.abs(o) <= oa * (1 + 1e-15))
+    _, oa2 = oracle.attention(q, k, np.abs(v), "f32", 0.5, causal=True, offset=2, lib=lib, with_abs=True)
+    assert np.max(np.abs(oa2 - o_abs)) < 1e-15
+
+
 def pin_attention_rows_subset(lib):
     """Computing a subset of rows gives those rows of the full result."""
     q, k, v = _qkv(19, 3, 8, 12, 8, "f16")
     o = oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, lib=lib).reshape(24, 8)
     rows = [23, 0, 7, 8, 15, 16]
-    assert np.array_equal(oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, rows=rows, lib=lib), o[rows])
+    o_r, oa_r = oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, rows=rows, lib=lib, with_abs=True)
+    _, oa = oracle.attention(q, k, v, "f16", 0.5, causal=True, offset=4, lib=lib, with_abs=True)
+    assert np.array_equal(o_r, o[rows]) and np.array_equal(oa_r, oa.reshape(24, 8)[rows])
 
 
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

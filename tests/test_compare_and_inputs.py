@@ -155,3 +155,22 @@ def test_f32_errors_reading_below_the_normal_range():
     assert compare.f32_errors(bits([np.nan, 2.0 ** -140, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]),
                               ref)[0] == float("inf")
     assert not compare.f32_errors(bits([1.0, np.nan, 3 * q, 0.0, 0.0, 2.0 ** -126, 2.0 ** -127]), ref)[1] <= 1.0
+
+
+def test_ulp_of_and_attention_bar():
+    """ulp_of: the spacing at the correctly rounded value (binade edges,
+    subnormals); the attention bar |y - ref| <= ulp + 2^-12 * A."""
+    assert list(compare.ulp_of(np.array([1.0, 1.9, 2.0, 0.75, 2.0 ** -130]), "bf16")) == \
+        [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -8, 2.0 ** -133]
+    assert list(compare.ulp_of(np.array([1.0, 1000.0, 2.0 ** -20]), "f16")) == [2.0 ** -10, 2.0 ** -1, 2.0 ** -24]
+    ref = np.array([1.0, 0.001, -0.5])
+    A = np.array([1.0, 0.8, 0.5])
+    bits = compare.round_to(ref, "bf16")
+    assert compare.attention_errors(bits, ref, A, "bf16") <= 0.5
+    # an output that cancels: 0.001 +- 2^-12 * 0.8 is inside, twice that is not
+    near = compare.round_to(np.array([1.0, 0.001 + 1.5e-4, -0.5]), "bf16")
+    far = compare.round_to(np.array([1.0, 0.001 + 5e-4, -0.5]), "bf16")
+    assert compare.attention_errors(near, ref, A, "bf16") <= 1.0 < compare.attention_errors(far, ref, A, "bf16")
+    nan = bits.copy()
+    nan[0] = 0x7FC0
+    assert compare.attention_errors(nan, ref, A, "bf16") == float("inf")

@@ -58,10 +58,11 @@ MUTANTS = {
     "attn_mask_ignores_offset": ("if (causal && i + offset + 1 < vis) vis = i + offset + 1;",
                                  "if (causal && i + 1 < vis) vis = i + 1;"),
     "attn_no_max_shift": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
-    "attn_value_first_column": ("or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));",
-                                "or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D));"),
-    "attn_value_of_query_head": ("or_acc_add(&acc, s[j] * or_load(dtype, v, (b * Lk + j) * D + c));",
-                                 "or_acc_add(&acc, s[j] * or_load(dtype, v, j * D + c));"),
+    "attn_value_first_column": ("const double vj = or_load(dtype, v, (b * Lk + j) * D + c);",
+                                "const double vj = or_load(dtype, v, (b * Lk + j) * D);"),
+    "attn_value_of_query_head": ("const double vj = or_load(dtype, v, (b * Lk + j) * D + c);",
+                                 "const double vj = or_load(dtype, v, j * D + c);"),
+    "attn_abs_drops_weights": ("if (oabs) or_acc_add(&aab, s[j] * fabs(vj));", "if (oabs) or_acc_add(&aab, fabs(vj));"),
     "attn_no_normalization": ("o[n * D + c] = or_acc_sum(&acc) / ls;", "o[n * D + c] = or_acc_sum(&acc);"),
     "attn_online_no_acc_rescale": ("for (int64_t c = 0; c < D; ++c) acc[c] *= alpha;",
                                    "for (int64_t c = 0; c < D; ++c) acc[c] *= 1.0;"),
