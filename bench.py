@@ -46,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak, TFLOP/s
 METRIC = "achieved HBM GB/s (and % of MI355X peak) for softmax/LayerNorm/RMSNorm rows"
 CACHE_BYTES = 256 << 20     # Infinity Cache (MALL) size
 # workload op -> nt_op code of nt_plan_launch
@@ -695,6 +696,48 @@ def wide_norm_traffic(torch, steps):
                       "forms": out}), flush=True)
 
 
+def attention_next_row(torch, np, nt, steps, warmup, warm_ms, stream):
+    """The attention forward at 32 heads x 4096 queries x 4096 keys x 128,
+    bf16, causal (workloads.ATTENTION): event-timed launches on the bench
+    stream; its roofline against the matrix-core peak (algorithmic flops:
+    4 D per visible query-key pair, Q K^T and P V) and its HBM bytes (q, k,
+    v read, o written).  Parity is the GPU tests' (test_gpu_attention.py)."""
+    import workloads
+    w = workloads.ATTENTION
+    BH, Lq, Lk, D, dt = w["BH"], w["Lq"], w["Lk"], w["D"], w["dt"]
+    q, k, v = workloads.attention_inputs(BH, Lq, Lk, D, dt)
+    q_t, k_t, v_t = (to_dev(x.reshape(BH * x.shape[1], D), dt, torch, np) for x in (q, k, v))
+    o = torch.empty_like(q_t)
+    sh = stream.cuda_stream
+
+    def launch():
+        rc = nt.nt_attention_fwd(BH, Lq, Lk, D, nt.NT_BF16, w["scale"], int(w["causal"]), w["offset"], q_t.data_ptr(),
+                                 k_t.data_ptr(), v_t.data_ptr(), o.data_ptr(), sh)
+        if rc != 0:
+            raise RuntimeError(f"attention: {nt.nt_status_string(rc)}")
+    warm_up(launch, warmup, warm_ms, torch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in evs]
+    avg = sum(durs) / len(durs)
+    pairs = workloads.attention_visible_pairs(BH, Lq, Lk, w["causal"], w["offset"])
+    flops = 4 * D * pairs
+    tflops = flops / (avg * 1e-3) / 1e12
+    hbm = 4 * BH * Lq * D * 2
+    return {"workload": w["name"], "op": "attention_fwd", "dtype": dt, "heads": BH, "Lq": Lq, "Lk": Lk, "D": D,
+            "causal": w["causal"], "scale": w["scale"], "visible_pairs": pairs, "flops": flops,
+            "avg_ms": round(avg, 5), "median_ms": round(statistics.median(durs), 5),
+            "p10_ms": round(pct(durs, 10), 5), "p90_ms": round(pct(durs, 90), 5),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": flops},
+            "hbm_bytes": hbm, "GBps": round(hbm / (avg * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -717,6 +760,8 @@ def main():
     ap.add_argument("--wide-norm-traffic", dest="wide_norm_traffic", action="store_true",
                     help="the three forms of a wide-row RMSNorm, for rocprofv3 counters (x read once or twice)")
     ap.add_argument("--sweep-md", default=None, help="with a sweep: also write a markdown summary here")
+    ap.add_argument("--attention", action="store_true",
+                    help="time only the attention forward row (32 x 4096 x 4096 x 128 bf16 causal)")
     ap.add_argument("--copy-at-sizes", action="store_true",
                     help="time the plain streaming copy at each workload's byte count instead")
     args = ap.parse_args()
@@ -747,6 +792,10 @@ def main():
         return
     if args.wide_norm_traffic:
         wide_norm_traffic(torch, args.steps)
+        return
+    if args.attention:
+        print(json.dumps(attention_next_row(torch, np, nt, args.steps, args.warmup, args.warm_ms,
+                                            torch.cuda.current_stream())), flush=True)
         return
     if args.copy_at_sizes:
         names = args.only.split(",") if args.only else [w.name for w in workloads.WORKLOADS]
@@ -867,6 +916,9 @@ def main():
                               "plan": nt.nt_plan_launch(op, w.M, w.N, j.dt_code, True)})
             log(f"[bench] next row {w.name}: {next_rows[-1]['GBps']} GB/s")
             del j, data
+        torch.cuda.empty_cache()
+        next_rows.append(attention_next_row(torch, np, nt, args.steps, args.warmup, args.warm_ms, stream))
+        log(f"[bench] next row {next_rows[-1]['workload']}: {next_rows[-1]['roofline']['achieved']} TFLOP/s")
         torch.cuda.empty_cache()
 
     cpu = None

@@ -304,6 +304,36 @@ nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  */
 nt_status nt_set_override(const char *name, const char *value);
 
+/*
+ * Attention forward with the online softmax ("Triton: Block-Level GPU
+ * Programming Without CUDA", section "How Flash Attention Uses Triton": the
+ * loop over key/value tiles that carries the running max and denominator
+ * and rescales the accumulator, never writing the scores out):
+ *   o[b, i, :] = sum_j w_j v[b, j, :] / sum_j w_j,
+ *   w_j = exp(s_j - max_j s_j),  s_j = scale * sum_c q[b, i, c] k[b, j, c],
+ * over the keys j visible to query i: all Lk keys, or when `causal` is 1
+ * only j <= i + offset (offset 0: square causal attention, the diagonal
+ * kept; Lk - Lq aligns the last query with the last key).
+ *
+ * q is [BH, Lq, D], k and v [BH, Lk, D], o [BH, Lq, D]: dense row-major
+ * arrays of `dt`, NT_F16 or NT_BF16 (else NT_ERR_DTYPE), each 16-byte
+ * aligned (NT_ERR_ALIGN), none NULL (NT_ERR_NULL).  D is 64 or 128; Lk >= 1,
+ * Lq >= 0, BH >= 0, offset >= 0, causal 0 or 1 (else NT_ERR_SHAPE).  scale
+ * must be finite and > 0 (NT_ERR_SCALE); 1/sqrt(D) is the usual choice.
+ * BH == 0 or Lq == 0 is a no-op.  o must not overlap q, k or v
+ * (NT_ERR_ALIAS).  Errors are returned before anything is enqueued; the
+ * work is enqueued on `stream`.
+ *
+ * Numerics: q.k on the matrix cores with fp32 accumulation, the softmax in
+ * fp32, the weights kept to 16 significant bits (each split into two 16-bit
+ * parts) for the weights-times-values product, accumulated in fp32; o is
+ * rounded once to `dt`.  An output is within one unit in the last place of
+ * the exact result plus 2^-12 times the size of the terms it sums
+ * (sum_j w_j |v_j| / sum_j w_j).  Results are bitwise repeatable.
+ */
+nt_status nt_attention_fwd(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, nt_dtype dt, float scale, int causal,
+                           int64_t offset, const void *q, const void *k, const void *v, void *o, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *nt_status_string(nt_status s);
 

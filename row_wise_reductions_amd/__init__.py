@@ -32,7 +32,7 @@ STATUS = {0: "NT_OK", 1: "NT_ERR_NULL", 2: "NT_ERR_SHAPE", 3: "NT_ERR_DTYPE", 4:
 EXPORTED = ("nt_softmax_workspace_bytes", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows",
             "nt_rmsnorm_rows", "nt_norm_workspace_bytes", "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws",
             "nt_add_layernorm_rows", "nt_add_rmsnorm_rows",
-            "nt_status_string", "nt_plan_launch", "nt_set_override", "nt_softmax_rows_noalloc")
+            "nt_status_string", "nt_plan_launch", "nt_set_override", "nt_softmax_rows_noalloc", "nt_attention_fwd")
 NT_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
@@ -71,6 +71,7 @@ def lib():
     L.nt_softmax_workspace_bytes.restype = sz
     L.nt_softmax_rows.argtypes = [i64, i64, i32, vp, vp, vp, sz, vp]
     L.nt_softmax_rows_noalloc.argtypes = [i64, i64, i32, vp, vp, vp]
+    L.nt_attention_fwd.argtypes = [i64, i64, i64, i64, i32, f32, i32, i64, vp, vp, vp, vp, vp]
     L.nt_softmax_causal_rows.argtypes = [i64, i64, i32, f32, i64, i64, vp, vp, vp, sz, vp]
     L.nt_layernorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     L.nt_rmsnorm_rows.argtypes = [i64, i64, i32, f32, vp, vp, vp, vp]
@@ -84,7 +85,7 @@ def lib():
     L.nt_status_string.restype = ctypes.c_char_p
     L.nt_plan_launch.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(nt_plan)]
     L.nt_set_override.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
-    for f in ("nt_set_override", "nt_softmax_rows_noalloc", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
+    for f in ("nt_set_override", "nt_softmax_rows_noalloc", "nt_attention_fwd", "nt_softmax_rows", "nt_softmax_causal_rows", "nt_layernorm_rows", "nt_rmsnorm_rows",
               "nt_layernorm_rows_ws", "nt_rmsnorm_rows_ws", "nt_add_layernorm_rows",
               "nt_add_rmsnorm_rows", "nt_plan_launch"):
         getattr(L, f).restype = i32
@@ -104,6 +105,10 @@ def nt_softmax_rows(M, N, dt, x, y, workspace, workspace_bytes, stream) -> int:
 
 def nt_softmax_rows_noalloc(M, N, dt, x, y, stream) -> int:
     return int(lib().nt_softmax_rows_noalloc(M, N, dt, x, y, stream))
+
+
+def nt_attention_fwd(BH, Lq, Lk, D, dt, scale, causal, offset, q, k, v, o, stream) -> int:
+    return int(lib().nt_attention_fwd(BH, Lq, Lk, D, dt, scale, causal, offset, q, k, v, o, stream))
 
 
 def nt_softmax_causal_rows(M, N, dt, scale, queries, offset, x, y, workspace, workspace_bytes, stream) -> int:

@@ -32,6 +32,7 @@ UNITS = [
     ("kernels_f32.o", "kernels_inst.hip", ["-DNTK_DT=0"]),
     ("kernels_f16.o", "kernels_inst.hip", ["-DNTK_DT=1"]),
     ("kernels_bf16.o", "kernels_inst.hip", ["-DNTK_DT=2"]),
+    ("attention.o", "attention.hip", []),
     ("nt_api.o", "nt_api.cpp", ["-x", "hip"]),
 ]
 

@@ -31,6 +31,7 @@
 #include <random>
 
 #include "../../include/nt.h"
+#include "attention.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -1013,6 +1014,48 @@ nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps, cons
     a.inv_nd = 1.0 / (double)N;
     a.eps = eps;
     return run(NT_OP_RMSNORM, M, N, dt, p, a, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+nt_status nt_attention_fwd(int64_t BH, int64_t Lq, int64_t Lk, int64_t D, nt_dtype dt, float scale, int causal,
+                           int64_t offset, const void *q, const void *k, const void *v, void *o, void *stream) {
+    if (dt != NT_F16 && dt != NT_BF16) return NT_ERR_DTYPE;
+    if (BH < 0 || Lq < 0 || Lk < 1 || (D != 64 && D != 128) || offset < 0 || (causal != 0 && causal != 1))
+        return NT_ERR_SHAPE;
+    // element counts BH*Lq*D and BH*Lk*D, times 2 bytes, must fit int64; the
+    // grid (one 256-thread workgroup per 128 queries of a head) the packet
+    if ((BH > 0 && (Lq > INT64_MAX / 4 / D / BH || Lk > INT64_MAX / 4 / D / BH))) return NT_ERR_SHAPE;
+    const int64_t nqb = (Lq + 127) / 128;
+    if (BH > 0 && nqb > ((int64_t)1 << 31) / 256 / BH) return NT_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return NT_ERR_SCALE;
+    if (BH == 0 || Lq == 0) return NT_OK;
+    if (!q || !k || !v || !o) return NT_ERR_NULL;
+    for (const void *p : {q, k, v, (const void *)o})
+        if (!aligned_to(p, 16)) return NT_ERR_ALIGN;
+    const uint64_t qb = (uint64_t)BH * (uint64_t)Lq * (uint64_t)D * 2, kvb = (uint64_t)BH * (uint64_t)Lk * (uint64_t)D * 2;
+    if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kvb) || overlaps(o, qb, v, kvb)) return NT_ERR_ALIAS;
+    ntk::AttnArgs a{};
+    a.q = static_cast<const char *>(q);
+    a.k = static_cast<const char *>(k);
+    a.v = static_cast<const char *>(v);
+    a.o = static_cast<char *>(o);
+    a.BH = BH;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.offset = offset;
+    a.nqb = nqb;
+    a.s2 = (float)((double)scale * 1.4426950408889634074);
+    a.causal = causal;
+    const hipError_t e = ntk::launch_attention(dt == NT_BF16 ? ntk::DT_BF16 : ntk::DT_F16, (int)D, a,
+                                               reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        if (debug_on()) std::fprintf(stderr, "[nt] attention launch failed: %s\n", hipGetErrorString(e));
+        return NT_ERR_HIP;
+    }
+    return NT_OK;
 }
 
 }  // extern "C"

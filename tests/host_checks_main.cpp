@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "attention.hpp"
 #include "launch.hpp"
 #include "nt.h"
 
@@ -33,6 +34,7 @@ hipError_t launch_split_bf16(int, int, bool, bool, const RowArgs &, hipStream_t)
 hipError_t launch_norm_split_f32(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
 hipError_t launch_norm_split_f16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
 hipError_t launch_norm_split_bf16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_STUB
+hipError_t launch_attention(int, int, const AttnArgs &, hipStream_t) NT_STUB
 #undef NT_STUB
 }  // namespace ntk
 
@@ -98,6 +100,22 @@ int main() {
     expect_error(nt_add_layernorm_rows(4, 8, NT_F32, 1e-5f, P, buf + 100, nullptr, nullptr, buf + 128, buf + 160,
                                        nullptr, nullptr, nullptr),
                  "add_layernorm residual out of x's phase");
+    // attention: every argument error before a launch
+    const int64_t big3 = INT64_MAX / 4;
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_F32, 0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn fp32");
+    expect_error(nt_attention_fwd(2, 8, 8, 96, NT_BF16, 0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn D");
+    expect_error(nt_attention_fwd(2, 8, 0, 64, NT_BF16, 0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn Lk 0");
+    expect_error(nt_attention_fwd(-1, 8, 8, 64, NT_BF16, 0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn BH < 0");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, 0.1f, 1, -1, P, P, P, buf + 128, nullptr), "attn offset");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, 0.1f, 3, 0, P, P, P, buf + 128, nullptr), "attn causal");
+    expect_error(nt_attention_fwd(2, big3, 8, 64, NT_BF16, 0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn size");
+    expect_error(nt_attention_fwd(1 << 20, 1 << 20, 8, 64, NT_BF16, 0.1f, 0, 0, P, P, P, buf + 128, nullptr),
+                 "attn grid");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, -0.1f, 0, 0, P, P, P, buf + 128, nullptr), "attn scale");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, 0.1f, 0, 0, nullptr, P, P, buf + 128, nullptr), "attn q NULL");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, 0.1f, 0, 0, buf + 66, P, P, buf + 128, nullptr),
+                 "attn misaligned");
+    expect_error(nt_attention_fwd(2, 8, 8, 64, NT_BF16, 0.1f, 0, 0, P, P, P, P, nullptr), "attn o over q");
     for (int s = -1; s <= 12; ++s) (void)nt_status_string((nt_status)s);
     // tuning overrides: unknown names and malformed values change nothing
     expect_error(nt_set_override(nullptr, "1"), "override NULL name");

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "attention.hpp"
 #include "launch.hpp"
 #include "nt.h"
 
@@ -77,6 +78,7 @@ hipError_t launch_split_bf16(int, int, bool, bool, const RowArgs &, hipStream_t)
 hipError_t launch_norm_split_f32(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_norm_split_f16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_norm_split_bf16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
+hipError_t launch_attention(int, int, const AttnArgs &, hipStream_t) NT_LAUNCH
 #undef NT_LAUNCH
 }  // namespace ntk
 
@@ -114,6 +116,7 @@ static void every_entry_point(char *base) {
     expect_ok(nt_add_rmsnorm_rows(16384, 8192, NT_BF16, 1e-6f, x, r, w, h, y, nullptr), "add + rmsnorm");
     expect_ok(nt_add_layernorm_rows(4096, 4096, NT_F16, 1e-5f, x, r, w, b, h, y, mean, rstd, nullptr),
               "add + layernorm");
+    expect_ok(nt_attention_fwd(32, 4096, 4096, 128, NT_BF16, 0.088f, 1, 0, x, r, h, y, nullptr), "attention");
     nt_plan p;
     expect_ok(nt_plan_launch(NT_OP_RMSNORM_WS, 16, 1 << 20, NT_BF16, 1, &p), "plan");
     (void)nt_softmax_workspace_bytes(64, 262144, NT_F32);
@@ -141,7 +144,7 @@ int main() {
     if (getenv_calls != 0) ++failures;
     if (attr_calls != 0 || attr_first > 1) ++failures;
     if (g_symbol.load() != 1) ++failures;
-    if (launches < 100 * 13) ++failures;
+    if (launches < 100 * 14) ++failures;
     std::printf("%s, %d failures\n", failures ? "FAILED" : "ok", failures);
     return failures ? 1 : 0;
 }

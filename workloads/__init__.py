@@ -246,3 +246,30 @@ NEXT_WORKLOADS = [
              extra={"queries": 4096, "heads": 32, "offset": 0, "scale": 1.0}),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
+
+
+# Attention forward (the online-softmax loop over key/value tiles of "How
+# Flash Attention Uses Triton"): q, k, v ~ N(0,1) in bf16, [heads, L, D].
+# The pages give no attention workload; this is a causal square shape at the
+# causal-score workload's size (32 heads x 4096 queries x 4096 keys), with
+# head dimension 128 and scale 1/sqrt(128).
+ATTENTION = {"name": "attention_fwd_bf16_32x4096x4096x128_causal", "dt": BF16, "BH": 32, "Lq": 4096,
+             "Lk": 4096, "D": 128, "causal": True, "offset": 0, "scale": float(1.0 / np.sqrt(128.0))}
+
+
+def attention_inputs(BH: int, Lq: int, Lk: int, D: int, dt: str, seed: int = 601, qk_scale: float = 1.0):
+    """q [BH, Lq, D], k and v [BH, Lk, D] of N(0,1) draws (q and k times
+    qk_scale), seeds seed, seed + 1, seed + 2, stored in `dt`."""
+    q = normal_rows(seed, BH * Lq, D, dt, scale=qk_scale).reshape(BH, Lq, D)
+    k = normal_rows(seed + 1, BH * Lk, D, dt, scale=qk_scale).reshape(BH, Lk, D)
+    v = normal_rows(seed + 2, BH * Lk, D, dt).reshape(BH, Lk, D)
+    return q, k, v
+
+
+def attention_visible_pairs(BH: int, Lq: int, Lk: int, causal: bool, offset: int = 0) -> int:
+    """(query, key) pairs the attention forward computes: BH * Lq * Lk, or,
+    causal, BH * sum_i min(Lk, i + offset + 1)."""
+    if not causal:
+        return BH * Lq * Lk
+    i = np.arange(Lq, dtype=np.int64)
+    return BH * int(np.minimum(Lk, i + offset + 1).sum())
