@@ -441,52 +441,71 @@ __device__ __forceinline__ void store_chunk(const RowGeom<DT, AL> &g, char *yr, 
     }
 }
 
+// Elements i of a chunk outside [lo, hi) set to the fill pattern (0 <= lo,
+// hi <= VEC): the out-of-row elements of a misaligned row's first and last
+// chunk.
+template <int DT>
+__device__ __forceinline__ uint4 mask_range(uint4 r, int lo, int hi, uint32_t fill) {
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (dt_info<DT>::E == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < lo || i >= hi) w[i] = fill;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < lo || i >= hi)
+                w[i >> 1] = (i & 1) ? ((w[i >> 1] & 0xFFFFu) | (fill & 0xFFFF0000u))
+                                    : ((w[i >> 1] & 0xFFFF0000u) | (fill & 0xFFFFu));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // First step of a row load: the K chunks a lane owns, every vector load in
 // flight at once.  Each lane issues each of its K loads unconditionally,
-// with the address clamped into the row's whole chunks (a slot past the row
+// with the chunk index clamped into the row's chunks (a slot past the row
 // re-reads a chunk that is already in cache); finish_row() later replaces
-// out-of-row slots with the fill pattern and gathers the partial first and
-// last chunk of a misaligned row element by element.
+// out-of-row slots and elements with the fill pattern.  A misaligned row's
+// partial first and last chunks are loaded whole as well: a 16-byte-aligned
+// chunk that holds an element of the row lies in the memory page holding
+// that element, so the load cannot fault, and its bytes outside the row are
+// masked in registers -- one memory round trip for the whole row.
 template <int DT, bool AL, int K, int TPR, bool NT = true>
 __device__ __forceinline__ void load_row(uint4 (&raw)[K], const RowGeom<DT, AL> &g, int t, int32_t N,
                                          int64_t cbase = 0) {
-    constexpr int VEC = dt_info<DT>::VEC;
-    // whole chunks of the row: [f0, f1] (empty when f1 < f0)
-    const int64_t f0 = AL ? 0 : (g.head ? 1 : 0);
-    const int64_t f1 = AL ? g.nch - 1 : ((int64_t)g.head + N) / VEC - 1;
-    // aligned rows always have a whole chunk (N >= 1): no branch, so the
-    // loaded registers need no copy (a copy would wait for the load)
-    if (AL || f1 >= f0) {
+    (void)N;
+    const int64_t last = g.nch - 1;            // the row touches chunks 0 .. nch - 1 (nch >= 1)
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            int64_t c = cbase + (int64_t)k * TPR + t;
-            c = c < f0 ? f0 : (c > f1 ? f1 : c);
-            raw[k] = NT ? ld16_nt(g.xb + c * 16) : ld16(g.xb + c * 16);
-        }
+    for (int k = 0; k < K; ++k) {
+        int64_t c = cbase + (int64_t)k * TPR + t;
+        c = c > last ? last : c;
+        raw[k] = NT ? ld16_nt(g.xb + c * 16) : ld16(g.xb + c * 16);
     }
 }
 
 // Second step of a row load, after every other load meant to be in flight
-// with the row (the parameter vectors) has been issued: out-of-row slots get
-// the fill pattern, partial chunks of a misaligned row are gathered, and an
-// empty asm statement pins the packed values, so their widening is not
-// moved into these branches and widened values are known to be canonical
-// floats (no quieting before v_max).
+// with the row (the parameter vectors) has been issued: slots past the row
+// get the fill pattern, the elements of a misaligned row's partial chunks
+// that lie outside the row too, and an empty asm statement pins the packed
+// values, so their widening is not moved into these branches and widened
+// values are known to be canonical floats (no quieting before v_max).
 template <int DT, bool AL, int K, int TPR>
 __device__ __forceinline__ void finish_row(uint4 (&raw)[K], const RowGeom<DT, AL> &g, const char *xr, int t,
                                            int32_t N, uint32_t fill, int64_t cbase = 0) {
+    (void)xr;
     constexpr int VEC = dt_info<DT>::VEC;
-    const int64_t f0 = AL ? 0 : (g.head ? 1 : 0);
-    const int64_t f1 = AL ? g.nch - 1 : ((int64_t)g.head + N) / VEC - 1;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t c = cbase + (int64_t)k * TPR + t;
         if (AL && cbase + ((int64_t)k + 1) * TPR <= g.nch) continue;   // whole slice: uniform
-        if (c < f0 || c > f1 || f1 < f0) {
-            if (!AL && c < g.nch) {
-                raw[k] = gather<DT>(xr, g.col0(c), N, fill);
-            } else {
-                raw[k] = make_uint4(fill, fill, fill, fill);
+        if (c >= g.nch) {
+            raw[k] = make_uint4(fill, fill, fill, fill);
+        } else if constexpr (!AL) {
+            const int64_t c0 = g.col0(c);                               // column of the chunk's element 0
+            if (c0 < 0 || c0 + VEC > N) {
+                const int lo = c0 < 0 ? (int)-c0 : 0;
+                const int hi = (int64_t)N - c0 < VEC ? (int)((int64_t)N - c0) : VEC;
+                raw[k] = mask_range<DT>(raw[k], lo, hi, fill);
             }
         }
     }
