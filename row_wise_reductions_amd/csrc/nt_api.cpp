@@ -321,9 +321,24 @@ bool persistent_pays(nt_op op, nt_dtype dt, bool res, Shape sh, int64_t nch) {
 // `res`: the fused residual add + norm, whose lanes also hold the residual's
 // words (at most 32 values per lane for RMSNorm; LayerNorm is capped at 16).
 // LayerNorm is built with at most 12 waves per row.
+// Only shapes with a kernel fit: the single-pass kernels are instantiated for
+// W x K in {1 x 1..16, 2 x 2..8, 4 x 1..8, 8 x 1..16, 16 x 1..2} (K a power of
+// two), plus LayerNorm's 7 x 2 and 5..7 x 4 (16-bit) and 12 x 4 (fp32);
+// LayerNorm has at most 12 waves per row and keeps at most 16 values per
+// lane, or 32 at 5 to 8 waves.
 bool shape_fits(nt_op op, nt_dtype dt, bool res, Shape sh) {
-    if (op == NT_OP_LAYERNORM && sh.W > 12) return false;      // not built
-    return !(res && op == NT_OP_RMSNORM && sh.K * elems_per_chunk(dt) > 32);
+    const int W = sh.W, K = sh.K, V = K * (int)elems_per_chunk(dt);
+    const bool pow2k = K >= 1 && K <= 16 && (K & (K - 1)) == 0;
+    bool built = (W == 1 && pow2k) || (W == 2 && pow2k && K >= 2 && K <= 8) || (W == 4 && pow2k && K <= 8) ||
+                 (W == 8 && pow2k) || (W == 16 && K <= 2 && pow2k);
+    if (op == NT_OP_LAYERNORM) {
+        if (dt != NT_F32) built = built || (W == 7 && K == 2) || (W >= 5 && W <= 7 && K == 4);
+        else built = built || (W == 12 && K == 4);
+        built = built && W <= 12 && (V <= 16 || (W >= 5 && W <= 8 && V == 32));
+    } else {
+        built = built && V <= (res ? 32 : 64);
+    }
+    return built;
 }
 
 // 16-bit softmax rows of exactly 512 chunks (not causal): 8 waves, 1 chunk.

@@ -3,6 +3,7 @@ every function include/nt.h declares, validates arguments before touching
 the device, and plans launches as documented.  The pointers passed here are
 never dereferenced: every call is expected to fail validation first."""
 import os
+import subprocess
 import re
 
 import pytest
@@ -271,6 +272,42 @@ def test_env_overrides(ntenv):
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 16, 4096, F32, True)
     assert p["split"] == 1 and p["row_chunks"] == 1
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16, 4096, F32, True)["split"] == 0
+
+
+def _kernel_symbols():
+    out = subprocess.run(["nm", "-C", nt.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    return set(re.findall(r"ntk::(row_resident|row_norm_persistent)<([^>]*)>", out))
+
+
+def test_forced_shapes_have_kernels(ntenv):
+    """A forced single-pass shape is taken only where its kernel is built (else
+    the plan ignores it): for every W, K up to 16 and each op and type, the
+    kernel the plan would launch is in the library."""
+    syms = _kernel_symbols()
+    assert len(syms) > 100
+    ops = {nt.NT_OP_SOFTMAX: 0, nt.NT_OP_LAYERNORM: 1, nt.NT_OP_RMSNORM: 2}
+    taken = 0
+    for op, kop in ops.items():
+        for dt in (F32, F16, BF16):
+            for W in range(1, 17):
+                for K in range(1, 17):
+                    ntenv.setenv("NT_FORCE_SHAPE", f"{W},{K}")
+                    N = 64 * W * K * (4 if dt == F32 else 8)      # exactly W x K chunks per row
+                    for aligned in (True, False):
+                        p = nt.nt_plan_launch(op, 4096, N - (0 if aligned else 1), dt, aligned)
+                        if p["split"] != 0 or (p["waves_per_row"], p["chunks_per_lane"]) != (W, K):
+                            continue
+                        taken += 1
+                        if p["persistent"]:
+                            name = ("row_norm_persistent", f"{kop}, {dt}, {W}, {K}, false")
+                        else:
+                            pr = "true" if op != nt.NT_OP_SOFTMAX else "false"
+                            name = ("row_resident", f"{kop}, {dt}, {W}, {K}, {str(aligned).lower()}, {pr}, false")
+                        assert name in syms, (op, dt, W, K, aligned, p)
+    assert taken > 50
+    ntenv.setenv("NT_FORCE_SHAPE", "2,4")   # 16-bit LayerNorm at 2 x 4 (32 values per lane) has no kernel
+    p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 4096, F16, True)
+    assert (p["waves_per_row"], p["chunks_per_lane"]) != (2, 4)
 
 
 def test_persistent_rule():
