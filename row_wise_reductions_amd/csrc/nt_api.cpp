@@ -348,6 +348,39 @@ bool full_row_shape(nt_op op, nt_dtype dt, int64_t nch, bool causal, Shape *s) {
     return true;
 }
 
+// Narrow rows (at most 256 chunks), where the menus give one wave per row
+// with 1 to 4 chunks per lane, take more waves per row in two cases
+// (softmax, RMSNorm, LayerNorm; the causal entry plans as the softmax; not
+// the fused add + norm entries, whose menus were swept separately):
+//  - few rows (M <= 1024: one wave per row would leave most of the 1024
+//    SIMDs with at most one wave): 4 waves x 1 chunk, 2-32% faster on rows
+//    of 40-256 chunks at 512 and 1024 rows, every op and type;
+//  - rows that are not 16-byte aligned, 65-256 chunks: 2 waves x 2 chunks up
+//    to 128 chunks, and for 16-bit softmax up to 256; 4 x 1 for fp32 rows
+//    and 16-bit norm rows of 129-256 chunks (16-bit LayerNorm keeps 1 x 2 up
+//    to 128, 1-16% ahead there).  1.04-1.53x over the one-wave shapes at
+//    2048-16384 rows (softmax fp32 781 wide: 1.30x at 16384 rows; bf16 1030
+//    wide: 1.53x).  On aligned rows of many rows the one-wave shapes stay
+//    ahead (0-5%).
+// Kernel-trace sweeps of every covering shape over 512-16384 rows of 40-256
+// chunks (softmax fp32/bf16, RMSNorm and LayerNorm fp32/16-bit) on MI355X.
+bool narrow_row_shape(nt_op op, nt_dtype dt, bool res, bool aligned, int64_t M, int64_t nch, Shape *s) {
+    if (res || nch > 256) return false;
+    if (M <= 1024) {
+        *s = {4, 1};
+        return true;
+    }
+    if (aligned || nch <= 64) return false;
+    const bool wide = dt == NT_F32;
+    if (nch <= 128) {
+        if (op == NT_OP_LAYERNORM && !wide) return false;
+        *s = {2, 2};
+        return true;
+    }
+    *s = (op == NT_OP_SOFTMAX && !wide) ? Shape{2, 2} : Shape{4, 1};
+    return true;
+}
+
 // The split norm's plan for M rows of nch chunks (norms with a workspace, rows
 // too wide for one pass): false for the plain (looped) plan.
 //   One pass (cooperative), at any row count, where the row has at most
@@ -420,6 +453,8 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         if (tune_shape(T_FORCE_SHAPE, &o) && (int64_t)64 * o.W * o.K >= nch && shape_fits(op, dt, res, o)) {
             pick = o;
         } else if (full_row_shape(op, dt, nch, causal, &o)) {
+            pick = o;
+        } else if (narrow_row_shape(op, dt, res, aligned, M, nch, &o) && shape_fits(op, dt, res, o)) {
             pick = o;
         } else {
             for (int i = 0; i < menu.n; ++i) {

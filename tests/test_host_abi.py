@@ -172,8 +172,8 @@ def test_workspace_bytes():
 
 def test_plans_of_the_workloads():
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 1024, 781, F32, True)     # 3124-byte rows: misaligned
-    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["aligned"]) == (0, 1, 4, 0)
-    assert p["rows_per_block"] == 4 and p["grid"] == 256
+    assert (p["split"], p["waves_per_row"], p["chunks_per_lane"], p["aligned"]) == (0, 4, 1, 0)
+    assert p["rows_per_block"] == 1 and p["grid"] == 1024
     p = nt.nt_plan_launch(nt.NT_OP_LAYERNORM, 4096, 4096, F16, True)
     assert (p["split"], p["aligned"]) == (0, 1) and 64 * p["waves_per_row"] * p["chunks_per_lane"] >= 512
     p = nt.nt_plan_launch(nt.NT_OP_RMSNORM, 16384, 8192, BF16, True)
@@ -184,6 +184,45 @@ def test_plans_of_the_workloads():
     assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 64 * 16
     assert (p["waves_per_row"], p["chunks_per_lane"]) == (8, 8)
     assert p["workspace_bytes"] == 64 * 16 * 16 and p["cooperative"] == 1
+
+
+def test_narrow_row_rule():
+    """Rows of at most 256 chunks: 4 waves x 1 chunk at up to 1024 rows;
+    beyond, misaligned rows of 65-256 chunks take 2 x 2 (up to 128 chunks,
+    and 16-bit softmax up to 256) or 4 x 1, and everything else the menu's
+    one-wave shapes.  The causal entry plans as the softmax; the fused add +
+    norm entries keep their menus."""
+    def shape(op, M, N, dt):
+        e = 4 if dt == F32 else 2
+        p = nt.nt_plan_launch(op, M, N, dt, (N * e) % 16 == 0)
+        return p["waves_per_row"], p["chunks_per_lane"]
+    S, L, R = nt.NT_OP_SOFTMAX, nt.NT_OP_LAYERNORM, nt.NT_OP_RMSNORM
+    for op in (S, L, R):
+        for dt in (F32, F16, BF16):
+            for N in (8, 300, 781, 1024, 2048 if dt != F32 else 1000):
+                assert shape(op, 1024, N, dt) == (4, 1), (op, dt, N)
+    # misaligned, 2048 rows and more
+    for M in (2048, 16384):
+        assert shape(S, M, 781, F32) == (4, 1)          # 196 chunks
+        assert shape(S, M, 301, F32) == (2, 2)          # 77 chunks
+        assert shape(S, M, 509, F32) == (2, 2)          # 128 chunks
+        assert shape(S, M, 1030, BF16) == (2, 2)        # 130 chunks
+        assert shape(S, M, 601, BF16) == (2, 2)
+        assert shape(R, M, 781, F32) == (4, 1) and shape(R, M, 301, F32) == (2, 2)
+        assert shape(R, M, 901, BF16) == (2, 2) and shape(R, M, 1500, BF16) == (4, 1)
+        assert shape(L, M, 781, F32) == (4, 1) and shape(L, M, 509, F32) == (2, 2)
+        assert shape(L, M, 901, F16) == (1, 2) and shape(L, M, 1500, F16) == (4, 1)
+        assert shape(S, M, 201, F32) == (1, 1)          # 52 chunks: the menu
+    # aligned rows beyond 1024 rows keep the menu
+    assert shape(S, 4096, 1000, F32) == (1, 4) and shape(S, 4096, 2048, BF16) == (1, 4)
+    assert shape(S, 1025, 520, F32) == (1, 4)
+    # the fused add + norm entries keep their menus
+    p = nt.nt_plan_launch(nt.NT_OP_ADD_RMSNORM, 1024, 781, F32, False)
+    assert (p["waves_per_row"], p["chunks_per_lane"]) == (1, 4)
+    for M, N, dt in ((1024, 781, F32), (4096, 781, F32), (4096, 1030, BF16), (4096, 1000, F32)):
+        a = nt.nt_plan_launch(nt.NT_OP_SOFTMAX_CAUSAL, M, N, dt, (N * (4 if dt == F32 else 2)) % 16 == 0)
+        b = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, dt, (N * (4 if dt == F32 else 2)) % 16 == 0)
+        assert a == b
 
 
 def test_cooperative_split_limits():
