@@ -24,10 +24,13 @@ Prints ONE JSON line.  Flags: --gpus (only 1 is supported), --steps, --warmup
 --warm-ms of wall time, default 200, have passed with the GPU busy),
 --only NAME[,NAME] (time a subset, rotating buffer sets so the 256 MiB
 Infinity Cache cannot serve them), --no-cpu-baseline, --no-next (skip the
-next rows -- fused residual add + norm, the causal softmax entry -- which
-are timed after the suite and reported under next_rows, outside value); --calibrate (the plain
-1 GiB copy: attainable bandwidth, and the counter calibration) and
---copy-at-sizes (the plain copy at each workload's byte count) and --sweep
+next rows -- fused residual add + norm, the causal softmax entry, the
+attention forward -- which are timed after the suite and reported under
+next_rows, outside value); --attention (only the attention forward row);
+--calibrate (the reference streams at 1 GiB: copy, read-only and write-only
+at 1, 2, 4 and 8 chunks per lane: attainable bandwidth, and the counter
+calibration) and --copy-at-sizes (each workload's kernel beside copies of its
+bytes, in one run) and --sweep
 (fp32 softmax and RMSNorm over the pages' benchmark widths, beside torch's
 softmax; --sweep-md FILE writes a summary) and --sweep-ops f32|f16|bf16 (all
 three ops over those widths in one type, each beside torch's kernel) replace
@@ -62,6 +65,12 @@ def to_dev(bits, dt, torch, np):
         return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
     tdt = torch.float16 if dt == "f16" else torch.bfloat16
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).cuda()
+
+
+def rows_aligned(w):
+    """Rows start 16-byte aligned in a fresh tensor when a row is a whole
+    number of 16-byte chunks (the allocator aligns the base)."""
+    return (w.N * w.elem_bytes) % 16 == 0
 
 
 class Job:
@@ -846,7 +855,8 @@ def main():
                     "p10_ms": round(pct(durs, 10), 5), "p90_ms": round(pct(durs, 90), 5),
                     "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "plan": nt.nt_plan_launch(OP_CODES[j.w.op], j.w.M, j.w.N, j.dt_code, True)})
+                    "frac_of_peak_median": round(j.bytes / (statistics.median(durs) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "plan": nt.nt_plan_launch(OP_CODES[j.w.op], j.w.M, j.w.N, j.dt_code, rows_aligned(j.w))})
     dom_i = max(range(len(jobs)), key=lambda i: per[i]["avg_ms"])
     dom_job = jobs[dom_i]
 
@@ -912,8 +922,10 @@ def main():
                               "p10_ms": round(pct(durs, 10), 5), "p90_ms": round(pct(durs, 90), 5),
                               "GBps": round(j.bytes / (avg * 1e-3) / 1e9, 1),
                               "frac_of_peak": round(j.bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "frac_of_peak_median": round(j.bytes / (statistics.median(durs) * 1e-3) / 1e9 /
+                                                           PEAK_HBM_GBS, 4),
                               "traffic": traffic_for(w.name, j.bytes),
-                              "plan": nt.nt_plan_launch(op, w.M, w.N, j.dt_code, True)})
+                              "plan": nt.nt_plan_launch(op, w.M, w.N, j.dt_code, rows_aligned(w))})
             log(f"[bench] next row {w.name}: {next_rows[-1]['GBps']} GB/s")
             del j, data
         torch.cuda.empty_cache()

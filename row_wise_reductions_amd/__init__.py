@@ -412,3 +412,30 @@ def add_rms_norm(x, residual, weight=None, eps=1e-6, h_out=None, out=None, strea
         _check(nt_add_rmsnorm_rows(M, N, dtype_code(x), float(eps), _ptr(x), _ptr(residual), _ptr(weight),
                                    _ptr(h), _ptr(y), _stream(stream, x)), "nt_add_rmsnorm_rows")
     return h, y
+
+
+def attention(q, k, v, scale=None, causal=False, offset=0, out=None, stream=None):
+    """Attention forward, o = softmax(scale * q k^T) v per (batch, head),
+    over the keys each query sees (all, or key <= query + offset when
+    causal).  q: [..., Lq, D], k and v: [..., Lk, D] with the same leading
+    dimensions, contiguous, fp16 or bf16, D = 64 or 128; scale defaults to
+    1/sqrt(D).  Returns o like q."""
+    import math
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() < 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with at least two dimensions")
+    if k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
+        raise ValueError("k and v must be [..., Lk, D] with q's leading dimensions and head size")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    _on_device(q, k, v)
+    Lq, D = q.shape[-2], q.shape[-1]
+    Lk = k.shape[-2]
+    BH = q.numel() // (Lq * D) if Lq * D else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    with _alloc_on(stream, q):
+        o = _out_like(q, out)
+        _check(nt_attention_fwd(BH, Lq, Lk, D, dtype_code(q), float(scale), 1 if causal else 0, int(offset),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream, q)), "nt_attention_fwd")
+    return o

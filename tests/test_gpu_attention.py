@@ -131,3 +131,24 @@ def test_attention_deterministic_and_errors():
     assert call(ptrs=(None, P[1], P[2], P[3])) == 1
     assert call(BH=0) == 0 and call(Lq=0) == 0
     torch.cuda.synchronize()
+
+
+def test_attention_torch_wrapper():
+    """nt.attention on [B, H, L, D] tensors: bitwise the C entry point's
+    result, default scale 1/sqrt(D), causal offset passed through; argument
+    mismatches raise."""
+    B, H, Lq, Lk, D, dt = 2, 3, 70, 90, 64, "f16"
+    q, k, v = workloads.attention_inputs(B * H, Lq, Lk, D, dt, seed=950)
+    q_t, k_t, v_t = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    say("case attention torch wrapper")
+    ref = to_host_bits(run(q_t, k_t, v_t, dt, 1.0 / math.sqrt(D), True, 20), dt)
+    o = nt.attention(q_t.view(B, H, Lq, D), k_t.view(B, H, Lk, D), v_t.view(B, H, Lk, D), causal=True, offset=20)
+    torch.cuda.synchronize()
+    assert o.shape == (B, H, Lq, D)
+    assert np.array_equal(to_host_bits(o.reshape(B * H, Lq, D), dt), ref)
+    with pytest.raises(ValueError):
+        nt.attention(q_t, k_t[:, :, :32].contiguous(), v_t)
+    with pytest.raises(ValueError):
+        nt.attention(q_t, k_t, v_t.float())
+    with pytest.raises(ValueError):
+        nt.attention(q_t.cpu(), k_t.cpu(), v_t.cpu())

@@ -1,9 +1,10 @@
 """Structural checks of the built gfx950 code object (CPU only): the device
 code embedded in libnt.so is unbundled and its kernel metadata read with the
 ROCm LLVM tools.  Every kernel must run in wave64 without scratch (no
-register spills), the library must contain no matrix-core (MFMA)
-instructions (this path is no contraction), and every launch shape the
-planner can choose must have an instantiated kernel."""
+register spills), the row-reduction kernels must contain no matrix-core
+(MFMA) instructions (they are no contraction) while the attention kernels
+must (Q K^T and P V are), and every launch shape the planner can choose must
+have an instantiated kernel."""
 import os
 import re
 import shutil
@@ -42,13 +43,19 @@ def test_no_spills_wave64(kernels):
 
 
 def test_no_mfma(code_objects):
+    seen_rows = seen_attention = False
     for co in code_objects:
         asm = subprocess.run([f"{LLVM}/llvm-objdump", "-d", str(co)], check=True,
                              capture_output=True, text=True).stdout
+        if "attention_fwd" in asm:
+            seen_attention = True
+            assert re.search(r"\bv_mfma_f32_32x32x16_bf16", asm) and re.search(r"\bv_mfma_f32_32x32x16_f16", asm)
         if "row_resident" not in asm:
             continue
+        seen_rows = True
         assert "global_load_dwordx4" in asm
         assert not re.search(r"\bv_mfma", asm), "MFMA instruction in a row-reduction kernel"
+    assert seen_rows and seen_attention
 
 
 def _vregs(spec):
