@@ -47,7 +47,7 @@ import os
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-CALIB_KERNEL = "ntcal_copy_kernel"
+CALIB_KERNEL = "ntcal_copy_kernel<1, 0>"   # the plain copy: one chunk per lane, non-temporal stores
 CALIB_BYTES = 1 << 30
 
 
@@ -126,6 +126,15 @@ def stats(args):
             gbs = f"{w.algorithmic_bytes() / (tot * 1e-6) / 1e9:.1f}" if i == len(found) - 1 else ""
             lines.append(f"| {w.name if i == 0 else ''} | `{k}` | {calls} | {avg:.2f} | "
                          f"{w.algorithmic_bytes() if i == 0 else ''} | {gbs} |")
+    a = workloads.ATTENTION
+    hit = [r for r in rows if "attention_fwd<2, 128>" in r["Name"]]
+    if hit:
+        flops = 4 * a["D"] * workloads.attention_visible_pairs(a["BH"], a["Lq"], a["Lk"], a["causal"], a["offset"])
+        avg = float(hit[0]["AverageNs"]) / 1000.0
+        lines += ["", "| attention forward | kernel | calls | avg duration (us) | flops / call (4 D per visible "
+                  "(query, key) pair) | TFLOP/s | % of 2.5 PFLOP/s (dense bf16) |", "|---|---|---|---|---|---|---|",
+                  f"| {a['name']} | `ntk::attention_fwd<2, 128>` | {int(hit[0]['Calls'])} | {avg:.2f} | {flops} | "
+                  f"{flops / (avg * 1e-6) / 1e12:.1f} | {flops / (avg * 1e-6) / 1e12 / 25:.1f}% |"]
     lines += ["", "Other kernels in the trace (input uploads and the like) are omitted.", ""]
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
