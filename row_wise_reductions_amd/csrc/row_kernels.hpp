@@ -478,7 +478,10 @@ __device__ __forceinline__ void load_row(uint4 (&raw)[K], const RowGeom<DT, AL> 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         int64_t c = cbase + (int64_t)k * TPR + t;
-        c = c > last ? last : c;
+        // (c >= 0 always; finish_row() repeats this exact test, which lets the
+        // compiler keep one predicate per slot instead of the 64-bit indices:
+        // the 8 x 8 fp32 cooperative softmax holds 56 instead of 66 VGPRs)
+        c = c < 0 ? 0 : (c > last ? last : c);
         raw[k] = NT ? ld16_nt(g.xb + c * 16) : ld16(g.xb + c * 16);
     }
 }
@@ -494,11 +497,12 @@ __device__ __forceinline__ void finish_row(uint4 (&raw)[K], const RowGeom<DT, AL
                                            int32_t N, uint32_t fill, int64_t cbase = 0) {
     (void)xr;
     constexpr int VEC = dt_info<DT>::VEC;
+    const int64_t last = g.nch - 1;        // the tests of load_row's clamp
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t c = cbase + (int64_t)k * TPR + t;
         if (AL && cbase + ((int64_t)k + 1) * TPR <= g.nch) continue;   // whole slice: uniform
-        if (c >= g.nch) {
+        if (c < 0 || c > last) {
             raw[k] = make_uint4(fill, fill, fill, fill);
         } else if constexpr (!AL) {
             const int64_t c0 = g.col0(c);                               // column of the chunk's element 0
