@@ -207,16 +207,37 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) at
         // tile: a clamped, unused reload)
         load_tile<D, KCH, VCH>(kr, vr, kb0, vb0, t + 1 < ntiles ? j0 + BN : j0, a.Lk, tid);
 
-        // ---- per 32-key block of the tile: S^T = K Q^T, mask, online
-        // softmax update, P^T (two 16-bit parts), O^T += V^T P^T
+        // ---- S^T = K Q^T for both 32-key blocks of the tile first, so the
+        // matrix cores work on the second block's scores while the vector
+        // ALUs run the first block's softmax
+        f32x16 sb[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            for (int r = 0; r < 16; ++r) sb[kb][r] = 0.f;
             const char *krow = ks + (kb * 32 + ql) * KSTR + 8 * h * 2;
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) s = Mma<DT>::mma(ld8<E8>(krow + 32 * st), qf[st], s);
+            for (int st = 0; st < D / 16; ++st) sb[kb] = Mma<DT>::mma(ld8<E8>(krow + 32 * st), qf[st], sb[kb]);
+        }
+
+        // ---- per 32-key block: mask, online softmax update, P^T (two
+        // 16-bit parts), O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = sb[kb];
+            // this block's V^T operands, read from LDS ahead of the softmax so
+            // their latency is hidden behind it: the keys lane l holds for
+            // MFMA step ss are kk + 4h + 0..3 and kk + 8 + 4h + 0..3
+            E8 va[2][D / 32];
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) {
+                const int kk = kb * 32 + 16 * ss;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const char *vrow = vs + (db * 32 + ql) * VSTR;
+                    va[ss][db] = ld4x2<E8>(vrow + (kk + 4 * h) * 2, vrow + (kk + 8 + 4 * h) * 2);
+                }
+            }
 
             // mask: blocks past Lk, or reaching past the wave's first query's diagonal
             const int64_t jb = j0 + kb * 32;
@@ -260,14 +281,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) at
                 }
                 E8 phi, plo;
                 split16<DT>(p, phi, plo);
-                // the step's keys held by this lane: kk + 4h + 0..3 and kk + 8 + 4h + 0..3
-                const int kk = kb * 32 + 16 * ss;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const char *vrow = vs + (db * 32 + ql) * VSTR;
-                    const E8 va = ld4x2<E8>(vrow + (kk + 4 * h) * 2, vrow + (kk + 8 + 4 * h) * 2);
-                    acc[db] = Mma<DT>::mma(va, phi, acc[db]);
-                    acc[db] = Mma<DT>::mma(va, plo, acc[db]);
+                    acc[db] = Mma<DT>::mma(va[ss][db], phi, acc[db]);
+                    acc[db] = Mma<DT>::mma(va[ss][db], plo, acc[db]);
                 }
             }
         }
