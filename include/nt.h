@@ -294,7 +294,9 @@ nt_status nt_add_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  *   NT_FORCE_SHAPE     "W,K": single-pass shape, ignored where it does not
  *                      fit the row or is not built
  *   NT_SPLIT_SHAPE     "W,K": chunk shape of the split softmax
- *   NT_COOP            "0": the two-kernel split forms throughout
+ *   NT_COOP            "0": the two-kernel split forms throughout;
+ *                      "rows1" / "rows2": the cooperative softmax with one /
+ *                      two rows per workgroup where it is used
  *   NT_COOP_SPIN       polls (0..65536, default 1024) of a cooperative
  *                      kernel before it recomputes a missing record
  *   NT_PERSISTENT      "0" never, "1" where it pays (default), "always"
@@ -369,9 +371,10 @@ typedef struct {
                                  and `grid` below is then an upper bound                  */
     int32_t cooperative;      /* split path: 1 when one kernel does both phases (x read once;
                                  the workgroups of a row exchange their partial results
-                                 through the workspace); 0: two kernels, x read twice.
-                                 In-place calls (y == x) and calls during stream capture
-                                 always use the two kernels                             */
+                                 through the workspace), 2 when it does so for two rows
+                                 per workgroup (softmax; rows_per_block 2); 0: two
+                                 kernels, x read twice.  In-place calls (y == x) and calls
+                                 during stream capture always use the two kernels        */
     int64_t grid;             /* workgroups per launch                                  */
     int64_t row_chunks;       /* split paths: chunks per row (0 otherwise)              */
     int64_t workspace_bytes;  /* split paths: workspace size (0 otherwise)              */

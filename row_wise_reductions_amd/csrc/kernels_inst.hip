@@ -165,9 +165,12 @@ hipError_t looped(int W, int K, bool al, const RowArgs &a, int64_t grid, hipStre
     return hipErrorInvalidValue;
 }
 
+// coop: 0 the two kernels, 1 the cooperative kernel, 2 the cooperative
+// kernel with two rows per workgroup
 template <int W, int K, bool AL, bool CAUSAL>
-hipError_t split_al(bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t split_al(int coop, const RowArgs &a, hipStream_t s) {
     const int64_t grid = a.M * a.P;
+    if (coop == 2) return launch_k(softmax_coop2<DT, W, K, AL, CAUSAL>, (a.M + 1) / 2 * a.P, 64 * W, s, a);
     if (coop) return launch_k(softmax_coop<DT, W, K, AL, CAUSAL>, grid, 64 * W, s, a);
     const hipError_t e = launch_k(softmax_split_partial<DT, W, K, AL, CAUSAL>, grid, 64 * W, s, a);
     if (e != hipSuccess) return e;
@@ -182,7 +185,7 @@ constexpr bool causal_split_built() {
 }
 
 template <int W, int K>
-hipError_t split_go(bool al, bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t split_go(bool al, int coop, const RowArgs &a, hipStream_t s) {
     if (a.queries > 0) {
         if constexpr (causal_split_built<W, K>())
             return al ? split_al<W, K, true, true>(coop, a, s) : split_al<W, K, false, true>(coop, a, s);
@@ -191,7 +194,7 @@ hipError_t split_go(bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return al ? split_al<W, K, true, false>(coop, a, s) : split_al<W, K, false, false>(coop, a, s);
 }
 
-hipError_t split(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t split(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s) {
 #define NTK_CASE(w, k) \
     if (W == w && K == k) return split_go<w, k>(al, coop, a, s);
     NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8) NTK_CASE(8, 1) NTK_CASE(8, 2) NTK_CASE(8, 4)
@@ -266,7 +269,7 @@ hipError_t resident_any(int op, int W, int K, bool al, const RowArgs &a, int64_t
 hipError_t launch_resident_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t launch_split_f32(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s) {
     return split(W, K, al, coop, a, s);
 }
 hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
@@ -283,7 +286,7 @@ hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const
 hipError_t launch_resident_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t launch_split_f16(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s) {
     return split(W, K, al, coop, a, s);
 }
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
@@ -300,7 +303,7 @@ hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const
 hipError_t launch_resident_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return resident_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
+hipError_t launch_split_bf16(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s) {
     return split(W, K, al, coop, a, s);
 }
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {

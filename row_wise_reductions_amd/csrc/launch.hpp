@@ -32,12 +32,13 @@ hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStre
 hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
                                   int64_t grid_override);
 
-// Launch the split softmax: with `coop`, the one cooperative kernel
-// (a.P <= COOP_PMAX, x not aliasing y, a.tag unique to the call); otherwise
-// the two kernels (partials, then merge + write).
-hipError_t launch_split_f32(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
-hipError_t launch_split_f16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
-hipError_t launch_split_bf16(int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s);
+// Launch the split softmax: with `coop` 1, the one cooperative kernel
+// (a.P <= COOP_PMAX, x not aliasing y, a.tag unique to the call); with 2,
+// the cooperative kernel with two rows per workgroup; with 0, the two
+// kernels (partials, then merge + write).
+hipError_t launch_split_f32(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_f16(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s);
+hipError_t launch_split_bf16(int W, int K, bool al, int coop, const RowArgs &a, hipStream_t s);
 
 // Launch the split norm (rows too wide for one pass, cut into a.P chunks of
 // 64*W*K 16-byte pieces, one workgroup per (row, chunk)): with `coop` the

@@ -149,7 +149,8 @@ enum TuneKey {
     T_FORCE_PATH,       // NT_FORCE_PATH: 0 none, 1 "split" (softmax), 2 "looped" (norms)
     T_FORCE_SHAPE,      // NT_FORCE_SHAPE "W,K": single-pass shape (ignored if it does not fit the row)
     T_SPLIT_SHAPE,      // NT_SPLIT_SHAPE "W,K": split softmax chunk shape
-    T_COOP,             // NT_COOP: "0" selects the two-kernel split forms
+    T_COOP,             // NT_COOP: "0" two-kernel split forms; "rows1" / "rows2": the cooperative
+                        // softmax with one / two rows per workgroup; else the planner's choice
     T_COOP_SPIN,        // NT_COOP_SPIN: polls before a missing record is recomputed (0..65536)
     T_PERSISTENT,       // NT_PERSISTENT: "0" never, "always" wherever built, "1" where it pays
     T_PERSIST_GRID,     // NT_PERSIST_GRID: workgroups of the persistent norm kernel (> 0)
@@ -187,6 +188,11 @@ bool parse_tune(int key, const char *s, int64_t *out) {
         return true;
     }
     case T_COOP:
+        if (std::strcmp(s, "0") == 0) *out = 0;
+        else if (std::strcmp(s, "rows1") == 0) *out = 2;
+        else if (std::strcmp(s, "rows2") == 0) *out = 3;
+        else *out = 1;
+        return true;
     case T_DEBUG:
         *out = std::strcmp(s, "0") == 0 ? 0 : 1;
         return true;
@@ -234,6 +240,20 @@ bool debug_on() { return tune(T_DEBUG) != 0; }
 
 // Cooperative split forms (one pass over x) unless NT_COOP=0.
 bool coop_enabled() { return tune(T_COOP) != 0; }
+
+// Rows per workgroup of the cooperative softmax for M rows of P chunks
+// (NT_COOP=rows1 / rows2 force one or the other).  Two rows (softmax_coop2:
+// one row's writes overlap the next row's reads) for fp32 rows from 1024
+// (row, chunk) pairs on: 1.10x on 64 x 262144, 1.08x on 256 x 65536,
+// 1.01-1.04x at 2048-4096 pairs; below 1024 pairs half the workgroups leave
+// CUs idle (0.78-0.88x at 256-512 pairs), and the 16-bit form, at 142
+// instead of 108 VGPRs, was slower at every size tried (0.83-0.94x).
+int coop_rows(int64_t M, int64_t P, nt_dtype dt) {
+    const int64_t v = tune(T_COOP);
+    if (M < 2 || v == 2) return 1;
+    if (v == 3) return 2;
+    return dt == NT_F32 && M * P >= 1024 ? 2 : 1;
+}
 
 // Polls of the cooperative kernels before they recompute a missing chunk's
 // record themselves (0 recomputes every record not there at the first look,
@@ -543,6 +563,11 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     // record; the two-kernel form uses the first 8 bytes as its (m_j, l_j)
     p->workspace_bytes = M * P * 16;
     p->cooperative = (P <= ntk::COOP_PMAX && coop_enabled()) ? 1 : 0;
+    if (p->cooperative && coop_rows(M, P, dt) == 2) {
+        p->cooperative = 2;
+        p->rows_per_block = 2;
+        p->grid = (M + 1) / 2 * P;
+    }
     return NT_OK;
 }
 
@@ -583,7 +608,8 @@ hipError_t launch_looped(nt_dtype dt, int op, const nt_plan &p, const ntk::RowAr
 }
 
 hipError_t launch_split(nt_dtype dt, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
-    const bool al = p.aligned != 0, coop = p.cooperative != 0;
+    const bool al = p.aligned != 0;
+    const int coop = p.cooperative;
     switch (dt) {
     case NT_F32: return ntk::launch_split_f32(p.waves_per_row, p.chunks_per_lane, al, coop, a, s);
     case NT_F16: return ntk::launch_split_f16(p.waves_per_row, p.chunks_per_lane, al, coop, a, s);

@@ -1706,6 +1706,121 @@ softmax_coop(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The cooperative split softmax with two rows per workgroup: workgroup
+// (g, j) takes chunk j of rows g and g + G (G = ceil(M / 2)), one after the
+// other, with the same record protocol as softmax_coop.  The second row's
+// loads are issued as soon as the first row's record is published, so they
+// are in flight while the first row's other records arrive and its output
+// is written: one row's reads overlap the other row's writes, where one row
+// per workgroup reads every row first and writes every row after.  Both
+// rows give the bits softmax_coop gives (same chunk_stats, merge, output).
+// ---------------------------------------------------------------------------
+
+template <int DT, int W, int K, bool AL, bool CAUSAL = false>
+__global__ void __launch_bounds__(64 * W)
+softmax_coop2(RowArgs a) {
+    using I = dt_info<DT>;
+    constexpr int TPR = 64 * W, NB = COOP_PMAX / 64;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int32_t N = a.N, P = a.P;
+    const int64_t G = (a.M + 1) / 2;
+    const int64_t g = blockIdx.x / P;
+    const int j = (int)(blockIdx.x - g * P);
+    const int64_t rowbytes = (int64_t)N * I::E;
+    const int64_t cbase = (int64_t)j * (TPR * K);
+    const float s2 = CAUSAL ? a.s2 : LOG2E;
+    const uint64_t tg = (uint64_t)a.tag << 32;
+    const bool two = g + G < a.M;                  // uniform: a second row exists
+    __shared__ float red[2][W];
+    __shared__ float2 qs[COOP_PMAX];
+    __shared__ uint64_t miss[NB];
+
+    uint4 raw[2][K];
+    {
+        const char *xr = a.x + g * rowbytes;
+        softmax_issue<DT, AL, K, TPR, CAUSAL>(raw[0], RowGeom<DT, AL>(xr, N), xr, t, N,
+                                              CAUSAL ? visible_len(a, g) : N, cbase);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (i == 1 && !two) break;
+        const int64_t row = g + i * G;
+        const char *xr = a.x + row * rowbytes;
+        char *yr = a.y + row * rowbytes;
+        const RowGeom<DT, AL> geo(xr, N);
+        bool yvec = true;
+        if constexpr (!AL) yvec = (((uintptr_t)yr ^ (uintptr_t)xr) & 15) == 0;
+        const int32_t L = CAUSAL ? visible_len(a, row) : N;
+        softmax_finish<DT, AL, K, TPR, CAUSAL>(raw[i], geo, xr, t, N, L, cbase);
+        const float2 mine = chunk_stats<DT, W, K>(raw[i], red, wv, lane, s2);
+
+        uint64_t *rec = reinterpret_cast<uint64_t *>(a.ws) + row * P * 2;
+        if (t == 0) {
+            __hip_atomic_store(rec + 2 * j, tg | __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(rec + 2 * j + 1, tg | __float_as_uint(mine.y), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            qs[j] = mine;
+        }
+        if (i == 0 && two) {
+            // the second row's loads, in flight during this row's exchange and output
+            asm volatile("" ::: "memory");
+            const char *xn = a.x + (g + G) * rowbytes;
+            softmax_issue<DT, AL, K, TPR, CAUSAL>(raw[1], RowGeom<DT, AL>(xn, N), xn, t, N,
+                                                  CAUSAL ? visible_len(a, g + G) : N, cbase);
+            asm volatile("" ::: "memory");
+        }
+        if (wv == 0) {
+            uint32_t pending = 0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int p = b * 64 + lane;
+                if (p < P && p != j) pending |= 1u << b;
+            }
+            for (int it = 0;; ++it) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (pending >> b & 1) {
+                        const int p = b * 64 + lane;
+                        const uint64_t w0 = __hip_atomic_load(rec + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const uint64_t w1 =
+                            __hip_atomic_load(rec + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if ((w0 >> 32) == a.tag && (w1 >> 32) == a.tag) {
+                            qs[p] = make_float2(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1));
+                            pending &= ~(1u << b);
+                        }
+                    }
+                }
+                if (__ballot(pending != 0) == 0 || it >= a.spin) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint64_t m = __ballot((pending >> b) & 1);
+                if (lane == 0) miss[b] = m;
+            }
+        }
+        __syncthreads();
+        // records that did not arrive: recompute them here (uniform loop)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint64_t m = miss[b];
+            while (m) {
+                const int q = b * 64 + __builtin_ctzll(m);
+                m &= m - 1;
+                const float2 e = chunk_stats_reload<DT, W, K, AL, CAUSAL>(geo, xr, t, N, L, (int64_t)q * (TPR * K),
+                                                                          red, wv, lane, s2);
+                if (t == 0) qs[q] = e;
+            }
+        }
+        __syncthreads();
+        float c, inv;
+        merge_pairs(static_cast<const float2 *>(qs), P, lane, c, inv, s2);
+        softmax_chunk_out<DT, W, K, AL>(raw[i], geo, yr, t, N, yvec, cbase, c, inv, s2);
+        __syncthreads();                           // qs and miss are the next row's
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Cooperative split norm: the split norm's chunks and arithmetic in ONE
 // pass, so x is read once.  The record exchange is the cooperative softmax's
 // (tagged 64-bit words, written and read as relaxed device-scope atomics, a

@@ -79,6 +79,8 @@ def kernels_of(w) -> list[str]:
     p = nt.nt_plan_launch(op, w.M, w.N, dt, True)
     W, K, al = p["waves_per_row"], p["chunks_per_lane"], _b(p["aligned"])
     c = _b(causal)
+    if p["split"] == 1 and p["cooperative"] == 2:
+        return [f"ntk::softmax_coop2<{dt}, {W}, {K}, {al}, {c}>"]
     if p["split"] == 1 and p["cooperative"]:
         return [f"ntk::softmax_coop<{dt}, {W}, {K}, {al}, {c}>"]
     if p["split"] == 1:

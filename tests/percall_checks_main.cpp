@@ -72,9 +72,9 @@ hipError_t launch_looped_bf16(int, int, int, bool, const RowArgs &, int64_t, hip
 hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
 hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
 hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
-hipError_t launch_split_f32(int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
-hipError_t launch_split_f16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
-hipError_t launch_split_bf16(int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
+hipError_t launch_split_f32(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH
+hipError_t launch_split_f16(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH
+hipError_t launch_split_bf16(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_norm_split_f32(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_norm_split_f16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_norm_split_bf16(int, int, int, bool, bool, const RowArgs &, hipStream_t) NT_LAUNCH

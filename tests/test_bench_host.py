@@ -112,15 +112,15 @@ def test_override_helper_restores():
     nested or not, and a bad setting changes nothing."""
     import row_wise_reductions_amd as nt
     plan = lambda: nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, nt.NT_F32, True)["cooperative"]  # noqa: E731
-    assert plan() == 1
+    assert plan() == 2                        # the cooperative kernel, two rows per workgroup
     with nt.override(NT_COOP="0", NT_NORM_SPLIT_ROWS="5"):
         assert plan() == 0
-        with nt.override(NT_COOP="1"):
+        with nt.override(NT_COOP="rows1"):
             assert plan() == 1
         assert plan() == 0
-    assert plan() == 1
+    assert plan() == 2
     with pytest.raises(nt.NtError):
         nt.set_override("NT_NO_SUCH_SETTING", "1")
     with pytest.raises(nt.NtError):
         nt.set_override("NT_COOP_SPIN", "-3")
-    assert plan() == 1
+    assert plan() == 2

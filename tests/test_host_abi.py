@@ -181,9 +181,10 @@ def test_plans_of_the_workloads():
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 131072, 4096, BF16, True)
     assert p["split"] == 0
     p = nt.nt_plan_launch(nt.NT_OP_SOFTMAX, 64, 262144, F32, True)
-    assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 64 * 16
+    # 1024 (row, chunk) pairs of fp32: two rows per cooperative workgroup
+    assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 32 * 16 and p["rows_per_block"] == 2
     assert (p["waves_per_row"], p["chunks_per_lane"]) == (8, 8)
-    assert p["workspace_bytes"] == 64 * 16 * 16 and p["cooperative"] == 1
+    assert p["workspace_bytes"] == 64 * 16 * 16 and p["cooperative"] == 2
 
 
 def test_narrow_row_rule():
