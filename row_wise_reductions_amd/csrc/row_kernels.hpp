@@ -170,6 +170,39 @@ __device__ __forceinline__ void st16_nt_at(const char *base, uint32_t soff, uint
 #endif
 }
 
+// Streaming store of one 16-byte chunk at base + voff that writes nothing
+// when voff + 16 > bytes: the buffer resource's range is [base, base +
+// bytes) and the buffer unit discards out-of-range stores, so lanes past
+// the row need no branch around their store.  Every lane then issues the
+// same stores on every path, and the compiler can wait for an earlier load
+// (the next row's, in the persistent kernel) without waiting for these
+// stores to complete.  `base` is wave-uniform, `bytes` a multiple of 16.
+__device__ __forceinline__ void st16_nt_bounded(const char *base, uint32_t bytes, uint32_t voff, uint4 v) {
+#if NTK_NT_STORES && NTK_STORE_SC1
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    const uint64_t pa = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>((((uint64_t)hi) << 32) | lo), 0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(t, rs, (int)voff, 0, CPOL_NT_SC1);
+#else
+    if (voff + 16 <= bytes) st16_nt_at(base, 0, voff, v);
+#endif
+}
+
+// One fp32 value at p + voff, written only where voff + 4 <= bytes (a
+// buffer store with that range; bytes = 0 writes nothing, p may then be
+// null).  A plain (cached) store: the per-row statistics.
+__device__ __forceinline__ void st4_bounded(const float *p, uint32_t bytes, uint32_t voff, float v) {
+    const uint64_t pa = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>((((uint64_t)hi) << 32) | lo), 0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, (int)voff, 0, 0);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
 // b mod 8).  Renumbering so that XCD x receives a contiguous band of row
 // blocks gives each XCD's L2 and memory queues a sequential stream.
@@ -1110,12 +1143,11 @@ row_norm_persistent(RowArgs a) {
                                                     (double)b32[LN_WIDE ? k : 0][LN_WIDE ? i : 0]);
                     }
                 }
-                store_slice<DT, true, TPR>(g, yr, k, t, N, true, pack<DT>(o));
+                st16_nt_bounded(yr, (uint32_t)rowbytes, (uint32_t)((k * TPR + t) * 16), pack<DT>(o));
             }
-            if (t == 0) {
-                if (a.mean) a.mean[row] = (float)(pv + m1);
-                if (a.rstd) a.rstd[row] = (float)rstd;
-            }
+            // lane 0 writes the statistics (the other lanes' offsets are out of range)
+            st4_bounded(a.mean ? a.mean + row : nullptr, a.mean ? 4u : 0u, (uint32_t)t * 4u, (float)(pv + m1));
+            st4_bounded(a.rstd ? a.rstd + row : nullptr, a.rstd ? 4u : 0u, (uint32_t)t * 4u, (float)rstd);
         } else {
             float ss = 0.f;
 #pragma unroll
@@ -1129,7 +1161,7 @@ row_norm_persistent(RowArgs a) {
                 float o[VEC];
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) o[i] = (v[k][i] * inv) * w32[k][i];
-                store_slice<DT, true, TPR>(g, yr, k, t, N, true, pack<DT>(o));
+                st16_nt_bounded(yr, (uint32_t)rowbytes, (uint32_t)((k * TPR + t) * 16), pack<DT>(o));
             }
         }
     }
