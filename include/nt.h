@@ -367,8 +367,9 @@ typedef struct {
     int32_t threads_per_block;
     int32_t aligned;          /* 1 when the 16-byte-aligned variant is used             */
     int32_t persistent;       /* 1: norm kernel with parameters held in registers across
-                                 rows; its grid is sized on the device from occupancy,
-                                 and `grid` below is then an upper bound                  */
+                                 rows; `grid` below is then k workgroups per compute unit
+                                 (k from the row's bytes), capped at launch by how many
+                                 fit on the device at once                                */
     int32_t cooperative;      /* split path: 1 when one kernel does both phases (x read once;
                                  the workgroups of a row exchange their partial results
                                  through the workspace), 2 when it does so for two rows

@@ -86,30 +86,28 @@ hipError_t resident(int W, int K, bool al, const RowArgs &a, int64_t grid, hipSt
     return hipErrorInvalidValue;
 }
 
-// Persistent norm kernel: as many workgroups as fit on the device at once
-// (occupancy x `cus` compute units, the occupancy cached per instantiation),
-// or `grid_override` when > 0 (the NT_PERSIST_GRID tuning override); never
-// more than there are rows.
+// Persistent norm kernel on `grid` workgroups (the plan's k per compute
+// unit, never more than there are rows), at most as many as fit on the
+// device at once when `cap_cus` > 0 (occupancy x `cap_cus` compute units, the
+// occupancy cached per instantiation).  The grid stays a multiple of the CU
+// count: uneven grids leave some CUs a row more than others (7-10% slower).
 template <int OP, int W, int K, bool RES>
-hipError_t persist_go(const RowArgs &a, hipStream_t s, int cus, int64_t grid_override) {
-    static std::atomic<int> per_cu{0};
-    int pc = per_cu.load(std::memory_order_relaxed);
-    if (pc == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_norm_persistent<OP, DT, W, K, RES>, 64 * W, 0) !=
-                hipSuccess || n <= 0)
-            n = 1;
-        per_cu.store(n, std::memory_order_relaxed);
-        pc = n;
+hipError_t persist_go(const RowArgs &a, hipStream_t s, int64_t grid, int cap_cus) {
+    if (cap_cus > 0) {
+        static std::atomic<int> per_cu{0};
+        int pc = per_cu.load(std::memory_order_relaxed);
+        if (pc == 0) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_norm_persistent<OP, DT, W, K, RES>, 64 * W, 0) !=
+                    hipSuccess || n <= 0)
+                n = 1;
+            per_cu.store(n, std::memory_order_relaxed);
+            pc = n;
+        }
+        if (grid > (int64_t)pc * cap_cus) grid = (int64_t)pc * cap_cus;
     }
-    // RMSNorm: half the resident workgroups per CU (rounded up) streams 2%
-    // faster than all of them on 8192- and 16384-wide bf16 rows; LayerNorm,
-    // whose rows take longer to reduce, is fastest with every slot filled.
-    // The grid stays a multiple of the CU count: uneven grids leave some CUs
-    // a row more than others (7-10% slower).
-    if constexpr (OP == OP_RMSNORM) pc = (pc + 1) / 2;
-    int64_t grid = grid_override > 0 ? grid_override : (int64_t)pc * cus;
     if (grid > a.M) grid = a.M;
+    if (grid < 1) grid = 1;
     return launch_k(row_norm_persistent<OP, DT, W, K, RES>, grid, 64 * W, s, a);
 }
 
@@ -118,22 +116,22 @@ hipError_t persist_go(const RowArgs &a, hipStream_t s, int cus, int64_t grid_ove
 // chunks; other norms stream faster one row per workgroup, and their
 // persistent forms are not built.
 template <int OP, int W, int K>
-hipError_t persist_pick(const RowArgs &a, hipStream_t s, int cus, int64_t go) {
+hipError_t persist_pick(const RowArgs &a, hipStream_t s, int64_t grid, int cap) {
     if (a.r) {
-        if constexpr (OP == OP_LAYERNORM) return persist_go<OP, W, K, true>(a, s, cus, go);
+        if constexpr (OP == OP_LAYERNORM) return persist_go<OP, W, K, true>(a, s, grid, cap);
         return hipErrorInvalidValue;
     }
-    if constexpr (OP == OP_LAYERNORM || !kWide || (W == 8 && K == 8)) return persist_go<OP, W, K, false>(a, s, cus, go);
+    if constexpr (OP == OP_LAYERNORM || !kWide || (W == 8 && K == 8)) return persist_go<OP, W, K, false>(a, s, grid, cap);
     return hipErrorInvalidValue;
 }
 
 template <int OP>
-hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s, int cus, int64_t go) {
+hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s, int64_t grid, int cap) {
 #define NTK_CASE(w, k)                                                   \
     if (W == w && K == k) {                                              \
         if constexpr (shape_built<OP, k, false, w>() && k * dt_info<DT>::VEC <= 32 &&                       \
                       !(OP == OP_LAYERNORM && kWide && k * dt_info<DT>::VEC > 16))                        \
-            return persist_pick<OP, w, k>(a, s, cus, go);                                                 \
+            return persist_pick<OP, w, k>(a, s, grid, cap);                                               \
         return hipErrorInvalidValue;                                     \
     }
     NTK_CASE(2, 2) NTK_CASE(2, 4) NTK_CASE(2, 8) NTK_CASE(4, 1) NTK_CASE(4, 2) NTK_CASE(4, 4) NTK_CASE(4, 8)
@@ -145,10 +143,10 @@ hipError_t persistent(int W, int K, const RowArgs &a, hipStream_t s, int cus, in
     return hipErrorInvalidValue;
 }
 
-hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus, int64_t go) {
+hipError_t persistent_any(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid, int cap) {
     switch (op) {
-    case OP_LAYERNORM: return persistent<OP_LAYERNORM>(W, K, a, s, cus, go);
-    case OP_RMSNORM: return persistent<OP_RMSNORM>(W, K, a, s, cus, go);
+    case OP_LAYERNORM: return persistent<OP_LAYERNORM>(W, K, a, s, grid, cap);
+    case OP_RMSNORM: return persistent<OP_RMSNORM>(W, K, a, s, grid, cap);
     }
     return hipErrorInvalidValue;
 }
@@ -275,9 +273,9 @@ hipError_t launch_split_f32(int W, int K, bool al, int coop, const RowArgs &a, h
 hipError_t launch_looped_f32(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                 int64_t grid_override) {
-    return persistent_any(op, W, K, a, s, cus, grid_override);
+hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid,
+                                 int cap_cus) {
+    return persistent_any(op, W, K, a, s, grid, cap_cus);
 }
 hipError_t launch_norm_split_f32(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);
@@ -292,9 +290,9 @@ hipError_t launch_split_f16(int W, int K, bool al, int coop, const RowArgs &a, h
 hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                 int64_t grid_override) {
-    return persistent_any(op, W, K, a, s, cus, grid_override);
+hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid,
+                                 int cap_cus) {
+    return persistent_any(op, W, K, a, s, grid, cap_cus);
 }
 hipError_t launch_norm_split_f16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);
@@ -309,9 +307,9 @@ hipError_t launch_split_bf16(int W, int K, bool al, int coop, const RowArgs &a, 
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s) {
     return looped_any(op, W, K, al, a, grid, s);
 }
-hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                 int64_t grid_override) {
-    return persistent_any(op, W, K, a, s, cus, grid_override);
+hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid,
+                                 int cap_cus) {
+    return persistent_any(op, W, K, a, s, grid, cap_cus);
 }
 hipError_t launch_norm_split_bf16(int op, int W, int K, bool al, bool coop, const RowArgs &a, hipStream_t s) {
     return norm_split_any(op, W, K, al, coop, a, s);

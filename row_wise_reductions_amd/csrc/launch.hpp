@@ -23,14 +23,11 @@ hipError_t launch_looped_f16(int op, int W, int K, bool al, const RowArgs &a, in
 hipError_t launch_looped_bf16(int op, int W, int K, bool al, const RowArgs &a, int64_t grid, hipStream_t s);
 
 // Launch the persistent norm kernel (aligned rows, every parameter vector
-// present); the grid is sized from the kernel's occupancy on a device of
-// `cus` compute units, or is `grid_override` when that is > 0.
-hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                 int64_t grid_override);
-hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                 int64_t grid_override);
-hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int cus,
-                                  int64_t grid_override);
+// present) on `grid` workgroups, capped at what fits on the device at once
+// on `cap_cus` compute units when that is > 0.
+hipError_t launch_persistent_f32(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid, int cap_cus);
+hipError_t launch_persistent_f16(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid, int cap_cus);
+hipError_t launch_persistent_bf16(int op, int W, int K, const RowArgs &a, hipStream_t s, int64_t grid, int cap_cus);
 
 // Launch the split softmax: with `coop` 1, the one cooperative kernel
 // (a.P <= COOP_PMAX, x not aliasing y, a.tag unique to the call); with 2,

@@ -338,6 +338,25 @@ bool persistent_pays(nt_op op, nt_dtype dt, bool res, Shape sh, int64_t nch) {
     return dt != NT_F32 ? nch >= 1024 : (sh.W == 8 && sh.K == 8 && nch <= 3072);
 }
 
+// Grid of the persistent norm kernel: k workgroups per compute unit, k from
+// the bytes of one row (interleaved kernel-trace sweeps of k = 1..8 with an
+// A/A control).  LayerNorm streams fastest with about 16 KiB of rows per CU
+// and at least two workgroups: k = max(2, ceil(16 KiB / row)), so 2 on
+// 4096-element 16-bit rows (3.7% over the 3 that fit), 3 on 3584-element
+// ones, 4 on 2048-element ones (6% over the 8 that fit), 2 on 2048-element
+// fp32 rows (10% over 6).  RMSNorm (16 to 48 KiB rows) is fastest with
+// floor(32 KiB / row), at least 1: half the workgroups that fit.  The
+// launcher caps k at the kernel's occupancy; NT_PERSIST_GRID sets the grid
+// itself, uncapped (tuning).
+int64_t persistent_grid(nt_op op, nt_dtype dt, int64_t M, int64_t N, int cus) {
+    const int64_t forced = tune(T_PERSIST_GRID);
+    if (forced > 0) return std::min(M, forced);
+    const int64_t row = N * elem_bytes(dt);
+    const int64_t k = op == NT_OP_RMSNORM ? std::max<int64_t>(1, 32768 / row)
+                                           : std::max<int64_t>(2, (16384 + row - 1) / row);
+    return std::min(M, k * cus);
+}
+
 // `res`: the fused residual add + norm, whose lanes also hold the residual's
 // words (at most 32 values per lane for RMSNorm; LayerNorm is capped at 16).
 // LayerNorm is built with at most 12 waves per row.
@@ -501,14 +520,16 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         p->grid = grid;
         // Norms on aligned rows with every parameter vector present can keep
         // the parameters widened in registers across rows: persistent
-        // workgroups (grid sized on the device from occupancy; `grid` is then
-        // an upper bound), where that pays (persistent_pays).  At most 32
+        // workgroups (k per compute unit, persistent_grid; capped at launch
+        // by how many fit at once), where that pays (persistent_pays).  At most 32
         // values per lane: the row, its prefetched successor and the cached
         // parameters must fit without spilling; built for 2 to 8 waves.
         if (op != NT_OP_SOFTMAX && aligned && params && pick.W >= 2 && pick.W <= 8 &&
             pick.K * elems_per_chunk(dt) <= 32 && persistent_built(op, dt, res, pick) &&
-            (persistent_mode() == 2 || (persistent_mode() == 1 && persistent_pays(op, dt, res, pick, nch))))
+            (persistent_mode() == 2 || (persistent_mode() == 1 && persistent_pays(op, dt, res, pick, nch)))) {
             p->persistent = 1;
+            p->grid = persistent_grid(op, dt, M, N, device_cus());
+        }
         return NT_OK;
     }
     Shape ns;
@@ -581,12 +602,12 @@ bool all_aligned16(int64_t N, nt_dtype dt, const void *x, const void *y, const v
 hipError_t launch_resident(nt_dtype dt, int op, const nt_plan &p, const ntk::RowArgs &a, hipStream_t s) {
     const bool al = p.aligned != 0;
     if (p.persistent) {
-        const int cus = device_cus();
-        const int64_t pg = tune(T_PERSIST_GRID);
+        // capped at the kernel's occupancy, unless the grid is forced
+        const int cap = tune(T_PERSIST_GRID) > 0 ? 0 : device_cus();
         switch (dt) {
-        case NT_F32: return ntk::launch_persistent_f32(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
-        case NT_F16: return ntk::launch_persistent_f16(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
-        case NT_BF16: return ntk::launch_persistent_bf16(op, p.waves_per_row, p.chunks_per_lane, a, s, cus, pg);
+        case NT_F32: return ntk::launch_persistent_f32(op, p.waves_per_row, p.chunks_per_lane, a, s, p.grid, cap);
+        case NT_F16: return ntk::launch_persistent_f16(op, p.waves_per_row, p.chunks_per_lane, a, s, p.grid, cap);
+        case NT_BF16: return ntk::launch_persistent_bf16(op, p.waves_per_row, p.chunks_per_lane, a, s, p.grid, cap);
         }
     }
     switch (dt) {

@@ -69,9 +69,9 @@ hipError_t launch_resident_bf16(int, int, int, bool, const RowArgs &, int64_t, h
 hipError_t launch_looped_f32(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_LAUNCH
 hipError_t launch_looped_f16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_LAUNCH
 hipError_t launch_looped_bf16(int, int, int, bool, const RowArgs &, int64_t, hipStream_t) NT_LAUNCH
-hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
-hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
-hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t, int, int64_t) NT_LAUNCH
+hipError_t launch_persistent_f32(int, int, int, const RowArgs &, hipStream_t, int64_t, int) NT_LAUNCH
+hipError_t launch_persistent_f16(int, int, int, const RowArgs &, hipStream_t, int64_t, int) NT_LAUNCH
+hipError_t launch_persistent_bf16(int, int, int, const RowArgs &, hipStream_t, int64_t, int) NT_LAUNCH
 hipError_t launch_split_f32(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_split_f16(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH
 hipError_t launch_split_bf16(int, int, bool, int, const RowArgs &, hipStream_t) NT_LAUNCH

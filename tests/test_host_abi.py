@@ -226,6 +226,35 @@ def test_narrow_row_rule():
         assert a == b
 
 
+def test_persistent_grid_rule(ntenv):
+    """The persistent norm kernel's grid: k workgroups per compute unit (256
+    on a host without a GPU, as on MI355X), k = max(2, ceil(16 KiB / row
+    bytes)) for LayerNorm and max(1, floor(32 KiB / row bytes)) for RMSNorm,
+    never more than there are rows; NT_PERSIST_GRID sets it."""
+    L, R, AL = nt.NT_OP_LAYERNORM, nt.NT_OP_RMSNORM, nt.NT_OP_ADD_LAYERNORM
+
+    def grid(op, M, N, dt):
+        p = nt.nt_plan_launch(op, M, N, dt, True)
+        assert p["persistent"] == 1, (op, M, N, dt, p)
+        return p["grid"]
+    assert grid(L, 4096, 4096, F16) == 2 * 256          # 8 KiB rows
+    assert grid(L, 4096, 4096, BF16) == 2 * 256
+    assert grid(L, 4096, 3584, F16) == 3 * 256          # 7 KiB
+    assert grid(L, 4096, 2048, F16) == 4 * 256          # 4 KiB
+    assert grid(L, 4096, 1032, F16) == 8 * 256          # 2064 B: ceil(7.9)
+    assert grid(L, 4096, 2048, F32) == 2 * 256          # 8 KiB
+    assert grid(L, 16384, 8192, F16) == 2 * 256         # 16 KiB: at least 2
+    assert grid(L, 16384, 16384, F16) == 2 * 256        # 32 KiB
+    assert grid(AL, 4096, 8192, F16) == 2 * 256
+    assert grid(R, 16384, 8192, BF16) == 2 * 256        # 16 KiB
+    assert grid(R, 16384, 16384, BF16) == 256           # 32 KiB
+    assert grid(R, 4096, 10240, F32) == 256             # 40 KiB
+    assert grid(L, 100, 4096, F16) == 100               # fewer rows than workgroups
+    ntenv.setenv("NT_PERSIST_GRID", "300")
+    assert grid(L, 4096, 4096, F16) == 300 and grid(R, 16384, 8192, BF16) == 300
+    assert grid(L, 100, 4096, F16) == 100
+
+
 def test_cooperative_split_limits():
     # one kernel up to 128 chunks per row (16384 elements each: 8 waves with
     # 32 values per lane), two kernels (16 KiB chunks) beyond
