@@ -23,6 +23,11 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
       kernels in a run that launches them directly (bench.py
       --wide-norm-traffic), beside the work's algorithmic bytes B.
 
+  python -m row_wise_reductions_amd.rocprof_summary requests --runs DIR,DIR,.. --calib DIR,DIR,.. --cmds FILE --md FILE.md
+      DIRs hold *_counter_collection.csv from `rocprofv3 --pmc` runs of
+      bench.py and of `bench.py --calibrate` with the L2 request counters
+      (REQ_COUNTERS): per-call request counts and the bytes they make.
+
   python -m row_wise_reductions_amd.rocprof_summary calib --big DIR --sizes DIR --cmds FILE --md FILE.md
       DIRs hold *_kernel_trace.csv from `rocprofv3 --kernel-trace` runs of
       `bench.py --calibrate` (reference streams at 1 GiB) and `bench.py
@@ -390,6 +395,88 @@ def calib(args):
     print("\n".join(lines))
 
 
+# L2 (TCC) request counters of the fabric interface, for a cross-check of
+# the calibrated FETCH_SIZE / WRITE_SIZE figures that needs no scale factor.
+REQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum",
+                "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum", "TCC_HIT_sum", "TCC_MISS_sum")
+L2_LINE = 128   # bytes per gfx950 L2 line
+
+
+def requests(args):
+    """Per-call L2 request counts of each workload, and the bytes they make
+    with reads counted as whole 128-byte lines and writes at their counted
+    32- or 64-byte sizes, beside the algorithmic bytes.  The calibration copy
+    checks the read reading: its read requests times 128 bytes should be the
+    1 GiB it reads."""
+    import workloads
+    runs, cruns = args.runs.split(","), args.calib.split(",")
+
+    def gather(dirs):
+        m = {}
+        for d in dirs:
+            for c in REQ_COUNTERS:
+                got = _counter_means(d, c)
+                if got:
+                    m[c] = got
+        return m
+    wm, cm = gather(runs), gather(cruns)
+    missing = [c for c in REQ_COUNTERS if c not in wm or c not in cm]
+    if missing:
+        raise SystemExit(f"counters missing from the runs: {missing}")
+
+    def per_call(m, keys):
+        tot = {c: 0.0 for c in REQ_COUNTERS}
+        for k in keys:
+            for c in REQ_COUNTERS:
+                v, _ = _lookup(m[c], k)
+                if v is None:
+                    return None
+                tot[c] += v
+        return tot
+
+    def read_bytes(t):
+        return L2_LINE * t["TCC_EA0_RDREQ_sum"]
+
+    def write_bytes(t):
+        w64 = t["TCC_EA0_WRREQ_64B_sum"]
+        return 64 * w64 + 32 * (t["TCC_EA0_WRREQ_sum"] - w64)
+    cal = per_call(cm, [CALIB_KERNEL])
+    if cal is None:
+        raise SystemExit("calibration copy kernel not found in the counter output")
+    with open(args.cmds) as fh:
+        cmds = fh.read().strip().splitlines()
+    lines = ["# L2 request counters: HBM-side bytes without a scale factor", "",
+             "Commands (one run per counter group, from the repository root on the GPU host):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "Per call, summed over the workload's kernels. Reads are counted as whole 128-byte L2 lines "
+              "(`TCC_EA0_RDREQ` x 128 B), writes at their counted sizes (64 B for `TCC_EA0_WRREQ_64B`, 32 B for the "
+              "rest). `FETCH_SIZE` prices every read request not counted by `TCC_BUBBLE` (128-byte reads) or "
+              "`TCC_EA0_RDREQ_32B` at 64 bytes; the copy row shows what that misses on this part.", "",
+              f"Calibration copy `{CALIB_KERNEL}` (1 GiB read, 1 GiB written): read requests "
+              f"{cal['TCC_EA0_RDREQ_sum']:.0f} (x 128 B = {read_bytes(cal) / CALIB_BYTES:.4f} GiB), of them 32-byte "
+              f"{cal['TCC_EA0_RDREQ_32B_sum']:.0f} and counted 128-byte (`TCC_BUBBLE`) {cal['TCC_BUBBLE_sum']:.0f}; "
+              f"write requests {cal['TCC_EA0_WRREQ_sum']:.0f} ({write_bytes(cal) / CALIB_BYTES:.4f} GiB).", "",
+              "| workload | read req | 32 B | to DRAM | write req | 64 B | to DRAM | L2 hit rate | read bytes | "
+              "written bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    rows = [("calibration copy 1 GiB", cal, 2 * CALIB_BYTES)]
+    for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS:
+        t = per_call(wm, kernels_of(w))
+        if t is not None:
+            rows.append((w.name, t, w.algorithmic_bytes()))
+    for name, t, alg in rows:
+        hm = t["TCC_HIT_sum"] + t["TCC_MISS_sum"]
+        hit = f"{t['TCC_HIT_sum'] / hm:.3f}" if hm else ""
+        rb, wb = read_bytes(t), write_bytes(t)
+        lines.append(f"| {name} | {t['TCC_EA0_RDREQ_sum']:.0f} | {t['TCC_EA0_RDREQ_32B_sum']:.0f} | "
+                     f"{t['TCC_EA0_RDREQ_DRAM_sum']:.0f} | {t['TCC_EA0_WRREQ_sum']:.0f} | "
+                     f"{t['TCC_EA0_WRREQ_64B_sum']:.0f} | {t['TCC_EA0_WRREQ_DRAM_sum']:.0f} | {hit} | {rb:.0f} | "
+                     f"{wb:.0f} | {alg} | {(rb + wb) / alg:.3f} |")
+    lines.append("")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -422,8 +509,14 @@ def main():
     o.add_argument("--valu", default=None, help="DIR of a `rocprofv3 --pmc VALUBusy` run")
     o.add_argument("--cmds", required=True)
     o.add_argument("--md", required=True)
+    r = sub.add_parser("requests")
+    r.add_argument("--runs", required=True, help="comma-separated DIRs of `--pmc` runs of bench.py")
+    r.add_argument("--calib", required=True, help="comma-separated DIRs of the same runs of bench.py --calibrate")
+    r.add_argument("--cmds", required=True)
+    r.add_argument("--md", required=True)
     a = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels, "calib": calib}[a.mode](a)
+    {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels, "calib": calib,
+     "requests": requests}[a.mode](a)
 
 
 if __name__ == "__main__":

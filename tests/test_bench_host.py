@@ -107,6 +107,46 @@ def test_kernels_summary_groups_and_scales(tmp_path):
     assert "    cmd one" in text
 
 
+def test_requests_summary_counts_lines(tmp_path):
+    """rocprof_summary's L2 request mode on synthetic counter files: reads
+    count as 128-byte lines, writes at 64 or 32 bytes, per call summed over
+    the workload's kernels, beside its algorithmic bytes."""
+    import csv
+    from row_wise_reductions_amd import rocprof_summary as rs
+
+    def counters(d, rows):
+        d.mkdir(parents=True)
+        with open(d / "x_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for name, vals in rows:
+                for c, v in vals.items():
+                    w.writerow({"Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+
+    zero = {c: 0 for c in rs.REQ_COUNTERS}
+    lines = (1 << 30) // 128
+    cal = dict(zero, TCC_EA0_RDREQ_sum=lines, TCC_EA0_RDREQ_DRAM_sum=lines, TCC_EA0_WRREQ_sum=2 * lines,
+               TCC_EA0_WRREQ_64B_sum=2 * lines, TCC_MISS_sum=3 * lines)
+    counters(tmp_path / "c", [(rs.CALIB_KERNEL, cal)])
+    w = workloads.BY_NAME["layernorm_f16_4096"]
+    k = rs.kernels_of(w)
+    assert len(k) == 1
+    alg = w.algorithmic_bytes()
+    rd = dict(zero, TCC_EA0_RDREQ_sum=1000, TCC_EA0_RDREQ_32B_sum=0, TCC_EA0_WRREQ_sum=3000,
+              TCC_EA0_WRREQ_64B_sum=2000, TCC_HIT_sum=1, TCC_MISS_sum=3)
+    counters(tmp_path / "r", [("void " + k[0] + "(ntk::RowArgs)", rd)])
+    cmds = tmp_path / "cmds.txt"
+    cmds.write_text("cmd one\n")
+    md = tmp_path / "out.md"
+    rs.requests(types.SimpleNamespace(runs=str(tmp_path / "r"), calib=str(tmp_path / "c"), cmds=str(cmds), md=str(md)))
+    text = md.read_text()
+    assert "(x 128 B = 1.0000 GiB)" in text and "write requests 16777216 (1.0000 GiB)" in text
+    assert f"| calibration copy 1 GiB | {lines} | 0 | {lines} | {2 * lines} |" in text
+    # 1000 x 128 read + 2000 x 64 + 1000 x 32 written = 288000 bytes
+    assert f"| layernorm_f16_4096 | 1000 | 0 | 0 | 3000 | 2000 | 0 | 0.250 | 128000 | 160000 | {alg} | " in text
+    assert "    cmd one" in text
+
+
 def test_override_helper_restores():
     """bench.py's tuning settings (nt.override) are restored on exit,
     nested or not, and a bad setting changes nothing."""
