@@ -28,6 +28,12 @@ the roofline ``traffic`` field.  Nothing here launches work on a GPU.
       bench.py and of `bench.py --calibrate` with the L2 request counters
       (REQ_COUNTERS): per-call request counts and the bytes they make.
 
+  python -m row_wise_reductions_amd.rocprof_summary waves --run DIR --cmds FILE --md FILE.md
+      DIR holds *_counter_collection.csv from a `rocprofv3 --pmc` run of
+      `bench.py --copy-at-sizes` with WAVE_COUNTERS: each workload's kernel
+      beside the one-chunk copy of its bytes, cycles per wave and where
+      they go.
+
   python -m row_wise_reductions_amd.rocprof_summary calib --big DIR --sizes DIR --cmds FILE --md FILE.md
       DIRs hold *_kernel_trace.csv from `rocprofv3 --kernel-trace` runs of
       `bench.py --calibrate` (reference streams at 1 GiB) and `bench.py
@@ -477,6 +483,71 @@ def requests(args):
     print("\n".join(lines))
 
 
+WAVE_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")
+
+
+def waves(args):
+    """Where a wave's life goes, each workload's kernel beside the one-chunk
+    streaming copy of its bytes (`ntcal_copy_kernel<1, 1>` at the grid
+    bench.py --copy-at-sizes gives it): cycles per wave, and the shares of
+    those cycles spent issuing instructions (SQ_ACTIVE_INST_ANY), ready but
+    waiting for an issue slot (SQ_WAIT_INST_ANY: other waves' instructions,
+    or a memory instruction held back by a full queue) and waiting on a
+    counter or barrier (SQ_WAIT_ANY: s_waitcnt for memory, LDS, barriers);
+    the three add up to the wave's cycles.  Medians over the dispatches of a
+    `--pmc` run of bench.py --copy-at-sizes."""
+    import workloads
+    rows = _rows(os.path.join(args.run, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") not in WAVE_COUNTERS:
+            continue
+        key = (r["Kernel_Name"], int(float(r.get("Grid_Size") or 0)))
+        acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+
+    def pick(match):
+        hit = [(k, v) for k, v in acc.items() if match(k)]
+        if not hit:
+            return None
+        k, v = hit[0]
+        if any(c not in v for c in WAVE_COUNTERS):
+            return None
+        return {c: statistics.median(v[c]) for c in WAVE_COUNTERS}
+
+    def cells(m):
+        wc = m["SQ_WAVE_CYCLES"]
+        return (f"{m['SQ_WAVES']:.0f} | {wc / m['SQ_WAVES']:.0f} | {m['SQ_ACTIVE_INST_ANY'] / wc:.3f} | "
+                f"{m['SQ_WAIT_INST_ANY'] / wc:.3f} | {m['SQ_WAIT_ANY'] / wc:.3f}")
+    with open(args.cmds) as fh:
+        cmds = fh.read().strip().splitlines()
+    lines = ["# Wave lifetimes: each workload's kernel beside the copy of its bytes (rocprofv3 SQ counters)", "",
+             "Command (repository root, GPU host):", ""] + [f"    {c}" for c in cmds] + [
+             "", "Per dispatch (median over the run's dispatches): waves launched, SQ_WAVE_CYCLES per wave, and the "
+             "shares of the waves' resident cycles spent issuing (SQ_ACTIVE_INST_ANY), ready but waiting for an "
+             "issue slot (SQ_WAIT_INST_ANY: other waves' instructions, or a memory instruction held back by a full "
+             "queue) and waiting on a counter or barrier (SQ_WAIT_ANY: s_waitcnt for memory or LDS, barriers); the "
+             "three add up to the wave's cycles. The copy is `ntcal_copy_kernel<1, 1>` (one 16-byte chunk per lane, device-scope "
+             "streaming stores) moving the workload's M x N x e bytes each way.", "",
+             "| workload | kernel | waves | cycles / wave | issuing | waiting to issue | waiting on counters, barriers |",
+             "|---|---|---|---|---|---|---|"]
+    for w in workloads.WORKLOADS:
+        ks = kernels_of(w)
+        if len(ks) != 1:
+            continue
+        km = pick(lambda k: _match(k[0], ks[0]))
+        n16 = w.M * w.N * w.elem_bytes // 16
+        grid = -(-n16 // 256)
+        cm = pick(lambda k: "ntcal_copy_kernel<1, 1>" in k[0] and k[1] in (grid, grid * 256))
+        if km is None or cm is None:
+            continue
+        lines.append(f"| {w.name} | `{ks[0]}` | {cells(km)} |")
+        lines.append(f"| | copy of its bytes | {cells(cm)} |")
+    lines.append("")
+    with open(args.md, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -514,9 +585,13 @@ def main():
     r.add_argument("--calib", required=True, help="comma-separated DIRs of the same runs of bench.py --calibrate")
     r.add_argument("--cmds", required=True)
     r.add_argument("--md", required=True)
+    v = sub.add_parser("waves")
+    v.add_argument("--run", required=True, help="DIR of a `--pmc` run of bench.py --copy-at-sizes (WAVE_COUNTERS)")
+    v.add_argument("--cmds", required=True)
+    v.add_argument("--md", required=True)
     a = ap.parse_args()
     {"stats": stats, "traffic": traffic, "occupancy": occupancy, "kernels": kernels, "calib": calib,
-     "requests": requests}[a.mode](a)
+     "requests": requests, "waves": waves}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -147,6 +147,34 @@ def test_requests_summary_counts_lines(tmp_path):
     assert "    cmd one" in text
 
 
+def test_waves_summary_pairs_kernel_and_copy(tmp_path):
+    """rocprof_summary's wave mode on a synthetic counter file: each
+    workload's kernel beside the one-chunk copy at its size (told apart from
+    other copies by grid), cycles per wave and the shares of them."""
+    import csv
+    from row_wise_reductions_amd import rocprof_summary as rs
+    w = workloads.BY_NAME["softmax_f32_1024x781"]
+    k = rs.kernels_of(w)[0]
+    grid = -(-(w.M * w.N * 4 // 16) // 256) * 256
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, g, vals in (("void " + k + "(ntk::RowArgs)", 262144, (4096, 409600, 40960, 8192, 327680)),
+                              ("void ntcal_copy_kernel<1, 1>(x)", grid, (3124, 312400, 3124, 0, 306152)),
+                              ("void ntcal_copy_kernel<1, 1>(x)", 2 * grid, (1, 1, 1, 1, 1))):
+            for c, v in zip(rs.WAVE_COUNTERS, vals):
+                wr.writerow({"Kernel_Name": name, "Grid_Size": g, "Counter_Name": c, "Counter_Value": v})
+    cmds = tmp_path / "cmds.txt"
+    cmds.write_text("cmd\n")
+    md = tmp_path / "w.md"
+    rs.waves(types.SimpleNamespace(run=str(d), cmds=str(cmds), md=str(md)))
+    text = md.read_text()
+    assert f"| softmax_f32_1024x781 | `{k}` | 4096 | 100 | 0.100 | 0.020 | 0.800 |" in text
+    assert "| | copy of its bytes | 3124 | 100 | 0.010 | 0.000 | 0.980 |" in text
+
+
 def test_override_helper_restores():
     """bench.py's tuning settings (nt.override) are restored on exit,
     nested or not, and a bad setting changes nothing."""
