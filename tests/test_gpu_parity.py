@@ -295,12 +295,15 @@ def test_looped_path_forced(op, dt, N, ntenv):
 
 @pytest.mark.parametrize("op,dt", [("layernorm", "f32"), ("layernorm", "f16"), ("layernorm", "bf16"),
                                    ("rmsnorm", "f32"), ("rmsnorm", "f16"), ("rmsnorm", "bf16")])
-@pytest.mark.parametrize("N,M,grid", [(4096, 37, 0), (8192, 300, 7), (4096, 5, 2), (8192, 64, 3)])
+@pytest.mark.parametrize("N,M,grid", [(4096, 37, 0), (8192, 300, 7), (4096, 5, 2), (8192, 64, 3), (4096, 3000, 0),
+                                    (16384, 3000, 2048)])
 def test_persistent_norms(op, dt, N, M, grid, ntenv):
     """Persistent norm kernel (parameters held across rows, next row prefetched):
     parity with the oracle and bitwise equality with the one-row-per-group
-    kernel, including grids much smaller than the row count.  (fp32 RMSNorm
-    plans it only on part-filled rows of 8 waves x 8 chunks: 10240 there.)"""
+    kernel, including grids much smaller than the row count, the planned
+    grid at a few rows per workgroup, and a forced grid of more workgroups
+    than fit on the device at once.  (fp32 RMSNorm plans it only on
+    part-filled rows of 8 waves x 8 chunks: 10240 there.)"""
     code = DT_CODE[dt]
     opc = {"layernorm": 1, "rmsnorm": 2}[op]
     # a width near N whose plan is the persistent kernel
