@@ -111,8 +111,9 @@ typedef NT_ENUM {
 /*
  * Bytes of device workspace nt_softmax_rows needs for this shape: 0 when each
  * row fits on chip (single pass), else 16 bytes per (row, row chunk) for the
- * per-chunk running max and denominator of the split online path.  Returns 0
- * for invalid arguments.  The contents need not be initialized and are
+ * per-chunk running max and denominator of the split online path, plus 16
+ * bytes for the record tag of a call captured into a graph.  Returns 0 for
+ * invalid arguments.  The contents need not be initialized and are
  * overwritten; two calls in flight at once must not share a workspace, and a
  * workspace overlapping x or y is NT_ERR_ALIAS.
  */
@@ -129,9 +130,13 @@ size_t nt_softmax_workspace_bytes(int64_t M, int64_t N, nt_dtype dt);
  * 128 chunks per row this is one kernel that reads x once (the workgroups of a
  * row exchange their pairs through the workspace; a pair that does not arrive
  * within a bounded wait is recomputed from x, so the result does not depend on
- * scheduling); wider rows, in-place calls and calls on a stream that is being
- * captured into a graph use two kernels and read x twice.  Either way the
- * results are bitwise the same.
+ * scheduling); wider rows and in-place calls use two kernels and read x
+ * twice.  Either way the results are bitwise the same.  The exchanged records
+ * carry a tag unique to the call; a call made while the stream is being
+ * captured into a graph reads its tag from a word in the 16 workspace bytes
+ * after the records (nt_plan_launch's workspace_bytes - 16), which a
+ * one-thread kernel captured ahead of it advances, so every replay of the
+ * graph tags its records afresh.
  */
 nt_status nt_softmax_rows(int64_t M, int64_t N, nt_dtype dt,
                           const void *x, void *y,
@@ -209,8 +214,9 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  * per row this is one pass: the row's workgroups exchange their sums as
  * tagged records, each keeping its chunk in registers, and a record that
  * does not arrive within a bounded wait is recomputed from x by the waiting
- * workgroup (so the result never depends on scheduling).  Beyond that, in
- * place (y == x) or while the stream captures a graph, two kernels: the
+ * workgroup (so the result never depends on scheduling; captured into a
+ * graph, the tag comes from the workspace as for the softmax).  Beyond that,
+ * or in place (y == x), two kernels: the
  * first writes the sums, the second combines them and writes the outputs,
  * reading x a second time.  Both forms combine a row's sums in the same
  * fixed order and give the same bits.  The statistics are those of the
@@ -221,7 +227,7 @@ nt_status nt_rmsnorm_rows(int64_t M, int64_t N, nt_dtype dt, float eps,
  * norms' sums.
  *
  * nt_norm_workspace_bytes(op, M, N, dt): bytes the split needs (32 per row
- * chunk, 8 per row) for op NT_OP_LAYERNORM or NT_OP_RMSNORM, 0 when the
+ * chunk, 8 per row, 16 for a captured call's tag) for op NT_OP_LAYERNORM or NT_OP_RMSNORM, 0 when the
  * plain plan is used (rows that fit one pass, or enough rows to fill the
  * GPU) or for invalid arguments.
  *
@@ -374,8 +380,8 @@ typedef struct {
                                  the workgroups of a row exchange their partial results
                                  through the workspace), 2 when it does so for two rows
                                  per workgroup (softmax; rows_per_block 2); 0: two
-                                 kernels, x read twice.  In-place calls (y == x) and calls
-                                 during stream capture always use the two kernels        */
+                                 kernels, x read twice.  In-place calls (y == x) always
+                                 use the two kernels                                     */
     int64_t grid;             /* workgroups per launch                                  */
     int64_t row_chunks;       /* split paths: chunks per row (0 otherwise)              */
     int64_t workspace_bytes;  /* split paths: workspace size (0 otherwise)              */

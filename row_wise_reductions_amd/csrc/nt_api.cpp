@@ -260,6 +260,27 @@ int coop_rows(int64_t M, int64_t P, nt_dtype dt) {
 // which tests use).
 int32_t coop_spin() { return (int32_t)tune(T_COOP_SPIN); }
 
+// Bytes after a split plan's records that hold the tag word of a cooperative
+// call captured into a graph (the workspace sizes include them).
+constexpr int64_t kTagBytes = 16;
+
+// One thread advances the tag word of a captured cooperative call; in the
+// graph it runs right before the cooperative launch, so every replay tags
+// its records with a value no earlier replay used (vector load and store).
+__global__ void __launch_bounds__(64) nt_tag_bump(uint32_t *p) {
+    if (threadIdx.x == 0) {
+        const uint32_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p, v + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+hipError_t bump_tag(const uint32_t *p, hipStream_t s) {
+    uint32_t *q = const_cast<uint32_t *>(p);
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(nt_tag_bump), dim3(1), dim3(64), args, 0, s);
+}
+
+
 // Compute units of each device, queried on the first call made on it.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
@@ -292,6 +313,22 @@ nt_status stream_capturing(void *stream, bool *capturing) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) return NT_ERR_HIP;
     *capturing = cs != hipStreamCaptureStatusNone;
+    return NT_OK;
+}
+
+// The record tag of a cooperative call: from the host, unique per call; or,
+// while the stream is being captured into a graph (whose replays repeat the
+// call's arguments), the device word after the records, which run() has a
+// one-thread kernel advance right before the cooperative launch.
+nt_status set_coop_tag(void *stream, char *ws, int64_t records_bytes, ntk::RowArgs &a) {
+    bool cap = false;
+    const nt_status st = stream_capturing(stream, &cap);
+    if (st != NT_OK) return st;
+    if (cap)
+        a.tagp = reinterpret_cast<const uint32_t *>(ws + records_bytes);
+    else
+        a.tag = next_tag();
+    a.spin = coop_spin();
     return NT_OK;
 }
 
@@ -551,7 +588,7 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
         // four tagged 64-bit words per chunk (the cooperative records; the
         // two kernels use half of that for their (s1, s2) pairs), then a
         // pivot per row
-        p->workspace_bytes = M * nP * 32 + M * 8;
+        p->workspace_bytes = M * nP * 32 + M * 8 + kTagBytes;
         return NT_OK;
     }
     if (op != NT_OP_SOFTMAX) {
@@ -581,8 +618,9 @@ nt_status make_plan(nt_op op, int64_t M, int64_t N, nt_dtype dt, bool aligned, n
     p->row_chunks = P;
     p->grid = M * P;
     // two 64-bit words per (row, chunk): the cooperative kernel's tagged
-    // record; the two-kernel form uses the first 8 bytes as its (m_j, l_j)
-    p->workspace_bytes = M * P * 16;
+    // record; the two-kernel form uses the first 8 bytes as its (m_j, l_j);
+    // then the tag word of a captured cooperative call
+    p->workspace_bytes = M * P * 16 + kTagBytes;
     p->cooperative = (P <= ntk::COOP_PMAX && coop_enabled()) ? 1 : 0;
     if (p->cooperative && coop_rows(M, P, dt) == 2) {
         p->cooperative = 2;
@@ -669,6 +707,14 @@ nt_status run(nt_op op, int64_t M, int64_t N, nt_dtype dt, const nt_plan &p, con
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // kernel op codes: the causal softmax is a kernel op of its own
     const int kop = (op == NT_OP_SOFTMAX && a.queries > 0) ? (int)ntk::OP_SOFTMAX_CAUSAL : (int)op;
+    // a captured cooperative call: advance its tag word on the device first
+    if (a.tagp && (p.split == 1 || p.split == 3) && p.cooperative) {
+        const hipError_t eb = bump_tag(a.tagp, s);
+        if (eb != hipSuccess) {
+            if (debug_on()) std::fprintf(stderr, "[nt] launch failed: %s\n", hipGetErrorString(eb));
+            return NT_ERR_HIP;
+        }
+    }
     hipError_t e = p.split == 1   ? launch_split(dt, p, a, s)
                    : p.split == 2 ? launch_looped(dt, kop, p, a, s)
                    : p.split == 3 ? launch_norm_split(dt, kop, p, a, s)
@@ -794,24 +840,19 @@ static nt_status softmax_launch(int64_t M, int64_t N, nt_dtype dt, const void *x
         if (!aligned_to(workspace, 8)) return NT_ERR_ALIGN;
         // The documented requirement (sized for misaligned rows) is enforced,
         // not the possibly smaller need of this particular call.
-        if (workspace_bytes < nt_softmax_workspace_bytes(M, N, dt)) return NT_ERR_WORKSPACE;
+        const size_t need = nt_softmax_workspace_bytes(M, N, dt);
+        if (workspace_bytes < need) return NT_ERR_WORKSPACE;
         if (workspace_apart(M, N, dt, x, y, workspace, workspace_bytes) != NT_OK) return NT_ERR_ALIAS;
         a.ws = static_cast<float2 *>(workspace);
         a.P = (int32_t)p.row_chunks;
         // in place, a chunk recomputed by another workgroup could already
         // hold outputs: the two-kernel form reads x completely first
         if (x == y) p.cooperative = 0;
-        // a captured graph would replay this call's tag, and a replay could
-        // take the previous replay's records for its own
         if (p.cooperative) {
-            bool cap = false;
-            const nt_status cst = stream_capturing(stream, &cap);
-            if (cst != NT_OK) return cst;
-            if (cap) p.cooperative = 0;
-        }
-        if (p.cooperative) {
-            a.tag = next_tag();
-            a.spin = coop_spin();
+            // the tag word: the 16 bytes after this plan's records
+            const nt_status tst =
+                set_coop_tag(stream, static_cast<char *>(workspace), p.workspace_bytes - kTagBytes, a);
+            if (tst != NT_OK) return tst;
         }
     }
     return run(NT_OP_SOFTMAX, M, N, dt, p, a, stream);
@@ -902,8 +943,7 @@ namespace {
 // Workspace of a split-norm plan, or an error status before anything is
 // launched; a NULL workspace selected the plain plan already.
 // The split norm's workspace checks, and the choice between its one-pass
-// (cooperative) and two-kernel forms: in place, or under graph capture,
-// the two kernels.
+// (cooperative) and two-kernel forms: in place, the two kernels.
 nt_status attach_workspace(nt_plan &p, void *ws, size_t wsb, int64_t M, int64_t N, nt_dtype dt, const void *x,
                            const void *y, void *stream, ntk::RowArgs &a) {
     if (p.split != 3) return NT_OK;
@@ -913,16 +953,8 @@ nt_status attach_workspace(nt_plan &p, void *ws, size_t wsb, int64_t M, int64_t 
     a.P = (int32_t)p.row_chunks;
     a.wsd = static_cast<double *>(ws);
     if (x == y) p.cooperative = 0;
-    if (p.cooperative) {
-        bool cap = false;
-        const nt_status st = stream_capturing(stream, &cap);
-        if (st != NT_OK) return st;
-        if (cap) p.cooperative = 0;
-    }
-    if (p.cooperative) {
-        a.tag = next_tag();
-        a.spin = coop_spin();
-    }
+    // the tag word: the 16 bytes after this plan's records
+    if (p.cooperative) return set_coop_tag(stream, static_cast<char *>(ws), p.workspace_bytes - kTagBytes, a);
     return NT_OK;
 }
 
@@ -1014,8 +1046,8 @@ size_t nt_norm_workspace_bytes(int op, int64_t M, int64_t N, nt_dtype dt) {
             int64_t P;
             bool c;
             if (split_norm_plan((nt_op)op, dt, M, row_chunks(N, dt, p.aligned != 0), coop, &s, &P, &c) &&
-                P <= (((int64_t)1 << 31) / (64 * s.W)) / M && (size_t)(M * P * 32 + M * 8) > need)
-                need = (size_t)(M * P * 32 + M * 8);
+                P <= (((int64_t)1 << 31) / (64 * s.W)) / M && (size_t)(M * P * 32 + M * 8 + kTagBytes) > need)
+                need = (size_t)(M * P * 32 + M * 8 + kTagBytes);
         }
     }
     return need;

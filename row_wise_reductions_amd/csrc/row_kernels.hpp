@@ -81,12 +81,23 @@ struct RowArgs {
     int32_t P;           // split softmax: chunks per row
     float eps;
     float inv_n;         // 1/N in fp32
-    uint32_t tag;        // cooperative split softmax: this call's record tag
+    uint32_t tag;        // cooperative split kernels: this call's record tag
     int32_t spin;        // cooperative split softmax: polls before recomputing
     int64_t queries;     // causal softmax: row r is query r mod queries (0: not causal)
     int64_t offset;      // causal softmax: query q sees keys k <= q + offset
     float s2;            // causal softmax: scale * log2(e), rounded to fp32
+    const uint32_t *tagp; // cooperative split kernels: when set, the record tag is read
+                          // from this device word (calls captured into a graph)
 };
+
+// The record tag of a cooperative split launch: the host's per-call value,
+// or, for a call captured into a graph, the device word that a one-thread
+// kernel ahead of it in the stream increments, so that each replay tags its
+// records afresh.  Every workgroup reads the same value.
+__device__ __forceinline__ uint32_t call_tag(const struct RowArgs &a) {
+    if (a.tagp) return __hip_atomic_load(a.tagp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return a.tag;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -1680,7 +1691,8 @@ softmax_coop(RowArgs a) {
     const float2 mine = chunk_stats<DT, W, K>(raw, red, wv, lane, s2);
 
     uint64_t *rec = reinterpret_cast<uint64_t *>(a.ws) + row * P * 2;
-    const uint64_t tg = (uint64_t)a.tag << 32;
+    const uint32_t tag = call_tag(a);
+    const uint64_t tg = (uint64_t)tag << 32;
     if (t == 0) {
         __hip_atomic_store(rec + 2 * j, tg | __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(rec + 2 * j + 1, tg | __float_as_uint(mine.y), __ATOMIC_RELAXED,
@@ -1703,7 +1715,7 @@ softmax_coop(RowArgs a) {
                     const uint64_t w0 = __hip_atomic_load(rec + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     const uint64_t w1 =
                         __hip_atomic_load(rec + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if ((w0 >> 32) == a.tag && (w1 >> 32) == a.tag) {
+                    if ((w0 >> 32) == tag && (w1 >> 32) == tag) {
                         qs[p] = make_float2(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1));
                         pending &= ~(1u << b);
                     }
@@ -1761,7 +1773,8 @@ softmax_coop2(RowArgs a) {
     const int64_t rowbytes = (int64_t)N * I::E;
     const int64_t cbase = (int64_t)j * (TPR * K);
     const float s2 = CAUSAL ? a.s2 : LOG2E;
-    const uint64_t tg = (uint64_t)a.tag << 32;
+    const uint32_t tag = call_tag(a);
+    const uint64_t tg = (uint64_t)tag << 32;
     const bool two = g + G < a.M;                  // uniform: a second row exists
     __shared__ float red[2][W];
     __shared__ float2 qs[COOP_PMAX];
@@ -1816,7 +1829,7 @@ softmax_coop2(RowArgs a) {
                         const uint64_t w0 = __hip_atomic_load(rec + 2 * p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         const uint64_t w1 =
                             __hip_atomic_load(rec + 2 * p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((w0 >> 32) == a.tag && (w1 >> 32) == a.tag) {
+                        if ((w0 >> 32) == tag && (w1 >> 32) == tag) {
                             qs[p] = make_float2(__uint_as_float((uint32_t)w0), __uint_as_float((uint32_t)w1));
                             pending &= ~(1u << b);
                         }
@@ -1899,7 +1912,8 @@ norm_coop(RowArgs a) {
     const double2 mine = norm_chunk_sums<OP, DT, W, K>(raw, pv, red[0], wv, lane);
 
     uint64_t *rec = reinterpret_cast<uint64_t *>(a.wsd) + row * P * NW;
-    const uint64_t tg = (uint64_t)a.tag << 32;
+    const uint32_t tag = call_tag(a);
+    const uint64_t tg = (uint64_t)tag << 32;
     if (t == 0) {
         const uint64_t b1 = (uint64_t)__double_as_longlong(mine.x), b2 = (uint64_t)__double_as_longlong(mine.y);
         uint64_t *r = rec + (int64_t)NW * j;
@@ -1929,7 +1943,7 @@ norm_coop(RowArgs a) {
 #pragma unroll
                     for (int q = 0; q < NW; ++q) {
                         w[q] = __hip_atomic_load(r + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        ok = ok && (w[q] >> 32) == a.tag;
+                        ok = ok && (w[q] >> 32) == tag;
                     }
                     if (ok) {
                         const double s2 = __longlong_as_double((long long)((w[0] & 0xffffffffu) | (w[1] << 32)));

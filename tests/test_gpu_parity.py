@@ -467,9 +467,11 @@ def test_bitwise_repeatable(N):
 def test_graph_capture_and_replay():
     """Calls captured into a HIP graph (torch.cuda.graph) and replayed with
     new inputs copied in (eagerly) between replays: every replay matches the
-    oracle.  Under capture the split softmax takes its two-kernel form (a
-    replayed call reuses its record tag, so the cooperative kernel is not
-    captured)."""
+    oracle and is bitwise the eager result on the same input.  The
+    cooperative split softmax is captured with its record tag read from the
+    word after the records, advanced on the device before each replay's
+    launch (one advance per replay), so no replay takes an earlier one's
+    records."""
     M, N = 8, 262144
     xs = [rand_bits(40 + i, M, N, "f32", scale=2.0 + i) for i in range(3)]
     rs = [rand_bits(50 + i, 16, 8192, "bf16") for i in range(3)]
@@ -480,12 +482,22 @@ def test_graph_capture_and_replay():
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     assert nt.nt_plan_launch(0, M, N, nt.NT_F32, True)["cooperative"] == 1
     assert nt.nt_plan_launch(2, 16, 8192, nt.NT_BF16, True)["persistent"] == 1
+    # and the two-rows-per-workgroup form on 64 vocabulary-wide rows
+    M2 = 64
+    x2s = [rand_bits(45 + i, M2, N, "f32", scale=1.5 + i) for i in range(3)]
+    x2_t = to_dev(x2s[0], "f32")
+    y2_t = torch.empty_like(x2_t)
+    wsb2 = nt.nt_softmax_workspace_bytes(M2, N, nt.NT_F32)
+    ws2 = torch.empty(wsb2, dtype=torch.uint8, device="cuda")
+    assert nt.nt_plan_launch(0, M2, N, nt.NT_F32, True)["cooperative"] == 2
 
     def calls(stream):
         assert nt.nt_softmax_rows(M, N, nt.NT_F32, x_t.data_ptr(), y_t.data_ptr(), ws.data_ptr(), wsb,
                                   stream) == 0
         assert nt.nt_rmsnorm_rows(16, 8192, nt.NT_BF16, 1e-6, r_t.data_ptr(), w_t.data_ptr(),
                                   ry_t.data_ptr(), stream) == 0
+        assert nt.nt_softmax_rows(M2, N, nt.NT_F32, x2_t.data_ptr(), y2_t.data_ptr(), ws2.data_ptr(), wsb2,
+                                  stream) == 0
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -493,17 +505,32 @@ def test_graph_capture_and_replay():
         calls(side.cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    eager = to_host_bits(y_t, "f32")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         calls(torch.cuda.current_stream().cuda_stream)
-    for i in (1, 0, 2, 2, 1):
+    # the tag word: in the 16 bytes after the plan's records
+    pw = nt.nt_plan_launch(0, M, N, nt.NT_F32, True)["workspace_bytes"]
+    pw2 = nt.nt_plan_launch(0, M2, N, nt.NT_F32, True)["workspace_bytes"]
+    tag_word = ws[pw - 16:pw - 12].view(torch.int32)
+    tag_word2 = ws2[pw2 - 16:pw2 - 12].view(torch.int32)
+    torch.cuda.synchronize()
+    tag0, tag0_2 = int(tag_word.item()), int(tag_word2.item())
+    for n, i in enumerate((1, 0, 2, 2, 1)):
         say(f"case graph replay inputs {i}")
         x_t.copy_(to_dev(xs[i], "f32"))
         r_t.copy_(to_dev(rs[i], "bf16"))
+        x2_t.copy_(to_dev(x2s[i], "f32"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        assert (int(tag_word.item()) - tag0) & 0xFFFFFFFF == n + 1, "one tag advance per replay"
+        assert (int(tag_word2.item()) - tag0_2) & 0xFFFFFFFF == n + 1, "one tag advance per replay"
+        check_output(to_host_bits(y2_t, "f32"), oracle_for("softmax", x2s[i], "f32")[0], "f32",
+                     f"graph two-row softmax {i}")
         check_output(to_host_bits(y_t, "f32"), oracle_for("softmax", xs[i], "f32")[0], "f32", f"graph softmax {i}")
+        if i == 0:
+            assert np.array_equal(to_host_bits(y_t, "f32"), eager)
         check_output(to_host_bits(ry_t, "bf16"), oracle_for("rmsnorm", rs[i], "bf16", 1e-6, w)[0], "bf16",
                      f"graph rmsnorm {i}")
 

@@ -273,9 +273,10 @@ def test_cooperative_split_norm_on_concurrent_streams():
 def test_split_norm_graph_capture_and_replay():
     """Split norms captured into a HIP graph and replayed with new inputs
     copied in (eagerly) between replays: every replay matches the oracle.
-    Under capture the one-pass form is not used (a replay would reuse the
-    call's record tag): the shape that runs in one pass eagerly is captured
-    as two kernels."""
+    The one-pass (cooperative) form is captured with its record tag read
+    from the word after the records, which a one-thread kernel advances
+    before each replay's launch: the word moves by one per replay, and a
+    replay on the eager call's inputs gives the eager bits."""
     M, N = 128, 262144
     xs = [rand_bits(70 + i, M, N, "bf16", scale=2.0 + i, loc=0.5) for i in range(3)]
     w = rand_bits(73, 1, N, "bf16", scale=0.3, loc=1.0)[0]
@@ -310,7 +311,12 @@ def test_split_norm_graph_capture_and_replay():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         calls(torch.cuda.current_stream().cuda_stream)
-    for i in (1, 0, 2, 2, 1):
+    # the tag word: in the 16 bytes after the plan's records
+    pw = nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, M, N, nt.NT_BF16, True)["workspace_bytes"]
+    tag_word = ws[pw - 16:pw - 12].view(torch.int32)
+    torch.cuda.synchronize()
+    tag0 = int(tag_word.item())
+    for n, i in enumerate((1, 0, 2, 2, 1)):
         say(f"case split-norm graph replay inputs {i}")
         x_t.copy_(to_dev(xs[i], "bf16"))
         lx_t.copy_(to_dev(lx[i], "f32"))
@@ -319,8 +325,8 @@ def test_split_norm_graph_capture_and_replay():
         torch.cuda.synchronize()
         check("rmsnorm", y_t, None, None, xs[i], "bf16", w, None, f"graph split rmsnorm {i}")
         check("layernorm", ly_t, mean, rstd, lx[i], "f32", g_, b_, f"graph split layernorm {i}")
+        assert (int(tag_word.item()) - tag0) & 0xFFFFFFFF == n + 1, "one tag advance per replay"
         if i == 0:
-            # the captured two kernels on the eager call's chunks: the eager one-pass bits
             assert np.array_equal(to_host_bits(y_t, "bf16"), eager)
 
 

@@ -164,8 +164,9 @@ def test_workspace_bytes():
     assert nt.nt_softmax_workspace_bytes(1024, 781, F32) == 0          # single pass
     assert nt.nt_softmax_workspace_bytes(131072, 4096, BF16) == 0
     # 1 MiB fp32 rows: 16 chunks of 64 KiB (+1 for a misaligned head) per
-    # row, a 16-byte record (two tagged 64-bit words) per chunk
-    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 17 * 16
+    # row, a 16-byte record (two tagged 64-bit words) per chunk, then 16
+    # bytes for the tag word of a call captured into a graph
+    assert nt.nt_softmax_workspace_bytes(64, 262144, F32) == 64 * 17 * 16 + 16
     assert nt.nt_softmax_workspace_bytes(-1, 8, F32) == 0
     assert nt.nt_softmax_workspace_bytes(4, 8, 9) == 0
 
@@ -184,7 +185,7 @@ def test_plans_of_the_workloads():
     # 1024 (row, chunk) pairs of fp32: two rows per cooperative workgroup
     assert p["split"] == 1 and p["row_chunks"] == 16 and p["grid"] == 32 * 16 and p["rows_per_block"] == 2
     assert (p["waves_per_row"], p["chunks_per_lane"]) == (8, 8)
-    assert p["workspace_bytes"] == 64 * 16 * 16 and p["cooperative"] == 2
+    assert p["workspace_bytes"] == 64 * 16 * 16 + 16 and p["cooperative"] == 2
 
 
 def test_narrow_row_rule():
@@ -456,9 +457,9 @@ def test_norm_workspace_bytes():
     assert nt.nt_norm_workspace_bytes(LN, 4096, 1 << 20, BF16) == 0
     # 64 fp32 rows of 1 MiB: 32 KiB chunks (8 waves x 4 chunks) -> 32 per row,
     # 33 for a misaligned head; 32 bytes per chunk (four tagged words) and 8 per row
-    assert nt.nt_norm_workspace_bytes(LN, 64, 262144, F32) == 64 * 33 * 32 + 64 * 8
+    assert nt.nt_norm_workspace_bytes(LN, 64, 262144, F32) == 64 * 33 * 32 + 64 * 8 + 16
     # 16 bf16 rows of 2 MiB: 8 KiB chunks fill the grid -> 256 per row (+1)
-    assert nt.nt_norm_workspace_bytes(RMS, 16, 1 << 20, BF16) == 16 * 257 * 32 + 16 * 8
+    assert nt.nt_norm_workspace_bytes(RMS, 16, 1 << 20, BF16) == 16 * 257 * 32 + 16 * 8 + 16
     # other ops and invalid arguments
     for bad in ((nt.NT_OP_SOFTMAX, 4, 1 << 20, F32), (LN, -1, 1 << 20, F32), (LN, 4, 0, F32), (RMS, 4, 1 << 20, 5)):
         assert nt.nt_norm_workspace_bytes(*bad) == 0
@@ -510,7 +511,7 @@ def test_split_norm_plans():
                         (op, dt, M, N, al, p)
                     per = 64 * p["waves_per_row"] * p["chunks_per_lane"]
                     assert p["row_chunks"] == -(-nch // per) and p["grid"] == M * p["row_chunks"]
-                    assert p["workspace_bytes"] == M * p["row_chunks"] * 32 + M * 8
+                    assert p["workspace_bytes"] == M * p["row_chunks"] * 32 + M * 8 + 16
                     assert p["workspace_bytes"] <= nt.nt_norm_workspace_bytes(base, M, N, dt)
         # many rows of many chunks: looped
         assert nt.nt_plan_launch(op, 4096, 1 << 20, BF16, True)["split"] == 2
@@ -546,7 +547,7 @@ def test_split_norm_cooperative_switch(ntenv):
     # the documented size covers both forms and both alignments (9 chunks
     # of 32 KiB with a misaligned head)
     need = nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32)
-    assert need == 256 * 9 * 32 + 256 * 8
+    assert need == 256 * 9 * 32 + 256 * 8 + 16
     ntenv.delenv("NT_COOP")
     assert nt.nt_norm_workspace_bytes(nt.NT_OP_RMSNORM, 256, 65536, F32) == need
     assert nt.nt_plan_launch(nt.NT_OP_RMSNORM_WS, 256, 65536, F32, True)["row_chunks"] == 8
