@@ -4,7 +4,8 @@ library): through the C ABI, its output equals nt_softmax_rows' bit for bit
 and meets the oracle's bar, on consecutive calls of shrinking size (the
 array keeps the previous call's contents), on both split forms and on rows
 that need no scratch; shapes needing more than the array are refused before
-anything is enqueued."""
+anything is enqueued; captured into a graph, every replay tags its records
+afresh."""
 from __future__ import annotations
 
 import sys
@@ -107,3 +108,37 @@ def test_noalloc_refuses_more_than_the_array():
     assert rc == 6, nt.nt_status_string(rc)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(buf)) == 0
+
+
+def test_noalloc_under_graph_capture():
+    """The entry point captured into a graph (the callers it is for) and
+    replayed with new inputs copied in between replays: the cooperative split
+    runs from the array with its tag advanced per replay, and every replay is
+    bitwise nt_softmax_rows' result on the same input and meets the oracle."""
+    M, N, dt = 64, 262144, "f32"
+    assert nt.nt_plan_launch(nt.NT_OP_SOFTMAX, M, N, DT_CODE[dt], True)["cooperative"] == 2
+    xs = [rows(300 + i, M, N, dt, scale=1.0 + i) for i in range(3)]
+    x_t = to_dev(xs[0], dt)
+    y_t = empty_like_dev((M, N), dt)
+    s = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        assert nt.nt_softmax_rows_noalloc(M, N, DT_CODE[dt], x_t.data_ptr(), y_t.data_ptr(), side.cuda_stream) == 0
+    s.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc = nt.nt_softmax_rows_noalloc(M, N, DT_CODE[dt], x_t.data_ptr(), y_t.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, nt.nt_status_string(rc)
+    for i in (1, 2, 0, 1):
+        say(f"case noalloc graph replay inputs {i}")
+        x_t.copy_(to_dev(xs[i], dt))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host_bits(y_t, dt)
+        ref = to_host_bits(with_workspace(to_dev(xs[i], dt), dt), dt)
+        assert np.array_equal(got, ref), f"replay {i} differs from nt_softmax_rows"
+        check_output(got, oracle.softmax(xs[i], dt), dt, f"noalloc graph replay {i}")
